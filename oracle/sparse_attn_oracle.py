@@ -1,0 +1,376 @@
+"""CPU oracle for dynamic page/block-sparse attention over a paged KV cache.
+
+TEST INFRASTRUCTURE.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import or call this module.  The
+library's product path never does, and shares no code with it.
+
+Plain, slow and direct: numpy float64 throughout (inputs arrive as exact
+upcasts of the bf16/fp32 bits), explicit loops over sequences, heads and
+pages, library primitives (sum, matmul, a stable sort) as steps, no blocking,
+fusion or reordering.  The quantities that decide an integer outcome (the page
+scores that top-k ranks) are rounded to fp32 exactly as the library hands them
+between its calls; both sides accumulate in float64 before that rounding.
+
+Sources (pages as titled on the web; sections named):
+  [UAE]   "Universal Attention Engine - Declarative Sparse Attention for
+          Production": section "The Product" (sink_tokens, local_window,
+          cache_budget), "Content-Dependent Dynamic Routing (Novel)" (router
+          top_k_blocks(q @ mean(k_blocks), k); selected blocks get full
+          fine-grained attention; only selected blocks are loaded),
+          "Milestones / Phase 1" (sink+local+sparse pattern),
+          "Architecture / Layer 3" (PagedAttention-compatible layout).
+  [TS]    "TileSparse: Arithmetic-Intensity-Aware Sparse Attention for
+          Compute-Bound LLM Decoding" (README): "Motivation" (QK 2D sparsity,
+          Tiered QK 2D sparsity: Critical tier of alpha pages with all query
+          heads, Ambient tier of beta pages with h heads), "Two
+          implementations, by design" (mask-based path == per-head page-list
+          Flash-decode), "Configuration" (critical_top_count, ambient_head_count,
+          key_top_count), TILESPARSE_MODE=streaming (sinks + window only).
+  [STS]   STS abstract (page titled "Vortex: Efficient and Programmable Sparse
+          Attention Serving for AI Agents"): draft-model scores build a
+          token-and-head-wise sparsity mask.
+  [CA]    CompactAttention abstract (page titled "Causal Attention on CPU: A
+          Cache-Aware and Load-Balanced Scheduling Kernel for Prefill"): 2D
+          block masks become GQA-aware per-group KV block tables by Q-block
+          union then intra-group union; tables keep every selected block and KV
+          is read in place from the paged cache under chunked prefill.
+
+Readings where the pages are silent (each is listed with its reason in the
+design notes): the router score is the unscaled dot product of the query summed
+over the selection head's query heads and query tokens with the page's mean key
+over its valid tokens; sink/window/top-k are counted in pages, forced pages are
+not top-k candidates, ranking is (score descending, logical index ascending)
+with NaN last; lists are ascending logical ids (tiered: Critical segment then
+Ambient segment); each query row softmaxes over exactly its own token set;
+an empty token set gives output 0 and lse -inf; the prefill union is taken over
+all Q-blocks of the chunk and every query of a group attends causally to the
+whole group table.
+
+Pins (tests/test_oracle_pins.py): brute force in pure Python on tiny inputs,
+torch's scaled_dot_product_attention (float64, CPU) for select-all and
+all-ones-mask cases, closed forms (constant V, single token, constant pages),
+invariants (pool permutation, linearity of the score, union contains the
+mask, split/merge), hand-derived golden lists under tests/golden/.
+"""
+from __future__ import annotations
+
+import math
+from typing import Iterable, List, Optional, Sequence, Tuple
+
+import numpy as np
+
+PER_KV_HEAD = "per_kv_head"
+PER_Q_HEAD = "per_q_head"
+
+
+def n_pages_of(seq_len: int, page_size: int) -> int:
+    return (int(seq_len) + page_size - 1) // page_size
+
+
+def valid_tokens(seq_len: int, logical_page: int, page_size: int) -> int:
+    """Tokens of logical page ``logical_page`` that lie below ``seq_len``."""
+    return max(0, min(page_size, int(seq_len) - logical_page * page_size))
+
+
+# --------------------------------------------------------------------- a0
+def page_summary(k_pool: np.ndarray, block_table: np.ndarray, seq_lens: np.ndarray,
+                 page_size: int, last_pages: int = 0) -> np.ndarray:
+    """Mean key of each referenced physical page, per KV head  [UAE routing: mean(k_blocks)].
+
+    mu[p, g, :] = (sum over the page's valid tokens j of K[p, g, j, :]) / n_valid,
+    accumulated in float64 and rounded to fp32.  ``last_pages`` > 0 restricts the
+    update to the last ``last_pages`` logical pages of each sequence.  Entries
+    of pages not updated are NaN.
+    """
+    n_phys, n_kv, P, d = k_pool.shape
+    mu = np.full((n_phys, n_kv, d), np.nan, dtype=np.float32)
+    for b in range(block_table.shape[0]):
+        n = n_pages_of(seq_lens[b], P)
+        first = 0 if last_pages <= 0 else max(0, n - last_pages)
+        for lp in range(first, n):
+            nv = valid_tokens(seq_lens[b], lp, P)
+            phys = int(block_table[b, lp])
+            rows = np.asarray(k_pool[phys, :, :nv, :], dtype=np.float64)   # [n_kv][nv][d]
+            mu[phys] = (rows.sum(axis=1) / nv).astype(np.float32)
+    return mu
+
+
+# --------------------------------------------------------------------- a1
+def selection_heads(s: int, mode: str, group: int) -> Tuple[List[int], int]:
+    """Query heads pooled by selection head ``s`` and the KV head it reads."""
+    if mode == PER_KV_HEAD:
+        return list(range(s * group, (s + 1) * group)), s
+    return [s], s // group
+
+
+def page_scores(q: np.ndarray, mu: np.ndarray, block_table: np.ndarray, seq_lens: np.ndarray,
+                page_size: int, n_kv_heads: int, mode: str) -> np.ndarray:
+    """Router score of every page  [UAE routing: q @ mean(k_blocks); STS/TS per-head selection].
+
+    s[b, sel, p] = fp32( sum_d Qbar[d] * mu[phys(b, p), g(sel), d] ),
+    Qbar = sum over query tokens t and the selection head's query heads h of
+    q[b, t, h, :] (float64).  Pages past the sequence's end get NaN.
+    """
+    B, T, Hq, d = q.shape
+    G = Hq // n_kv_heads
+    n_sel = n_kv_heads if mode == PER_KV_HEAD else Hq
+    max_pages = block_table.shape[1]
+    out = np.full((B, n_sel, max_pages), np.nan, dtype=np.float32)
+    for b in range(B):
+        n = n_pages_of(seq_lens[b], page_size)
+        for s in range(n_sel):
+            heads, g = selection_heads(s, mode, G)
+            qbar = np.zeros(d, dtype=np.float64)
+            for t in range(T):
+                for h in heads:
+                    qbar += q[b, t, h].astype(np.float64)
+            for lp in range(n):
+                m = mu[int(block_table[b, lp]), g].astype(np.float64)
+                out[b, s, lp] = np.float32(np.dot(qbar, m))
+    return out
+
+
+# --------------------------------------------------------------------- a2
+def forced_pages(n: int, sink_pages: int, window_pages: int) -> List[int]:
+    """Sink pages [0, sink) and window pages [n - window, n), clipped  [UAE: sink_tokens, local_window]."""
+    f = set(range(0, min(sink_pages, n))) | set(range(max(0, n - window_pages), n))
+    return sorted(f)
+
+
+def rank_candidates(scores_row: np.ndarray, candidates: Sequence[int]) -> List[int]:
+    """Candidates ordered by (score descending, logical index ascending), NaN last."""
+    cand = np.asarray(candidates, dtype=np.int64)
+    if cand.size == 0:
+        return []
+    sc = scores_row[cand].astype(np.float64)
+    nan = np.isnan(sc)
+    neg = np.where(nan, np.inf, -sc)          # -0.0 and +0.0 compare equal
+    order = np.lexsort((cand, neg, nan))      # primary: NaN flag, then -score, then index
+    return [int(x) for x in cand[order]]
+
+
+def select_pages(scores: np.ndarray, n_pages: Sequence[int], sink_pages: int, window_pages: int,
+                 top_k: int, critical_k: Optional[int] = None):
+    """Per-selection-head page lists  [UAE sink+local+sparse; TS tiers; STS top-k masks].
+
+    F = forced pages; C = the other pages; the first min(top_k, |C|) of C in
+    rank order are selected.  Untiered: list = ascending(F u selected).
+    Tiered: Critical = ascending(F u first critical_k selected), Ambient =
+    ascending(remaining selected); list = Critical then Ambient.
+    Returns (lists [B][S][stride] int32 padded with -1, counts [B][S],
+    critical counts [B][S] or None).
+    """
+    B, S, max_pages = scores.shape
+    stride = max_pages
+    lists = np.full((B, S, stride), -1, dtype=np.int32)
+    counts = np.zeros((B, S), dtype=np.int32)
+    ccounts = np.zeros((B, S), dtype=np.int32) if critical_k is not None else None
+    for b in range(B):
+        n = int(n_pages[b])
+        forced = forced_pages(n, sink_pages, window_pages)
+        fset = set(forced)
+        cand = [i for i in range(n) if i not in fset]
+        for s in range(S):
+            order = rank_candidates(scores[b, s], cand)
+            k_eff = min(max(top_k, 0), len(order))
+            chosen = order[:k_eff]
+            if critical_k is None:
+                lst = sorted(fset | set(chosen))
+            else:
+                ck = min(max(critical_k, 0), k_eff)
+                crit = sorted(fset | set(chosen[:ck]))
+                amb = sorted(chosen[ck:])
+                lst = crit + amb
+                ccounts[b, s] = len(crit)
+            counts[b, s] = len(lst)
+            lists[b, s, :len(lst)] = lst
+    return lists, counts, ccounts
+
+
+# ----------------------------------------------------------------- a3-a5
+def head_bit(mask_words: np.ndarray, h: int) -> bool:
+    return bool((int(mask_words[h // 32]) >> (h % 32)) & 1)
+
+
+def row_pages(b: int, s: int, h: int, page_lists, page_counts, critical_counts, ambient_mask) -> List[int]:
+    """Logical pages query head h of selection head s attends  [TS Tiered QK 2D sparsity].
+
+    Untiered: the whole list.  Tiered: the Critical segment plus each Ambient
+    page whose head mask has bit h.
+    """
+    cnt = int(page_counts[b, s])
+    pages = [int(x) for x in page_lists[b, s, :cnt]]
+    if critical_counts is None:
+        return pages
+    cc = int(critical_counts[b, s])
+    amb = [p for p in pages[cc:] if head_bit(ambient_mask[b, p], h)]
+    return pages[:cc] + amb
+
+
+def gather_tokens(k_pool, v_pool, block_table, b, g, pages, seq_len, page_size, d_v):
+    """Keys/values of the given logical pages (valid tokens only), in ascending token order.
+
+    K pool is [phys][g][token][d]; V pool is page-transposed [phys][g][d_v][token];
+    with no V pool, V is the first d_v dims of the K row (MLA latent).
+    """
+    ks, vs = [], []
+    for lp in sorted(pages):
+        nv = valid_tokens(seq_len, lp, page_size)
+        if nv == 0:
+            continue
+        phys = int(block_table[b, lp])
+        k = np.asarray(k_pool[phys, g, :nv, :], dtype=np.float64)
+        if v_pool is None:
+            v = k[:, :d_v]
+        else:
+            v = np.asarray(v_pool[phys, g, :, :nv], dtype=np.float64).T
+        ks.append(k)
+        vs.append(v)
+    if not ks:
+        return None, None
+    return np.concatenate(ks, axis=0), np.concatenate(vs, axis=0)
+
+
+def softmax_attend(qrow: np.ndarray, K: Optional[np.ndarray], V: Optional[np.ndarray], sm_scale: float,
+                   d_v: int):
+    """Softmax attention of one query over exactly the given tokens  [UAE: selected blocks get full attention].
+
+    z_j = sm_scale * q . K_j; o = sum_j softmax(z)_j V_j; lse = log sum_j exp(z_j).
+    Empty token set: o = 0, lse = -inf.
+    """
+    if K is None or K.shape[0] == 0:
+        return np.zeros(d_v, dtype=np.float64), -np.inf
+    z = sm_scale * (K @ qrow.astype(np.float64))
+    m = z.max()
+    e = np.exp(z - m)
+    l = e.sum()
+    return (e @ V) / l, m + math.log(l)
+
+
+def sparse_decode(q, k_pool, v_pool, block_table, seq_lens, page_size, page_lists, page_counts,
+                  n_kv_heads, mode, sm_scale, critical_counts=None, ambient_mask=None, d_v=None,
+                  rows: Optional[Iterable[Tuple[int, int, int]]] = None):
+    """Decode attention of every query row over its selected pages  [TS page-list Flash-decode; UAE gather decode].
+
+    Returns (out [B][T][Hq][d_v] float64, lse [B][T][Hq] float64).  With
+    ``rows`` only those (b, t, h) entries are computed (others stay 0 / NaN).
+    """
+    B, T, Hq, _ = q.shape
+    G = Hq // n_kv_heads
+    P = page_size
+    if d_v is None:
+        d_v = v_pool.shape[2]
+    out = np.zeros((B, T, Hq, d_v), dtype=np.float64)
+    lse = np.full((B, T, Hq), np.nan, dtype=np.float64)
+    if rows is None:
+        rows = [(b, t, h) for b in range(B) for t in range(T) for h in range(Hq)]
+    for (b, t, h) in rows:
+        s = h // G if mode == PER_KV_HEAD else h
+        g = h // G
+        pages = row_pages(b, s, h, page_lists, page_counts, critical_counts, ambient_mask)
+        K, V = gather_tokens(k_pool, v_pool, block_table, b, g, pages, seq_lens[b], P, d_v)
+        out[b, t, h], lse[b, t, h] = softmax_attend(q[b, t, h], K, V, sm_scale, d_v)
+    return out, lse
+
+
+def split_ranges(count: int, num_splits: int) -> List[Tuple[int, int]]:
+    """Contiguous chunks of a list of ``count`` entries whose sizes differ by at most one."""
+    base, extra = divmod(count, num_splits)
+    out, start = [], 0
+    for i in range(num_splits):
+        n = base + (1 if i < extra else 0)
+        out.append((start, start + n))
+        start += n
+    return out
+
+
+def lse_merge(o_parts: np.ndarray, lse_parts: np.ndarray):
+    """Combine per-split partial outputs: o = sum_s w_s o_s / sum_s w_s, w_s = exp(lse_s - max).
+
+    o_parts [S][d_v] (each normalised over its own tokens), lse_parts [S].
+    All-empty gives o = 0, lse = -inf.
+    """
+    M = np.max(lse_parts)
+    if not np.isfinite(M):
+        return np.zeros(o_parts.shape[1]), -np.inf
+    w = np.exp(lse_parts - M)
+    L = w.sum()
+    return (w[:, None] * o_parts).sum(axis=0) / L, M + math.log(L)
+
+
+# ------------------------------------------------------------------- a6-a7
+def gqa_union_block_table(block_mask: np.ndarray, n_kv_heads: int):
+    """GQA-aware per-group KV block tables  [CA: Q-block union then intra-group union].
+
+    U[h, kb] = OR over Q-blocks of mask[h, qb, kb]; T[g, kb] = OR over the
+    group's heads of U[h, kb]; table_g = ascending {kb : T[g, kb]}.
+    Returns (tables [n_kv_heads][n_kv_blocks] int32 padded with -1, counts).
+    """
+    Hq, nqb, nkb = block_mask.shape
+    G = Hq // n_kv_heads
+    tables = np.full((n_kv_heads, nkb), -1, dtype=np.int32)
+    counts = np.zeros(n_kv_heads, dtype=np.int32)
+    for g in range(n_kv_heads):
+        union = np.zeros(nkb, dtype=bool)
+        for h in range(g * G, (g + 1) * G):
+            for qb in range(nqb):
+                union |= block_mask[h, qb] != 0
+        ids = np.flatnonzero(union)
+        tables[g, :ids.size] = ids
+        counts[g] = ids.size
+    return tables, counts
+
+
+def block_sparse_prefill(q, k_pool, v_pool, block_table_row, seq_len, page_size, q_start,
+                         tables, counts, n_kv_heads, sm_scale,
+                         rows: Optional[Iterable[Tuple[int, int]]] = None):
+    """Chunked-prefill attention in place over the group block tables  [CA].
+
+    Query i sits at position q_start + i; head h attends the tokens j of the
+    blocks in table_{g(h)} with j <= q_start + i and j < seq_len.
+    q [q_len][Hq][d]; returns (out [q_len][Hq][d] float64, lse [q_len][Hq]).
+    ``rows`` restricts to the given (i, h) pairs.
+    """
+    q_len, Hq, d = q.shape
+    G = Hq // n_kv_heads
+    P = page_size
+    out = np.zeros((q_len, Hq, d), dtype=np.float64)
+    lse = np.full((q_len, Hq), np.nan, dtype=np.float64)
+    if rows is None:
+        rows = [(i, h) for i in range(q_len) for h in range(Hq)]
+    by_group = {}
+    for (i, h) in rows:
+        by_group.setdefault(h // G, []).append((i, h))
+    for g, grp_rows in by_group.items():
+        pos, ks, vs = [], [], []
+        for kb in [int(x) for x in tables[g, :int(counts[g])]]:
+            nv = valid_tokens(seq_len, kb, P)
+            if nv == 0:
+                continue
+            phys = int(block_table_row[kb])
+            ks.append(np.asarray(k_pool[phys, g, :nv, :], dtype=np.float64))
+            vs.append(np.asarray(v_pool[phys, g, :, :nv], dtype=np.float64).T)
+            pos.append(kb * P + np.arange(nv))
+        if not ks:
+            for (i, h) in grp_rows:
+                out[i, h], lse[i, h] = np.zeros(d), -np.inf
+            continue
+        K, V, J = np.concatenate(ks), np.concatenate(vs), np.concatenate(pos)
+        heads = sorted({h for (_, h) in grp_rows})
+        for h in heads:
+            qi = np.array([i for (i, hh) in grp_rows if hh == h], dtype=np.int64)
+            Qh = np.asarray(q[qi, h, :], dtype=np.float64)              # [rows][d]
+            Z = sm_scale * (Qh @ K.T)                                   # [rows][tokens]
+            visible = J[None, :] <= (q_start + qi)[:, None]             # causal: j <= position
+            Z = np.where(visible, Z, -np.inf)
+            m = Z.max(axis=1)
+            empty = ~np.isfinite(m)
+            m_safe = np.where(empty, 0.0, m)
+            E = np.exp(Z - m_safe[:, None])                             # exp(-inf) = 0
+            L = E.sum(axis=1)
+            L_safe = np.where(empty, 1.0, L)
+            O = (E @ V) / L_safe[:, None]
+            out[qi, h] = np.where(empty[:, None], 0.0, O)
+            with np.errstate(divide="ignore"):
+                lse[qi, h] = np.where(empty, -np.inf, m_safe + np.log(L_safe))
+    return out, lse

@@ -1,0 +1,522 @@
+"""Checks that pin the CPU oracle to things other than itself.
+
+Each ``check_*`` raises AssertionError on failure.  They are run as tests in
+test_oracle_pins.py and, with mistakes planted into the oracle, in
+test_oracle_mutations.py (each planted mistake must trip at least one check).
+
+Independent references used here:
+  * pure-Python brute force (``sorted`` with an explicit key, ``math.fsum``,
+    explicit set unions) on tiny inputs;
+  * torch's scaled_dot_product_attention / logsumexp in float64 on the CPU,
+    over dense K/V that the test scatters into a shuffled paged pool itself;
+  * closed forms (constant V, single token, integer-exact scores);
+  * hand-derived golden cases under tests/golden/.
+"""
+from __future__ import annotations
+
+import json
+import math
+import os
+import random
+
+import numpy as np
+import torch
+
+import oracle.sparse_attn_oracle as O
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+# ------------------------------------------------------------------ helpers
+def scatter_to_pool(K, V, page_size, rng, extra_pages=0):
+    """Dense K [B][Hkv][L][d], V [B][Hkv][L][dv] -> shuffled paged pool.
+
+    Returns (k_pool [n_phys][Hkv][P][d], v_pool [n_phys][Hkv][dv][P],
+    block_table [B][max_pages]).  Written as a direct scatter, independent of
+    the oracle's gather.
+    """
+    B, Hkv, L, d = K.shape
+    dv = V.shape[-1]
+    P = page_size
+    npg = (L + P - 1) // P
+    n_phys = B * npg + extra_pages
+    perm = rng.permutation(n_phys)
+    kp = rng.standard_normal((n_phys, Hkv, P, d)) * 1e3      # junk where no token lands
+    vp = rng.standard_normal((n_phys, Hkv, dv, P)) * 1e3
+    bt = np.full((B, npg), -1, dtype=np.int32)
+    for b in range(B):
+        for lp in range(npg):
+            phys = int(perm[b * npg + lp])
+            bt[b, lp] = phys
+            for r in range(P):
+                j = lp * P + r
+                if j >= L:
+                    continue
+                for g in range(Hkv):
+                    kp[phys, g, r, :] = K[b, g, j, :]
+                    vp[phys, g, :, r] = V[b, g, j, :]
+    return kp, vp, bt
+
+
+def sdpa(qrows, K, V, scale, allowed):
+    """torch float64 SDPA + logsumexp for query rows [n][d] over K [L][d], V [L][dv], mask [n][L]."""
+    qt = torch.from_numpy(np.asarray(qrows, dtype=np.float64))[None, None]
+    kt = torch.from_numpy(np.asarray(K, dtype=np.float64))[None, None]
+    vt = torch.from_numpy(np.asarray(V, dtype=np.float64))[None, None]
+    mt = torch.from_numpy(np.asarray(allowed, dtype=bool))[None, None]
+    o = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, attn_mask=mt, scale=scale)[0, 0]
+    z = scale * (qt[0, 0] @ kt[0, 0].T)
+    z = z.masked_fill(~mt[0, 0], float("-inf"))
+    lse = torch.logsumexp(z, dim=-1)
+    return o.numpy(), lse.numpy()
+
+
+def _lists_from(sel_sets, stride):
+    B = len(sel_sets)
+    S = len(sel_sets[0])
+    lists = np.full((B, S, stride), -1, dtype=np.int32)
+    counts = np.zeros((B, S), dtype=np.int32)
+    for b in range(B):
+        for s in range(S):
+            ls = sorted(sel_sets[b][s])
+            lists[b, s, :len(ls)] = ls
+            counts[b, s] = len(ls)
+    return lists, counts
+
+
+# -------------------------------------------------------------------- a0
+def check_summary_constant_pages():
+    rng = np.random.default_rng(1)
+    B, Hkv, P, d, L = 2, 2, 4, 3, 10
+    K = np.zeros((B, Hkv, L, d))
+    for b in range(B):
+        for lp in range(3):
+            for g in range(Hkv):
+                K[b, g, lp * P:(lp + 1) * P, :] = (b + 1) * 10 + lp + 0.25 * g
+    kp, _, bt = scatter_to_pool(K, K, P, rng)
+    mu = O.page_summary(kp, bt, np.array([L, L]), P)
+    for b in range(B):
+        for lp in range(3):
+            for g in range(Hkv):
+                exp = (b + 1) * 10 + lp + 0.25 * g
+                assert np.all(mu[bt[b, lp], g] == np.float32(exp)), (b, lp, g)
+
+
+def check_summary_bruteforce():
+    rng = np.random.default_rng(2)
+    B, Hkv, P, d = 2, 2, 4, 5
+    lens = [11, 6]
+    L = max(lens)
+    K = rng.standard_normal((B, Hkv, L, d))
+    kp, _, bt = scatter_to_pool(K, K, P, rng)
+    mu = O.page_summary(kp, bt, np.array(lens), P)
+    for b in range(B):
+        for lp in range((lens[b] + P - 1) // P):
+            toks = [j for j in range(lp * P, (lp + 1) * P) if j < lens[b]]
+            for g in range(Hkv):
+                for e in range(d):
+                    exp = math.fsum(K[b, g, j, e] for j in toks) / len(toks)
+                    got = float(mu[bt[b, lp], g, e])
+                    assert abs(got - exp) <= 1e-6 * max(1.0, abs(exp)), (b, lp, g, e, got, exp)
+    # last_pages=1 touches only each sequence's last page
+    mu1 = O.page_summary(kp, bt, np.array(lens), P, last_pages=1)
+    for b in range(B):
+        n = (lens[b] + P - 1) // P
+        for lp in range(n):
+            touched = not np.isnan(mu1[bt[b, lp]]).any()
+            assert touched == (lp == n - 1)
+
+
+# -------------------------------------------------------------------- a1
+def check_scores_exact_integers():
+    """Small integers make every sum exact: compare with integer arithmetic."""
+    rng = np.random.default_rng(3)
+    B, T, Hq, Hkv, P, d, L = 2, 2, 4, 2, 4, 6, 16
+    q = rng.integers(-3, 4, size=(B, T, Hq, d)).astype(np.float64)
+    K = rng.integers(-4, 5, size=(B, Hkv, L, d)).astype(np.float64)
+    kp, _, bt = scatter_to_pool(K, K, P, rng)
+    mu = O.page_summary(kp, bt, np.array([L] * B), P)
+    G = Hq // Hkv
+    for mode in (O.PER_KV_HEAD, O.PER_Q_HEAD):
+        sc = O.page_scores(q, mu, bt, np.array([L] * B), P, Hkv, mode)
+        S = Hkv if mode == O.PER_KV_HEAD else Hq
+        for b in range(B):
+            for s in range(S):
+                heads = list(range(s * G, (s + 1) * G)) if mode == O.PER_KV_HEAD else [s]
+                g = s if mode == O.PER_KV_HEAD else s // G
+                for lp in range(L // P):
+                    num = 0
+                    for e in range(d):
+                        qs = sum(int(q[b, t, h, e]) for t in range(T) for h in heads)
+                        ks = sum(int(K[b, g, j, e]) for j in range(lp * P, (lp + 1) * P))
+                        num += qs * ks
+                    assert float(sc[b, s, lp]) == num / P, (mode, b, s, lp)
+
+
+def check_scores_linearity_and_unfactored():
+    """Group score = sum of the group's per-head scores = mean over tokens of sum_{t,h} q.k_j."""
+    rng = np.random.default_rng(4)
+    B, T, Hq, Hkv, P, d = 2, 2, 6, 2, 8, 16
+    lens = [37, 24]
+    L = max(lens)
+    q = rng.standard_normal((B, T, Hq, d))
+    K = rng.standard_normal((B, Hkv, L, d))
+    kp, _, bt = scatter_to_pool(K, K, P, rng)
+    mu = O.page_summary(kp, bt, np.array(lens), P)
+    sg = O.page_scores(q, mu, bt, np.array(lens), P, Hkv, O.PER_KV_HEAD)
+    sq = O.page_scores(q, mu, bt, np.array(lens), P, Hkv, O.PER_Q_HEAD)
+    G = Hq // Hkv
+    for b in range(B):
+        n = (lens[b] + P - 1) // P
+        for g in range(Hkv):
+            for lp in range(n):
+                per_head = math.fsum(float(sq[b, h, lp]) for h in range(g * G, (g + 1) * G))
+                assert abs(float(sg[b, g, lp]) - per_head) <= 1e-5 * (1 + abs(per_head))
+                toks = [j for j in range(lp * P, (lp + 1) * P) if j < lens[b]]
+                unf = math.fsum(float(q[b, t, h] @ K[b, g, j]) for j in toks for t in range(T)
+                                for h in range(g * G, (g + 1) * G)) / len(toks)
+                assert abs(float(sg[b, g, lp]) - unf) <= 1e-5 * (1 + abs(unf)), (b, g, lp)
+    # pages past the end of a sequence carry no score
+    assert np.isnan(sg[1, :, 3:]).all()
+
+
+# -------------------------------------------------------------------- a2
+def _brute_select(scores, n, sink, window, top_k, critical_k):
+    forced = sorted(set(range(min(sink, n))) | set(range(max(0, n - window), n)))
+    cand = [i for i in range(n) if i not in forced]
+
+    def key(i):
+        s = float(scores[i])
+        return (1, 0.0, i) if math.isnan(s) else (0, -s, i)
+
+    ranked = sorted(cand, key=key)
+    k = min(max(top_k, 0), len(ranked))
+    chosen = ranked[:k]
+    if critical_k is None:
+        return sorted(set(forced) | set(chosen)), None
+    ck = min(critical_k, k)
+    crit = sorted(set(forced) | set(chosen[:ck]))
+    return crit + sorted(chosen[ck:]), len(crit)
+
+
+def check_select_bruteforce():
+    rng = np.random.default_rng(5)
+    for trial in range(60):
+        B, S = 2, 3
+        n_pages = [int(rng.integers(1, 40)), int(rng.integers(1, 40))]
+        mp = max(n_pages)
+        # few distinct values -> many exact ties; a few NaNs and signed zeros
+        scores = rng.integers(-3, 4, size=(B, S, mp)).astype(np.float32)
+        scores[rng.random((B, S, mp)) < 0.05] = np.nan
+        scores[rng.random((B, S, mp)) < 0.05] = -0.0
+        sink, window = int(rng.integers(0, 4)), int(rng.integers(0, 6))
+        top_k = int(rng.integers(0, 45))
+        critical_k = None if trial % 2 == 0 else int(rng.integers(0, top_k + 2))
+        lists, counts, cc = O.select_pages(scores, n_pages, sink, window, top_k, critical_k)
+        for b in range(B):
+            for s in range(S):
+                exp, ecc = _brute_select(scores[b, s], n_pages[b], sink, window, top_k, critical_k)
+                got = [int(x) for x in lists[b, s, :counts[b, s]]]
+                assert got == exp, (trial, b, s, got, exp)
+                assert (lists[b, s, counts[b, s]:] == -1).all()
+                if critical_k is not None:
+                    assert int(cc[b, s]) == ecc
+
+
+def check_select_golden():
+    with open(os.path.join(GOLDEN, "select_cases.json")) as f:
+        cases = json.load(f)["cases"]
+    for c in cases:
+        sc = np.array([float(x) for x in c["scores"]], dtype=np.float32)[None, None, :]
+        lists, counts, cc = O.select_pages(sc, [sc.shape[-1]], c["sink"], c["window"], c["top_k"],
+                                           c["critical_k"])
+        got = [int(x) for x in lists[0, 0, :counts[0, 0]]]
+        assert got == c["list"], (c["name"], got, c["list"])
+        if c["critical_count"] is not None:
+            assert int(cc[0, 0]) == c["critical_count"], c["name"]
+
+
+# ----------------------------------------------------------------- a3-a5
+def _dense_decode_case(rng, B=2, T=2, Hq=4, Hkv=2, P=4, d=8, dv=8, lens=(19, 12)):
+    L = max(lens)
+    q = rng.standard_normal((B, T, Hq, d))
+    K = rng.standard_normal((B, Hkv, L, d))
+    V = rng.standard_normal((B, Hkv, L, dv))
+    kp, vp, bt = scatter_to_pool(K, V, P, rng, extra_pages=3)
+    return q, K, V, kp, vp, bt, np.array(lens)
+
+
+def check_decode_select_all_sdpa():
+    rng = np.random.default_rng(6)
+    q, K, V, kp, vp, bt, lens = _dense_decode_case(rng)
+    B, T, Hq, d = q.shape
+    Hkv, P = K.shape[1], 4
+    G = Hq // Hkv
+    sets = [[set(range((int(lens[b]) + P - 1) // P)) for _ in range(Hkv)] for b in range(B)]
+    lists, counts = _lists_from(sets, bt.shape[1])
+    scale = 0.37
+    out, lse = O.sparse_decode(q, kp, vp, bt, lens, P, lists, counts, Hkv, O.PER_KV_HEAD, scale)
+    for b in range(B):
+        L = int(lens[b])
+        for h in range(Hq):
+            g = h // G
+            eo, el = sdpa(q[b, :, h], K[b, g, :L], V[b, g, :L], scale, np.ones((T, L), bool))
+            assert np.allclose(out[b, :, h], eo, atol=1e-12, rtol=1e-10), (b, h)
+            assert np.allclose(lse[b, :, h], el, atol=1e-12, rtol=1e-10), (b, h)
+
+
+def check_decode_masked_sdpa():
+    """Page-list attention == dense attention with unselected tokens masked (per q head)."""
+    rng = np.random.default_rng(7)
+    q, K, V, kp, vp, bt, lens = _dense_decode_case(rng, Hq=6, Hkv=2, lens=(23, 17))
+    B, T, Hq, _ = q.shape
+    Hkv, P = 2, 4
+    G = Hq // Hkv
+    sets = []
+    for b in range(B):
+        n = (int(lens[b]) + P - 1) // P
+        sets.append([set(int(x) for x in rng.choice(n, size=int(rng.integers(1, n + 1)), replace=False))
+                     for _ in range(Hq)])
+    lists, counts = _lists_from(sets, bt.shape[1])
+    scale = 0.5
+    out, lse = O.sparse_decode(q, kp, vp, bt, lens, P, lists, counts, Hkv, O.PER_Q_HEAD, scale)
+    for b in range(B):
+        L = int(lens[b])
+        for h in range(Hq):
+            allowed = np.array([(j // P) in sets[b][h] for j in range(L)])[None, :].repeat(T, 0)
+            eo, el = sdpa(q[b, :, h], K[b, h // G, :L], V[b, h // G, :L], scale, allowed)
+            assert np.allclose(out[b, :, h], eo, atol=1e-12, rtol=1e-10), (b, h)
+            assert np.allclose(lse[b, :, h], el, atol=1e-12, rtol=1e-10), (b, h)
+
+
+def check_decode_golden():
+    with open(os.path.join(GOLDEN, "decode_cases.json")) as f:
+        cases = json.load(f)["cases"]
+    for c in cases:
+        kp = np.array(c["k_pool"], dtype=np.float64)
+        vp = np.array(c["v_pool"], dtype=np.float64)
+        bt = np.array([c["block_table"]], dtype=np.int32)
+        q = np.array(c["q"], dtype=np.float64)[None, None, None, :]
+        lst = np.array([[c["list"] + [-1] * (bt.shape[1] - len(c["list"]))]], dtype=np.int32)
+        cnt = np.array([[len(c["list"])]], dtype=np.int32)
+        out, lse = O.sparse_decode(q, kp, vp, bt, np.array([c["seq_len"]]), c["page_size"], lst, cnt,
+                                   1, O.PER_KV_HEAD, c["sm_scale"])
+        assert np.allclose(out[0, 0, 0], c["o"], atol=1e-12), (c["name"], out[0, 0, 0])
+        assert abs(lse[0, 0, 0] - c["lse"]) < 1e-12, (c["name"], lse[0, 0, 0])
+
+
+def check_decode_closed_forms():
+    rng = np.random.default_rng(8)
+    q, K, V, kp, vp, bt, lens = _dense_decode_case(rng, B=1, T=1, Hq=2, Hkv=1, lens=(13,))
+    P = 4
+    # V = const  ->  o = const for any selection
+    Vc = np.full_like(V, 2.5)
+    kpc, vpc, btc = scatter_to_pool(K, Vc, P, rng)
+    lists, counts = _lists_from([[{0, 2, 3}]], btc.shape[1])
+    out, _ = O.sparse_decode(q, kpc, vpc, btc, lens, P, lists, counts, 1, O.PER_KV_HEAD, 0.3)
+    assert np.allclose(out, 2.5, atol=1e-13)
+    # single valid token (last page holds 1 token of 13) -> o = V_j, lse = z_j
+    lists, counts = _lists_from([[{3}]], bt.shape[1])
+    out, lse = O.sparse_decode(q, kp, vp, bt, lens, P, lists, counts, 1, O.PER_KV_HEAD, 0.3)
+    for h in range(2):
+        assert np.allclose(out[0, 0, h], V[0, 0, 12], atol=1e-13)
+        assert abs(lse[0, 0, h] - 0.3 * float(q[0, 0, h] @ K[0, 0, 12])) < 1e-12
+    # one-hot V rows -> o is the softmax weight vector: non-negative, sums to 1
+    L = 13
+    Vid = np.eye(L)[None, None]
+    kpi, vpi, bti = scatter_to_pool(K, Vid, P, rng)
+    lists, counts = _lists_from([[{0, 1, 2, 3}]], bti.shape[1])
+    out, _ = O.sparse_decode(q, kpi, vpi, bti, lens, P, lists, counts, 1, O.PER_KV_HEAD, 0.3, d_v=L)
+    w = out[0, 0]
+    assert (w >= 0).all() and np.allclose(w.sum(axis=-1), 1.0, atol=1e-14)
+    # empty list -> o = 0, lse = -inf
+    lists, counts = _lists_from([[set()]], bt.shape[1])
+    out, lse = O.sparse_decode(q, kp, vp, bt, lens, P, lists, counts, 1, O.PER_KV_HEAD, 0.3)
+    assert (out == 0).all() and np.isneginf(lse).all()
+
+
+def check_decode_large_logits():
+    rng = np.random.default_rng(9)
+    q, K, V, kp, vp, bt, lens = _dense_decode_case(rng, B=1, T=1, Hq=2, Hkv=1, lens=(16,))
+    P = 4
+    scale = 300.0            # logits in the thousands: exp overflows without the max shift
+    lists, counts = _lists_from([[{0, 1, 2, 3}]], bt.shape[1])
+    out, lse = O.sparse_decode(q, kp, vp, bt, lens, P, lists, counts, 1, O.PER_KV_HEAD, scale)
+    assert np.isfinite(out).all() and np.isfinite(lse).all()
+    for h in range(2):
+        eo, el = sdpa(q[0, :, h], K[0, 0], V[0, 0], scale, np.ones((1, 16), bool))
+        assert np.allclose(out[0, :, h], eo, atol=1e-9) and np.allclose(lse[0, :, h], el, rtol=1e-12)
+
+
+def check_decode_pool_permutation():
+    """The physical placement of pages never changes the result (bit-identical)."""
+    rng = np.random.default_rng(10)
+    q, K, V, kp, vp, bt, lens = _dense_decode_case(rng)
+    kp2, vp2, bt2 = scatter_to_pool(K, V, 4, np.random.default_rng(99), extra_pages=7)
+    sets = [[{0, 2, 4}, {1, 3}], [{0, 1}, {2}]]
+    lists, counts = _lists_from(sets, bt.shape[1])
+    a = O.sparse_decode(q, kp, vp, bt, lens, 4, lists, counts, 2, O.PER_KV_HEAD, 0.4)
+    b = O.sparse_decode(q, kp2, vp2, bt2, lens, 4, lists, counts, 2, O.PER_KV_HEAD, 0.4)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+def check_decode_modes_and_tiers():
+    rng = np.random.default_rng(11)
+    q, K, V, kp, vp, bt, lens = _dense_decode_case(rng, Hq=4, Hkv=2, lens=(29, 21))
+    B, T, Hq, _ = q.shape
+    Hkv, P, G = 2, 4, 2
+    sets = [[{0, 3, 5}, {1, 2}], [{0, 4}, {5}]]
+    lists, counts = _lists_from(sets, bt.shape[1])
+    grp = O.sparse_decode(q, kp, vp, bt, lens, P, lists, counts, Hkv, O.PER_KV_HEAD, 0.4)
+    # per-q mode with each head given its group's list == group mode, bit for bit
+    qsets = [[sets[b][h // G] for h in range(Hq)] for b in range(B)]
+    ql, qc = _lists_from(qsets, bt.shape[1])
+    per = O.sparse_decode(q, kp, vp, bt, lens, P, ql, qc, Hkv, O.PER_Q_HEAD, 0.4)
+    assert np.array_equal(grp[0], per[0]) and np.array_equal(grp[1], per[1])
+    # tiered: list = Critical (first 1 entry) + Ambient; every head in every mask == untiered
+    cc = np.ones((B, Hkv), dtype=np.int32)
+    all_heads = np.full((B, bt.shape[1], 1), (1 << Hq) - 1, dtype=np.int64)
+    tier = O.sparse_decode(q, kp, vp, bt, lens, P, lists, counts, Hkv, O.PER_KV_HEAD, 0.4, cc, all_heads)
+    assert np.array_equal(tier[0], grp[0])
+    # no head in any Ambient mask == untiered over the Critical segment only
+    none = np.zeros((B, bt.shape[1], 1), dtype=np.int64)
+    tier0 = O.sparse_decode(q, kp, vp, bt, lens, P, lists, counts, Hkv, O.PER_KV_HEAD, 0.4, cc, none)
+    crit = _lists_from([[{min(s)} for s in sets[b]] for b in range(B)], bt.shape[1])
+    ref0 = O.sparse_decode(q, kp, vp, bt, lens, P, crit[0], crit[1], Hkv, O.PER_KV_HEAD, 0.4)
+    assert np.array_equal(tier0[0], ref0[0])
+    # mixed mask: head h sees Ambient page p iff bit h of p's mask -> masked SDPA per head
+    mixed = rng.integers(0, 1 << Hq, size=(B, bt.shape[1], 1)).astype(np.int64)
+    tm = O.sparse_decode(q, kp, vp, bt, lens, P, lists, counts, Hkv, O.PER_KV_HEAD, 0.4, cc, mixed)
+    for b in range(B):
+        L = int(lens[b])
+        for h in range(Hq):
+            s = h // G
+            ordered = sorted(sets[b][s])
+            seen = {ordered[0]} | {p for p in ordered[1:] if (int(mixed[b, p, 0]) >> h) & 1}
+            allowed = np.array([(j // P) in seen for j in range(L)])[None, :].repeat(T, 0)
+            eo, el = sdpa(q[b, :, h], K[b, s, :L], V[b, s, :L], 0.4, allowed)
+            assert np.allclose(tm[0][b, :, h], eo, atol=1e-12) and np.allclose(tm[1][b, :, h], el, atol=1e-12)
+
+
+def check_decode_split_merge():
+    rng = np.random.default_rng(12)
+    q, K, V, kp, vp, bt, lens = _dense_decode_case(rng, B=1, T=1, Hq=2, Hkv=1, lens=(40,))
+    P = 4
+    full = list(range(10))
+    lists, counts = _lists_from([[set(full)]], bt.shape[1])
+    ref_o, ref_l = O.sparse_decode(q, kp, vp, bt, lens, P, lists, counts, 1, O.PER_KV_HEAD, 0.3)
+    for ns in (1, 2, 3, 4, 7, 10, 13):
+        rngs = O.split_ranges(len(full), ns)
+        assert [r for r in rngs if r[1] > r[0]][-1][1] == len(full)
+        sizes = [e - s for s, e in rngs]
+        assert max(sizes) - min(sizes) <= 1 and sum(sizes) == len(full)
+        po, pl = [], []
+        for (s0, s1) in rngs:
+            sub = _lists_from([[set(full[s0:s1])]], bt.shape[1])
+            o, l = O.sparse_decode(q, kp, vp, bt, lens, P, sub[0], sub[1], 1, O.PER_KV_HEAD, 0.3)
+            po.append(o[0, 0])
+            pl.append(l[0, 0])
+        po, pl = np.stack(po, 1), np.stack(pl, 1)   # [Hq][S][dv], [Hq][S]
+        for h in range(2):
+            mo, ml = O.lse_merge(po[h], pl[h])
+            assert np.allclose(mo, ref_o[0, 0, h], atol=1e-13, rtol=1e-12), ns
+            assert abs(ml - ref_l[0, 0, h]) < 1e-12
+
+
+# ------------------------------------------------------------------- a6-a7
+def check_union_bruteforce():
+    rng = np.random.default_rng(13)
+    for trial in range(30):
+        Hkv = int(rng.integers(1, 4))
+        G = int(rng.integers(1, 4))
+        Hq, nqb, nkb = Hkv * G, int(rng.integers(1, 5)), int(rng.integers(1, 30))
+        mask = (rng.random((Hq, nqb, nkb)) < rng.random() * 0.3).astype(np.uint8)
+        tables, counts = O.gqa_union_block_table(mask, Hkv)
+        for g in range(Hkv):
+            exp = set()
+            for h in range(g * G, (g + 1) * G):
+                for qb in range(nqb):
+                    for kb in range(nkb):
+                        if mask[h, qb, kb]:
+                            exp.add(kb)
+            got = [int(x) for x in tables[g, :counts[g]]]
+            assert got == sorted(exp), (trial, g)
+            assert (tables[g, counts[g]:] == -1).all()
+    # group size 1 with one Q-block: the table is the mask row itself
+    m = (rng.random((3, 1, 17)) < 0.4).astype(np.uint8)
+    t, c = O.gqa_union_block_table(m, 3)
+    for h in range(3):
+        assert [int(x) for x in t[h, :c[h]]] == list(np.flatnonzero(m[h, 0]))
+
+
+def check_union_golden():
+    with open(os.path.join(GOLDEN, "union_cases.json")) as f:
+        cases = json.load(f)["cases"]
+    for c in cases:
+        t, n = O.gqa_union_block_table(np.array(c["mask"], dtype=np.uint8), c["n_kv_heads"])
+        assert t.tolist() == c["tables"] and n.tolist() == c["counts"], c["name"]
+
+
+def _prefill_case(rng, Hq=4, Hkv=2, P=4, d=8, q_len=9, q_start=13):
+    L = q_start + q_len
+    q = rng.standard_normal((q_len, Hq, d))
+    K = rng.standard_normal((1, Hkv, L, d))
+    V = rng.standard_normal((1, Hkv, L, d))
+    kp, vp, bt = scatter_to_pool(K, V, P, rng, extra_pages=2)
+    return q, K, V, kp, vp, bt, L
+
+
+def check_prefill_causal_sdpa():
+    """All-causal-blocks mask == dense causal attention at offset q_start."""
+    rng = np.random.default_rng(14)
+    q, K, V, kp, vp, bt, L = _prefill_case(rng)
+    q_len, Hq, d = q.shape
+    Hkv, P, q_start, G = 2, 4, 13, 2
+    nkb = (L + P - 1) // P
+    tables = np.tile(np.arange(nkb, dtype=np.int32), (Hkv, 1))
+    counts = np.full(Hkv, nkb, dtype=np.int32)
+    out, lse = O.block_sparse_prefill(q, kp, vp, bt[0], L, P, q_start, tables, counts, Hkv, 0.35)
+    causal = np.arange(L)[None, :] <= (q_start + np.arange(q_len))[:, None]
+    for h in range(Hq):
+        eo, el = sdpa(q[:, h], K[0, h // G], V[0, h // G], 0.35, causal)
+        assert np.allclose(out[:, h], eo, atol=1e-12) and np.allclose(lse[:, h], el, atol=1e-12), h
+    # rows subset gives the same numbers
+    sub = [(0, 1), (8, 3), (4, 0)]
+    so, sl = O.block_sparse_prefill(q, kp, vp, bt[0], L, P, q_start, tables, counts, Hkv, 0.35, rows=sub)
+    for (i, h) in sub:
+        # (BLAS may order a different row count differently: last-bit agreement only)
+        assert np.allclose(so[i, h], out[i, h], atol=1e-14, rtol=1e-12) and abs(sl[i, h] - lse[i, h]) < 1e-12
+
+
+def check_prefill_masked_sdpa():
+    """Random block mask: every query of a group sees exactly the group's union blocks, causally."""
+    rng = np.random.default_rng(15)
+    q, K, V, kp, vp, bt, L = _prefill_case(rng, Hq=6, Hkv=2, q_len=11, q_start=21)
+    q_len, Hq, d = q.shape
+    Hkv, P, q_start, G = 2, 4, 21, 3
+    nkb = (L + P - 1) // P
+    nqb = 3
+    mask = (rng.random((Hq, nqb, nkb)) < 0.3).astype(np.uint8)
+    tables, counts = O.gqa_union_block_table(mask, Hkv)
+    out, lse = O.block_sparse_prefill(q, kp, vp, bt[0], L, P, q_start, tables, counts, Hkv, 0.35)
+    for h in range(Hq):
+        g = h // G
+        blocks = set(int(x) for x in tables[g, :counts[g]])
+        allowed = np.array([[(j // P) in blocks and j <= q_start + i for j in range(L)] for i in range(q_len)])
+        eo, el = sdpa(q[:, h], K[0, g], V[0, g], 0.35, allowed)
+        empty = ~allowed.any(axis=1)
+        assert np.allclose(out[~empty, h], eo[~empty], atol=1e-12), h
+        assert np.allclose(lse[~empty, h], el[~empty], atol=1e-12), h
+        assert (out[empty, h] == 0).all() and np.isneginf(lse[empty, h]).all()
+
+
+ALL_CHECKS = [
+    check_summary_constant_pages, check_summary_bruteforce,
+    check_scores_exact_integers, check_scores_linearity_and_unfactored,
+    check_select_bruteforce, check_select_golden,
+    check_decode_select_all_sdpa, check_decode_masked_sdpa, check_decode_golden,
+    check_decode_closed_forms, check_decode_large_logits, check_decode_pool_permutation,
+    check_decode_modes_and_tiers, check_decode_split_merge,
+    check_union_bruteforce, check_union_golden,
+    check_prefill_causal_sdpa, check_prefill_masked_sdpa,
+]
