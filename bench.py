@@ -1,0 +1,257 @@
+"""Benchmark of the sparse-decode hot path on one MI355X.
+
+Default workload (the headline metric): Llama-3-8B-shaped decode layer,
+batch 32, 32 query / 8 KV heads, d 128, bf16, 32768 tokens per sequence in
+pages of 64 in a shuffled shared pool, sink 1 page + window 8 pages + top-41
+pages per KV head (3200 of 32768 tokens, ~90% sparsity).
+
+One step = one decode layer's sparse-attention work for one batch:
+  sa_page_summary(last_pages=1)  mean key of the page the newest token landed in
+  sa_select_pages                router scores + sink/window/top-k lists
+  sa_sparse_decode               split-K flash-decode over the lists (+ merge)
+Inputs are resident in HBM before timing; steps rotate over 3 independently
+drawn input sets (4.2 GB each) so no step finds its pages in the 256 MB
+last-level cache left warm by the previous one.
+
+Prints one JSON line: value = selected K+V bytes per step / step time (GB/s);
+roofline of the dominant kernel (the decode) from HIP events on the launch
+stream; cpu_baseline = the CPU oracle on a bounded sample of the same
+workload (two sequences), in the same unit.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+import workloads as W
+
+HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="llama3_8b_decode_32k",
+                    choices=["llama3_8b_decode_32k", "token_head_decode_128k", "mla_tiered_decode_64k",
+                             "chunked_prefill_128k", "tiny_decode"])
+    ap.add_argument("--sets", type=int, default=3, help="independent input sets rotated over")
+    ap.add_argument("--splits", type=int, default=-1, help="decode splits (-1: workload default)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    return ap.parse_args()
+
+
+class Timer:
+    """Per-call HIP event pairs on the current (launch) stream."""
+
+    def __init__(self):
+        self.pairs = {}
+
+    def start(self, name):
+        e = torch.cuda.Event(enable_timing=True)
+        e.record()
+        self.pairs.setdefault(name, []).append([e, None])
+
+    def stop(self, name):
+        e = torch.cuda.Event(enable_timing=True)
+        e.record()
+        self.pairs[name][-1][1] = e
+
+    def avg_us(self, name):
+        ps = self.pairs.get(name, [])
+        return 1000.0 * sum(a.elapsed_time(b) for a, b in ps) / max(1, len(ps))
+
+    def reset(self):
+        self.pairs = {}
+
+
+def decode_step_fn(S, wl, inp, mu, splits, timer):
+    kv = S.PagedKV(inp["k_pool"], inp["v_pool"], inp["block_table"], inp["seq_lens"], d_v=wl.d_v)
+    mode = S.SA_SEL_PER_KV_HEAD if wl.mode == "per_kv_head" else S.SA_SEL_PER_Q_HEAD
+    stride = max(1, min(wl.max_pages, wl.sink_pages + wl.window_pages + wl.top_k))
+    dev = inp["q"].device
+    n_sel = wl.n_sel
+    lists = torch.full((wl.batch, n_sel, stride), -1, dtype=torch.int32, device=dev)
+    counts = torch.zeros((wl.batch, n_sel), dtype=torch.int32, device=dev)
+    ccounts = torch.zeros_like(counts) if wl.tiered else None
+    sel_ws = torch.empty(max(1, S.sa_select_pages_workspace_size(wl.batch, n_sel, wl.max_pages)),
+                         dtype=torch.uint8, device=dev)
+    dec_ws = torch.zeros(max(1, S.sa_sparse_decode_workspace_size(kv, wl.q_tokens, wl.n_q_heads, stride, mode,
+                                                                   splits)), dtype=torch.uint8, device=dev)
+    out = torch.empty((wl.batch, wl.q_tokens, wl.n_q_heads, wl.d_v), dtype=inp["q"].dtype, device=dev)
+    lse = torch.empty((wl.batch, wl.q_tokens, wl.n_q_heads), dtype=torch.float32, device=dev)
+
+    def step():
+        if mu is not None:
+            timer.start("summary")
+            S.sa_page_summary(kv, last_pages=1, out=mu)
+            timer.stop("summary")
+        timer.start("select")
+        S.sa_select_pages(kv, n_q_heads=wl.n_q_heads, mode=mode, sink_pages=wl.sink_pages,
+                          window_pages=wl.window_pages, top_k=wl.top_k, q=inp["q"] if mu is not None else None,
+                          page_summary=mu, scores=inp["scores"], critical_k=wl.critical_k, list_stride=stride,
+                          workspace=sel_ws, out=(lists, counts, ccounts))
+        timer.stop("select")
+        timer.start("decode")
+        S.sa_sparse_decode(kv, inp["q"], lists, counts, mode=mode, sm_scale=wl.sm_scale,
+                           critical_counts=ccounts, ambient_head_mask=inp["ambient_mask"], num_splits=splits,
+                           out=out, out_lse=lse, workspace=dec_ws)
+        timer.stop("decode")
+
+    return step, (lists, counts, ccounts)
+
+
+def selected_bytes(wl, inp, lists, counts, ccounts):
+    """Algorithmic decode bytes: each selected (page, KV head) K and V once (valid tokens)."""
+    P = wl.page_size
+    el = 2 if wl.dtype == "bf16" else 4
+    lens = inp["seq_lens"].cpu().numpy()
+    L = lists.cpu().numpy()
+    C = counts.cpu().numpy()
+    per_tok = (wl.d_qk + (0 if wl.latent else wl.d_v)) * el
+    total = 0
+    uniq = 0
+    for b in range(wl.batch):
+        for s in range(wl.n_sel):
+            for lp in L[b, s, :C[b, s]]:
+                total += min(P, int(lens[b]) - int(lp) * P) * per_tok
+        if wl.mode == "per_q_head":
+            G = wl.group
+            for g in range(wl.n_kv_heads):
+                pages = set()
+                for s in range(g * G, (g + 1) * G):
+                    pages.update(int(x) for x in L[b, s, :C[b, s]])
+                uniq += sum(min(P, int(lens[b]) - p * P) for p in pages) * per_tok
+    return total, (uniq if wl.mode == "per_q_head" else total)
+
+
+def cpu_baseline_decode(wl, inp, n_seq=2):
+    """The oracle, as is, on the first n_seq sequences of one input set."""
+    import oracle.sparse_attn_oracle as O
+    from threadpoolctl import threadpool_info
+    P = wl.page_size
+    lens = inp["seq_lens"].cpu().numpy()[:n_seq]
+    bt_full = inp["block_table"].cpu()
+    pages = [bt_full[b, :math.ceil(int(lens[b]) / P)].long() for b in range(n_seq)]
+    allp = torch.cat(pages)
+    kp = inp["k_pool"][allp].float().cpu().numpy().astype(np.float64)
+    vp = None if inp["v_pool"] is None else inp["v_pool"][allp].float().cpu().numpy().astype(np.float64)
+    bt = np.full((n_seq, wl.max_pages), -1, dtype=np.int32)
+    off = 0
+    for b, pg in enumerate(pages):
+        bt[b, :len(pg)] = np.arange(off, off + len(pg))
+        off += len(pg)
+    q = inp["q"][:n_seq].float().cpu().numpy().astype(np.float64)
+    t0 = time.perf_counter()
+    npg = [O.n_pages_of(L, P) for L in lens]
+    if wl.scores == "gumbel":
+        scores = inp["scores"][:n_seq].cpu().numpy()
+    else:
+        mu = O.page_summary(kp, bt, lens, P, last_pages=1) if False else O.page_summary(kp, bt, lens, P)
+        scores = O.page_scores(q, mu, bt, lens, P, wl.n_kv_heads, wl.mode)
+    lists, counts, cc = O.select_pages(scores, npg, wl.sink_pages, wl.window_pages, wl.top_k, wl.critical_k)
+    am = None if inp["ambient_mask"] is None else inp["ambient_mask"][:n_seq].cpu().numpy().astype(np.int64) & 0xffffffff
+    O.sparse_decode(q, kp, vp, bt, lens, P, lists, counts, wl.n_kv_heads, wl.mode, wl.sm_scale, cc, am,
+                    d_v=wl.d_v)
+    dt = time.perf_counter() - t0
+    el = 2 if wl.dtype == "bf16" else 4
+    per_tok = (wl.d_qk + (0 if wl.latent else wl.d_v)) * el
+    nbytes = sum(min(P, int(lens[b]) - int(lp) * P) * per_tok
+                 for b in range(n_seq) for s in range(wl.n_sel) for lp in lists[b, s, :counts[b, s]])
+    threads = max([t.get("num_threads", 1) for t in threadpool_info()] + [1])
+    return dict(value=round(nbytes / dt / 1e9, 6), unit="GB/s", cores=threads, kind="oracle",
+                sample=f"{n_seq} of {wl.batch} sequences, full step incl. page means over all their pages "
+                       f"(numpy float64 oracle; {dt:.2f} s)", seconds=round(dt, 3))
+
+
+def run_decode(args):
+    import sparse_attention_long_page_amd as S
+    wl = W.FULL[args.workload]
+    dev = torch.device("cuda:0")
+    splits = wl.num_splits if args.splits < 0 else args.splits
+    sets = []
+    for i in range(args.sets):
+        inp = W.make_decode_inputs(wl, dev, seed=1000 + i)
+        mu = None
+        if wl.scores == "summary":
+            kv = S.PagedKV(inp["k_pool"], inp["v_pool"], inp["block_table"], inp["seq_lens"], d_v=wl.d_v)
+            mu = S.sa_page_summary(kv)       # amortised: built once per filled page
+        sets.append((inp, mu))
+    torch.cuda.synchronize()
+    timer = Timer()
+    steps = []
+    for inp, mu in sets:
+        fn, res = decode_step_fn(S, wl, inp, mu, splits, timer)
+        steps.append((fn, res, inp))
+    for i in range(args.warmup):
+        steps[i % len(steps)][0]()
+    torch.cuda.synchronize()
+    timer.reset()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        steps[i % len(steps)][0]()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = 1000.0 * wall / args.steps
+
+    fn, (lists, counts, ccounts), inp = steps[0]
+    nbytes, uniq = selected_bytes(wl, inp, lists, counts, ccounts)
+    dec_us = timer.avg_us("decode")
+    sel_us = timer.avg_us("select")
+    sum_us = timer.avg_us("summary")
+    algo_bytes = uniq if wl.mode == "per_q_head" else nbytes
+    achieved = algo_bytes / (dec_us * 1e-6) / 1e9
+    value = nbytes / (ms_per_step * 1e-3) / 1e9
+    res = {
+        "metric": "sparse-decode selected-KV GB/s (% of HBM peak) + us/layer at 32K ctx, 90% sparsity",
+        "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": wl.dtype, "data": "synthetic (seeded; N(0,1) q/K/V, planted pages)",
+        "config": {"workload": wl.name, "batch": wl.batch, "context": wl.context, "q_heads": wl.n_q_heads,
+                   "kv_heads": wl.n_kv_heads, "head_dim": wl.d_qk, "page_size": wl.page_size,
+                   "sink_pages": wl.sink_pages, "window_pages": wl.window_pages, "top_k": wl.top_k,
+                   "kept_tokens_per_head": int(counts.float().mean().item() * wl.page_size),
+                   "splits": splits, "input_sets": args.sets},
+        "us_per_layer": round(1000.0 * ms_per_step, 2),
+        "pct_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
+        "stage_us": {"summary": round(sum_us, 2), "select": round(sel_us, 2), "decode": round(dec_us, 2)},
+        "selected_bytes": nbytes,
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "sa_sparse_decode (decode + split merge)", "algorithmic_bytes": algo_bytes},
+    }
+    if wl.mode == "per_q_head":
+        res["pair_counted_bytes"] = nbytes
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline_decode(wl, steps[0][2])
+    return res
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (run with --gpus 1).",
+              file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU (torch.cuda.is_available() is False)", file=sys.stderr)
+        sys.exit(2)
+    if args.workload == "chunked_prefill_128k":
+        from bench_prefill import run_prefill  # noqa
+        res = run_prefill(args)
+    else:
+        res = run_decode(args)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

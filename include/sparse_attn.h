@@ -1,0 +1,228 @@
+/*
+ * sparse_attn.h -- C ABI of a gfx950 (MI355X) library for dynamic page- and
+ * block-sparse attention over a paged KV cache.
+ *
+ * Method sources (web pages, cited by title and section):
+ *  [UAE] "Universal Attention Engine - Declarative Sparse Attention for
+ *        Production": "The Product" (sink tokens, local window, cache budget),
+ *        "Content-Dependent Dynamic Routing (Novel)" (router
+ *        top_k_blocks(q @ mean(k_blocks), k): block-granular routing, full
+ *        attention on the selected blocks, only selected blocks loaded),
+ *        "Key Design Decisions" 3 (decode optimised for bytes loaded, prefill
+ *        for FLOPs), "Architecture" Layer 2/3 (gather-based sparse-KV decode,
+ *        block-sparse prefill, PagedAttention-compatible layout).
+ *  [TS]  "TileSparse: Arithmetic-Intensity-Aware Sparse Attention for
+ *        Compute-Bound LLM Decoding" (README): "Motivation" (QK 2D sparsity;
+ *        Tiered QK 2D sparsity with a Critical tier of alpha pages on all
+ *        query heads and an Ambient tier of beta pages on h heads), "Two
+ *        implementations, by design" (true per-head page-list Flash-decode),
+ *        "Configuration" (critical_top_count, ambient_head_count).
+ *  [STS] STS abstract on the page titled "Vortex: Efficient and Programmable
+ *        Sparse Attention Serving for AI Agents" (token-and-head-wise masks
+ *        built from draft-model attention scores).
+ *  [CA]  CompactAttention abstract on the page titled "Causal Attention on
+ *        CPU: A Cache-Aware and Load-Balanced Scheduling Kernel for Prefill"
+ *        (2D block masks -> GQA-aware per-group KV block tables by Q-block union
+ *        then intra-group union; KV read in place under chunked prefill).
+ *
+ * Conventions for every call below.
+ *  - Memory: every tensor pointer is a DEVICE pointer owned by the caller.
+ *    The library allocates no device memory; calls that need scratch take a
+ *    caller-provided `workspace` of at least the size its *_workspace_size
+ *    function returns (256-byte aligned).
+ *  - Streams: all work is enqueued on `stream`; calls return without
+ *    synchronising.  Calls sharing a workspace must be ordered by the caller.
+ *  - Errors: arguments are validated on the host before anything is
+ *    launched.  On error the call returns a non-SA_OK status, enqueues
+ *    nothing, writes no output, records a message for sa_last_error_message()
+ *    (thread-local) and never aborts.  A launch failure returns SA_ERR_DEVICE.
+ *    Device data (page ids, list entries, lengths) is trusted: out-of-range
+ *    page ids are undefined behaviour.
+ *  - Layout of the paged KV cache (sa_paged_kv), all row-major:
+ *      k_pool      [n_phys_pages][n_kv_heads][page_size][d_qk]   (token-major page)
+ *      v_pool      [n_phys_pages][n_kv_heads][d_v][page_size]    (page-transposed,
+ *                  the PagedAttention value layout); NULL means V is the first
+ *                  d_v dims of each K row (MLA latent cache, d_qk 576 / d_v 512)
+ *      block_table [batch][max_pages] int32: logical page -> physical page
+ *      seq_lens    [batch] int32: valid tokens per sequence; logical page p of
+ *                  sequence b holds tokens [p*page_size, min((p+1)*page_size, len))
+ *  - Supported shapes: page_size 16 or 64; (d_qk, d_v) = (64, 64) or (128, 128)
+ *    with a V pool, (576, 512) without one; dtype bf16, or fp32 for the decode
+ *    side (summary, select, decode) at d 64/128.  Anything else returns
+ *    SA_ERR_UNSUPPORTED.
+ */
+#ifndef SPARSE_ATTN_H_
+#define SPARSE_ATTN_H_
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  SA_OK = 0,
+  SA_ERR_INVALID_ARGUMENT = 1,
+  SA_ERR_UNSUPPORTED = 2,
+  SA_ERR_WORKSPACE_TOO_SMALL = 3,
+  SA_ERR_DEVICE = 4
+} sa_status;
+
+typedef enum { SA_DTYPE_BF16 = 0, SA_DTYPE_FP32 = 1 } sa_dtype;
+
+/* Selection granularity.  PER_KV_HEAD: one list per KV head, scored with the
+ * query summed over the head's query group (GQA) and query tokens.
+ * PER_Q_HEAD: one list per query head ([TS] QK 2D sparsity, [STS] head-wise
+ * masks). */
+typedef enum { SA_SEL_PER_KV_HEAD = 0, SA_SEL_PER_Q_HEAD = 1 } sa_sel_mode;
+
+typedef struct {
+  const void* k_pool;
+  const void* v_pool;            /* may be NULL (latent cache) */
+  const int32_t* block_table;
+  const int32_t* seq_lens;
+  int32_t n_phys_pages;
+  int32_t n_kv_heads;
+  int32_t page_size;
+  int32_t d_qk;
+  int32_t d_v;
+  int32_t max_pages;             /* row stride of block_table */
+  sa_dtype dtype;                /* element type of q, k_pool, v_pool and outputs */
+} sa_paged_kv;
+
+/* ------------------------------------------------------------------------
+ * sa_page_summary -- per-page mean key, the block summary the router scores
+ * against ([UAE] "Content-Dependent Dynamic Routing": mean(k_blocks)).
+ *
+ *   page_summary[phys][g][:] = mean over the page's valid tokens of k_pool[phys][g][j][:]
+ *
+ * Accumulated in float64, rounded once to fp32.  Written for logical pages
+ * [0, n) of every sequence (n = ceil(seq_len/page_size)), or only the last
+ * `last_pages` of them when last_pages > 0 (the pages a decode step's new
+ * tokens touched).  Entries of other physical pages are left untouched.
+ *   page_summary: out [n_phys_pages][n_kv_heads][d_qk] fp32.
+ * ---------------------------------------------------------------------- */
+sa_status sa_page_summary(const sa_paged_kv* kv, int32_t batch, int32_t last_pages,
+                          float* page_summary, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * sa_select_pages -- per-selection-head page lists: forced sink pages and
+ * local-window pages plus the top-k other pages by router score
+ * ([UAE] "The Product" sink/local window, "Content-Dependent Dynamic
+ * Routing" top_k_blocks; [TS] tiers; [STS] head-wise masks).
+ *
+ * Score of logical page p for selection head s of sequence b:
+ *   score = fp32( sum_d Qbar[d] * page_summary[phys(b,p)][g(s)][d] ),
+ *   Qbar = sum over the q_tokens query tokens and the query heads of s
+ *          (PER_KV_HEAD: the n_q_heads/n_kv_heads heads of KV head s;
+ *           PER_Q_HEAD: head s alone, KV head s / group) of q, in float64.
+ * With `scores` given, those values are used as-is instead (q and
+ * page_summary may then be NULL).
+ * Forced pages F = [0, sink_pages) u [n - window_pages, n), clipped to [0, n).
+ * The other pages are ranked by (score descending, logical index ascending),
+ * NaN last, -0 == +0; the first k = min(top_k, n - |F|) are selected.
+ *   untiered (critical_counts == NULL): list = ascending(F u selected)
+ *   tiered: Critical = ascending(F u first min(critical_k, k) selected),
+ *           Ambient  = ascending(the remaining selected); list = Critical
+ *           then Ambient; critical_counts = |Critical|.
+ *   q            [batch][q_tokens][n_q_heads][d_qk] (kv->dtype) or NULL
+ *   page_summary [n_phys_pages][n_kv_heads][d_qk] fp32 or NULL
+ *   scores       [batch][n_sel][scores_stride] fp32 or NULL, scores_stride >= max_pages
+ *   page_lists   out [batch][n_sel][list_stride] int32 logical ids, entries
+ *                past the count are left untouched;
+ *                list_stride >= min(max_pages, sink_pages + window_pages + top_k)
+ *   page_counts  out [batch][n_sel];  critical_counts out [batch][n_sel] or NULL
+ *   scores_out   optional out [batch][n_sel][max_pages] fp32 router scores (NaN
+ *                past each sequence's last page); ignored when scores given
+ * n_sel = n_kv_heads (PER_KV_HEAD) or n_q_heads (PER_Q_HEAD).  max_pages <= 16384.
+ * ---------------------------------------------------------------------- */
+size_t sa_select_pages_workspace_size(int32_t batch, int32_t n_sel, int32_t max_pages);
+
+sa_status sa_select_pages(const sa_paged_kv* kv, int32_t batch,
+                          const void* q, int32_t q_tokens, int32_t n_q_heads,
+                          const float* page_summary,
+                          const float* scores, int32_t scores_stride,
+                          sa_sel_mode mode,
+                          int32_t sink_pages, int32_t window_pages, int32_t top_k,
+                          int32_t critical_k,
+                          int32_t* page_lists, int32_t list_stride,
+                          int32_t* page_counts, int32_t* critical_counts,
+                          float* scores_out,
+                          void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * sa_sparse_decode -- split-K paged flash-decode over per-head page lists
+ * ([UAE] gather-based sparse-KV decode; [TS] per-head page-list Flash-decode
+ * and Tiered QK 2D sparsity).
+ *
+ * Query row (b, t, h) attends exactly the valid tokens of its pages:
+ *   untiered: every page in its selection head's list;
+ *   tiered (critical_counts != NULL): the first critical_counts[b][s] list
+ *   entries (Critical, all heads) plus each later entry p (Ambient) whose
+ *   ambient_head_mask[b][p] has bit h.
+ *   o = softmax(sm_scale * q K^T) V over that token set, lse = log-sum-exp of
+ *   the scaled logits; an empty set gives o = 0 and lse = -inf.
+ * Each list is cut into num_splits contiguous chunks (sizes differ by at most
+ * one); chunk partials (o_s, lse_s) are combined by an LSE merge.
+ *   q                 [batch][q_tokens][n_q_heads][d_qk]
+ *   page_lists/counts as produced by sa_select_pages (logical page ids)
+ *   ambient_head_mask [batch][max_pages][ceil(n_q_heads/32)] uint32 (tiered only)
+ *   num_splits        0: the library chooses; otherwise 1..64
+ *   out               [batch][q_tokens][n_q_heads][d_v] (kv->dtype)
+ *   out_lse           [batch][q_tokens][n_q_heads] fp32 natural-log units, or NULL
+ * Per-KV-head lists need q_tokens*group <= 16 at d 64/128 (one 16-row MFMA
+ * tile per KV head); the latent path needs n_kv_heads == 1, n_q_heads a
+ * multiple of 16 and q_tokens*n_q_heads <= 256.
+ * ---------------------------------------------------------------------- */
+size_t sa_sparse_decode_workspace_size(const sa_paged_kv* kv, int32_t batch, int32_t q_tokens,
+                                       int32_t n_q_heads, int32_t list_stride, sa_sel_mode mode,
+                                       int32_t num_splits);
+
+sa_status sa_sparse_decode(const sa_paged_kv* kv, int32_t batch,
+                           const void* q, int32_t q_tokens, int32_t n_q_heads,
+                           const int32_t* page_lists, const int32_t* page_counts,
+                           int32_t list_stride, sa_sel_mode mode,
+                           const int32_t* critical_counts, const uint32_t* ambient_head_mask,
+                           float sm_scale, int32_t num_splits,
+                           void* out, float* out_lse,
+                           void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * sa_block_sparse_prefill -- chunked-prefill attention with a 2D block mask
+ * turned into GQA-union KV block tables ([CA]; [UAE] block-sparse prefill).
+ *
+ *   U_h[kb]  = OR over Q-blocks qb of block_mask[h][qb][kb]
+ *   T_g[kb]  = OR over the query heads h of KV head g of U_h[kb]
+ *   block_table_out[g][0..count) = ascending {kb : T_g[kb]}, block_counts_out[g] = count
+ * then query i (position q_start + i) of head h attends, in place in the
+ * paged pool row `seq`, every token j of the blocks in T_{g(h)} with
+ * j <= q_start + i and j < seq_lens[seq]:  o = softmax(sm_scale q K^T) V.
+ *   q          [q_len][n_q_heads][d_qk]
+ *   block_mask [n_q_heads][ceil(q_len/block_q)][n_kv_blocks] uint8 (nonzero = keep);
+ *              KV block kb is logical page kb (block size = page_size)
+ *   block_table_out  out [n_kv_heads][n_kv_blocks] int32 (entries past the
+ *              count are left untouched); block_counts_out out [n_kv_heads]
+ *   out        [q_len][n_q_heads][d_v];  out_lse [q_len][n_q_heads] fp32 or NULL
+ * Needs bf16, d_qk == d_v == 128, page_size 64, n_kv_blocks <= max_pages.
+ * ---------------------------------------------------------------------- */
+size_t sa_block_sparse_prefill_workspace_size(const sa_paged_kv* kv, int32_t q_len,
+                                              int32_t n_q_heads, int32_t n_kv_blocks);
+
+sa_status sa_block_sparse_prefill(const sa_paged_kv* kv, int32_t seq,
+                                  const void* q, int32_t q_len, int32_t q_start, int32_t n_q_heads,
+                                  const uint8_t* block_mask, int32_t block_q, int32_t n_kv_blocks,
+                                  int32_t* block_table_out, int32_t* block_counts_out,
+                                  float sm_scale, void* out, float* out_lse,
+                                  void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------------ utilities */
+const char* sa_status_string(sa_status s);
+const char* sa_last_error_message(void);   /* thread-local; "" when the last call succeeded */
+int sa_version(void);                      /* major*10000 + minor*100 + patch */
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* SPARSE_ATTN_H_ */

@@ -1,0 +1,414 @@
+// Host side of the C ABI declared in include/sparse_attn.h: argument
+// validation (before anything is launched), workspace sizing, launch-shape
+// choice and dispatch to the gfx950 kernels.  Allocates no device memory and
+// keeps no device state beyond a cached compute-unit count.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "../../include/sparse_attn.h"
+#include "common.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+sa_status fail(sa_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+sa_status ok() {
+  g_last_error.clear();
+  return SA_OK;
+}
+
+sa_status device_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ok();
+  return fail(SA_ERR_DEVICE, "%s: %s", what, hipGetErrorString(e));
+}
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+int device_cu_count() {
+  static thread_local int cached_dev = -1, cached_cus = 0;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 256;
+  if (dev != cached_dev) {
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+      cus = 256;
+    cached_dev = dev;
+    cached_cus = cus;
+  }
+  return cached_cus;
+}
+
+bool is_latent(const sa_paged_kv* kv) { return kv->v_pool == nullptr; }
+
+// Shape checks shared by every call.  `need_pools`: k_pool/v_pool must be set.
+sa_status check_kv(const sa_paged_kv* kv, bool need_pools) {
+  if (!kv) return fail(SA_ERR_INVALID_ARGUMENT, "kv is NULL");
+  if (!kv->block_table || !kv->seq_lens) return fail(SA_ERR_INVALID_ARGUMENT, "block_table/seq_lens NULL");
+  if (need_pools && !kv->k_pool) return fail(SA_ERR_INVALID_ARGUMENT, "k_pool is NULL");
+  if (kv->n_phys_pages <= 0 || kv->n_kv_heads <= 0 || kv->max_pages <= 0)
+    return fail(SA_ERR_INVALID_ARGUMENT, "n_phys_pages/n_kv_heads/max_pages must be positive");
+  if (kv->dtype != SA_DTYPE_BF16 && kv->dtype != SA_DTYPE_FP32)
+    return fail(SA_ERR_INVALID_ARGUMENT, "unknown dtype %d", (int)kv->dtype);
+  if (kv->page_size != 16 && kv->page_size != 64)
+    return fail(SA_ERR_UNSUPPORTED, "page_size %d unsupported (16 or 64)", kv->page_size);
+  const bool latent = kv->v_pool == nullptr;
+  if (latent) {
+    if (!(kv->d_qk == 576 && kv->d_v == 512))
+      return fail(SA_ERR_UNSUPPORTED, "a latent cache (v_pool NULL) needs d_qk 576 / d_v 512, got %d/%d",
+                  kv->d_qk, kv->d_v);
+    if (kv->dtype != SA_DTYPE_BF16) return fail(SA_ERR_UNSUPPORTED, "latent cache must be bf16");
+  } else {
+    if (!((kv->d_qk == 64 && kv->d_v == 64) || (kv->d_qk == 128 && kv->d_v == 128)))
+      return fail(SA_ERR_UNSUPPORTED, "(d_qk, d_v) = (%d, %d) unsupported with a V pool", kv->d_qk, kv->d_v);
+  }
+  return SA_OK;
+}
+
+int n_sel_of(const sa_paged_kv* kv, int n_q_heads, sa_sel_mode mode) {
+  return mode == SA_SEL_PER_KV_HEAD ? kv->n_kv_heads : n_q_heads;
+}
+
+// Splits per selection head for the decode kernels.
+int choose_splits(const sa_paged_kv* kv, int batch, int n_sel, int list_stride) {
+  const int units = std::max(1, batch * n_sel);
+  const int cus = device_cu_count();
+  if (is_latent(kv)) {
+    // latent path: one unit per (sequence, 16-row tile group); split by pages
+    const int target = 2 * cus;
+    int s = (target + units - 1) / units;
+    s = std::min(s, std::max(1, list_stride / 2));
+    return std::max(1, std::min(s, 64));
+  }
+  const int per_chunk = 64 / kv->page_size;
+  const int chunks = (list_stride + per_chunk - 1) / per_chunk;
+  const int target = 2 * cus;                // 2 workgroups (8 waves) per CU
+  int s = (target + units - 1) / units;
+  s = std::min(s, std::max(1, chunks / 4));  // at least one chunk per wave
+  return std::max(1, std::min(s, 64));
+}
+
+size_t decode_partials_bytes(const sa_paged_kv* kv, int batch, int q_tokens, int n_q_heads, int splits) {
+  if (splits <= 1) return 0;
+  const size_t rows = (size_t)batch * q_tokens * n_q_heads;
+  return align_up(rows * splits * kv->d_v * sizeof(float)) + align_up(rows * splits * sizeof(float));
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* sa_status_string(sa_status s) {
+  switch (s) {
+    case SA_OK: return "SA_OK";
+    case SA_ERR_INVALID_ARGUMENT: return "SA_ERR_INVALID_ARGUMENT";
+    case SA_ERR_UNSUPPORTED: return "SA_ERR_UNSUPPORTED";
+    case SA_ERR_WORKSPACE_TOO_SMALL: return "SA_ERR_WORKSPACE_TOO_SMALL";
+    case SA_ERR_DEVICE: return "SA_ERR_DEVICE";
+  }
+  return "SA_ERR_UNKNOWN";
+}
+
+const char* sa_last_error_message(void) { return g_last_error.c_str(); }
+
+int sa_version(void) { return 100; }   // 0.1.0
+
+// ------------------------------------------------------------------ summary
+sa_status sa_page_summary(const sa_paged_kv* kv, int32_t batch, int32_t last_pages, float* page_summary,
+                          hipStream_t stream) {
+  sa_status st = check_kv(kv, true);
+  if (st != SA_OK) return st;
+  if (batch <= 0) return fail(SA_ERR_INVALID_ARGUMENT, "batch must be positive");
+  if (last_pages < 0) return fail(SA_ERR_INVALID_ARGUMENT, "last_pages must be >= 0");
+  if (!page_summary) return fail(SA_ERR_INVALID_ARGUMENT, "page_summary is NULL");
+  sa::SummaryParams p{};
+  p.k_pool = kv->k_pool;
+  p.block_table = kv->block_table;
+  p.seq_lens = kv->seq_lens;
+  p.mu = page_summary;
+  p.n_kv = kv->n_kv_heads;
+  p.P = kv->page_size;
+  p.d = kv->d_qk;
+  p.max_pages = kv->max_pages;
+  p.last_pages = std::min(last_pages, kv->max_pages);
+  return device_status(sa::launch_page_summary(p, batch, kv->dtype == SA_DTYPE_BF16, stream), "page_summary launch");
+}
+
+// ------------------------------------------------------------------- select
+size_t sa_select_pages_workspace_size(int32_t batch, int32_t n_sel, int32_t max_pages) {
+  if (batch <= 0 || n_sel <= 0 || max_pages <= 0) return 0;
+  // router scores + float64 pooled queries (d_qk <= 576)
+  return align_up((size_t)batch * n_sel * max_pages * sizeof(float)) +
+         align_up((size_t)batch * n_sel * 576 * sizeof(double));
+}
+
+sa_status sa_select_pages(const sa_paged_kv* kv, int32_t batch, const void* q, int32_t q_tokens,
+                          int32_t n_q_heads, const float* page_summary, const float* scores,
+                          int32_t scores_stride, sa_sel_mode mode, int32_t sink_pages, int32_t window_pages,
+                          int32_t top_k, int32_t critical_k, int32_t* page_lists, int32_t list_stride,
+                          int32_t* page_counts, int32_t* critical_counts, float* scores_out, void* workspace,
+                          size_t workspace_bytes, hipStream_t stream) {
+  sa_status st = check_kv(kv, false);
+  if (st != SA_OK) return st;
+  if (batch <= 0) return fail(SA_ERR_INVALID_ARGUMENT, "batch must be positive");
+  if (mode != SA_SEL_PER_KV_HEAD && mode != SA_SEL_PER_Q_HEAD)
+    return fail(SA_ERR_INVALID_ARGUMENT, "unknown selection mode %d", (int)mode);
+  if (n_q_heads <= 0 || n_q_heads % kv->n_kv_heads != 0)
+    return fail(SA_ERR_INVALID_ARGUMENT, "n_q_heads (%d) must be a positive multiple of n_kv_heads (%d)",
+                n_q_heads, kv->n_kv_heads);
+  if (sink_pages < 0 || window_pages < 0 || top_k < 0)
+    return fail(SA_ERR_INVALID_ARGUMENT, "sink_pages, window_pages and top_k must be >= 0");
+  if (critical_counts && critical_k < 0) return fail(SA_ERR_INVALID_ARGUMENT, "critical_k must be >= 0");
+  if (!page_lists || !page_counts) return fail(SA_ERR_INVALID_ARGUMENT, "page_lists/page_counts NULL");
+  if (kv->max_pages > 16384) return fail(SA_ERR_UNSUPPORTED, "max_pages %d > 16384", kv->max_pages);
+  const long need_stride = std::min<long>(kv->max_pages, (long)sink_pages + window_pages + top_k);
+  if (list_stride < need_stride)
+    return fail(SA_ERR_INVALID_ARGUMENT, "list_stride %d < min(max_pages, sink+window+top_k) = %ld", list_stride,
+                need_stride);
+  const int n_sel = n_sel_of(kv, n_q_heads, mode);
+  if (scores) {
+    if (scores_stride < kv->max_pages)
+      return fail(SA_ERR_INVALID_ARGUMENT, "scores_stride %d < max_pages %d", scores_stride, kv->max_pages);
+  } else {
+    if (!q || !page_summary) return fail(SA_ERR_INVALID_ARGUMENT, "q and page_summary needed without scores");
+    if (q_tokens <= 0) return fail(SA_ERR_INVALID_ARGUMENT, "q_tokens must be positive");
+    const size_t need = sa_select_pages_workspace_size(batch, n_sel, kv->max_pages);
+    if (workspace_bytes < need || (!workspace && need))
+      return fail(SA_ERR_WORKSPACE_TOO_SMALL, "workspace %zu < %zu bytes", workspace_bytes, need);
+  }
+
+  const float* sc = scores;
+  int stride = scores_stride;
+  if (!scores) {
+    float* buf = scores_out ? scores_out : reinterpret_cast<float*>(workspace);
+    double* qbar = reinterpret_cast<double*>(reinterpret_cast<char*>(workspace) +
+                                             align_up((size_t)batch * n_sel * kv->max_pages * sizeof(float)));
+    sa::ScoreParams p{};
+    p.q = q;
+    p.mu = page_summary;
+    p.block_table = kv->block_table;
+    p.seq_lens = kv->seq_lens;
+    p.scores = buf;
+    p.B = batch;
+    p.T = q_tokens;
+    p.Hq = n_q_heads;
+    p.Hkv = kv->n_kv_heads;
+    p.G = n_q_heads / kv->n_kv_heads;
+    p.n_sel = n_sel;
+    p.d = kv->d_qk;
+    p.P = kv->page_size;
+    p.max_pages = kv->max_pages;
+    p.per_q = mode == SA_SEL_PER_Q_HEAD;
+    hipError_t e = sa::launch_page_scores_ws(p, kv->dtype == SA_DTYPE_BF16, qbar, stream);
+    if (e != hipSuccess) return device_status(e, "page_scores launch");
+    sc = buf;
+    stride = kv->max_pages;
+  }
+  sa::SelectParams sp{};
+  sp.scores = sc;
+  sp.seq_lens = kv->seq_lens;
+  sp.lists = page_lists;
+  sp.counts = page_counts;
+  sp.ccounts = critical_counts;
+  sp.scores_stride = stride;
+  sp.n_sel = n_sel;
+  sp.P = kv->page_size;
+  sp.list_stride = list_stride;
+  sp.sink = sink_pages;
+  sp.window = window_pages;
+  sp.top_k = top_k;
+  sp.critical_k = critical_k;
+  sp.tiered = critical_counts != nullptr;
+  return device_status(sa::launch_select(sp, batch, kv->max_pages, stream), "select launch");
+}
+
+// ------------------------------------------------------------------- decode
+static sa_status check_decode_shape(const sa_paged_kv* kv, int32_t batch, int32_t q_tokens, int32_t n_q_heads,
+                                    sa_sel_mode mode) {
+  if (batch <= 0 || q_tokens <= 0) return fail(SA_ERR_INVALID_ARGUMENT, "batch and q_tokens must be positive");
+  if (mode != SA_SEL_PER_KV_HEAD && mode != SA_SEL_PER_Q_HEAD)
+    return fail(SA_ERR_INVALID_ARGUMENT, "unknown selection mode %d", (int)mode);
+  if (n_q_heads <= 0 || n_q_heads % kv->n_kv_heads != 0)
+    return fail(SA_ERR_INVALID_ARGUMENT, "n_q_heads (%d) must be a positive multiple of n_kv_heads (%d)",
+                n_q_heads, kv->n_kv_heads);
+  const int G = n_q_heads / kv->n_kv_heads;
+  if (is_latent(kv)) {
+    if (kv->n_kv_heads != 1) return fail(SA_ERR_UNSUPPORTED, "latent decode needs n_kv_heads == 1");
+    if (mode != SA_SEL_PER_KV_HEAD) return fail(SA_ERR_UNSUPPORTED, "latent decode uses per-KV-head lists");
+    if (n_q_heads % 16 != 0 || q_tokens * n_q_heads > 256)
+      return fail(SA_ERR_UNSUPPORTED, "latent decode needs n_q_heads %% 16 == 0 and q_tokens*n_q_heads <= 256");
+    if (kv->page_size != 64) return fail(SA_ERR_UNSUPPORTED, "latent decode needs page_size 64");
+  } else if (kv->dtype == SA_DTYPE_BF16) {
+    const int rows = mode == SA_SEL_PER_KV_HEAD ? q_tokens * G : q_tokens;
+    if (rows > 16)
+      return fail(SA_ERR_UNSUPPORTED, "%d query rows share a KV head; the bf16 decode tile holds 16", rows);
+  }
+  return SA_OK;
+}
+
+size_t sa_sparse_decode_workspace_size(const sa_paged_kv* kv, int32_t batch, int32_t q_tokens, int32_t n_q_heads,
+                                       int32_t list_stride, sa_sel_mode mode, int32_t num_splits) {
+  if (!kv || batch <= 0 || q_tokens <= 0 || n_q_heads <= 0 || list_stride <= 0 || kv->n_kv_heads <= 0) return 0;
+  const int n_sel = n_sel_of(kv, n_q_heads, mode);
+  const int splits = num_splits > 0 ? num_splits : choose_splits(kv, batch, n_sel, list_stride);
+  return decode_partials_bytes(kv, batch, q_tokens, n_q_heads, splits);
+}
+
+sa_status sa_sparse_decode(const sa_paged_kv* kv, int32_t batch, const void* q, int32_t q_tokens,
+                           int32_t n_q_heads, const int32_t* page_lists, const int32_t* page_counts,
+                           int32_t list_stride, sa_sel_mode mode, const int32_t* critical_counts,
+                           const uint32_t* ambient_head_mask, float sm_scale, int32_t num_splits, void* out,
+                           float* out_lse, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  sa_status st = check_kv(kv, true);
+  if (st != SA_OK) return st;
+  st = check_decode_shape(kv, batch, q_tokens, n_q_heads, mode);
+  if (st != SA_OK) return st;
+  if (!q || !page_lists || !page_counts || !out)
+    return fail(SA_ERR_INVALID_ARGUMENT, "q, page_lists, page_counts and out must be set");
+  if (list_stride <= 0) return fail(SA_ERR_INVALID_ARGUMENT, "list_stride must be positive");
+  if ((critical_counts == nullptr) != (ambient_head_mask == nullptr))
+    return fail(SA_ERR_INVALID_ARGUMENT, "critical_counts and ambient_head_mask go together");
+  if (!std::isfinite(sm_scale)) return fail(SA_ERR_INVALID_ARGUMENT, "sm_scale must be finite");
+  if (num_splits < 0 || num_splits > 64) return fail(SA_ERR_INVALID_ARGUMENT, "num_splits must be in 0..64");
+  const int n_sel = n_sel_of(kv, n_q_heads, mode);
+  const int splits = num_splits > 0 ? num_splits : choose_splits(kv, batch, n_sel, list_stride);
+  const size_t need = decode_partials_bytes(kv, batch, q_tokens, n_q_heads, splits);
+  if (workspace_bytes < need || (need && !workspace))
+    return fail(SA_ERR_WORKSPACE_TOO_SMALL, "workspace %zu < %zu bytes", workspace_bytes, need);
+
+  sa::DecodeParams p{};
+  p.q = q;
+  p.k_pool = kv->k_pool;
+  p.v_pool = kv->v_pool;
+  p.block_table = kv->block_table;
+  p.seq_lens = kv->seq_lens;
+  p.lists = page_lists;
+  p.counts = page_counts;
+  p.ccounts = critical_counts;
+  p.amask = ambient_head_mask;
+  p.out = out;
+  p.out_lse = out_lse;
+  const size_t rows = (size_t)batch * q_tokens * n_q_heads;
+  if (splits > 1) {
+    p.part_o = reinterpret_cast<float*>(workspace);
+    p.part_lse = reinterpret_cast<float*>(reinterpret_cast<char*>(workspace) +
+                                          align_up(rows * splits * kv->d_v * sizeof(float)));
+  }
+  p.B = batch;
+  p.T = q_tokens;
+  p.Hq = n_q_heads;
+  p.Hkv = kv->n_kv_heads;
+  p.G = n_q_heads / kv->n_kv_heads;
+  p.n_sel = n_sel;
+  p.per_q = mode == SA_SEL_PER_Q_HEAD;
+  p.list_stride = list_stride;
+  p.max_pages = kv->max_pages;
+  p.mask_words = (n_q_heads + 31) / 32;
+  p.P = kv->page_size;
+  p.d_qk = kv->d_qk;
+  p.d_v = kv->d_v;
+  p.splits = splits;
+  p.scale_log2 = sm_scale * sa::kLog2e;
+  hipError_t e = is_latent(kv) ? sa::launch_mla_decode(p, stream)
+                               : sa::launch_decode(p, kv->dtype == SA_DTYPE_BF16, stream);
+  if (e != hipSuccess) return device_status(e, "decode launch");
+  if (splits > 1) {
+    sa::MergeParams mp{};
+    mp.part_o = p.part_o;
+    mp.part_lse = p.part_lse;
+    mp.out = out;
+    mp.out_lse = out_lse;
+    mp.rows = (int)rows;
+    mp.splits = splits;
+    mp.d_v = kv->d_v;
+    mp.out_fp32 = kv->dtype == SA_DTYPE_FP32;
+    e = sa::launch_merge(mp, stream);
+    if (e != hipSuccess) return device_status(e, "merge launch");
+  }
+  return ok();
+}
+
+// ------------------------------------------------------------------ prefill
+size_t sa_block_sparse_prefill_workspace_size(const sa_paged_kv* kv, int32_t q_len, int32_t n_q_heads,
+                                              int32_t n_kv_blocks) {
+  (void)kv; (void)q_len; (void)n_q_heads; (void)n_kv_blocks;
+  return 0;
+}
+
+sa_status sa_block_sparse_prefill(const sa_paged_kv* kv, int32_t seq, const void* q, int32_t q_len,
+                                  int32_t q_start, int32_t n_q_heads, const uint8_t* block_mask, int32_t block_q,
+                                  int32_t n_kv_blocks, int32_t* block_table_out, int32_t* block_counts_out,
+                                  float sm_scale, void* out, float* out_lse, void* workspace,
+                                  size_t workspace_bytes, hipStream_t stream) {
+  (void)workspace; (void)workspace_bytes;
+  sa_status st = check_kv(kv, true);
+  if (st != SA_OK) return st;
+  if (kv->dtype != SA_DTYPE_BF16 || is_latent(kv) || kv->d_qk != 128 || kv->page_size != 64)
+    return fail(SA_ERR_UNSUPPORTED, "prefill needs bf16, a V pool, d 128 and page_size 64");
+  if (seq < 0) return fail(SA_ERR_INVALID_ARGUMENT, "seq must be >= 0");
+  if (!q || !block_mask || !block_table_out || !block_counts_out || !out)
+    return fail(SA_ERR_INVALID_ARGUMENT, "q, block_mask, block_table_out, block_counts_out and out must be set");
+  if (q_len <= 0 || q_start < 0 || block_q <= 0)
+    return fail(SA_ERR_INVALID_ARGUMENT, "q_len and block_q must be positive, q_start >= 0");
+  if (n_q_heads <= 0 || n_q_heads % kv->n_kv_heads != 0)
+    return fail(SA_ERR_INVALID_ARGUMENT, "n_q_heads must be a positive multiple of n_kv_heads");
+  const long need_blocks = ((long)q_start + q_len + kv->page_size - 1) / kv->page_size;
+  if (n_kv_blocks < need_blocks || n_kv_blocks > kv->max_pages)
+    return fail(SA_ERR_INVALID_ARGUMENT, "n_kv_blocks %d must cover q_start+q_len (%ld) and be <= max_pages %d",
+                n_kv_blocks, need_blocks, kv->max_pages);
+  if (!std::isfinite(sm_scale)) return fail(SA_ERR_INVALID_ARGUMENT, "sm_scale must be finite");
+  const int G = n_q_heads / kv->n_kv_heads;
+  if (G > 8) return fail(SA_ERR_UNSUPPORTED, "prefill supports up to 8 query heads per KV head");
+
+  sa::UnionParams up{};
+  up.mask = block_mask;
+  up.table = block_table_out;
+  up.counts = block_counts_out;
+  up.Hq = n_q_heads;
+  up.Hkv = kv->n_kv_heads;
+  up.G = G;
+  up.nqb = (q_len + block_q - 1) / block_q;
+  up.nkb = n_kv_blocks;
+  hipError_t e = sa::launch_union(up, stream);
+  if (e != hipSuccess) return device_status(e, "union launch");
+
+  sa::PrefillParams p{};
+  p.q = q;
+  p.k_pool = kv->k_pool;
+  p.v_pool = kv->v_pool;
+  p.bt_row = kv->block_table + (size_t)seq * kv->max_pages;
+  p.seq_len = kv->seq_lens + seq;
+  p.table = block_table_out;
+  p.counts = block_counts_out;
+  p.out = out;
+  p.out_lse = out_lse;
+  p.q_len = q_len;
+  p.q_start = q_start;
+  p.Hq = n_q_heads;
+  p.Hkv = kv->n_kv_heads;
+  p.G = G;
+  p.nkb = n_kv_blocks;
+  p.P = kv->page_size;
+  p.scale_log2 = sm_scale * sa::kLog2e;
+  e = sa::launch_prefill(p, stream);
+  if (e != hipSuccess) return device_status(e, "prefill launch");
+  return ok();
+}
+
+}  // extern "C"

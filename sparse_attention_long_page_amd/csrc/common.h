@@ -1,0 +1,140 @@
+// Internal definitions shared by the library's host layer and its gfx950
+// kernels.  Not part of the public interface (include/sparse_attn.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sa {
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
+typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t u32x4;
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t bits16) {
+  return __uint_as_float(bits16 << 16);
+}
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// float -> bf16 bits, round to nearest even (native v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float x) {
+  __bf16 h = (__bf16)x;
+  return __builtin_bit_cast(uint16_t, h);
+}
+
+// Full-wave (64 lanes) reductions.
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+__device__ __forceinline__ double wave_sum_f64(double v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+// Number of valid tokens of logical page `lp` in a sequence of `len` tokens.
+__device__ __forceinline__ int page_valid(int len, int lp, int P) {
+  int r = len - lp * P;
+  return r < 0 ? 0 : (r > P ? P : r);
+}
+
+// ---------------------------------------------------------------- launch params
+struct SummaryParams {
+  const void* k_pool;
+  const int32_t* block_table;
+  const int32_t* seq_lens;
+  float* mu;
+  int n_kv, P, d, max_pages, last_pages;
+};
+
+struct ScoreParams {
+  const void* q;             // [B][T][Hq][d]
+  const float* mu;           // [n_phys][Hkv][d]
+  const int32_t* block_table;
+  const int32_t* seq_lens;
+  float* scores;             // [B][n_sel][max_pages]
+  int B, T, Hq, Hkv, G, n_sel, d, P, max_pages;
+  int per_q;                 // 1: PER_Q_HEAD
+};
+
+struct SelectParams {
+  const float* scores;       // [B][n_sel][stride]
+  const int32_t* seq_lens;
+  int32_t* lists;            // [B][n_sel][list_stride]
+  int32_t* counts;           // [B][n_sel]
+  int32_t* ccounts;          // [B][n_sel] or null
+  int scores_stride, n_sel, P, list_stride;
+  int sink, window, top_k, critical_k, tiered;
+};
+
+struct DecodeParams {
+  const void* q;             // [B][T][Hq][d_qk]
+  const void* k_pool;        // [n_phys][Hkv][P][d_qk]
+  const void* v_pool;        // [n_phys][Hkv][d_v][P]  (null: latent)
+  const int32_t* block_table;
+  const int32_t* seq_lens;
+  const int32_t* lists;      // [B][n_sel][list_stride]
+  const int32_t* counts;     // [B][n_sel]
+  const int32_t* ccounts;    // [B][n_sel] or null
+  const uint32_t* amask;     // [B][max_pages][mask_words] or null
+  void* out;                 // [B][T][Hq][d_v]
+  float* out_lse;            // [B][T][Hq] or null
+  float* part_o;             // [B][T][Hq][splits][d_v]
+  float* part_lse;           // [B][T][Hq][splits]
+  int B, T, Hq, Hkv, G, n_sel, per_q, list_stride, max_pages, mask_words;
+  int P, d_qk, d_v, splits;
+  float scale_log2;          // sm_scale * log2(e)
+};
+
+struct MergeParams {
+  const float* part_o;
+  const float* part_lse;
+  void* out;
+  float* out_lse;
+  int rows, splits, d_v, out_fp32;
+};
+
+struct UnionParams {
+  const uint8_t* mask;       // [Hq][nqb][nkb]
+  int32_t* table;            // [Hkv][nkb]
+  int32_t* counts;           // [Hkv]
+  int Hq, Hkv, G, nqb, nkb;
+};
+
+struct PrefillParams {
+  const void* q;             // [q_len][Hq][d]
+  const void* k_pool;
+  const void* v_pool;
+  const int32_t* bt_row;     // block_table row of the sequence
+  const int32_t* seq_len;    // pointer to seq_lens[seq]
+  const int32_t* table;      // [Hkv][nkb]
+  const int32_t* counts;     // [Hkv]
+  void* out;                 // [q_len][Hq][d]
+  float* out_lse;            // [q_len][Hq] or null
+  int q_len, q_start, Hq, Hkv, G, nkb, P;
+  int n_qtiles;
+  float scale_log2;
+};
+
+// ------------------------------------------------------------- launchers
+hipError_t launch_page_summary(const SummaryParams& p, int batch, int bf16, hipStream_t s);
+hipError_t launch_page_scores_ws(const ScoreParams& p, int bf16, double* qbar_ws, hipStream_t s);
+hipError_t launch_select(const SelectParams& p, int batch, int max_pages, hipStream_t s);
+hipError_t launch_decode(const DecodeParams& p, int bf16, hipStream_t s);
+hipError_t launch_merge(const MergeParams& p, hipStream_t s);
+hipError_t launch_mla_decode(const DecodeParams& p, hipStream_t s);
+hipError_t launch_union(const UnionParams& p, hipStream_t s);
+hipError_t launch_prefill(const PrefillParams& p, hipStream_t s);
+
+}  // namespace sa

@@ -1,0 +1,368 @@
+// Split-K paged flash-decode over per-head page lists, and the LSE merge.
+//
+// Method: each query row attends exactly the valid tokens of its selected
+// pages ("Universal Attention Engine", "Content-Dependent Dynamic Routing":
+// selected blocks get full attention, only they are loaded; TileSparse README,
+// "Two implementations, by design": a true per-head page-list Flash-decode;
+// "Motivation": Tiered QK 2D sparsity, Ambient pages on a subset of heads).
+//
+// bf16 kernel (d 64/128).  Decode is HBM-bound ("Key Design Decisions" 3:
+// optimise bytes loaded), so the design goal is streaming each selected
+// (page, KV head) exactly once with full 16-byte loads, straight into MFMA
+// operand registers (no LDS staging; nothing is reused across waves):
+//  * workgroup = (sequence, selection head, split), 4 waves; the query rows
+//    that share the KV head (GQA group x query tokens, or one head's tokens)
+//    form the 16 columns of one MFMA tile, so each K/V element is read once
+//    for all of them;
+//  * the split's list is walked in 64-token chunks (1 page of 64 or 4 pages
+//    of 16), chunk c by wave c % 4;
+//  * S^T = K Q^T with v_mfma_f32_16x16x32_bf16: K rows are the A operand
+//    read directly from the token-major page; the token->row assignment is
+//    permuted so that the fp32 S^T accumulators of two tiles are exactly the
+//    B operand layout of the PV product (no shuffle between QK and PV);
+//  * O^T += V^T P^T with V^T read directly from the page-transposed V pool
+//    (8 consecutive tokens of one dim = one 16-byte load);
+//  * online softmax in base 2 on the S^T fragments (max/sum over the 16
+//    tokens a lane holds, then 2 cross-lane steps);
+//  * the 4 waves' (m, l, O) are combined in LDS; with one split the result
+//    is written directly, otherwise fp32 partials go to the workspace and a
+//    merge kernel combines the splits.
+#include "common.h"
+
+namespace sa {
+
+// ---------------------------------------------------------------- bf16 / MFMA
+template <int D, int P, bool TIERED>
+__global__ __launch_bounds__(256, 2) void decode_bf16_kernel(DecodeParams p) {
+  constexpr int KSTEPS = D / 32;
+  constexpr int DTILES = D / 16;
+  constexpr int E = 64 / P;            // list entries per 64-token chunk
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int col = lane & 15, kg = lane >> 4;
+
+  int u = blockIdx.x;
+  const int split = u % p.splits;
+  u /= p.splits;
+  const int s = u % p.n_sel;
+  const int b = u / p.n_sel;
+  const int g = p.per_q ? s / p.G : s;
+  const int R = p.per_q ? p.T : p.T * p.G;
+  const int sel = b * p.n_sel + s;
+  const int count = p.counts[sel];
+  const int32_t* list = p.lists + (size_t)sel * p.list_stride;
+  const int cc = TIERED ? p.ccounts[sel] : count;
+  const int sbase = count / p.splits, sextra = count % p.splits;
+  const int beg = split * sbase + min(split, sextra);
+  const int len = sbase + (split < sextra ? 1 : 0);
+  const int end = beg + len;
+  const int seq_len = p.seq_lens[b];
+
+  // query row of this lane's MFMA column
+  const bool row_ok = col < R;
+  int t_row = 0, h_row = 0;
+  if (row_ok) {
+    if (p.per_q) { t_row = col; h_row = s; }
+    else { t_row = col / p.G; h_row = s * p.G + col % p.G; }
+  }
+  const uint16_t* qp = reinterpret_cast<const uint16_t*>(p.q);
+  bf16x8 qreg[KSTEPS];
+#pragma unroll
+  for (int kk = 0; kk < KSTEPS; ++kk) {
+    if (row_ok)
+      qreg[kk] = *reinterpret_cast<const bf16x8*>(
+          qp + (((size_t)b * p.T + t_row) * p.Hq + h_row) * D + 8 * kg + 32 * kk);
+    else
+      qreg[kk] = bf16x8{};
+  }
+
+  f32x4 oacc[DTILES];
+#pragma unroll
+  for (int i = 0; i < DTILES; ++i) oacc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY, l_run = 0.f;
+
+  const uint16_t* kpool = reinterpret_cast<const uint16_t*>(p.k_pool);
+  const uint16_t* vpool = reinterpret_cast<const uint16_t*>(p.v_pool);
+  const int nchunks = (len + E - 1) / E;
+
+  for (int c = wave; c < nchunks; c += 4) {
+    const int e0 = beg + c * E;
+    int phys[E], nval[E];
+    bool act[E];
+#pragma unroll
+    for (int j = 0; j < E; ++j) {
+      const int e = e0 + j;
+      if (e < end) {
+        const int lp = list[e];
+        phys[j] = p.block_table[(size_t)b * p.max_pages + lp];
+        nval[j] = page_valid(seq_len, lp, P);
+        bool a = true;
+        if (TIERED && e >= cc) {
+          const uint32_t w = p.amask[((size_t)b * p.max_pages + lp) * p.mask_words + (h_row >> 5)];
+          a = row_ok && ((w >> (h_row & 31)) & 1u);
+        }
+        act[j] = a;
+      } else {
+        phys[j] = 0;
+        nval[j] = 0;
+        act[j] = false;
+      }
+    }
+
+    // K: A operand of tile j4, row m = col holds token
+    //   tau = 32*(j4/2) + 8*(m/4) + 4*(j4%2) + m%4
+    bf16x8 kreg[4][KSTEPS];
+#pragma unroll
+    for (int j4 = 0; j4 < 4; ++j4) {
+      const int tau = 32 * (j4 >> 1) + 8 * (col >> 2) + 4 * (j4 & 1) + (col & 3);
+      const int ent = tau / P, r = tau % P;
+      const uint16_t* kb = kpool + (((size_t)phys[ent] * p.Hkv + g) * P + r) * D + 8 * kg;
+      const bool ld = nval[ent] > 0;
+#pragma unroll
+      for (int kk = 0; kk < KSTEPS; ++kk)
+        kreg[j4][kk] = ld ? *reinterpret_cast<const bf16x8*>(kb + 32 * kk) : bf16x8{};
+    }
+    // V^T: A operand of PV tile dt, k-step kp: dim 16*dt + col, tokens 32*kp + 8*kg + 0..7
+    bf16x8 vreg[DTILES][2];
+#pragma unroll
+    for (int kp = 0; kp < 2; ++kp) {
+      const int t0 = 32 * kp + 8 * kg;
+      const int ent = t0 / P, r0 = t0 % P;
+      const uint16_t* vb = vpool + (((size_t)phys[ent] * p.Hkv + g) * D + col) * P + r0;
+      const bool ld = nval[ent] > 0;
+#pragma unroll
+      for (int dt = 0; dt < DTILES; ++dt)
+        vreg[dt][kp] = ld ? *reinterpret_cast<const bf16x8*>(vb + (size_t)16 * dt * P) : bf16x8{};
+    }
+
+    f32x4 sacc[4];
+#pragma unroll
+    for (int j4 = 0; j4 < 4; ++j4) {
+      sacc[j4] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kk = 0; kk < KSTEPS; ++kk)
+        sacc[j4] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kreg[j4][kk], qreg[kk], sacc[j4], 0, 0, 0);
+    }
+
+    // lane holds S^T[token 32*(j4/2) + 8*kg + 4*(j4%2) + i][row col]
+    float z[4][4];
+    float mloc = -INFINITY;
+#pragma unroll
+    for (int j4 = 0; j4 < 4; ++j4) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int tau = 32 * (j4 >> 1) + 8 * kg + 4 * (j4 & 1) + i;
+        const int ent = tau / P, r = tau % P;
+        const bool ok = (r < nval[ent]) && act[ent];
+        z[j4][i] = ok ? sacc[j4][i] * p.scale_log2 : -INFINITY;
+        mloc = fmaxf(mloc, z[j4][i]);
+      }
+    }
+    mloc = fmaxf(mloc, __shfl_xor(mloc, 16, 64));
+    mloc = fmaxf(mloc, __shfl_xor(mloc, 32, 64));
+    const float m_new = fmaxf(m_run, mloc);
+    const bool none = m_new == -INFINITY;
+    const float alpha = none ? 1.f : exp2f(m_run - m_new);
+    const float msub = none ? 0.f : m_new;
+    float psum = 0.f;
+    bf16x8 pb[2];
+#pragma unroll
+    for (int j4 = 0; j4 < 4; ++j4) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float pv = exp2f(z[j4][i] - msub);
+        psum += pv;
+        pb[j4 >> 1][4 * (j4 & 1) + i] = (__bf16)pv;
+      }
+    }
+    l_run = l_run * alpha + psum;
+#pragma unroll
+    for (int dt = 0; dt < DTILES; ++dt) {
+      oacc[dt][0] *= alpha; oacc[dt][1] *= alpha; oacc[dt][2] *= alpha; oacc[dt][3] *= alpha;
+    }
+    m_run = m_new;
+#pragma unroll
+    for (int kp = 0; kp < 2; ++kp)
+#pragma unroll
+      for (int dt = 0; dt < DTILES; ++dt)
+        oacc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vreg[dt][kp], pb[kp], oacc[dt], 0, 0, 0);
+  }
+
+  // combine the 4 waves
+  l_run += __shfl_xor(l_run, 16, 64);
+  l_run += __shfl_xor(l_run, 32, 64);
+  __shared__ float sm_m[4][16], sm_l[4][16];
+  __shared__ float sm_o[4][16][D + 4];
+  if (kg == 0) { sm_m[wave][col] = m_run; sm_l[wave][col] = l_run; }
+#pragma unroll
+  for (int dt = 0; dt < DTILES; ++dt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sm_o[wave][col][16 * dt + 4 * kg + i] = oacc[dt][i];
+  __syncthreads();
+  for (int idx = threadIdx.x; idx < R * D; idx += 256) {
+    const int r = idx / D, d = idx % D;
+    float M = fmaxf(fmaxf(sm_m[0][r], sm_m[1][r]), fmaxf(sm_m[2][r], sm_m[3][r]));
+    float o = 0.f, lse = -INFINITY;
+    if (M != -INFINITY) {
+      float L = 0.f, acc = 0.f;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const float sc = exp2f(sm_m[w][r] - M);
+        L += sc * sm_l[w][r];
+        acc += sc * sm_o[w][r][d];
+      }
+      o = acc / L;
+      lse = (M + log2f(L)) * kLn2;
+    }
+    int t, h;
+    if (p.per_q) { t = r; h = s; } else { t = r / p.G; h = s * p.G + r % p.G; }
+    const size_t orow = ((size_t)b * p.T + t) * p.Hq + h;
+    if (p.splits == 1) {
+      reinterpret_cast<uint16_t*>(p.out)[orow * D + d] = f32_to_bf16_bits(o);
+      if (d == 0 && p.out_lse) p.out_lse[orow] = lse;
+    } else {
+      p.part_o[(orow * p.splits + split) * D + d] = o;
+      if (d == 0) p.part_lse[orow * p.splits + split] = lse;
+    }
+  }
+}
+
+// ------------------------------------------------------------------- fp32
+// Plain VALU kernel for fp32 caches: one wave per query row, one lane per
+// token of a page for the logits, one lane per output dim for PV.
+template <int D>
+__global__ __launch_bounds__(256) void decode_f32_kernel(DecodeParams p) {
+  constexpr int DPL = D / 64;          // output dims per lane
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int u = blockIdx.x;
+  const int split = u % p.splits;
+  u /= p.splits;
+  const int s = u % p.n_sel;
+  const int b = u / p.n_sel;
+  const int g = p.per_q ? s / p.G : s;
+  const int R = p.per_q ? p.T : p.T * p.G;
+  const int sel = b * p.n_sel + s;
+  const int count = p.counts[sel];
+  const int32_t* list = p.lists + (size_t)sel * p.list_stride;
+  const int cc = p.ccounts ? p.ccounts[sel] : count;
+  const int sbase = count / p.splits, sextra = count % p.splits;
+  const int beg = split * sbase + min(split, sextra);
+  const int end = beg + sbase + (split < sextra ? 1 : 0);
+  const int seq_len = p.seq_lens[b];
+  const int P = p.P;
+  const float* kpool = reinterpret_cast<const float*>(p.k_pool);
+  const float* vpool = reinterpret_cast<const float*>(p.v_pool);
+
+  for (int r = wave; r < R; r += 4) {
+    int t, h;
+    if (p.per_q) { t = r; h = s; } else { t = r / p.G; h = s * p.G + r % p.G; }
+    const size_t orow = ((size_t)b * p.T + t) * p.Hq + h;
+    const float* qrow = reinterpret_cast<const float*>(p.q) + orow * D;   // broadcast reads
+    float m_run = -INFINITY, l_run = 0.f;
+    float o[DPL];
+#pragma unroll
+    for (int i = 0; i < DPL; ++i) o[i] = 0.f;
+    for (int e = beg; e < end; ++e) {
+      const int lp = list[e];
+      const int phys = p.block_table[(size_t)b * p.max_pages + lp];
+      const int nv = page_valid(seq_len, lp, P);
+      bool act = true;
+      if (p.ccounts && e >= cc) {
+        const uint32_t w = p.amask[((size_t)b * p.max_pages + lp) * p.mask_words + (h >> 5)];
+        act = (w >> (h & 31)) & 1u;
+      }
+      if (!act || nv == 0) continue;
+      float z = -INFINITY;
+      if (lane < nv) {
+        const float* krow = kpool + (((size_t)phys * p.Hkv + g) * P + lane) * D;
+        float acc = 0.f;
+        for (int d = 0; d < D; d += 4) {
+          const f32x4 kv = *reinterpret_cast<const f32x4*>(krow + d);
+          const f32x4 qv = *reinterpret_cast<const f32x4*>(qrow + d);
+          acc += kv[0] * qv[0] + kv[1] * qv[1] + kv[2] * qv[2] + kv[3] * qv[3];
+        }
+        z = acc * p.scale_log2;
+      }
+      const float mc = wave_max(z);
+      const float m_new = fmaxf(m_run, mc);
+      const float alpha = exp2f(m_run - m_new);
+      const float pz = lane < nv ? exp2f(z - m_new) : 0.f;
+      l_run = l_run * alpha + wave_sum(pz);
+#pragma unroll
+      for (int i = 0; i < DPL; ++i) {
+        const int d = lane + 64 * i;
+        const float* vrow = vpool + (((size_t)phys * p.Hkv + g) * D + d) * P;
+        float acc = o[i] * alpha;
+        for (int j = 0; j < nv; ++j) acc += __shfl(pz, j, 64) * vrow[j];
+        o[i] = acc;
+      }
+      m_run = m_new;
+    }
+    const bool empty = m_run == -INFINITY;
+    const float lse = empty ? -INFINITY : (m_run + log2f(l_run)) * kLn2;
+#pragma unroll
+    for (int i = 0; i < DPL; ++i) {
+      const int d = lane + 64 * i;
+      const float val = empty ? 0.f : o[i] / l_run;
+      if (p.splits == 1) reinterpret_cast<float*>(p.out)[orow * D + d] = val;
+      else p.part_o[(orow * p.splits + split) * D + d] = val;
+    }
+    if (lane == 0) {
+      if (p.splits == 1) { if (p.out_lse) p.out_lse[orow] = lse; }
+      else p.part_lse[orow * p.splits + split] = lse;
+    }
+  }
+}
+
+// ------------------------------------------------------------------- merge
+// One wave per query row: o = sum_s w_s o_s / sum_s w_s, w_s = exp(lse_s - max).
+__global__ __launch_bounds__(256) void lse_merge_kernel(MergeParams p) {
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= p.rows) return;
+  const float* pl = p.part_lse + (size_t)row * p.splits;
+  const float mine = lane < p.splits ? pl[lane] : -INFINITY;
+  const float M = wave_max(mine);
+  float w = 0.f;
+  if (M != -INFINITY && lane < p.splits) w = __expf(mine - M);
+  const float L = wave_sum(w);
+  const float* po = p.part_o + (size_t)row * p.splits * p.d_v;
+  for (int d = lane; d < p.d_v; d += 64) {
+    float acc = 0.f;
+    for (int sidx = 0; sidx < p.splits; ++sidx) {
+      const float ws = __shfl(w, sidx, 64);
+      if (ws != 0.f) acc += ws * po[(size_t)sidx * p.d_v + d];
+    }
+    const float o = M == -INFINITY ? 0.f : acc / L;
+    if (p.out_fp32) reinterpret_cast<float*>(p.out)[(size_t)row * p.d_v + d] = o;
+    else reinterpret_cast<uint16_t*>(p.out)[(size_t)row * p.d_v + d] = f32_to_bf16_bits(o);
+  }
+  if (lane == 0 && p.out_lse) p.out_lse[row] = M == -INFINITY ? -INFINITY : M + __logf(L);
+}
+
+hipError_t launch_merge(const MergeParams& p, hipStream_t s) {
+  hipLaunchKernelGGL(lse_merge_kernel, dim3((p.rows + 3) / 4), dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_decode(const DecodeParams& p, int bf16, hipStream_t s) {
+  const dim3 grid(p.B * p.n_sel * p.splits), block(256);
+  const bool tiered = p.ccounts != nullptr;
+  if (!bf16) {
+    if (p.d_qk == 64) hipLaunchKernelGGL(decode_f32_kernel<64>, grid, block, 0, s, p);
+    else hipLaunchKernelGGL(decode_f32_kernel<128>, grid, block, 0, s, p);
+    return hipGetLastError();
+  }
+#define SA_DECODE_LAUNCH(D_, P_)                                                        \
+  do {                                                                                  \
+    if (tiered) hipLaunchKernelGGL((decode_bf16_kernel<D_, P_, true>), grid, block, 0, s, p); \
+    else hipLaunchKernelGGL((decode_bf16_kernel<D_, P_, false>), grid, block, 0, s, p);      \
+  } while (0)
+  if (p.d_qk == 64 && p.P == 16) SA_DECODE_LAUNCH(64, 16);
+  else if (p.d_qk == 64 && p.P == 64) SA_DECODE_LAUNCH(64, 64);
+  else if (p.d_qk == 128 && p.P == 16) SA_DECODE_LAUNCH(128, 16);
+  else SA_DECODE_LAUNCH(128, 64);
+#undef SA_DECODE_LAUNCH
+  return hipGetLastError();
+}
+
+}  // namespace sa

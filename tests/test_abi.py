@@ -1,0 +1,168 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+include/sparse_attn.h declares, sizes workspaces, and rejects bad arguments
+on the host before anything is launched (no compute call is made)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import sparse_attention_long_page_amd as S
+from sparse_attention_long_page_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sparse_attn.h")
+
+
+def header_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(sa_[a-z_]+)\s*\(", src)))
+
+
+def test_header_declares_the_boundary():
+    fns = header_functions()
+    for name in ("sa_select_pages", "sa_sparse_decode", "sa_block_sparse_prefill", "sa_page_summary"):
+        assert name in fns
+    assert set(fns) == set(B.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = S.load_library()
+    for name in header_functions():
+        assert hasattr(lib, name), name
+        assert ctypes.cast(getattr(lib, name), ctypes.c_void_p).value
+
+
+def test_status_strings_and_version():
+    lib = S.load_library()
+    assert lib.sa_status_string(0) == b"SA_OK"
+    assert lib.sa_status_string(3) == b"SA_ERR_WORKSPACE_TOO_SMALL"
+    assert S.sa_version() >= 100
+
+
+FAKE = 0x10000   # never dereferenced on the host
+
+
+def kv(**over):
+    d = dict(k_pool=FAKE, v_pool=FAKE, block_table=FAKE, seq_lens=FAKE, n_phys_pages=64, n_kv_heads=2,
+             page_size=64, d_qk=128, d_v=128, max_pages=32, dtype=B.SA_DTYPE_BF16)
+    d.update(over)
+    return B.sa_paged_kv(**d)
+
+
+def select(kvd, **over):
+    a = dict(batch=2, q=FAKE, q_tokens=1, n_q_heads=8, page_summary=FAKE, scores=None, scores_stride=0,
+             mode=B.SA_SEL_PER_KV_HEAD, sink=1, window=2, top_k=4, critical_k=0, lists=FAKE, stride=7,
+             counts=FAKE, ccounts=None, scores_out=None, ws=FAKE, ws_bytes=1 << 30)
+    a.update(over)
+    lib = S.load_library()
+    return lib.sa_select_pages(ctypes.byref(kvd), a["batch"], a["q"], a["q_tokens"], a["n_q_heads"],
+                               a["page_summary"], a["scores"], a["scores_stride"], a["mode"], a["sink"],
+                               a["window"], a["top_k"], a["critical_k"], a["lists"], a["stride"], a["counts"],
+                               a["ccounts"], a["scores_out"], a["ws"], a["ws_bytes"], None)
+
+
+def decode(kvd, **over):
+    a = dict(batch=2, q=FAKE, q_tokens=1, n_q_heads=8, lists=FAKE, counts=FAKE, stride=7,
+             mode=B.SA_SEL_PER_KV_HEAD, ccounts=None, amask=None, scale=0.1, splits=1, out=FAKE, lse=None,
+             ws=FAKE, ws_bytes=1 << 30)
+    a.update(over)
+    lib = S.load_library()
+    return lib.sa_sparse_decode(ctypes.byref(kvd), a["batch"], a["q"], a["q_tokens"], a["n_q_heads"], a["lists"],
+                                a["counts"], a["stride"], a["mode"], a["ccounts"], a["amask"], a["scale"],
+                                a["splits"], a["out"], a["lse"], a["ws"], a["ws_bytes"], None)
+
+
+def prefill(kvd, **over):
+    a = dict(seq=0, q=FAKE, q_len=128, q_start=64, n_q_heads=8, mask=FAKE, block_q=64, nkb=3, table=FAKE,
+             counts=FAKE, scale=0.1, out=FAKE, lse=None, ws=None, ws_bytes=0)
+    a.update(over)
+    lib = S.load_library()
+    return lib.sa_block_sparse_prefill(ctypes.byref(kvd), a["seq"], a["q"], a["q_len"], a["q_start"],
+                                       a["n_q_heads"], a["mask"], a["block_q"], a["nkb"], a["table"], a["counts"],
+                                       a["scale"], a["out"], a["lse"], a["ws"], a["ws_bytes"], None)
+
+
+INV, UNS, WS = B.SA_ERR_INVALID_ARGUMENT, B.SA_ERR_UNSUPPORTED, B.SA_ERR_WORKSPACE_TOO_SMALL
+
+SELECT_CASES = [
+    ("null kv block_table", dict(kv=dict(block_table=None)), {}, INV),
+    ("page size 32", dict(kv=dict(page_size=32)), {}, UNS),
+    ("d 96", dict(kv=dict(d_qk=96, d_v=96)), {}, UNS),
+    ("latent with d 128", dict(kv=dict(v_pool=None)), {}, UNS),
+    ("bad dtype", dict(kv=dict(dtype=7)), {}, INV),
+    ("heads not multiple", {}, dict(n_q_heads=7), INV),
+    ("negative top_k", {}, dict(top_k=-1), INV),
+    ("negative sink", {}, dict(sink=-2), INV),
+    ("negative critical_k", {}, dict(ccounts=FAKE, critical_k=-1), INV),
+    ("short list stride", {}, dict(stride=6), INV),
+    ("missing lists", {}, dict(lists=None), INV),
+    ("no q without scores", {}, dict(q=None), INV),
+    ("short scores stride", {}, dict(scores=FAKE, scores_stride=31), INV),
+    ("bad mode", {}, dict(mode=5), INV),
+    ("too many pages", dict(kv=dict(max_pages=20000)), {}, UNS),
+    ("workspace too small", {}, dict(ws_bytes=16), WS),
+]
+
+
+@pytest.mark.parametrize("name,kvo,argo,status", SELECT_CASES, ids=[c[0] for c in SELECT_CASES])
+def test_select_rejects(name, kvo, argo, status):
+    st = select(kv(**kvo.get("kv", {})), **argo)
+    assert st == status
+    assert S.load_library().sa_last_error_message()
+
+
+DECODE_CASES = [
+    ("rows exceed tile", {}, dict(q_tokens=5), UNS),
+    ("splits out of range", {}, dict(splits=65), INV),
+    ("negative splits", {}, dict(splits=-1), INV),
+    ("tier args unpaired", {}, dict(ccounts=FAKE), INV),
+    ("nan scale", {}, dict(scale=float("nan")), INV),
+    ("missing out", {}, dict(out=None), INV),
+    ("zero stride", {}, dict(stride=0), INV),
+    ("latent with 2 kv heads", dict(kv=dict(v_pool=None, d_qk=576, d_v=512)), {}, UNS),
+    ("latent heads not multiple of 16", dict(kv=dict(v_pool=None, d_qk=576, d_v=512, n_kv_heads=1)),
+     dict(n_q_heads=8), UNS),
+    ("latent too many rows", dict(kv=dict(v_pool=None, d_qk=576, d_v=512, n_kv_heads=1)),
+     dict(n_q_heads=128, q_tokens=3), UNS),
+    ("workspace too small", {}, dict(splits=4, ws_bytes=100), WS),
+    ("no workspace", {}, dict(splits=4, ws=None, ws_bytes=0), WS),
+]
+
+
+@pytest.mark.parametrize("name,kvo,argo,status", DECODE_CASES, ids=[c[0] for c in DECODE_CASES])
+def test_decode_rejects(name, kvo, argo, status):
+    st = decode(kv(**kvo.get("kv", {})), **argo)
+    assert st == status, S.load_library().sa_last_error_message()
+    assert S.load_library().sa_last_error_message()
+
+
+PREFILL_CASES = [
+    ("fp32", dict(kv=dict(dtype=B.SA_DTYPE_FP32)), {}, UNS),
+    ("page 16", dict(kv=dict(page_size=16)), {}, UNS),
+    ("too few kv blocks", {}, dict(nkb=2), INV),
+    ("kv blocks past table", {}, dict(nkb=40), INV),
+    ("negative start", {}, dict(q_start=-1), INV),
+    ("zero block_q", {}, dict(block_q=0), INV),
+    ("null mask", {}, dict(mask=None), INV),
+    ("group too large", dict(kv=dict(n_kv_heads=1)), dict(n_q_heads=16), UNS),
+]
+
+
+@pytest.mark.parametrize("name,kvo,argo,status", PREFILL_CASES, ids=[c[0] for c in PREFILL_CASES])
+def test_prefill_rejects(name, kvo, argo, status):
+    st = prefill(kv(**kvo.get("kv", {})), **argo)
+    assert st == status, S.load_library().sa_last_error_message()
+
+
+def test_workspace_sizes():
+    lib = S.load_library()
+    # select: fp32 scores [B][n_sel][max_pages] + fp64 pooled queries, 256-aligned pieces
+    assert lib.sa_select_pages_workspace_size(2, 3, 100) == 2560 + 27648
+    k = kv()
+    # decode with an explicit split count: fp32 partials o [rows][splits][d_v] + lse [rows][splits]
+    rows = 2 * 1 * 8
+    expect = ((rows * 4 * 128 * 4 + 255) // 256) * 256 + ((rows * 4 * 4 + 255) // 256) * 256
+    assert lib.sa_sparse_decode_workspace_size(ctypes.byref(k), 2, 1, 8, 7, 0, 4) == expect
+    assert lib.sa_sparse_decode_workspace_size(ctypes.byref(k), 2, 1, 8, 7, 0, 1) == 0

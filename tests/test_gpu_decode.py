@@ -1,0 +1,243 @@
+"""HIP decode path (page summary, router scores, selection, split-K decode,
+LSE merge) against the CPU oracle, through the C ABI."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle.sparse_attn_oracle as O
+import sparse_attention_long_page_amd as S
+import workloads as W
+from _parity import check_page_lists, compare_outputs, np64, npi, sub_pool
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+MODE = {"per_kv_head": S.SA_SEL_PER_KV_HEAD, "per_q_head": S.SA_SEL_PER_Q_HEAD}
+DECODE_SMALL = [n for n, w in W.SMALL.items() if isinstance(w, W.DecodeWorkload) and not w.latent]
+
+
+def gpu_inputs(cpu):
+    return {k: (v.to(DEV) if v is not None else None) for k, v in cpu.items()}
+
+
+def make_kv(inp, wl):
+    return S.PagedKV(inp["k_pool"], inp["v_pool"], inp["block_table"], inp["seq_lens"], d_v=wl.d_v)
+
+
+def oracle_chain(cpu, wl):
+    """Oracle mean keys, scores and lists from the CPU copy of the inputs."""
+    bt, lens = npi(cpu["block_table"]), npi(cpu["seq_lens"])
+    npg = [O.n_pages_of(L, wl.page_size) for L in lens]
+    mu = scores = None
+    if wl.scores == "gumbel":
+        scores = npi(cpu["scores"])
+    else:
+        mu = O.page_summary(np64(cpu["k_pool"]), bt, lens, wl.page_size)
+        scores = O.page_scores(np64(cpu["q"]), mu, bt, lens, wl.page_size, wl.n_kv_heads, wl.mode)
+    lists, counts, cc = O.select_pages(scores, npg, wl.sink_pages, wl.window_pages, wl.top_k, wl.critical_k)
+    return mu, scores, lists, counts, cc, npg
+
+
+def gpu_select(inp, wl, kv, mu=None):
+    if wl.scores == "gumbel":
+        return S.sa_select_pages(kv, n_q_heads=wl.n_q_heads, mode=MODE[wl.mode], sink_pages=wl.sink_pages,
+                                 window_pages=wl.window_pages, top_k=wl.top_k, scores=inp["scores"],
+                                 critical_k=wl.critical_k), None
+    scores_out = torch.empty((wl.batch, wl.n_sel, wl.max_pages), dtype=torch.float32, device=DEV)
+    res = S.sa_select_pages(kv, n_q_heads=wl.n_q_heads, mode=MODE[wl.mode], sink_pages=wl.sink_pages,
+                            window_pages=wl.window_pages, top_k=wl.top_k, q=inp["q"], page_summary=mu,
+                            critical_k=wl.critical_k, scores_out=scores_out)
+    return res, scores_out
+
+
+@pytest.mark.parametrize("name", [n for n in DECODE_SMALL if W.SMALL[n].scores == "summary"])
+def test_page_summary_matches_oracle(name):
+    wl = W.SMALL[name]
+    cpu = W.make_decode_inputs(wl, "cpu", seed=1)
+    inp = gpu_inputs(cpu)
+    mu_gpu = S.sa_page_summary(make_kv(inp, wl))
+    torch.cuda.synchronize()
+    mu_ref = O.page_summary(np64(cpu["k_pool"]), npi(cpu["block_table"]), npi(cpu["seq_lens"]), wl.page_size)
+    got = mu_gpu.cpu().numpy()
+    ref_pages = ~np.isnan(mu_ref[:, 0, 0])
+    assert np.isnan(got[~ref_pages]).all(), "pages outside every sequence must stay untouched"
+    diff = np.abs(got[ref_pages].astype(np.float64) - mu_ref[ref_pages])
+    ulp = np.spacing(np.abs(mu_ref[ref_pages]).astype(np.float32)).astype(np.float64)
+    assert (diff <= ulp).all(), f"max diff {diff.max()}"
+    # incremental update of the last page only touches those pages
+    mu2 = torch.full_like(mu_gpu, float("nan"))
+    S.sa_page_summary(make_kv(inp, wl), last_pages=1, out=mu2)
+    torch.cuda.synchronize()
+    m2 = mu2.cpu().numpy()
+    bt, lens = npi(cpu["block_table"]), npi(cpu["seq_lens"])
+    last = {int(bt[b, O.n_pages_of(L, wl.page_size) - 1]) for b, L in enumerate(lens)}
+    touched = {int(p) for p in np.flatnonzero(~np.isnan(m2[:, 0, 0]))}
+    assert touched == last
+    for p in last:
+        assert np.array_equal(m2[p], got[p])
+
+
+@pytest.mark.parametrize("name", DECODE_SMALL)
+def test_select_matches_oracle(name):
+    wl = W.SMALL[name]
+    cpu = W.make_decode_inputs(wl, "cpu", seed=2)
+    inp = gpu_inputs(cpu)
+    kv = make_kv(inp, wl)
+    mu = S.sa_page_summary(kv) if wl.scores == "summary" else None
+    (lists, counts, cc), scores_out = gpu_select(inp, wl, kv, mu)
+    torch.cuda.synchronize()
+    _, o_scores, o_lists, o_counts, o_cc, npg = oracle_chain(cpu, wl)
+    if scores_out is not None:
+        g = scores_out.cpu().numpy()
+        assert np.array_equal(np.isnan(g), np.isnan(o_scores))
+        fin = ~np.isnan(g)
+        rel = np.abs(g[fin].astype(np.float64) - o_scores[fin]) / np.maximum(1.0, np.abs(o_scores[fin]))
+        assert rel.max() <= 1e-6, rel.max()
+    rep = check_page_lists(npi(lists), npi(counts), None if cc is None else npi(cc), o_scores, npg,
+                           wl.sink_pages, wl.window_pages, wl.top_k, wl.critical_k)
+    assert not rep.failures, rep.failures[:5]
+    assert rep.exact + rep.band_events == rep.units
+
+
+@pytest.mark.parametrize("name", DECODE_SMALL)
+@pytest.mark.parametrize("splits", [1, 2, 3, 0])
+def test_decode_matches_oracle(name, splits):
+    wl = W.SMALL[name]
+    cpu = W.make_decode_inputs(wl, "cpu", seed=3)
+    inp = gpu_inputs(cpu)
+    kv = make_kv(inp, wl)
+    _, _, o_lists, o_counts, o_cc, _ = oracle_chain(cpu, wl)
+    lists = torch.from_numpy(o_lists).to(DEV)
+    counts = torch.from_numpy(o_counts).to(DEV)
+    out, lse = S.sa_sparse_decode(kv, inp["q"], lists, counts, mode=MODE[wl.mode], sm_scale=wl.sm_scale,
+                                  num_splits=splits)
+    torch.cuda.synchronize()
+    ref_o, ref_l = O.sparse_decode(np64(cpu["q"]), np64(cpu["k_pool"]), np64(cpu["v_pool"]),
+                                   npi(cpu["block_table"]), npi(cpu["seq_lens"]), wl.page_size, o_lists,
+                                   o_counts, wl.n_kv_heads, wl.mode, wl.sm_scale)
+    compare_outputs(out, lse, ref_o, ref_l, fp32=wl.dtype == "fp32")
+
+
+@pytest.mark.parametrize("name", ["llama3_decode_small", "token_head_decode_small"])
+def test_tiered_small_heads_matches_oracle(name):
+    """Critical/Ambient tiers on the d-128 kernel: Ambient pages only for masked heads."""
+    base = W.SMALL[name]
+    wl = base.replace(critical_k=2, ambient_heads=max(1, base.n_q_heads // 3))
+    cpu = W.make_decode_inputs(wl, "cpu", seed=4)
+    inp = gpu_inputs(cpu)
+    kv = make_kv(inp, wl)
+    _, o_scores, o_lists, o_counts, o_cc, npg = oracle_chain(cpu, wl)
+    mu = S.sa_page_summary(kv) if wl.scores == "summary" else None
+    (lists, counts, cc), _ = gpu_select(inp, wl, kv, mu)
+    torch.cuda.synchronize()
+    rep = check_page_lists(npi(lists), npi(counts), npi(cc), o_scores, npg, wl.sink_pages, wl.window_pages,
+                           wl.top_k, wl.critical_k)
+    assert not rep.failures, rep.failures[:5]
+    amask = inp["ambient_mask"]
+    out, lse = S.sa_sparse_decode(kv, inp["q"], torch.from_numpy(o_lists).to(DEV),
+                                  torch.from_numpy(o_counts).to(DEV), mode=MODE[wl.mode], sm_scale=wl.sm_scale,
+                                  critical_counts=torch.from_numpy(o_cc).to(DEV), ambient_head_mask=amask,
+                                  num_splits=2)
+    torch.cuda.synchronize()
+    ref_o, ref_l = O.sparse_decode(np64(cpu["q"]), np64(cpu["k_pool"]), np64(cpu["v_pool"]),
+                                   npi(cpu["block_table"]), npi(cpu["seq_lens"]), wl.page_size, o_lists,
+                                   o_counts, wl.n_kv_heads, wl.mode, wl.sm_scale, o_cc,
+                                   npi(cpu["ambient_mask"]).astype(np.int64) & 0xffffffff)
+    compare_outputs(out, lse, ref_o, ref_l)
+
+
+def test_decode_deterministic_and_pool_permutation_invariant():
+    wl = W.SMALL["llama3_decode_small"]
+    cpu = W.make_decode_inputs(wl, "cpu", seed=5)
+    inp = gpu_inputs(cpu)
+    kv = make_kv(inp, wl)
+    _, _, o_lists, o_counts, _, _ = oracle_chain(cpu, wl)
+    lists, counts = torch.from_numpy(o_lists).to(DEV), torch.from_numpy(o_counts).to(DEV)
+    a = S.sa_sparse_decode(kv, inp["q"], lists, counts, mode=0, sm_scale=wl.sm_scale, num_splits=3)
+    b = S.sa_sparse_decode(kv, inp["q"], lists, counts, mode=0, sm_scale=wl.sm_scale, num_splits=3)
+    torch.cuda.synchronize()
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+    # move every page to another physical slot; same logical content -> same bits
+    n_phys = inp["k_pool"].shape[0]
+    perm = torch.randperm(n_phys, generator=torch.Generator().manual_seed(7)).to(DEV)
+    k2 = torch.empty_like(inp["k_pool"]); k2[perm] = inp["k_pool"]
+    v2 = torch.empty_like(inp["v_pool"]); v2[perm] = inp["v_pool"]
+    bt = inp["block_table"]
+    bt2 = torch.where(bt >= 0, perm[bt.clamp(min=0).long()].to(torch.int32), bt)
+    kv2 = S.PagedKV(k2, v2, bt2.contiguous(), inp["seq_lens"])
+    c = S.sa_sparse_decode(kv2, inp["q"], lists, counts, mode=0, sm_scale=wl.sm_scale, num_splits=3)
+    torch.cuda.synchronize()
+    assert torch.equal(a[0], c[0]) and torch.equal(a[1], c[1])
+
+
+def test_empty_lists_and_streaming_mode():
+    wl = W.SMALL["llama3_decode_small"].replace(top_k=0)
+    cpu = W.make_decode_inputs(wl, "cpu", seed=6)
+    inp = gpu_inputs(cpu)
+    kv = make_kv(inp, wl)
+    mu = S.sa_page_summary(kv)
+    (lists, counts, _), _ = gpu_select(inp, wl, kv, mu)
+    torch.cuda.synchronize()
+    npg = [O.n_pages_of(L, wl.page_size) for L in wl.lengths()]
+    for b in range(wl.batch):
+        exp = O.forced_pages(npg[b], wl.sink_pages, wl.window_pages)
+        for s in range(wl.n_sel):
+            assert npi(lists)[b, s, :npi(counts)[b, s]].tolist() == exp
+    # empty lists: o = 0, lse = -inf
+    zeros = torch.zeros_like(counts)
+    out, lse = S.sa_sparse_decode(kv, inp["q"], lists, zeros, mode=0, sm_scale=wl.sm_scale, num_splits=2)
+    torch.cuda.synchronize()
+    assert (out.float() == 0).all() and torch.isneginf(lse).all()
+
+
+def _full_size_check(wl, seed, n_sample):
+    """Full-size inputs on the GPU; the oracle checks a seeded sample of sequences."""
+    inp = W.make_decode_inputs(wl, DEV, seed=seed)
+    kv = make_kv(inp, wl)
+    mu = S.sa_page_summary(kv) if wl.scores == "summary" else None
+    (lists, counts, cc), scores_out = gpu_select(inp, wl, kv, mu)
+    out, lse = S.sa_sparse_decode(kv, inp["q"], lists, counts, mode=MODE[wl.mode], sm_scale=wl.sm_scale,
+                                  num_splits=wl.num_splits,
+                                  critical_counts=cc, ambient_head_mask=inp["ambient_mask"])
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(seed)
+    picks = sorted(rng.choice(wl.batch, size=min(n_sample, wl.batch), replace=False).tolist())
+    kp, vp, bt, lens = sub_pool(inp, picks)
+    npg = [O.n_pages_of(L, wl.page_size) for L in lens]
+    if wl.scores == "gumbel":
+        o_scores = npi(inp["scores"])[picks]
+    else:
+        o_mu = O.page_summary(kp, bt, lens, wl.page_size)
+        o_scores = O.page_scores(np64(inp["q"])[picks], o_mu, bt, lens, wl.page_size, wl.n_kv_heads, wl.mode)
+    g_lists, g_counts = npi(lists)[picks], npi(counts)[picks]
+    g_cc = None if cc is None else npi(cc)[picks]
+    rep = check_page_lists(g_lists, g_counts, g_cc, o_scores, npg, wl.sink_pages, wl.window_pages, wl.top_k,
+                           wl.critical_k)
+    assert not rep.failures, rep.failures[:5]
+    # attention checked on the oracle's own lists where they equal the GPU's (all units when no band event)
+    o_lists, o_counts, o_cc = O.select_pages(o_scores, npg, wl.sink_pages, wl.window_pages, wl.top_k,
+                                             wl.critical_k)
+    same = np.array([[np.array_equal(g_lists[i, s, :g_counts[i, s]], o_lists[i, s, :o_counts[i, s]])
+                      for s in range(wl.n_sel)] for i in range(len(picks))])
+    amask = None if inp["ambient_mask"] is None else npi(inp["ambient_mask"])[picks].astype(np.int64) & 0xffffffff
+    ref_o, ref_l = O.sparse_decode(np64(inp["q"])[picks], kp, vp, bt, lens, wl.page_size, o_lists, o_counts,
+                                   wl.n_kv_heads, wl.mode, wl.sm_scale, o_cc, amask, d_v=wl.d_v)
+    G = wl.group
+    rows_ok = np.zeros(ref_l.shape, dtype=bool)
+    for i in range(len(picks)):
+        for h in range(wl.n_q_heads):
+            s = h // G if wl.mode == "per_kv_head" else h
+            rows_ok[i, :, h] = same[i, s]
+    assert rows_ok.mean() > 0.9
+    return compare_outputs(out[picks], lse[picks], ref_o, ref_l, rows_mask=rows_ok), rep
+
+
+def test_full_size_llama3_decode_32k_sampled():
+    (mx, mean, lse_err), rep = _full_size_check(W.LLAMA3_DECODE_32K, seed=11, n_sample=4)
+    print(f"max_abs {mx:.3e} mean_abs {mean:.3e} lse {lse_err:.3e} band events {rep.band_events}/{rep.units}")
+
+
+def test_full_size_token_head_decode_128k_sampled():
+    (mx, mean, lse_err), rep = _full_size_check(W.TOKEN_HEAD_DECODE_128K, seed=12, n_sample=2)
+    print(f"max_abs {mx:.3e} mean_abs {mean:.3e} lse {lse_err:.3e} band events {rep.band_events}/{rep.units}")
