@@ -1,5 +1,318 @@
+// Chunked block-sparse prefill: 2D block mask -> GQA-union KV block tables,
+// then causal attention in place over the paged KV (CompactAttention abstract,
+// on the page titled "Causal Attention on CPU: A Cache-Aware and Load-Balanced
+// Scheduling Kernel for Prefill": Q-block union then intra-group union, KV
+// blocks read in place with no compaction; "Universal Attention Engine",
+// "Key Design Decisions" 3: prefill is compute-bound, optimise FLOPs).
+//
+// Union kernel: one workgroup per KV head; each thread ORs one KV-block column
+// over the group's heads and Q-blocks (coalesced byte rows), then an
+// index-ordered workgroup prefix sum writes the ascending table.
+//
+// Attention kernel (bf16, d 128, pages of 64):
+//  * workgroup = (KV head g, tile of 64 query positions); one wave per query
+//    head of the group, so every K/V tile staged in LDS serves all G heads
+//    (GQA packing: 64*G rows per tile);
+//  * workgroup ids are remapped so the tiles of one KV head run on one XCD
+//    and share its L2 while they sweep the same KV blocks;
+//  * per KV block: K (token-major) and V^T (page-transposed) are copied from
+//    the pool into padded LDS rows (conflict-free 16-byte reads), the next
+//    block's copy is in flight in registers while the current one computes;
+//  * S^T = K Q^T and O^T += V^T P^T on v_mfma_f32_16x16x32_bf16 (Q^T resident
+//    in registers, 64 rows per wave), with the token permutation that makes
+//    the S^T fragments the PV operand directly;
+//  * causal and sequence-end masks only on blocks that cross a row's
+//    position; the ascending table stops the sweep past the tile's last row;
+//  * online softmax in base 2 with a lazily moved reference maximum: the
+//    accumulators are rescaled only when a row's maximum grows by more than
+//    2^8 (exact: the final normalisation uses the same reference).
 #include "common.h"
+
 namespace sa {
-hipError_t launch_union(const UnionParams& p, hipStream_t s) { (void)p; (void)s; return hipErrorNotSupported; }
-hipError_t launch_prefill(const PrefillParams& p, hipStream_t s) { (void)p; (void)s; return hipErrorNotSupported; }
+
+// ------------------------------------------------------------------- union
+constexpr int kUnionThreads = 1024;
+
+__global__ __launch_bounds__(kUnionThreads) void union_kernel(UnionParams p) {
+  __shared__ uint32_t wsum[kUnionThreads / 64];
+  const int g = blockIdx.x;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  uint32_t run = 0;
+  int32_t* out = p.table + (size_t)g * p.nkb;
+  for (int base = 0; base < p.nkb; base += kUnionThreads) {
+    const int kb = base + threadIdx.x;
+    uint32_t any = 0;
+    if (kb < p.nkb) {
+      for (int h = g * p.G; h < (g + 1) * p.G && !any; ++h)
+        for (int qb = 0; qb < p.nqb; ++qb)
+          any |= p.mask[((size_t)h * p.nqb + qb) * p.nkb + kb];
+    }
+    const uint32_t f = any ? 1u : 0u;
+    // exclusive prefix over the workgroup in thread (= block index) order
+    uint32_t x = f;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const uint32_t y = __shfl_up(x, o, 64);
+      if (lane >= o) x += y;
+    }
+    if (lane == 63) wsum[wave] = x;
+    __syncthreads();
+    uint32_t before = 0, all = 0;
+    for (int w = 0; w < kUnionThreads / 64; ++w) {
+      const uint32_t t = wsum[w];
+      if (w < wave) before += t;
+      all += t;
+    }
+    __syncthreads();
+    if (f) out[run + before + x - f] = kb;
+    run += all;
+  }
+  if (threadIdx.x == 0) p.counts[g] = (int32_t)run;
 }
+
+hipError_t launch_union(const UnionParams& p, hipStream_t s) {
+  hipLaunchKernelGGL(union_kernel, dim3(p.Hkv), dim3(kUnionThreads), 0, s, p);
+  return hipGetLastError();
+}
+
+// --------------------------------------------------------------- attention
+constexpr int kPD = 128;          // head dim
+constexpr int kPP = 64;           // page (KV block) size
+constexpr int kBQ = 64;           // query positions per tile
+constexpr int kRT = 2;            // 16-row MFMA tiles per wave: 32 query rows
+constexpr int kKRow = kPD + 8;    // padded K row in LDS (bf16 elements): 272 B
+constexpr int kVRow = kPP + 8;    // padded V^T row in LDS: 144 B
+constexpr int kKTile = kPP * kKRow;
+constexpr int kVTile = kPD * kVRow;
+constexpr float kRescaleThreshold = 8.0f;   // log2 units
+
+// HW query heads per workgroup, two waves per head (query rows 0-31 and
+// 32-63 of the tile).  A group larger than HW is split over G/HW workgroups.
+template <int HW>
+__global__ __launch_bounds__(128 * HW) void prefill_kernel(PrefillParams p) {
+  __shared__ __attribute__((aligned(16))) uint16_t sk[2][kKTile];
+  __shared__ __attribute__((aligned(16))) uint16_t sv[2][kVTile];
+  constexpr int nthr = 128 * HW;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int col = lane & 15, kg = lane >> 4;
+
+  const int nwg = gridDim.x, w = blockIdx.x;
+  const int logical = (nwg % 8 == 0) ? (w % 8) * (nwg / 8) + w / 8 : w;
+  const int hsplit = p.G / HW;                       // workgroups per (KV head, tile)
+  const int g = logical / (p.n_qtiles * hsplit);
+  const int rem = logical % (p.n_qtiles * hsplit);
+  const int qt = rem / hsplit;
+  const int h = g * p.G + (rem % hsplit) * HW + (wave >> 1);
+  const int q0 = qt * kBQ;                           // tile's first query
+  const int qw = q0 + 32 * (wave & 1);               // this wave's first query
+  const int rows_valid = min(kBQ, p.q_len - q0);
+  const int seq_len = *p.seq_len;
+  const int pos_hi = p.q_start + q0 + rows_valid - 1;
+  const int wpos_lo = p.q_start + qw;
+  const int count = p.counts[g];
+  const int32_t* table = p.table + (size_t)g * p.nkb;
+  const uint16_t* kpool = reinterpret_cast<const uint16_t*>(p.k_pool);
+  const uint16_t* vpool = reinterpret_cast<const uint16_t*>(p.v_pool);
+  const uint16_t* qp = reinterpret_cast<const uint16_t*>(p.q);
+
+  // Q^T operand: row-tile rt, k-step kk: query qw + 16*rt + col, dims 8*kg + 32*kk .. +8
+  bf16x8 qreg[kRT][4];
+#pragma unroll
+  for (int rt = 0; rt < kRT; ++rt) {
+    const int i = qw + 16 * rt + col;
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk)
+      qreg[rt][kk] = i < p.q_len
+          ? *reinterpret_cast<const bf16x8*>(qp + ((size_t)i * p.Hq + h) * kPD + 8 * kg + 32 * kk)
+          : bf16x8{};
+  }
+
+  f32x4 oacc[8][kRT];
+#pragma unroll
+  for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+    for (int rt = 0; rt < kRT; ++rt) oacc[dt][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_ref[kRT], l_run[kRT];
+#pragma unroll
+  for (int rt = 0; rt < kRT; ++rt) { m_ref[rt] = -INFINITY; l_run[rt] = 0.f; }
+
+  // table entries at or before the tile's last position (the table ascends)
+  int nblk = 0;
+  {
+    int lo = 0, hi = count;
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      if (table[mid] * kPP > pos_hi) hi = mid; else lo = mid + 1;
+    }
+    nblk = lo;
+  }
+
+  // per-thread share of a block copy: 1024 16-byte chunks of K and of V^T
+  constexpr int per_thr = 1024 / nthr;
+  u32x4 stk[per_thr], stv[per_thr];
+  auto fetch = [&](int t) {
+    const int kb = table[t];
+    const int phys = p.bt_row[kb];
+    const uint16_t* kb_base = kpool + ((size_t)phys * p.Hkv + g) * kPP * kPD;
+    const uint16_t* vb_base = vpool + ((size_t)phys * p.Hkv + g) * kPD * kPP;
+#pragma unroll
+    for (int j = 0; j < per_thr; ++j) {
+      const int c = tid + j * nthr;
+      stk[j] = *reinterpret_cast<const u32x4*>(kb_base + (c >> 4) * kPD + (c & 15) * 8);
+      stv[j] = *reinterpret_cast<const u32x4*>(vb_base + (c >> 3) * kPP + (c & 7) * 8);
+    }
+  };
+  auto stash = [&](int stage) {
+#pragma unroll
+    for (int j = 0; j < per_thr; ++j) {
+      const int c = tid + j * nthr;
+      *reinterpret_cast<u32x4*>(&sk[stage][(c >> 4) * kKRow + (c & 15) * 8]) = stk[j];
+      *reinterpret_cast<u32x4*>(&sv[stage][(c >> 3) * kVRow + (c & 7) * 8]) = stv[j];
+    }
+  };
+
+  if (nblk > 0) {
+    fetch(0);
+    stash(0);
+  }
+  __syncthreads();
+
+  for (int t = 0; t < nblk; ++t) {
+    const int stage = t & 1;
+    const int kb = table[t];
+    const bool more = t + 1 < nblk;
+    if (more) fetch(t + 1);
+
+    const uint16_t* K = sk[stage];
+    const uint16_t* V = sv[stage];
+    const int tok0 = kb * kPP;
+    // blocks entirely past this wave's rows contribute nothing (the tile's
+    // other wave may still need them)
+    if (tok0 <= p.q_start + min(qw + 31, p.q_len - 1)) {
+      // S^T = K Q^T
+      f32x4 sacc[4][kRT];
+#pragma unroll
+      for (int j4 = 0; j4 < 4; ++j4)
+#pragma unroll
+        for (int rt = 0; rt < kRT; ++rt) sacc[j4][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int j4 = 0; j4 < 4; ++j4) {
+        const int tau = 32 * (j4 >> 1) + 8 * (col >> 2) + 4 * (j4 & 1) + (col & 3);
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+          const bf16x8 a = *reinterpret_cast<const bf16x8*>(K + tau * kKRow + 8 * kg + 32 * kk);
+#pragma unroll
+          for (int rt = 0; rt < kRT; ++rt)
+            sacc[j4][rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qreg[rt][kk], sacc[j4][rt], 0, 0, 0);
+        }
+      }
+
+      // softmax (lane: row 16*rt + col, tokens 32*(j4/2) + 8*kg + 4*(j4%2) + i)
+      const bool full = (tok0 + kPP - 1 <= wpos_lo) && (tok0 + kPP <= seq_len);
+      bf16x8 pb[kRT][2];
+      float alpha[kRT];
+      bool need_rescale = false;
+#pragma unroll
+      for (int rt = 0; rt < kRT; ++rt) {
+        const int row_pos = wpos_lo + 16 * rt + col;
+        float mloc = -INFINITY;
+#pragma unroll
+        for (int j4 = 0; j4 < 4; ++j4)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            float z = sacc[j4][rt][i] * p.scale_log2;
+            if (!full) {
+              const int j = tok0 + 32 * (j4 >> 1) + 8 * kg + 4 * (j4 & 1) + i;
+              if (j > row_pos || j >= seq_len) z = -INFINITY;
+            }
+            sacc[j4][rt][i] = z;
+            mloc = fmaxf(mloc, z);
+          }
+        mloc = fmaxf(mloc, __shfl_xor(mloc, 16, 64));
+        mloc = fmaxf(mloc, __shfl_xor(mloc, 32, 64));
+        // move the reference only when the row maximum outgrows it
+        float mref = m_ref[rt];
+        alpha[rt] = 1.f;
+        if (mloc > mref + kRescaleThreshold || (mref == -INFINITY && mloc != -INFINITY)) {
+          alpha[rt] = mref == -INFINITY ? 0.f : exp2f(mref - mloc);
+          mref = mloc;
+          need_rescale = true;
+        }
+        m_ref[rt] = mref;
+        const float msub = mref == -INFINITY ? 0.f : mref;
+        float psum = 0.f;
+#pragma unroll
+        for (int j4 = 0; j4 < 4; ++j4)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float pv = exp2f(sacc[j4][rt][i] - msub);
+            psum += pv;
+            pb[rt][j4 >> 1][4 * (j4 & 1) + i] = (__bf16)pv;
+          }
+        l_run[rt] = l_run[rt] * alpha[rt] + psum;
+      }
+      if (__any(need_rescale)) {
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+          for (int rt = 0; rt < kRT; ++rt) {
+            oacc[dt][rt][0] *= alpha[rt]; oacc[dt][rt][1] *= alpha[rt];
+            oacc[dt][rt][2] *= alpha[rt]; oacc[dt][rt][3] *= alpha[rt];
+          }
+      }
+
+      // O^T += V^T P^T
+#pragma unroll
+      for (int kp = 0; kp < 2; ++kp)
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt) {
+          const bf16x8 a = *reinterpret_cast<const bf16x8*>(V + (16 * dt + col) * kVRow + 32 * kp + 8 * kg);
+#pragma unroll
+          for (int rt = 0; rt < kRT; ++rt)
+            oacc[dt][rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb[rt][kp], oacc[dt][rt], 0, 0, 0);
+        }
+    }
+
+    if (more) stash(stage ^ 1);
+    __syncthreads();
+  }
+
+  // epilogue: O = O^T / l per row
+  uint16_t* out = reinterpret_cast<uint16_t*>(p.out);
+#pragma unroll
+  for (int rt = 0; rt < kRT; ++rt) {
+    float l = l_run[rt];
+    l += __shfl_xor(l, 16, 64);
+    l += __shfl_xor(l, 32, 64);
+    const int i = qw + 16 * rt + col;
+    if (i >= p.q_len) continue;
+    const bool empty = m_ref[rt] == -INFINITY;
+    const float inv = empty ? 0.f : 1.f / l;
+    const size_t orow = (size_t)i * p.Hq + h;
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) {
+      uint16_t v4[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v4[e] = f32_to_bf16_bits(oacc[dt][rt][e] * inv);
+      uint2 pk;
+      pk.x = (uint32_t)v4[0] | ((uint32_t)v4[1] << 16);
+      pk.y = (uint32_t)v4[2] | ((uint32_t)v4[3] << 16);
+      *reinterpret_cast<uint2*>(out + orow * kPD + 16 * dt + 4 * kg) = pk;
+    }
+    if (kg == 0 && p.out_lse) p.out_lse[orow] = empty ? -INFINITY : (m_ref[rt] + log2f(l)) * kLn2;
+  }
+}
+
+hipError_t launch_prefill(const PrefillParams& p0, hipStream_t s) {
+  PrefillParams p = p0;
+  p.n_qtiles = (p.q_len + kBQ - 1) / kBQ;
+  const int hw = p.G % 4 == 0 ? 4 : (p.G % 2 == 0 ? 2 : 1);
+  const int nwg = p.Hkv * p.n_qtiles * (p.G / hw);
+  if (hw == 4) hipLaunchKernelGGL(prefill_kernel<4>, dim3(nwg), dim3(512), 0, s, p);
+  else if (hw == 2) hipLaunchKernelGGL(prefill_kernel<2>, dim3(nwg), dim3(256), 0, s, p);
+  else hipLaunchKernelGGL(prefill_kernel<1>, dim3(nwg), dim3(128), 0, s, p);
+  return hipGetLastError();
+}
+
+}  // namespace sa
