@@ -134,7 +134,7 @@ def selected_bytes(wl, inp, lists, counts, ccounts):
     return total, (uniq if wl.mode == "per_q_head" else total)
 
 
-def cpu_baseline_decode(wl, inp, n_seq=2):
+def cpu_baseline_decode(wl, inp, n_seq=8):
     """The oracle, as is, on the first n_seq sequences of one input set."""
     import oracle.sparse_attn_oracle as O
     from threadpoolctl import threadpool_info
@@ -236,6 +236,108 @@ def run_decode(args):
     return res
 
 
+def prefill_flops(wl, table, counts):
+    """Algorithmic prefill FLOPs: 4*d per (query row, head, visible token), the
+    visible tokens of row i being those of its group's table blocks at or
+    before position q_start + i (QK^T and PV, 2 flops per MAC each)."""
+    P = wl.page_size
+    pos = wl.q_start + np.arange(wl.q_len, dtype=np.int64)
+    T, C = table.cpu().numpy(), counts.cpu().numpy()
+    visible = 0
+    for g in range(wl.n_kv_heads):
+        starts = T[g, :C[g]].astype(np.int64) * P
+        seen = np.clip(pos[:, None] - starts[None, :] + 1, 0, P)     # [q_len][blocks]
+        visible += int(seen.sum()) * wl.group
+    return 4 * wl.d * visible, visible
+
+
+def cpu_baseline_prefill(wl, inp, table, counts):
+    """The oracle, as is, on the first and last Q-block of every head of KV head 0."""
+    import oracle.sparse_attn_oracle as O
+    from threadpoolctl import threadpool_info
+    P = wl.page_size
+    rows = [(i, h) for i in list(range(0, 64)) + list(range(wl.q_len - 64, wl.q_len)) for h in range(wl.group)]
+    T, C = table.cpu().numpy(), counts.cpu().numpy()
+    q = inp["q"].float().cpu().numpy().astype(np.float64)
+    bt = inp["block_table"].cpu().numpy()[0]
+    used = T[0, :C[0]]
+    # only KV head 0 of the pages the table names is read; copy just those
+    kp = np.zeros((wl.n_phys_pages, 1, P, wl.d))
+    vp = np.zeros((wl.n_phys_pages, 1, wl.d, P))
+    phys = torch.as_tensor(bt[used].astype(np.int64), device=inp["k_pool"].device)
+    kp[bt[used], 0] = inp["k_pool"][phys, 0].float().cpu().numpy()
+    vp[bt[used], 0] = inp["v_pool"][phys, 0].float().cpu().numpy()
+    t0 = time.perf_counter()
+    O.block_sparse_prefill(q[:, :wl.group], kp, vp, bt, int(inp["seq_lens"][0]), P, wl.q_start,
+                           T[:1], C[:1], 1, wl.sm_scale, rows=rows)
+    dt = time.perf_counter() - t0
+    pos = wl.q_start + np.array([i for i, _ in rows], dtype=np.int64)
+    starts = used.astype(np.int64) * P
+    vis = int(np.clip(pos[:, None] - starts[None, :] + 1, 0, P).sum())
+    threads = max([t.get("num_threads", 1) for t in threadpool_info()] + [1])
+    return dict(value=round(4 * wl.d * vis / dt / 1e12, 6), unit="TFLOP/s", cores=threads, kind="oracle",
+                sample=f"{len(rows)} (row, head) pairs: first and last 64-row Q-block, all heads of KV head 0 "
+                       f"(numpy float64 oracle; {dt:.2f} s)", seconds=round(dt, 3))
+
+
+def run_prefill(args):
+    import sparse_attention_long_page_amd as S
+    wl = W.FULL[args.workload]
+    dev = torch.device("cuda:0")
+    sets = []
+    for i in range(args.sets):
+        inp = W.make_prefill_inputs(wl, dev, seed=2000 + i)
+        kv = S.PagedKV(inp["k_pool"], inp["v_pool"], inp["block_table"], inp["seq_lens"])
+        out = torch.empty((wl.q_len, wl.n_q_heads, wl.d), dtype=torch.bfloat16, device=dev)
+        lse = torch.empty((wl.q_len, wl.n_q_heads), dtype=torch.float32, device=dev)
+        table = torch.full((wl.n_kv_heads, wl.n_kv_blocks), -1, dtype=torch.int32, device=dev)
+        counts = torch.zeros((wl.n_kv_heads,), dtype=torch.int32, device=dev)
+        sets.append((inp, kv, out, lse, table, counts))
+    timer = Timer()
+
+    def step(i):
+        inp, kv, out, lse, table, counts = sets[i % len(sets)]
+        timer.start("prefill")
+        S.sa_block_sparse_prefill(kv, 0, inp["q"], wl.q_start, inp["block_mask"], wl.block_q, wl.sm_scale,
+                                  out=out, out_lse=lse, block_table_out=table, block_counts_out=counts)
+        timer.stop("prefill")
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    timer.reset()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = 1000.0 * wall / args.steps
+    inp, kv, out, lse, table, counts = sets[0]
+    flops, visible = prefill_flops(wl, table, counts)
+    k_us = timer.avg_us("prefill")
+    achieved = flops / (k_us * 1e-6) / 1e12
+    res = {
+        "metric": "block-sparse chunked prefill TFLOP/s (% of bf16 MFMA peak) at 128K ctx",
+        "value": round(flops / (ms_per_step * 1e-3) / 1e12, 2), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded; N(0,1) q/K/V, random 2D block mask)",
+        "config": {"workload": wl.name, "q_len": wl.q_len, "q_start": wl.q_start, "kv_tokens": wl.kv_len,
+                   "q_heads": wl.n_q_heads, "kv_heads": wl.n_kv_heads, "head_dim": wl.d,
+                   "page_size": wl.page_size, "block_q": wl.block_q, "random_fraction": wl.random_fraction,
+                   "input_sets": args.sets},
+        "union_blocks_per_kv_head": [int(c) for c in counts.cpu().tolist()],
+        "mask_density": round(float(inp["block_mask"].float().mean().item()), 5),
+        "visible_pairs": visible,
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
+                     "kernel": "sa_block_sparse_prefill (union + attention)", "algorithmic_flops": flops},
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline_prefill(wl, inp, table, counts)
+    return res
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -246,7 +348,6 @@ def main():
         print("bench.py needs a GPU (torch.cuda.is_available() is False)", file=sys.stderr)
         sys.exit(2)
     if args.workload == "chunked_prefill_128k":
-        from bench_prefill import run_prefill  # noqa
         res = run_prefill(args)
     else:
         res = run_decode(args)
