@@ -134,6 +134,30 @@ def selected_bytes(wl, inp, lists, counts, ccounts):
     return total, (uniq if wl.mode == "per_q_head" else total)
 
 
+def tiered_flops(wl, inp, lists, counts, ccounts):
+    """Algorithmic MLA decode FLOPs: 2*(d_qk + d_v) per (query row, attended
+    token); a row attends its Critical pages and the Ambient pages whose head
+    set holds its head."""
+    P = wl.page_size
+    lens = inp["seq_lens"].cpu().numpy()
+    L, C, CC = lists.cpu().numpy(), counts.cpu().numpy(), ccounts.cpu().numpy()
+    am = inp["ambient_mask"].cpu().numpy().astype(np.int64) & 0xffffffff
+    heads = np.arange(wl.n_q_heads)
+    total = 0
+    for b in range(wl.batch):
+        toks = np.zeros(wl.n_q_heads, dtype=np.int64)
+        for e in range(C[b, 0]):
+            lp = int(L[b, 0, e])
+            nv = max(0, min(P, int(lens[b]) - lp * P))
+            if e < CC[b, 0]:
+                toks += nv
+            else:
+                bits = (am[b, lp, heads // 32] >> (heads % 32)) & 1
+                toks += nv * bits
+        total += int(toks.sum()) * wl.q_tokens
+    return 2 * (wl.d_qk + wl.d_v) * total
+
+
 def cpu_baseline_decode(wl, inp, n_seq=8):
     """The oracle, as is, on the first n_seq sequences of one input set."""
     import oracle.sparse_attn_oracle as O
@@ -231,6 +255,14 @@ def run_decode(args):
     }
     if wl.mode == "per_q_head":
         res["pair_counted_bytes"] = nbytes
+    if wl.latent:
+        flops = tiered_flops(wl, inp, lists, counts, ccounts)
+        tf = flops / (dec_us * 1e-6) / 1e12
+        res["metric"] = "MLA tiered sparse decode: selected-KV GB/s and TFLOP/s (% of HBM and bf16 MFMA peak)"
+        res["algorithmic_flops"] = flops
+        res["roofline_mfma"] = {"bound": "mfma", "achieved": round(tf, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
+                                "unit": "TFLOP/s", "frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4),
+                                "kernel": "sa_sparse_decode (latent tiered + split merge)"}
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline_decode(wl, steps[0][2])
     return res

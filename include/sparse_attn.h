@@ -173,8 +173,9 @@ sa_status sa_select_pages(const sa_paged_kv* kv, int32_t batch,
  *   out               [batch][q_tokens][n_q_heads][d_v] (kv->dtype)
  *   out_lse           [batch][q_tokens][n_q_heads] fp32 natural-log units, or NULL
  * Per-KV-head lists need q_tokens*group <= 16 at d 64/128 (one 16-row MFMA
- * tile per KV head); the latent path needs n_kv_heads == 1, n_q_heads a
- * multiple of 16 and q_tokens*n_q_heads <= 256.
+ * tile per KV head); the latent path needs n_kv_heads == 1, per-KV-head
+ * lists, page_size 64 and q_tokens in {1, 2, 4, 8, 16} (the query tokens of
+ * one head share a 16-row tile and its Ambient bit).
  * ---------------------------------------------------------------------- */
 size_t sa_sparse_decode_workspace_size(const sa_paged_kv* kv, int32_t batch, int32_t q_tokens,
                                        int32_t n_q_heads, int32_t list_stride, sa_sel_mode mode,

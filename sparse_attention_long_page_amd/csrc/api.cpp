@@ -86,12 +86,14 @@ int n_sel_of(const sa_paged_kv* kv, int n_q_heads, sa_sel_mode mode) {
 }
 
 // Splits per selection head for the decode kernels.
-int choose_splits(const sa_paged_kv* kv, int batch, int n_sel, int list_stride) {
-  const int units = std::max(1, batch * n_sel);
+int choose_splits(const sa_paged_kv* kv, int batch, int n_sel, int list_stride, int q_tokens, int n_q_heads) {
+  int units = std::max(1, batch * n_sel);
+  if (is_latent(kv)) units = batch * ((n_q_heads * q_tokens + 127) / 128);
   const int cus = device_cu_count();
   if (is_latent(kv)) {
-    // latent path: one unit per (sequence, 16-row tile group); split by pages
-    const int target = 2 * cus;
+    // latent path: units are (sequence, group of 128 query rows); one
+    // workgroup per CU, at least 2 pages per split
+    const int target = cus;
     int s = (target + units - 1) / units;
     s = std::min(s, std::max(1, list_stride / 2));
     return std::max(1, std::min(s, 64));
@@ -251,8 +253,8 @@ static sa_status check_decode_shape(const sa_paged_kv* kv, int32_t batch, int32_
   if (is_latent(kv)) {
     if (kv->n_kv_heads != 1) return fail(SA_ERR_UNSUPPORTED, "latent decode needs n_kv_heads == 1");
     if (mode != SA_SEL_PER_KV_HEAD) return fail(SA_ERR_UNSUPPORTED, "latent decode uses per-KV-head lists");
-    if (n_q_heads % 16 != 0 || q_tokens * n_q_heads > 256)
-      return fail(SA_ERR_UNSUPPORTED, "latent decode needs n_q_heads %% 16 == 0 and q_tokens*n_q_heads <= 256");
+    if (16 % q_tokens != 0)
+      return fail(SA_ERR_UNSUPPORTED, "latent decode needs q_tokens in {1, 2, 4, 8, 16}, got %d", q_tokens);
     if (kv->page_size != 64) return fail(SA_ERR_UNSUPPORTED, "latent decode needs page_size 64");
   } else if (kv->dtype == SA_DTYPE_BF16) {
     const int rows = mode == SA_SEL_PER_KV_HEAD ? q_tokens * G : q_tokens;
@@ -266,7 +268,7 @@ size_t sa_sparse_decode_workspace_size(const sa_paged_kv* kv, int32_t batch, int
                                        int32_t list_stride, sa_sel_mode mode, int32_t num_splits) {
   if (!kv || batch <= 0 || q_tokens <= 0 || n_q_heads <= 0 || list_stride <= 0 || kv->n_kv_heads <= 0) return 0;
   const int n_sel = n_sel_of(kv, n_q_heads, mode);
-  const int splits = num_splits > 0 ? num_splits : choose_splits(kv, batch, n_sel, list_stride);
+  const int splits = num_splits > 0 ? num_splits : choose_splits(kv, batch, n_sel, list_stride, q_tokens, n_q_heads);
   return decode_partials_bytes(kv, batch, q_tokens, n_q_heads, splits);
 }
 
@@ -287,7 +289,7 @@ sa_status sa_sparse_decode(const sa_paged_kv* kv, int32_t batch, const void* q, 
   if (!std::isfinite(sm_scale)) return fail(SA_ERR_INVALID_ARGUMENT, "sm_scale must be finite");
   if (num_splits < 0 || num_splits > 64) return fail(SA_ERR_INVALID_ARGUMENT, "num_splits must be in 0..64");
   const int n_sel = n_sel_of(kv, n_q_heads, mode);
-  const int splits = num_splits > 0 ? num_splits : choose_splits(kv, batch, n_sel, list_stride);
+  const int splits = num_splits > 0 ? num_splits : choose_splits(kv, batch, n_sel, list_stride, q_tokens, n_q_heads);
   const size_t need = decode_partials_bytes(kv, batch, q_tokens, n_q_heads, splits);
   if (workspace_bytes < need || (need && !workspace))
     return fail(SA_ERR_WORKSPACE_TOO_SMALL, "workspace %zu < %zu bytes", workspace_bytes, need);

@@ -315,6 +315,8 @@ __global__ __launch_bounds__(256) void decode_f32_kernel(DecodeParams p) {
 
 // ------------------------------------------------------------------- merge
 // One wave per query row: o = sum_s w_s o_s / sum_s w_s, w_s = exp(lse_s - max).
+// Lanes own 4 consecutive dims (16-byte loads); the loads of up to 8 splits
+// are issued before any is consumed.
 __global__ __launch_bounds__(256) void lse_merge_kernel(MergeParams p) {
   const int lane = threadIdx.x & 63;
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -325,16 +327,34 @@ __global__ __launch_bounds__(256) void lse_merge_kernel(MergeParams p) {
   float w = 0.f;
   if (M != -INFINITY && lane < p.splits) w = __expf(mine - M);
   const float L = wave_sum(w);
+  const float inv = M == -INFINITY ? 0.f : 1.f / L;
   const float* po = p.part_o + (size_t)row * p.splits * p.d_v;
-  for (int d = lane; d < p.d_v; d += 64) {
-    float acc = 0.f;
-    for (int sidx = 0; sidx < p.splits; ++sidx) {
-      const float ws = __shfl(w, sidx, 64);
-      if (ws != 0.f) acc += ws * po[(size_t)sidx * p.d_v + d];
+  for (int d4 = lane; d4 < p.d_v / 4; d4 += 64) {
+    f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int s0 = 0; s0 < p.splits; s0 += 8) {
+      f32x4 v[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        v[j] = s0 + j < p.splits ? *reinterpret_cast<const f32x4*>(po + (size_t)(s0 + j) * p.d_v + 4 * d4)
+                                 : f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float ws = __shfl(w, (s0 + j) & 63, 64);
+        if (s0 + j < p.splits && ws != 0.f) {
+          acc[0] += ws * v[j][0]; acc[1] += ws * v[j][1]; acc[2] += ws * v[j][2]; acc[3] += ws * v[j][3];
+        }
+      }
     }
-    const float o = M == -INFINITY ? 0.f : acc / L;
-    if (p.out_fp32) reinterpret_cast<float*>(p.out)[(size_t)row * p.d_v + d] = o;
-    else reinterpret_cast<uint16_t*>(p.out)[(size_t)row * p.d_v + d] = f32_to_bf16_bits(o);
+    const size_t o = (size_t)row * p.d_v + 4 * d4;
+    if (p.out_fp32) {
+      *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(p.out) + o) =
+          f32x4{acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv};
+    } else {
+      uint2 pk;
+      pk.x = (uint32_t)f32_to_bf16_bits(acc[0] * inv) | ((uint32_t)f32_to_bf16_bits(acc[1] * inv) << 16);
+      pk.y = (uint32_t)f32_to_bf16_bits(acc[2] * inv) | ((uint32_t)f32_to_bf16_bits(acc[3] * inv) << 16);
+      *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(p.out) + o) = pk;
+    }
   }
   if (lane == 0 && p.out_lse) p.out_lse[row] = M == -INFINITY ? -INFINITY : M + __logf(L);
 }

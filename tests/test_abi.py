@@ -122,10 +122,10 @@ DECODE_CASES = [
     ("missing out", {}, dict(out=None), INV),
     ("zero stride", {}, dict(stride=0), INV),
     ("latent with 2 kv heads", dict(kv=dict(v_pool=None, d_qk=576, d_v=512)), {}, UNS),
-    ("latent heads not multiple of 16", dict(kv=dict(v_pool=None, d_qk=576, d_v=512, n_kv_heads=1)),
-     dict(n_q_heads=8), UNS),
-    ("latent too many rows", dict(kv=dict(v_pool=None, d_qk=576, d_v=512, n_kv_heads=1)),
+    ("latent q_tokens not dividing 16", dict(kv=dict(v_pool=None, d_qk=576, d_v=512, n_kv_heads=1)),
      dict(n_q_heads=128, q_tokens=3), UNS),
+    ("latent page 16", dict(kv=dict(v_pool=None, d_qk=576, d_v=512, n_kv_heads=1, page_size=16)),
+     dict(n_q_heads=16), UNS),
     ("workspace too small", {}, dict(splits=4, ws_bytes=100), WS),
     ("no workspace", {}, dict(splits=4, ws=None, ws_bytes=0), WS),
 ]
