@@ -9,9 +9,12 @@ One step = one decode layer's sparse-attention work for one batch:
   sa_page_summary(last_pages=1)  mean key of the page the newest token landed in
   sa_select_pages                router scores + sink/window/top-k lists
   sa_sparse_decode               split-K flash-decode over the lists (+ merge)
-Inputs are resident in HBM before timing; steps rotate over 3 independently
-drawn input sets (4.2 GB each) so no step finds its pages in the 256 MB
-last-level cache left warm by the previous one.
+Each step is replayed from one HIP graph captured once per input set, so the
+host's launch cost does not leave the GPU idle between kernels; every kernel
+runs in every step.  Inputs are
+resident in HBM before timing; steps rotate over 3 independently drawn input
+sets (4.2 GB each) so no step finds its pages in the 256 MB last-level cache
+left warm by the previous one.
 
 Prints one JSON line: value = selected K+V bytes per step / step time (GB/s);
 roofline of the dominant kernel (the decode) from HIP events on the launch
@@ -43,7 +46,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="llama3_8b_decode_32k",
                     choices=["llama3_8b_decode_32k", "token_head_decode_128k", "mla_tiered_decode_64k",
-                             "chunked_prefill_128k", "tiny_decode"])
+                             "chunked_prefill_128k", "tiny_decode", "hbm_copy"])
     ap.add_argument("--sets", type=int, default=3, help="independent input sets rotated over")
     ap.add_argument("--splits", type=int, default=-1, help="decode splits (-1: workload default)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -74,7 +77,11 @@ class Timer:
         self.pairs = {}
 
 
-def decode_step_fn(S, wl, inp, mu, splits, timer):
+def decode_step_fn(S, wl, inp, mu, splits):
+    """One decode step as one HIP graph on the current stream: page summary of
+    the newest page, selection, split-K decode and LSE merge.  Graph replay
+    removes the host launch cost between kernels; every kernel still runs in
+    every replay."""
     kv = S.PagedKV(inp["k_pool"], inp["v_pool"], inp["block_table"], inp["seq_lens"], d_v=wl.d_v)
     mode = S.SA_SEL_PER_KV_HEAD if wl.mode == "per_kv_head" else S.SA_SEL_PER_Q_HEAD
     stride = max(1, min(wl.max_pages, wl.sink_pages + wl.window_pages + wl.top_k))
@@ -90,24 +97,66 @@ def decode_step_fn(S, wl, inp, mu, splits, timer):
     out = torch.empty((wl.batch, wl.q_tokens, wl.n_q_heads, wl.d_v), dtype=inp["q"].dtype, device=dev)
     lse = torch.empty((wl.batch, wl.q_tokens, wl.n_q_heads), dtype=torch.float32, device=dev)
 
-    def step():
+    def select():
         if mu is not None:
-            timer.start("summary")
             S.sa_page_summary(kv, last_pages=1, out=mu)
-            timer.stop("summary")
-        timer.start("select")
         S.sa_select_pages(kv, n_q_heads=wl.n_q_heads, mode=mode, sink_pages=wl.sink_pages,
                           window_pages=wl.window_pages, top_k=wl.top_k, q=inp["q"] if mu is not None else None,
                           page_summary=mu, scores=inp["scores"], critical_k=wl.critical_k, list_stride=stride,
                           workspace=sel_ws, out=(lists, counts, ccounts))
-        timer.stop("select")
-        timer.start("decode")
+
+    def decode():
         S.sa_sparse_decode(kv, inp["q"], lists, counts, mode=mode, sm_scale=wl.sm_scale,
                            critical_counts=ccounts, ambient_head_mask=inp["ambient_mask"], num_splits=splits,
                            out=out, out_lse=lse, workspace=dec_ws)
-        timer.stop("decode")
 
-    return step, (lists, counts, ccounts)
+    select()
+    decode()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        select()
+        decode()
+    return g, (lists, counts, ccounts), decode
+
+
+def recorded_traffic(name):
+    """HBM bytes per launch of a kernel from the rocprofv3 FETCH_SIZE /
+    WRITE_SIZE counters recorded under profiles/ (scaled by the same counters
+    on a copy of known size), or None when the kernel's sources have changed
+    since the counters were taken."""
+    import hashlib
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles", name)
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    h = hashlib.sha256()
+    root = os.path.dirname(os.path.abspath(__file__))
+    for src in rec["sources"]:
+        h.update(open(os.path.join(root, src), "rb").read())
+    if h.hexdigest() != rec["source_sha256"]:
+        return None
+    return int(round(rec["fetch_size_kib_per_dispatch"] * 1024 * rec["fetch_scale"]
+                     + rec["write_size_kib_per_dispatch"] * 1024 * rec["write_scale"]))
+
+
+def time_back_to_back(calls, reps):
+    """Average duration of one call when `reps` calls (cycling over `calls`,
+    one per input set) are captured into one HIP graph and replayed between two
+    HIP events on the current stream: the kernels run back to back, so the
+    figure is their own duration plus the dispatch gaps between them."""
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(reps):
+            calls[i % len(calls)]()
+    g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    return 1000.0 * e0.elapsed_time(e1) / reps
 
 
 def selected_bytes(wl, inp, lists, counts, ccounts):
@@ -211,29 +260,36 @@ def run_decode(args):
             mu = S.sa_page_summary(kv)       # amortised: built once per filled page
         sets.append((inp, mu))
     torch.cuda.synchronize()
-    timer = Timer()
     steps = []
     for inp, mu in sets:
-        fn, res = decode_step_fn(S, wl, inp, mu, splits, timer)
-        steps.append((fn, res, inp))
+        graphs, res, dec = decode_step_fn(S, wl, inp, mu, splits)
+        steps.append((graphs, res, inp, dec))
+    timer = Timer()
+
+    def step(i):
+        g, _, _, _ = steps[i % len(steps)]
+        timer.start("step")
+        g.replay()
+        timer.stop("step")
+
     for i in range(args.warmup):
-        steps[i % len(steps)][0]()
+        step(i)
     torch.cuda.synchronize()
     timer.reset()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        steps[i % len(steps)][0]()
+        step(i)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_per_step = 1000.0 * wall / args.steps
 
-    fn, (lists, counts, ccounts), inp = steps[0]
+    _, (lists, counts, ccounts), inp, _ = steps[0]
+    # the dominant kernel alone: decode calls back to back, inputs rotating
+    dec_b2b_us = time_back_to_back([st[3] for st in steps], 4 * len(steps))
     nbytes, uniq = selected_bytes(wl, inp, lists, counts, ccounts)
-    dec_us = timer.avg_us("decode")
-    sel_us = timer.avg_us("select")
-    sum_us = timer.avg_us("summary")
+    step_gpu_us = timer.avg_us("step")
     algo_bytes = uniq if wl.mode == "per_q_head" else nbytes
-    achieved = algo_bytes / (dec_us * 1e-6) / 1e9
+    achieved = algo_bytes / (dec_b2b_us * 1e-6) / 1e9
     value = nbytes / (ms_per_step * 1e-3) / 1e9
     res = {
         "metric": "sparse-decode selected-KV GB/s (% of HBM peak) + us/layer at 32K ctx, 90% sparsity",
@@ -247,17 +303,19 @@ def run_decode(args):
                    "splits": splits, "input_sets": args.sets},
         "us_per_layer": round(1000.0 * ms_per_step, 2),
         "pct_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
-        "stage_us": {"summary": round(sum_us, 2), "select": round(sel_us, 2), "decode": round(dec_us, 2)},
+        "step_gpu_us": round(step_gpu_us, 2),
         "selected_bytes": nbytes,
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                     "kernel": "sa_sparse_decode (decode + split merge)", "algorithmic_bytes": algo_bytes},
+                     "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": recorded_traffic(f"decode_bf16_{wl.name}_traffic.json"),
+                     "kernel": "sa_sparse_decode (decode kernel + split merge)", "algorithmic_bytes": algo_bytes,
+                     "launch_us": round(dec_b2b_us, 2)},
     }
     if wl.mode == "per_q_head":
         res["pair_counted_bytes"] = nbytes
     if wl.latent:
         flops = tiered_flops(wl, inp, lists, counts, ccounts)
-        tf = flops / (dec_us * 1e-6) / 1e12
+        tf = flops / (dec_b2b_us * 1e-6) / 1e12
         res["metric"] = "MLA tiered sparse decode: selected-KV GB/s and TFLOP/s (% of HBM and bf16 MFMA peak)"
         res["algorithmic_flops"] = flops
         res["roofline_mfma"] = {"bound": "mfma", "achieved": round(tf, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
@@ -370,6 +428,31 @@ def run_prefill(args):
     return res
 
 
+def run_hbm_copy(args):
+    """Device-to-device copy of a 1 GiB buffer: the measured streaming ceiling
+    of this HBM, and the known-size reference that scales the FETCH_SIZE /
+    WRITE_SIZE counters of the library's kernels (1 GiB read + 1 GiB written
+    per dispatch)."""
+    dev = torch.device("cuda:0")
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(args.warmup):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.steps):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    return {"metric": "HBM device-to-device copy GB/s (read + write)", "value": round(2 * n / (ms * 1e-3) / 1e9, 1),
+            "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "u8", "data": "synthetic",
+            "config": {"workload": "hbm_copy", "bytes_read": n, "bytes_written": n}}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -381,6 +464,8 @@ def main():
         sys.exit(2)
     if args.workload == "chunked_prefill_128k":
         res = run_prefill(args)
+    elif args.workload == "hbm_copy":
+        res = run_hbm_copy(args)
     else:
         res = run_decode(args)
     print(json.dumps(res), flush=True)

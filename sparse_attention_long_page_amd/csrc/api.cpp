@@ -155,9 +155,9 @@ sa_status sa_page_summary(const sa_paged_kv* kv, int32_t batch, int32_t last_pag
 // ------------------------------------------------------------------- select
 size_t sa_select_pages_workspace_size(int32_t batch, int32_t n_sel, int32_t max_pages) {
   if (batch <= 0 || n_sel <= 0 || max_pages <= 0) return 0;
-  // router scores + float64 pooled queries (d_qk <= 576)
+  // router scores + float64 pooled-query partials (8 row chunks, d_qk <= 576)
   return align_up((size_t)batch * n_sel * max_pages * sizeof(float)) +
-         align_up((size_t)batch * n_sel * 576 * sizeof(double));
+         align_up((size_t)batch * n_sel * 8 * 576 * sizeof(double));
 }
 
 sa_status sa_select_pages(const sa_paged_kv* kv, int32_t batch, const void* q, int32_t q_tokens,
@@ -195,8 +195,44 @@ sa_status sa_select_pages(const sa_paged_kv* kv, int32_t batch, const void* q, i
       return fail(SA_ERR_WORKSPACE_TOO_SMALL, "workspace %zu < %zu bytes", workspace_bytes, need);
   }
 
+  sa::SelectParams sp{};
+  sp.seq_lens = kv->seq_lens;
+  sp.lists = page_lists;
+  sp.counts = page_counts;
+  sp.ccounts = critical_counts;
+  sp.n_sel = n_sel;
+  sp.P = kv->page_size;
+  sp.list_stride = list_stride;
+  sp.sink = sink_pages;
+  sp.window = window_pages;
+  sp.top_k = top_k;
+  sp.critical_k = critical_k;
+  sp.tiered = critical_counts != nullptr;
+
   const float* sc = scores;
   int stride = scores_stride;
+  const int pooled_rows = mode == SA_SEL_PER_KV_HEAD ? q_tokens * (n_q_heads / kv->n_kv_heads) : q_tokens;
+  if (!scores && batch * n_sel >= 128 && pooled_rows <= 32) {
+    // enough lists to fill the GPU: score and select in one workgroup per list
+    sa::ScoreParams p{};
+    p.q = q;
+    p.mu = page_summary;
+    p.block_table = kv->block_table;
+    p.seq_lens = kv->seq_lens;
+    p.scores = scores_out;
+    p.B = batch;
+    p.T = q_tokens;
+    p.Hq = n_q_heads;
+    p.Hkv = kv->n_kv_heads;
+    p.G = n_q_heads / kv->n_kv_heads;
+    p.n_sel = n_sel;
+    p.d = kv->d_qk;
+    p.P = kv->page_size;
+    p.max_pages = kv->max_pages;
+    p.per_q = mode == SA_SEL_PER_Q_HEAD;
+    return device_status(sa::launch_score_select(p, sp, batch, kv->dtype == SA_DTYPE_BF16, stream),
+                         "score_select launch");
+  }
   if (!scores) {
     float* buf = scores_out ? scores_out : reinterpret_cast<float*>(workspace);
     double* qbar = reinterpret_cast<double*>(reinterpret_cast<char*>(workspace) +
@@ -222,21 +258,8 @@ sa_status sa_select_pages(const sa_paged_kv* kv, int32_t batch, const void* q, i
     sc = buf;
     stride = kv->max_pages;
   }
-  sa::SelectParams sp{};
   sp.scores = sc;
-  sp.seq_lens = kv->seq_lens;
-  sp.lists = page_lists;
-  sp.counts = page_counts;
-  sp.ccounts = critical_counts;
   sp.scores_stride = stride;
-  sp.n_sel = n_sel;
-  sp.P = kv->page_size;
-  sp.list_stride = list_stride;
-  sp.sink = sink_pages;
-  sp.window = window_pages;
-  sp.top_k = top_k;
-  sp.critical_k = critical_k;
-  sp.tiered = critical_counts != nullptr;
   return device_status(sa::launch_select(sp, batch, kv->max_pages, stream), "select launch");
 }
 

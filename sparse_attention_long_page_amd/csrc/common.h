@@ -131,6 +131,7 @@ struct PrefillParams {
 hipError_t launch_page_summary(const SummaryParams& p, int batch, int bf16, hipStream_t s);
 hipError_t launch_page_scores_ws(const ScoreParams& p, int bf16, double* qbar_ws, hipStream_t s);
 hipError_t launch_select(const SelectParams& p, int batch, int max_pages, hipStream_t s);
+hipError_t launch_score_select(const ScoreParams& sp, const SelectParams& p, int batch, int bf16, hipStream_t s);
 hipError_t launch_decode(const DecodeParams& p, int bf16, hipStream_t s);
 hipError_t launch_merge(const MergeParams& p, hipStream_t s);
 hipError_t launch_mla_decode(const DecodeParams& p, hipStream_t s);

@@ -5,9 +5,9 @@
 // blocks read in place with no compaction; "Universal Attention Engine",
 // "Key Design Decisions" 3: prefill is compute-bound, optimise FLOPs).
 //
-// Union kernel: one workgroup per KV head; each thread ORs one KV-block column
-// over the group's heads and Q-blocks (coalesced byte rows), then an
-// index-ordered workgroup prefix sum writes the ascending table.
+// Union kernel: one workgroup per KV head; each thread ORs four KV-block
+// columns over the group's heads and Q-blocks (4-byte loads, many in flight),
+// then an index-ordered workgroup prefix sum writes the ascending table.
 //
 // Attention kernel (bf16, d 128, pages of 64):
 //  * workgroup = (KV head g, tile of 64 query positions); one wave per query
@@ -33,22 +33,45 @@ namespace sa {
 // ------------------------------------------------------------------- union
 constexpr int kUnionThreads = 1024;
 
+// One workgroup per KV head.  Thread t owns KV-block columns 4t .. 4t+3 of a
+// 4096-column pass and ORs them over the group's heads and Q-blocks with
+// 4-byte loads (16 loads in flight per step); an index-ordered workgroup
+// prefix sum over the per-thread counts writes the ascending table.
+template <bool VEC4>
 __global__ __launch_bounds__(kUnionThreads) void union_kernel(UnionParams p) {
   __shared__ uint32_t wsum[kUnionThreads / 64];
   const int g = blockIdx.x;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int nrows = p.G * p.nqb;                       // (head, Q-block) rows of this group
+  const uint8_t* mbase = p.mask + (size_t)g * p.G * p.nqb * p.nkb;
   uint32_t run = 0;
   int32_t* out = p.table + (size_t)g * p.nkb;
-  for (int base = 0; base < p.nkb; base += kUnionThreads) {
-    const int kb = base + threadIdx.x;
-    uint32_t any = 0;
-    if (kb < p.nkb) {
-      for (int h = g * p.G; h < (g + 1) * p.G && !any; ++h)
-        for (int qb = 0; qb < p.nqb; ++qb)
-          any |= p.mask[((size_t)h * p.nqb + qb) * p.nkb + kb];
+  for (int base = 0; base < p.nkb; base += 4 * kUnionThreads) {
+    const int kb0 = base + 4 * threadIdx.x;
+    uint32_t any = 0;                                   // byte j nonzero <=> column kb0 + j kept
+    if (kb0 < p.nkb) {
+      if (VEC4) {
+        int r = 0;
+        for (; r + 16 <= nrows; r += 16) {
+          uint32_t w[16];
+#pragma unroll
+          for (int j = 0; j < 16; ++j) w[j] = *reinterpret_cast<const uint32_t*>(mbase + (size_t)(r + j) * p.nkb + kb0);
+#pragma unroll
+          for (int j = 0; j < 16; ++j) any |= w[j];
+        }
+        for (; r < nrows; ++r) any |= *reinterpret_cast<const uint32_t*>(mbase + (size_t)r * p.nkb + kb0);
+      } else {
+        for (int r = 0; r < nrows; ++r)
+          for (int j = 0; j < 4; ++j)
+            if (kb0 + j < p.nkb && mbase[(size_t)r * p.nkb + kb0 + j]) any |= 1u << (8 * j);
+      }
     }
-    const uint32_t f = any ? 1u : 0u;
-    // exclusive prefix over the workgroup in thread (= block index) order
+    uint32_t flags = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      if (kb0 + j < p.nkb && ((any >> (8 * j)) & 0xffu)) flags |= 1u << j;
+    const uint32_t f = __popc(flags);
+    // exclusive prefix over the workgroup in thread (= column) order
     uint32_t x = f;
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
@@ -64,14 +87,20 @@ __global__ __launch_bounds__(kUnionThreads) void union_kernel(UnionParams p) {
       all += t;
     }
     __syncthreads();
-    if (f) out[run + before + x - f] = kb;
+    uint32_t pos = run + before + x - f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      if ((flags >> j) & 1u) out[pos++] = kb0 + j;
     run += all;
   }
   if (threadIdx.x == 0) p.counts[g] = (int32_t)run;
 }
 
 hipError_t launch_union(const UnionParams& p, hipStream_t s) {
-  hipLaunchKernelGGL(union_kernel, dim3(p.Hkv), dim3(kUnionThreads), 0, s, p);
+  if (p.nkb % 4 == 0 && reinterpret_cast<uintptr_t>(p.mask) % 4 == 0)
+    hipLaunchKernelGGL(union_kernel<true>, dim3(p.Hkv), dim3(kUnionThreads), 0, s, p);
+  else
+    hipLaunchKernelGGL(union_kernel<false>, dim3(p.Hkv), dim3(kUnionThreads), 0, s, p);
   return hipGetLastError();
 }
 

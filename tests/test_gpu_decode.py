@@ -78,9 +78,21 @@ def test_page_summary_matches_oracle(name):
         assert np.array_equal(m2[p], got[p])
 
 
-@pytest.mark.parametrize("name", DECODE_SMALL)
+# enough lists (batch x selection heads >= 128) for the fused score+select kernel
+MANY_LISTS = {
+    "llama3_many_lists": W.SMALL["llama3_decode_small"].replace(
+        name="llama3_many_lists", batch=17, n_q_heads=32, n_kv_heads=8,
+        seq_lens=tuple(64 * (9 + 3 * i) + (i * 13) % 64 for i in range(17))),
+    "per_q_summary_many_lists": W.SMALL["token_head_decode_small"].replace(
+        name="per_q_summary_many_lists", batch=4, n_q_heads=32, n_kv_heads=8, scores="summary",
+        context=16 * 90 + 7, top_k=12, sink_pages=1, window_pages=3, num_splits=2),
+}
+SELECT_CASES = {**{n: W.SMALL[n] for n in DECODE_SMALL}, **MANY_LISTS}
+
+
+@pytest.mark.parametrize("name", list(SELECT_CASES))
 def test_select_matches_oracle(name):
-    wl = W.SMALL[name]
+    wl = SELECT_CASES[name]
     cpu = W.make_decode_inputs(wl, "cpu", seed=2)
     inp = gpu_inputs(cpu)
     kv = make_kv(inp, wl)

@@ -1,0 +1,110 @@
+"""The library's calls captured in a HIP graph give the same bits on every
+replay as the eager calls, with unrelated eager work and synchronisations
+between the replays (the benchmark replays captured steps)."""
+import numpy as np
+import pytest
+import torch
+
+import sparse_attention_long_page_amd as S
+import workloads as W
+from test_gpu_decode import MODE, gpu_inputs, make_kv
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def _step_fns(wl, inp):
+    kv = make_kv(inp, wl)
+    mode = MODE[wl.mode]
+    stride = wl.list_stride
+    mu = S.sa_page_summary(kv) if wl.scores == "summary" else None
+    lists = torch.full((wl.batch, wl.n_sel, stride), -1, dtype=torch.int32, device=DEV)
+    counts = torch.zeros((wl.batch, wl.n_sel), dtype=torch.int32, device=DEV)
+    cc = torch.zeros_like(counts) if wl.tiered else None
+    sel_ws = torch.empty(max(1, S.sa_select_pages_workspace_size(wl.batch, wl.n_sel, wl.max_pages)),
+                         dtype=torch.uint8, device=DEV)
+    dec_ws = torch.empty(max(1, S.sa_sparse_decode_workspace_size(kv, wl.q_tokens, wl.n_q_heads, stride, mode, 3)),
+                         dtype=torch.uint8, device=DEV)
+    out = torch.empty((wl.batch, wl.q_tokens, wl.n_q_heads, wl.d_v), dtype=inp["q"].dtype, device=DEV)
+    lse = torch.empty((wl.batch, wl.q_tokens, wl.n_q_heads), dtype=torch.float32, device=DEV)
+
+    def step():
+        if mu is not None:
+            S.sa_page_summary(kv, last_pages=1, out=mu)
+        S.sa_select_pages(kv, n_q_heads=wl.n_q_heads, mode=mode, sink_pages=wl.sink_pages,
+                          window_pages=wl.window_pages, top_k=wl.top_k, q=inp["q"] if mu is not None else None,
+                          page_summary=mu, scores=inp["scores"], critical_k=wl.critical_k, list_stride=stride,
+                          workspace=sel_ws, out=(lists, counts, cc))
+        S.sa_sparse_decode(kv, inp["q"], lists, counts, mode=mode, sm_scale=wl.sm_scale, critical_counts=cc,
+                           ambient_head_mask=inp["ambient_mask"], num_splits=3, out=out, out_lse=lse,
+                           workspace=dec_ws)
+
+    results = [lists, counts, out, lse] + ([cc] if cc is not None else [])
+    return step, results
+
+
+@pytest.mark.parametrize("name", ["llama3_decode_small", "token_head_decode_small", "mla_tiered_decode_small"])
+def test_graph_replays_match_eager(name):
+    wl = W.SMALL[name]
+    inp = gpu_inputs(W.make_decode_inputs(wl, "cpu", seed=41))
+    step, results = _step_fns(wl, inp)
+    step()
+    torch.cuda.synchronize()
+    eager = [r.clone() for r in results]
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for rep in range(4):
+        for r in results:                      # poison the outputs between replays
+            r.fill_(-7)
+        other = torch.randn(1 << 20, device=DEV).sum()   # unrelated eager work
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.isfinite(other)
+        _assert_same(results, eager, rep)
+
+
+def _assert_same(results, eager, rep):
+    """Lists are compared up to their counts (entries past a count are left
+    untouched by the library); everything else element by element."""
+    lists, counts = results[0], results[1]
+    assert torch.equal(counts, eager[1]), f"replay {rep}: counts differ"
+    L, E, C = lists.cpu().numpy(), eager[0].cpu().numpy(), counts.cpu().numpy()
+    for idx in np.ndindex(*C.shape):
+        n = int(C[idx])
+        assert np.array_equal(L[idx][:n], E[idx][:n]), f"replay {rep}: list {idx} differs"
+    for a, b in zip(results[2:], eager[2:]):
+        assert torch.equal(a, b), f"replay {rep} differs from the eager result"
+
+
+def test_prefill_graph_replays_match_eager():
+    wl = W.SMALL["chunked_prefill_small"]
+    inp = gpu_inputs(W.make_prefill_inputs(wl, "cpu", seed=42))
+    kv = S.PagedKV(inp["k_pool"], inp["v_pool"], inp["block_table"], inp["seq_lens"])
+    out = torch.empty((wl.q_len, wl.n_q_heads, wl.d), dtype=torch.bfloat16, device=DEV)
+    lse = torch.empty((wl.q_len, wl.n_q_heads), dtype=torch.float32, device=DEV)
+    table = torch.full((wl.n_kv_heads, wl.n_kv_blocks), -1, dtype=torch.int32, device=DEV)
+    counts = torch.zeros((wl.n_kv_heads,), dtype=torch.int32, device=DEV)
+
+    def step():
+        S.sa_block_sparse_prefill(kv, 0, inp["q"], wl.q_start, inp["block_mask"], wl.block_q, wl.sm_scale,
+                                  out=out, out_lse=lse, block_table_out=table, block_counts_out=counts)
+
+    step()
+    torch.cuda.synchronize()
+    eager = [t.clone() for t in (out, lse, table, counts)]
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for rep in range(3):
+        for t in (out, lse, table, counts):
+            t.fill_(-3)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(counts, eager[3])
+        for g_ in range(wl.n_kv_heads):
+            n = int(counts[g_])
+            assert torch.equal(table[g_, :n], eager[2][g_, :n]), f"replay {rep}: table {g_} differs"
+        assert torch.equal(out, eager[0]) and torch.equal(lse, eager[1]), f"replay {rep} differs"
