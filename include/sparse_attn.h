@@ -163,7 +163,8 @@ sa_status sa_select_pages(const sa_paged_kv* kv, int32_t batch,
  *   entries (Critical, all heads) plus each later entry p (Ambient) whose
  *   ambient_head_mask[b][p] has bit h.
  *   o = softmax(sm_scale * q K^T) V over that token set, lse = log-sum-exp of
- *   the scaled logits; an empty set gives o = 0 and lse = -inf.
+ *   the scaled logits; an empty set gives o = 0 and lse = -inf.  sm_scale
+ *   must be finite and positive (SA_ERR_INVALID_ARGUMENT otherwise).
  * Each list is cut into num_splits contiguous chunks (sizes differ by at most
  * one); chunk partials (o_s, lse_s) are combined by an LSE merge.
  *   q                 [batch][q_tokens][n_q_heads][d_qk]
@@ -199,7 +200,8 @@ sa_status sa_sparse_decode(const sa_paged_kv* kv, int32_t batch,
  *   block_table_out[g][0..count) = ascending {kb : T_g[kb]}, block_counts_out[g] = count
  * then query i (position q_start + i) of head h attends, in place in the
  * paged pool row `seq`, every token j of the blocks in T_{g(h)} with
- * j <= q_start + i and j < seq_lens[seq]:  o = softmax(sm_scale q K^T) V.
+ * j <= q_start + i and j < seq_lens[seq]:  o = softmax(sm_scale q K^T) V
+ * (sm_scale finite and positive).
  *   q          [q_len][n_q_heads][d_qk]
  *   block_mask [n_q_heads][ceil(q_len/block_q)][n_kv_blocks] uint8 (nonzero = keep);
  *              KV block kb is logical page kb (block size = page_size)

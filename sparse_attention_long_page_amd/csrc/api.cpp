@@ -309,7 +309,8 @@ sa_status sa_sparse_decode(const sa_paged_kv* kv, int32_t batch, const void* q, 
   if (list_stride <= 0) return fail(SA_ERR_INVALID_ARGUMENT, "list_stride must be positive");
   if ((critical_counts == nullptr) != (ambient_head_mask == nullptr))
     return fail(SA_ERR_INVALID_ARGUMENT, "critical_counts and ambient_head_mask go together");
-  if (!std::isfinite(sm_scale)) return fail(SA_ERR_INVALID_ARGUMENT, "sm_scale must be finite");
+  if (!std::isfinite(sm_scale) || !(sm_scale > 0.f))
+    return fail(SA_ERR_INVALID_ARGUMENT, "sm_scale must be finite and positive");
   if (num_splits < 0 || num_splits > 64) return fail(SA_ERR_INVALID_ARGUMENT, "num_splits must be in 0..64");
   const int n_sel = n_sel_of(kv, n_q_heads, mode);
   const int splits = num_splits > 0 ? num_splits : choose_splits(kv, batch, n_sel, list_stride, q_tokens, n_q_heads);
@@ -397,7 +398,8 @@ sa_status sa_block_sparse_prefill(const sa_paged_kv* kv, int32_t seq, const void
   if (n_kv_blocks < need_blocks || n_kv_blocks > kv->max_pages)
     return fail(SA_ERR_INVALID_ARGUMENT, "n_kv_blocks %d must cover q_start+q_len (%ld) and be <= max_pages %d",
                 n_kv_blocks, need_blocks, kv->max_pages);
-  if (!std::isfinite(sm_scale)) return fail(SA_ERR_INVALID_ARGUMENT, "sm_scale must be finite");
+  if (!std::isfinite(sm_scale) || !(sm_scale > 0.f))
+    return fail(SA_ERR_INVALID_ARGUMENT, "sm_scale must be finite and positive");
   const int G = n_q_heads / kv->n_kv_heads;
   if (G > 8) return fail(SA_ERR_UNSUPPORTED, "prefill supports up to 8 query heads per KV head");
 

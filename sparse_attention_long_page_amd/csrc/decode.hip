@@ -143,9 +143,10 @@ __global__ __launch_bounds__(256, 2) void decode_bf16_kernel(DecodeParams p) {
         sacc[j4] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kreg[j4][kk], qreg[kk], sacc[j4], 0, 0, 0);
     }
 
-    // lane holds S^T[token 32*(j4/2) + 8*kg + 4*(j4%2) + i][row col]
-    float z[4][4];
-    float mloc = -INFINITY;
+    // lane holds S^T[token 32*(j4/2) + 8*kg + 4*(j4%2) + i][row col]; the
+    // row maximum is taken on the raw logits (the scale is positive), then
+    // p = 2^(s * scale_log2 - m) is one FMA and one v_exp_f32
+    float mraw = -INFINITY;
 #pragma unroll
     for (int j4 = 0; j4 < 4; ++j4) {
 #pragma unroll
@@ -153,15 +154,16 @@ __global__ __launch_bounds__(256, 2) void decode_bf16_kernel(DecodeParams p) {
         const int tau = 32 * (j4 >> 1) + 8 * kg + 4 * (j4 & 1) + i;
         const int ent = tau / P, r = tau % P;
         const bool ok = (r < nval[ent]) && act[ent];
-        z[j4][i] = ok ? sacc[j4][i] * p.scale_log2 : -INFINITY;
-        mloc = fmaxf(mloc, z[j4][i]);
+        if (!ok) sacc[j4][i] = -INFINITY;
+        mraw = fmaxf(mraw, sacc[j4][i]);
       }
     }
-    mloc = fmaxf(mloc, __shfl_xor(mloc, 16, 64));
-    mloc = fmaxf(mloc, __shfl_xor(mloc, 32, 64));
+    mraw = fmaxf(mraw, __shfl_xor(mraw, 16, 64));
+    mraw = fmaxf(mraw, __shfl_xor(mraw, 32, 64));
+    const float mloc = mraw == -INFINITY ? -INFINITY : mraw * p.scale_log2;
     const float m_new = fmaxf(m_run, mloc);
     const bool none = m_new == -INFINITY;
-    const float alpha = none ? 1.f : exp2f(m_run - m_new);
+    const float alpha = none ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
     const float msub = none ? 0.f : m_new;
     float psum = 0.f;
     bf16x8 pb[2];
@@ -169,7 +171,7 @@ __global__ __launch_bounds__(256, 2) void decode_bf16_kernel(DecodeParams p) {
     for (int j4 = 0; j4 < 4; ++j4) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const float pv = exp2f(z[j4][i] - msub);
+        const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[j4][i], p.scale_log2, -msub));
         psum += pv;
         pb[j4 >> 1][4 * (j4 & 1) + i] = (__bf16)pv;
       }

@@ -264,18 +264,20 @@ __global__ __launch_bounds__(256, 1) void mla_decode_kernel(DecodeParams p) {
         bf16x8 pb[2];
 #pragma unroll
         for (int rt = 0; rt < 2; ++rt) {
-          float mloc = -INFINITY;
+          // row maximum on the raw logits (the scale is positive); then
+          // p = 2^(s * scale_log2 - m) is one FMA and one v_exp_f32
+          float mraw = -INFINITY;
 #pragma unroll
           for (int j = 0; j < 2; ++j)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
               const int tok = tok_of(2 * half + j, 4 * kg + i);
-              const float z = (act[rt] && tok < nv) ? sacc[j][rt][i] * p.scale_log2 : -INFINITY;
-              sacc[j][rt][i] = z;
-              mloc = fmaxf(mloc, z);
+              if (!(act[rt] && tok < nv)) sacc[j][rt][i] = -INFINITY;
+              mraw = fmaxf(mraw, sacc[j][rt][i]);
             }
-          mloc = fmaxf(mloc, __shfl_xor(mloc, 16, 64));
-          mloc = fmaxf(mloc, __shfl_xor(mloc, 32, 64));
+          mraw = fmaxf(mraw, __shfl_xor(mraw, 16, 64));
+          mraw = fmaxf(mraw, __shfl_xor(mraw, 32, 64));
+          const float mloc = mraw == -INFINITY ? -INFINITY : mraw * p.scale_log2;
           if (attempt == 1) {
             m_ref[rt] = fmaxf(m_ref[rt], mloc);
             continue;
@@ -290,7 +292,7 @@ __global__ __launch_bounds__(256, 1) void mla_decode_kernel(DecodeParams p) {
           for (int j = 0; j < 2; ++j)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-              const float pv = exp2f(sacc[j][rt][i] - msub);
+              const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[j][rt][i], p.scale_log2, -msub));
               psum += pv;
               pb[rt][4 * j + i] = (__bf16)pv;
             }

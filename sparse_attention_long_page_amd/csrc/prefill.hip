@@ -115,6 +115,12 @@ constexpr int kKTile = kPP * kKRow;
 constexpr int kVTile = kPD * kVRow;
 constexpr float kRescaleThreshold = 8.0f;   // log2 units
 
+// 16-byte column chunk c (0..15) of K row r sits at chunk kswz(r, c) of its
+// LDS row.  The 8 lanes of one LDS pass read rows R + {0..3, 8..11} (the
+// token permutation below); with 272-byte rows those pairs 8 rows apart would
+// share banks, and the XOR moves the second four 16 dwords away.
+__device__ __forceinline__ int kswz(int r, int c) { return c ^ (4 * ((r >> 3) & 1)); }
+
 // HW query heads per workgroup, two waves per head (query rows 0-31 and
 // 32-63 of the tile).  A group larger than HW is split over G/HW workgroups.
 template <int HW>
@@ -196,7 +202,7 @@ __global__ __launch_bounds__(128 * HW) void prefill_kernel(PrefillParams p) {
 #pragma unroll
     for (int j = 0; j < per_thr; ++j) {
       const int c = tid + j * nthr;
-      *reinterpret_cast<u32x4*>(&sk[stage][(c >> 4) * kKRow + (c & 15) * 8]) = stk[j];
+      *reinterpret_cast<u32x4*>(&sk[stage][(c >> 4) * kKRow + kswz(c >> 4, c & 15) * 8]) = stk[j];
       *reinterpret_cast<u32x4*>(&sv[stage][(c >> 3) * kVRow + (c & 7) * 8]) = stv[j];
     }
   };
@@ -230,14 +236,18 @@ __global__ __launch_bounds__(128 * HW) void prefill_kernel(PrefillParams p) {
         const int tau = 32 * (j4 >> 1) + 8 * (col >> 2) + 4 * (j4 & 1) + (col & 3);
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) {
-          const bf16x8 a = *reinterpret_cast<const bf16x8*>(K + tau * kKRow + 8 * kg + 32 * kk);
+          const bf16x8 a = *reinterpret_cast<const bf16x8*>(K + tau * kKRow + 8 * kswz(tau, kg + 4 * kk));
 #pragma unroll
           for (int rt = 0; rt < kRT; ++rt)
             sacc[j4][rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qreg[rt][kk], sacc[j4][rt], 0, 0, 0);
         }
       }
 
-      // softmax (lane: row 16*rt + col, tokens 32*(j4/2) + 8*kg + 4*(j4%2) + i)
+      // softmax (lane: row 16*rt + col, tokens 32*(j4/2) + 8*kg + 4*(j4%2) + i).
+      // The row maximum is taken on the raw logits (the scale is positive),
+      // then p = 2^(s * scale_log2 - m) is one FMA and one v_exp_f32
+      // (results below 2^-126 flush to zero: their weight relative to the
+      // row maximum is below 2^-126).
       const bool full = (tok0 + kPP - 1 <= wpos_lo) && (tok0 + kPP <= seq_len);
       bf16x8 pb[kRT][2];
       float alpha[kRT];
@@ -245,26 +255,25 @@ __global__ __launch_bounds__(128 * HW) void prefill_kernel(PrefillParams p) {
 #pragma unroll
       for (int rt = 0; rt < kRT; ++rt) {
         const int row_pos = wpos_lo + 16 * rt + col;
-        float mloc = -INFINITY;
+        float mraw = -INFINITY;
 #pragma unroll
         for (int j4 = 0; j4 < 4; ++j4)
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            float z = sacc[j4][rt][i] * p.scale_log2;
             if (!full) {
               const int j = tok0 + 32 * (j4 >> 1) + 8 * kg + 4 * (j4 & 1) + i;
-              if (j > row_pos || j >= seq_len) z = -INFINITY;
+              if (j > row_pos || j >= seq_len) sacc[j4][rt][i] = -INFINITY;
             }
-            sacc[j4][rt][i] = z;
-            mloc = fmaxf(mloc, z);
+            mraw = fmaxf(mraw, sacc[j4][rt][i]);
           }
-        mloc = fmaxf(mloc, __shfl_xor(mloc, 16, 64));
-        mloc = fmaxf(mloc, __shfl_xor(mloc, 32, 64));
+        mraw = fmaxf(mraw, __shfl_xor(mraw, 16, 64));
+        mraw = fmaxf(mraw, __shfl_xor(mraw, 32, 64));
+        const float mloc = mraw == -INFINITY ? -INFINITY : mraw * p.scale_log2;
         // move the reference only when the row maximum outgrows it
         float mref = m_ref[rt];
         alpha[rt] = 1.f;
         if (mloc > mref + kRescaleThreshold || (mref == -INFINITY && mloc != -INFINITY)) {
-          alpha[rt] = mref == -INFINITY ? 0.f : exp2f(mref - mloc);
+          alpha[rt] = mref == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mref - mloc);
           mref = mloc;
           need_rescale = true;
         }
@@ -275,7 +284,7 @@ __global__ __launch_bounds__(128 * HW) void prefill_kernel(PrefillParams p) {
         for (int j4 = 0; j4 < 4; ++j4)
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            const float pv = exp2f(sacc[j4][rt][i] - msub);
+            const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[j4][rt][i], p.scale_log2, -msub));
             psum += pv;
             pb[rt][j4 >> 1][4 * (j4 & 1) + i] = (__bf16)pv;
           }

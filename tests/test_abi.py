@@ -119,6 +119,8 @@ DECODE_CASES = [
     ("negative splits", {}, dict(splits=-1), INV),
     ("tier args unpaired", {}, dict(ccounts=FAKE), INV),
     ("nan scale", {}, dict(scale=float("nan")), INV),
+    ("negative scale", {}, dict(scale=-0.5), INV),
+    ("zero scale", {}, dict(scale=0.0), INV),
     ("missing out", {}, dict(out=None), INV),
     ("zero stride", {}, dict(stride=0), INV),
     ("latent with 2 kv heads", dict(kv=dict(v_pool=None, d_qk=576, d_v=512)), {}, UNS),
@@ -146,6 +148,7 @@ PREFILL_CASES = [
     ("negative start", {}, dict(q_start=-1), INV),
     ("zero block_q", {}, dict(block_q=0), INV),
     ("null mask", {}, dict(mask=None), INV),
+    ("negative scale", {}, dict(scale=-1.0), INV),
     ("group too large", dict(kv=dict(n_kv_heads=1)), dict(n_q_heads=16), UNS),
 ]
 
