@@ -208,7 +208,8 @@ sa_status sa_sparse_decode(const sa_paged_kv* kv, int32_t batch,
  *   block_table_out  out [n_kv_heads][n_kv_blocks] int32 (entries past the
  *              count are left untouched); block_counts_out out [n_kv_heads]
  *   out        [q_len][n_q_heads][d_v];  out_lse [q_len][n_q_heads] fp32 or NULL
- * Needs bf16, d_qk == d_v == 128, page_size 64, n_kv_blocks <= max_pages.
+ * Needs bf16, d_qk == d_v == 128, page_size 64, n_kv_blocks <= max_pages and
+ * n_kv_blocks <= 4096 (262144 tokens).
  * ---------------------------------------------------------------------- */
 size_t sa_block_sparse_prefill_workspace_size(const sa_paged_kv* kv, int32_t q_len,
                                               int32_t n_q_heads, int32_t n_kv_blocks);

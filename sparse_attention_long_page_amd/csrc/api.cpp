@@ -395,6 +395,8 @@ sa_status sa_block_sparse_prefill(const sa_paged_kv* kv, int32_t seq, const void
   if (n_q_heads <= 0 || n_q_heads % kv->n_kv_heads != 0)
     return fail(SA_ERR_INVALID_ARGUMENT, "n_q_heads must be a positive multiple of n_kv_heads");
   const long need_blocks = ((long)q_start + q_len + kv->page_size - 1) / kv->page_size;
+  if (n_kv_blocks > 4096)
+    return fail(SA_ERR_UNSUPPORTED, "prefill supports up to 4096 KV blocks (got %d)", n_kv_blocks);
   if (n_kv_blocks < need_blocks || n_kv_blocks > kv->max_pages)
     return fail(SA_ERR_INVALID_ARGUMENT, "n_kv_blocks %d must cover q_start+q_len (%ld) and be <= max_pages %d",
                 n_kv_blocks, need_blocks, kv->max_pages);

@@ -113,6 +113,15 @@ constexpr int kKRow = kPD + 8;    // padded K row in LDS (bf16 elements): 272 B
 constexpr int kVRow = kPP + 8;    // padded V^T row in LDS: 144 B
 constexpr int kKTile = kPP * kKRow;
 constexpr int kVTile = kPD * kVRow;
+// One pipeline stage holds a block's K tile (64 rows of 16 data chunks + 1 pad
+// chunk) followed by its V^T tile (128 rows of 8 data chunks + 1 pad chunk):
+// 2240 16-byte chunks, filled by 35 wave-wide LDS-DMA loads.
+constexpr int kKChunks = kPP * (kKRow / 8);      // 1088
+constexpr int kVChunks = kPD * (kVRow / 8);      // 1152
+constexpr int kStageInstr = (kKChunks + kVChunks) / 64;   // 35
+constexpr int kStageElems = kKTile + kVTile;     // bf16 elements per stage (35840 B)
+static_assert((kKChunks + kVChunks) % 64 == 0, "stage must be whole wave loads");
+constexpr int kPrefillMaxBlocks = 4096;           // KV blocks a tile may sweep (262144 tokens)
 constexpr float kRescaleThreshold = 8.0f;   // log2 units
 
 // 16-byte column chunk c (0..15) of K row r sits at chunk kswz(r, c) of its
@@ -121,15 +130,26 @@ constexpr float kRescaleThreshold = 8.0f;   // log2 units
 // share banks, and the XOR moves the second four 16 dwords away.
 __device__ __forceinline__ int kswz(int r, int c) { return c ^ (4 * ((r >> 3) & 1)); }
 
+template <int V>
+struct Stage {
+  static constexpr int value = V;
+};
+
 // HW query heads per workgroup, two waves per head (query rows 0-31 and
 // 32-63 of the tile).  A group larger than HW is split over G/HW workgroups.
 template <int HW>
 __global__ __launch_bounds__(128 * HW) void prefill_kernel(PrefillParams p) {
-  __shared__ __attribute__((aligned(16))) uint16_t sk[2][kKTile];
-  __shared__ __attribute__((aligned(16))) uint16_t sv[2][kVTile];
-  constexpr int nthr = 128 * HW;
+  // three pipeline stages as distinct LDS objects: the copy of block t+2 runs
+  // while block t is computed and block t+1 has landed
+  __shared__ __attribute__((aligned(16))) uint16_t st0[kStageElems];
+  __shared__ __attribute__((aligned(16))) uint16_t st1[kStageElems];
+  __shared__ __attribute__((aligned(16))) uint16_t st2[kStageElems];
+  __shared__ int kb_s[kPrefillMaxBlocks], ph_s[kPrefillMaxBlocks];
+  constexpr int NW = 2 * HW;                                  // waves per workgroup
+  constexpr int NI = (kStageInstr + NW - 1) / NW;             // copy loads per wave per block
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 15, kg = lane >> 4;
 
   const int nwg = gridDim.x, w = blockIdx.x;
@@ -183,44 +203,47 @@ __global__ __launch_bounds__(128 * HW) void prefill_kernel(PrefillParams p) {
     nblk = lo;
   }
 
-  // per-thread share of a block copy: 1024 16-byte chunks of K and of V^T
-  constexpr int per_thr = 1024 / nthr;
-  u32x4 stk[per_thr], stv[per_thr];
-  auto fetch = [&](int t) {
-    const int kb = table[t];
-    const int phys = p.bt_row[kb];
+  // LDS-DMA copy of table entry t into a stage: wave-wide load i covers stage
+  // chunks [64 i, 64 i + 64).  K chunk slot (r, c) of row r receives data
+  // chunk kswz(r, c) (an involution), V^T slots copy straight; pad slots
+  // re-read chunk 0 of their row.  Every wave issues exactly NI loads (the
+  // last real load is repeated to fill), so the wait below can count them.
+  auto stage_copy = [&](uint16_t* st, int t) {
+    const int kb = kb_s[t];
+    const int phys = ph_s[t];
     const uint16_t* kb_base = kpool + ((size_t)phys * p.Hkv + g) * kPP * kPD;
     const uint16_t* vb_base = vpool + ((size_t)phys * p.Hkv + g) * kPD * kPP;
 #pragma unroll
-    for (int j = 0; j < per_thr; ++j) {
-      const int c = tid + j * nthr;
-      stk[j] = *reinterpret_cast<const u32x4*>(kb_base + (c >> 4) * kPD + (c & 15) * 8);
-      stv[j] = *reinterpret_cast<const u32x4*>(vb_base + (c >> 3) * kPP + (c & 7) * 8);
+    for (int j = 0; j < NI; ++j) {
+      const int i = min(wave + NW * j, kStageInstr - 1);
+      const int c = 64 * i + lane;
+      const uint16_t* src;
+      if (c < kKChunks) {
+        const int r = c / (kKRow / 8), slot = c % (kKRow / 8);
+        src = kb_base + r * kPD + 8 * (slot < 16 ? kswz(r, slot) : 0);
+      } else {
+        const int cv = c - kKChunks;
+        const int r = cv / (kVRow / 8), slot = cv % (kVRow / 8);
+        src = vb_base + r * kPP + 8 * (slot < 8 ? slot : 0);
+      }
+      __builtin_amdgcn_global_load_lds(src, st + i * 512, 16, 0, 0);
     }
   };
-  auto stash = [&](int stage) {
-#pragma unroll
-    for (int j = 0; j < per_thr; ++j) {
-      const int c = tid + j * nthr;
-      *reinterpret_cast<u32x4*>(&sk[stage][(c >> 4) * kKRow + kswz(c >> 4, c & 15) * 8]) = stk[j];
-      *reinterpret_cast<u32x4*>(&sv[stage][(c >> 3) * kVRow + (c & 7) * 8]) = stv[j];
-    }
-  };
 
-  if (nblk > 0) {
-    fetch(0);
-    stash(0);
-  }
-  __syncthreads();
-
-  for (int t = 0; t < nblk; ++t) {
-    const int stage = t & 1;
-    const int kb = table[t];
-    const bool more = t + 1 < nblk;
-    if (more) fetch(t + 1);
-
-    const uint16_t* K = sk[stage];
-    const uint16_t* V = sv[stage];
+  // one block: wait for its copy (the next block's NI loads may stay in
+  // flight), barrier, start the copy two blocks ahead, compute
+  auto block = [&](auto sidx, int t) {
+    uint16_t* cur = sidx.value == 0 ? st0 : (sidx.value == 1 ? st1 : st2);
+    uint16_t* ahead = sidx.value == 0 ? st2 : (sidx.value == 1 ? st0 : st1);
+    // (a plain s_barrier: a __syncthreads() fence would also drain the copy
+    // of the next block; every LDS read of the stage about to be refilled was
+    // consumed before its wave reached this point)
+    if (t + 1 < nblk) asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" :: "n"(NI) : "memory");
+    else asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+    if (t + 2 < nblk) stage_copy(ahead, t + 2);
+    const int kb = kb_s[t];
+    const uint16_t* K = cur;
+    const uint16_t* V = cur + kKTile;
     const int tok0 = kb * kPP;
     // blocks entirely past this wave's rows contribute nothing (the tile's
     // other wave may still need them)
@@ -312,8 +335,23 @@ __global__ __launch_bounds__(128 * HW) void prefill_kernel(PrefillParams p) {
         }
     }
 
-    if (more) stash(stage ^ 1);
-    __syncthreads();
+  };
+
+  // the tile's table entries and their physical pages, read once into LDS so
+  // that no global load is waited on while block copies are in flight (the
+  // load counter completes in issue order)
+  for (int t = tid; t < nblk; t += 128 * HW) kb_s[t] = table[t];
+  __syncthreads();
+  for (int t = tid; t < nblk; t += 128 * HW) ph_s[t] = p.bt_row[kb_s[t]];
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+
+  if (nblk > 0) stage_copy(st0, 0);
+  if (nblk > 1) stage_copy(st1, 1);
+  for (int t = 0; t < nblk; t += 3) {
+    block(Stage<0>{}, t);
+    if (t + 1 < nblk) block(Stage<1>{}, t + 1);
+    if (t + 2 < nblk) block(Stage<2>{}, t + 2);
   }
 
   // epilogue: O = O^T / l per row
