@@ -32,12 +32,20 @@
 namespace sa {
 
 // ---------------------------------------------------------------- bf16 / MFMA
+// The list, block table, lengths and counts arrive as restrict kernel
+// arguments: the kernel never writes them, so their wave-uniform reads compile
+// to scalar loads, which complete on their own counter and never wait behind
+// the K/V vector loads in flight.
 template <int D, int P, bool TIERED>
-__global__ __launch_bounds__(256, 2) void decode_bf16_kernel(DecodeParams p) {
+__global__ __launch_bounds__(256, 2) void decode_bf16_kernel(DecodeParams p, const int32_t* __restrict__ lists,
+                                                            const int32_t* __restrict__ btab,
+                                                            const int32_t* __restrict__ seq_lens,
+                                                            const int32_t* __restrict__ counts) {
   constexpr int KSTEPS = D / 32;
   constexpr int DTILES = D / 16;
   constexpr int E = 64 / P;            // list entries per 64-token chunk
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int col = lane & 15, kg = lane >> 4;
 
   int u = blockIdx.x;
@@ -48,14 +56,15 @@ __global__ __launch_bounds__(256, 2) void decode_bf16_kernel(DecodeParams p) {
   const int g = p.per_q ? s / p.G : s;
   const int R = p.per_q ? p.T : p.T * p.G;
   const int sel = b * p.n_sel + s;
-  const int count = p.counts[sel];
-  const int32_t* list = p.lists + (size_t)sel * p.list_stride;
+  const int count = counts[sel];
+  const int32_t* list = lists + (size_t)sel * p.list_stride;
   const int cc = TIERED ? p.ccounts[sel] : count;
   const int sbase = count / p.splits, sextra = count % p.splits;
   const int beg = split * sbase + min(split, sextra);
   const int len = sbase + (split < sextra ? 1 : 0);
   const int end = beg + len;
-  const int seq_len = p.seq_lens[b];
+  const int seq_len = seq_lens[b];
+  const int32_t* bt = btab + (size_t)b * p.max_pages;
 
   // query row of this lane's MFMA column
   const bool row_ok = col < R;
@@ -82,31 +91,50 @@ __global__ __launch_bounds__(256, 2) void decode_bf16_kernel(DecodeParams p) {
 
   const uint16_t* kpool = reinterpret_cast<const uint16_t*>(p.k_pool);
   const uint16_t* vpool = reinterpret_cast<const uint16_t*>(p.v_pool);
-  const int nchunks = (len + E - 1) / E;
+  const int nchunks = seq_len > 0 ? (len + E - 1) / E : 0;
 
-  for (int c = wave; c < nchunks; c += 4) {
+  // Chunk metadata is pipelined over two iterations with no branches, so its
+  // scalar loads never wait in the middle of a chunk: the list entries of
+  // chunk c+8 and the block-table entries of chunk c+4 are read while chunk c
+  // computes.  Entries past the split, or pages with no valid token, point at
+  // the sequence's first page (allocated whenever seq_len > 0) so that every
+  // K/V load is unconditional; their tokens are masked, and their V rows only
+  // meet zero probabilities.
+  const int bt0 = seq_len > 0 ? bt[0] : 0;
+  auto load_lps = [&](int c, int* lp) {
     const int e0 = beg + c * E;
-    int phys[E], nval[E];
-    bool act[E];
+#pragma unroll
+    for (int j = 0; j < E; ++j) lp[j] = list[min(e0 + j, end - 1)];
+  };
+  auto resolve = [&](int c, const int* lp, int* phys, int* nval, bool* act) {
+    const int e0 = beg + c * E;
+#pragma unroll
+    for (int j = 0; j < E; ++j) phys[j] = bt[lp[j]];   // used only where nval > 0 (see page_of)
 #pragma unroll
     for (int j = 0; j < E; ++j) {
       const int e = e0 + j;
-      if (e < end) {
-        const int lp = list[e];
-        phys[j] = p.block_table[(size_t)b * p.max_pages + lp];
-        nval[j] = page_valid(seq_len, lp, P);
-        bool a = true;
-        if (TIERED && e >= cc) {
-          const uint32_t w = p.amask[((size_t)b * p.max_pages + lp) * p.mask_words + (h_row >> 5)];
-          a = row_ok && ((w >> (h_row & 31)) & 1u);
-        }
-        act[j] = a;
-      } else {
-        phys[j] = 0;
-        nval[j] = 0;
-        act[j] = false;
+      nval[j] = e < end ? page_valid(seq_len, lp[j], P) : 0;
+      bool a = e < end;
+      if (TIERED && e < end && e >= cc) {
+        const uint32_t w = p.amask[((size_t)b * p.max_pages + lp[j]) * p.mask_words + (h_row >> 5)];
+        a = row_ok && ((w >> (h_row & 31)) & 1u);
       }
+      act[j] = a;
     }
+  };
+
+  int phys[E], nval[E], lp_next[E];
+  bool act[E];
+  if (wave < nchunks) {
+    int lp0[E];
+    load_lps(wave, lp0);
+    resolve(wave, lp0, phys, nval, act);
+    if (wave + 4 < nchunks) load_lps(wave + 4, lp_next);
+  }
+  for (int c = wave; c < nchunks; c += 4) {
+    // physical page of chunk entry j: the sequence's first page stands in for
+    // entries with no valid token
+    auto page_of = [&](int j) { return nval[j] > 0 ? phys[j] : bt0; };
 
     // K: A operand of tile j4, row m = col holds token
     //   tau = 32*(j4/2) + 8*(m/4) + 4*(j4%2) + m%4
@@ -115,11 +143,9 @@ __global__ __launch_bounds__(256, 2) void decode_bf16_kernel(DecodeParams p) {
     for (int j4 = 0; j4 < 4; ++j4) {
       const int tau = 32 * (j4 >> 1) + 8 * (col >> 2) + 4 * (j4 & 1) + (col & 3);
       const int ent = tau / P, r = tau % P;
-      const uint16_t* kb = kpool + (((size_t)phys[ent] * p.Hkv + g) * P + r) * D + 8 * kg;
-      const bool ld = nval[ent] > 0;
+      const uint16_t* kb = kpool + (((size_t)page_of(ent) * p.Hkv + g) * P + r) * D + 8 * kg;
 #pragma unroll
-      for (int kk = 0; kk < KSTEPS; ++kk)
-        kreg[j4][kk] = ld ? *reinterpret_cast<const bf16x8*>(kb + 32 * kk) : bf16x8{};
+      for (int kk = 0; kk < KSTEPS; ++kk) kreg[j4][kk] = *reinterpret_cast<const bf16x8*>(kb + 32 * kk);
     }
     // V^T: A operand of PV tile dt, k-step kp: dim 16*dt + col, tokens 32*kp + 8*kg + 0..7
     bf16x8 vreg[DTILES][2];
@@ -127,12 +153,16 @@ __global__ __launch_bounds__(256, 2) void decode_bf16_kernel(DecodeParams p) {
     for (int kp = 0; kp < 2; ++kp) {
       const int t0 = 32 * kp + 8 * kg;
       const int ent = t0 / P, r0 = t0 % P;
-      const uint16_t* vb = vpool + (((size_t)phys[ent] * p.Hkv + g) * D + col) * P + r0;
-      const bool ld = nval[ent] > 0;
+      const uint16_t* vb = vpool + (((size_t)page_of(ent) * p.Hkv + g) * D + col) * P + r0;
 #pragma unroll
-      for (int dt = 0; dt < DTILES; ++dt)
-        vreg[dt][kp] = ld ? *reinterpret_cast<const bf16x8*>(vb + (size_t)16 * dt * P) : bf16x8{};
+      for (int dt = 0; dt < DTILES; ++dt) vreg[dt][kp] = *reinterpret_cast<const bf16x8*>(vb + (size_t)16 * dt * P);
     }
+
+    // metadata of the next two chunks (scalar loads) while this one computes
+    int nphys[E], nnval[E], lp_after[E];
+    bool nact[E];
+    if (c + 4 < nchunks) resolve(c + 4, lp_next, nphys, nnval, nact);
+    if (c + 8 < nchunks) load_lps(c + 8, lp_after);
 
     f32x4 sacc[4];
 #pragma unroll
@@ -187,6 +217,13 @@ __global__ __launch_bounds__(256, 2) void decode_bf16_kernel(DecodeParams p) {
 #pragma unroll
       for (int dt = 0; dt < DTILES; ++dt)
         oacc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vreg[dt][kp], pb[kp], oacc[dt], 0, 0, 0);
+#pragma unroll
+    for (int j = 0; j < E; ++j) {
+      phys[j] = nphys[j];
+      nval[j] = nnval[j];
+      act[j] = nact[j];
+      lp_next[j] = lp_after[j];
+    }
   }
 
   // combine the 4 waves
@@ -374,10 +411,14 @@ hipError_t launch_decode(const DecodeParams& p, int bf16, hipStream_t s) {
     else hipLaunchKernelGGL(decode_f32_kernel<128>, grid, block, 0, s, p);
     return hipGetLastError();
   }
-#define SA_DECODE_LAUNCH(D_, P_)                                                        \
-  do {                                                                                  \
-    if (tiered) hipLaunchKernelGGL((decode_bf16_kernel<D_, P_, true>), grid, block, 0, s, p); \
-    else hipLaunchKernelGGL((decode_bf16_kernel<D_, P_, false>), grid, block, 0, s, p);      \
+#define SA_DECODE_LAUNCH(D_, P_)                                                                        \
+  do {                                                                                                  \
+    if (tiered)                                                                                         \
+      hipLaunchKernelGGL((decode_bf16_kernel<D_, P_, true>), grid, block, 0, s, p, p.lists, p.block_table, \
+                         p.seq_lens, p.counts);                                                         \
+    else                                                                                                \
+      hipLaunchKernelGGL((decode_bf16_kernel<D_, P_, false>), grid, block, 0, s, p, p.lists, p.block_table, \
+                         p.seq_lens, p.counts);                                                         \
   } while (0)
   if (p.d_qk == 64 && p.P == 16) SA_DECODE_LAUNCH(64, 16);
   else if (p.d_qk == 64 && p.P == 64) SA_DECODE_LAUNCH(64, 64);
