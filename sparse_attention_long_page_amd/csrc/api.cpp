@@ -98,9 +98,12 @@ int choose_splits(const sa_paged_kv* kv, int batch, int n_sel, int list_stride, 
     s = std::min(s, std::max(1, list_stride / 2));
     return std::max(1, std::min(s, 64));
   }
+  // The decode kernel is bound by its K/V loads once every CU holds one
+  // workgroup (4 waves, 32 KiB of loads in flight each); more splits then
+  // only add partials and the merge.
   const int per_chunk = 64 / kv->page_size;
   const int chunks = (list_stride + per_chunk - 1) / per_chunk;
-  const int target = 2 * cus;                // 2 workgroups (8 waves) per CU
+  const int target = cus;
   int s = (target + units - 1) / units;
   s = std::min(s, std::max(1, chunks / 4));  // at least one chunk per wave
   return std::max(1, std::min(s, 64));

@@ -47,6 +47,7 @@ constexpr int kMTile = kMP * kMRS;       // elements per staged page
 constexpr int kMInstr = kMP * kMRowChunks / 64;   // 73 wave-wide 16-byte DMA loads per page
 constexpr int kMKSteps = kMD / 32;       // 18
 constexpr int kMDTiles = kMDV / 16;      // 32
+constexpr int kMetaWin = 256;            // pages of page metadata held in LDS
 constexpr float kMMargin = 64.0f;         // log2 units a logit may exceed its row's reference
 
 // Token of row m (0..15) of the 16-token MFMA tile j4 of a page.  Rows
@@ -76,6 +77,10 @@ __global__ __launch_bounds__(256, 1) void mla_decode_kernel(DecodeParams p) {
   // tell an LDS-DMA into one from reads of the other
   __shared__ __attribute__((aligned(16))) uint16_t sk0[kMTile];
   __shared__ __attribute__((aligned(16))) uint16_t sk1[kMTile];
+  // metadata of a window of the split's pages: physical page, valid tokens,
+  // and the Ambient head-mask words covering this workgroup's heads
+  __shared__ int m_phys[kMetaWin], m_nv[kMetaWin];
+  __shared__ uint32_t m_word[kMetaWin][4];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform per wave
   const int col = lane & 15, kg = lane >> 4;
@@ -115,6 +120,7 @@ __global__ __launch_bounds__(256, 1) void mla_decode_kernel(DecodeParams p) {
     row_ok[rt] = h_row[rt] < p.Hq;
   }
   const bool wave_rows = rg * heads_per_wg + wave * 2 * heads_per_tile < p.Hq;   // uniform
+  const int word0 = (rg * heads_per_wg) >> 5;      // the workgroup's heads span words word0 .. word0+3
 
   // Q^T operand, resident: tile rt, k-step kk -> row col, dims 8*kg + 32*kk .. +8
   const uint16_t* qp = reinterpret_cast<const uint16_t*>(p.q);
@@ -181,32 +187,41 @@ __global__ __launch_bounds__(256, 1) void mla_decode_kernel(DecodeParams p) {
     const bool do_pv = attempt != 1;
 
     // metadata of the page being computed (cur_*) and of the next one
-    int cur_lp = 0, cur_nv = 0;
-    if (beg < end) {
-      cur_lp = list[beg];
-      cur_nv = page_valid(seq_len, cur_lp, kMP);
-      if (cur_nv > 0) stage(sk0, btab[cur_lp]);
-    }
+    // page metadata for pages [w0, w0 + kMetaWin) of the split, read into LDS
+    // while no page copy is in flight (global loads complete in issue order)
+    int w0 = beg;
+    auto load_meta = [&](int first) {
+      for (int i = threadIdx.x; i < kMetaWin && first + i < end; i += 256) {
+        const int e = first + i;
+        const int lp = list[e];
+        const int nv = page_valid(seq_len, lp, kMP);
+        m_nv[i] = nv;
+        m_phys[i] = nv > 0 ? btab[lp] : 0;
+        const bool ambient = p.ccounts && e >= cc;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const int widx = word0 + k;
+          m_word[i][k] = (ambient && widx < p.mask_words)
+                             ? p.amask[((size_t)b * p.max_pages + lp) * p.mask_words + widx]
+                             : 0xffffffffu;
+        }
+      }
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
+    };
+    load_meta(beg);
+    if (beg < end && m_nv[0] > 0) stage(sk0, m_phys[0]);
 
     // one page: compute from `cur` while the next page is copied into `nxt`
     auto page = [&](auto parity, int e) {
       uint16_t* cur = parity.value ? sk1 : sk0;
       uint16_t* nxt = parity.value ? sk0 : sk1;
-      const int lp = cur_lp, nv = cur_nv;
-      uint32_t word[2] = {0xffffffffu, 0xffffffffu};
-      if (p.ccounts && e >= cc) {
-#pragma unroll
-        for (int rt = 0; rt < 2; ++rt)
-          word[rt] = p.amask[((size_t)b * p.max_pages + lp) * p.mask_words + tile_word[rt]];
-      }
-      int nlp = 0, nnv = 0, nphys = 0;
-      if (e + 1 < end) {
-        nlp = list[e + 1];
-        nnv = page_valid(seq_len, nlp, kMP);
-        if (nnv > 0) nphys = btab[nlp];
-      }
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       __syncthreads();
+      const int nv = m_nv[e - w0];
+      uint32_t word[2];
+#pragma unroll
+      for (int rt = 0; rt < 2; ++rt) word[rt] = m_word[e - w0][tile_word[rt] - word0];
       if (nv > 0 && nv < kMP) {
         // tokens past the sequence end: zero their rows (V operand must be finite)
         for (int idx = threadIdx.x; idx < (kMP - nv) * 72; idx += 256) {
@@ -215,8 +230,15 @@ __global__ __launch_bounds__(256, 1) void mla_decode_kernel(DecodeParams p) {
         }
         __syncthreads();
       }
-      // which of this wave's rows attend the page (decided before the next
-      // copy is issued: its completion is awaited in order with these loads)
+      if (e + 1 < end) {
+        if (e + 1 - w0 == kMetaWin) {           // next window (long splits only)
+          __syncthreads();
+          w0 = e + 1;
+          load_meta(w0);
+        }
+        if (m_nv[e + 1 - w0] > 0) stage(nxt, m_phys[e + 1 - w0]);
+      }
+      // which of this wave's rows attend the page
       bool act[2];
       bool any_row = false;
 #pragma unroll
@@ -224,9 +246,6 @@ __global__ __launch_bounds__(256, 1) void mla_decode_kernel(DecodeParams p) {
         act[rt] = row_ok[rt] && ((word[rt] >> (h_row[rt] & 31)) & 1u);
         any_row |= __any(act[rt]) != 0;
       }
-      if (nnv > 0) stage(nxt, nphys);
-      cur_lp = nlp;
-      cur_nv = nnv;
       if (nv == 0 || !wave_rows || !any_row) return;
 
       const uint16_t* K = cur;
@@ -341,37 +360,53 @@ __global__ __launch_bounds__(256, 1) void mla_decode_kernel(DecodeParams p) {
   }
 
   // epilogue: O = O^T / l per row; lane holds dims 16*dt + 4*kg + 0..3 of row col
+  float lse_row[2];
+  size_t orow[2];
 #pragma unroll
   for (int rt = 0; rt < 2; ++rt) {
     float l = l_run[rt];
     l += __shfl_xor(l, 16, 64);
     l += __shfl_xor(l, 32, 64);
-    if (!row_ok[rt]) continue;
     const bool empty = m_ref[rt] == -INFINITY;
     const float inv = empty ? 0.f : 1.f / l;
-    const float lse = empty ? -INFINITY : (m_ref[rt] + log2f(l)) * kLn2;
-    const size_t orow = ((size_t)b * T + t_row[rt]) * p.Hq + h_row[rt];
+    lse_row[rt] = empty ? -INFINITY : (m_ref[rt] + log2f(l)) * kLn2;
+    orow[rt] = ((size_t)b * T + t_row[rt]) * p.Hq + h_row[rt];
+    if (!row_ok[rt]) continue;
     if (p.splits == 1) {
-      uint16_t* out = reinterpret_cast<uint16_t*>(p.out) + orow * kMDV;
+      uint16_t* out = reinterpret_cast<uint16_t*>(p.out) + orow[rt] * kMDV;
 #pragma unroll
       for (int dt = 0; dt < kMDTiles; ++dt) {
+        f32x4 v = oacc[dt][rt];
+        v[0] *= inv; v[1] *= inv; v[2] *= inv; v[3] *= inv;
         uint2 pk;
-        pk.x = (uint32_t)f32_to_bf16_bits(oacc[dt][rt][0] * inv) |
-               ((uint32_t)f32_to_bf16_bits(oacc[dt][rt][1] * inv) << 16);
-        pk.y = (uint32_t)f32_to_bf16_bits(oacc[dt][rt][2] * inv) |
-               ((uint32_t)f32_to_bf16_bits(oacc[dt][rt][3] * inv) << 16);
+        pk.x = (uint32_t)f32_to_bf16_bits(v[0]) | ((uint32_t)f32_to_bf16_bits(v[1]) << 16);
+        pk.y = (uint32_t)f32_to_bf16_bits(v[2]) | ((uint32_t)f32_to_bf16_bits(v[3]) << 16);
         *reinterpret_cast<uint2*>(out + 16 * dt + 4 * kg) = pk;
       }
-      if (kg == 0 && p.out_lse) p.out_lse[orow] = lse;
     } else {
-      float* po = p.part_o + (orow * p.splits + split) * kMDV;
+      float* po = p.part_o + (orow[rt] * p.splits + split) * kMDV;
 #pragma unroll
       for (int dt = 0; dt < kMDTiles; ++dt) {
         f32x4 v = oacc[dt][rt];
         v[0] *= inv; v[1] *= inv; v[2] *= inv; v[3] *= inv;
         *reinterpret_cast<f32x4*>(po + 16 * dt + 4 * kg) = v;
       }
-      if (kg == 0) p.part_lse[orow * p.splits + split] = lse;
+    }
+  }
+  // One lane per row stores the log-sum-exp, after every output store: with
+  // no register live past this branch, none can be restored from a spill
+  // under its narrowed lane mask (the compiler in use did that, clobbering
+  // accumulators of the other 48 lanes, when these stores sat between the
+  // two row tiles).
+  if (kg == 0) {
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt) {
+      if (!row_ok[rt]) continue;
+      if (p.splits == 1) {
+        if (p.out_lse) p.out_lse[orow[rt]] = lse_row[rt];
+      } else {
+        p.part_lse[orow[rt] * p.splits + split] = lse_row[rt];
+      }
     }
   }
 }

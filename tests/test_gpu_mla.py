@@ -58,6 +58,8 @@ CASES = {
     "h144": SMALL.replace(n_q_heads=144, ambient_heads=40, batch=1),
     # no Ambient head at all for some pages' heads; no tiers beyond Critical
     "critical_only": SMALL.replace(top_k=4, critical_k=4, ambient_heads=3),
+    # a split longer than the kernel's 256-page metadata window
+    "long_split": SMALL.replace(batch=1, context=64 * 400 + 17, top_k=270, critical_k=30, ambient_heads=8),
 }
 
 
