@@ -81,7 +81,9 @@ def decode_step_fn(S, wl, inp, mu, splits):
     """One decode step as one HIP graph on the current stream: page summary of
     the newest page, selection, split-K decode and LSE merge.  Graph replay
     removes the host launch cost between kernels; every kernel still runs in
-    every replay."""
+    every replay.  A captured graph does not own the memory its kernels use,
+    so the last value returned holds every buffer the graph touches; keep it
+    as long as the graph."""
     kv = S.PagedKV(inp["k_pool"], inp["v_pool"], inp["block_table"], inp["seq_lens"], d_v=wl.d_v)
     mode = S.SA_SEL_PER_KV_HEAD if wl.mode == "per_kv_head" else S.SA_SEL_PER_Q_HEAD
     stride = max(1, min(wl.max_pages, wl.sink_pages + wl.window_pages + wl.top_k))
@@ -117,7 +119,8 @@ def decode_step_fn(S, wl, inp, mu, splits):
     with torch.cuda.graph(g):
         select()
         decode()
-    return g, (lists, counts, ccounts), decode
+    keep = (kv, inp, mu, lists, counts, ccounts, sel_ws, dec_ws, out, lse)
+    return g, (lists, counts, ccounts), decode, keep
 
 
 def recorded_traffic(name):
@@ -207,8 +210,13 @@ def tiered_flops(wl, inp, lists, counts, ccounts):
     return 2 * (wl.d_qk + wl.d_v) * total
 
 
+CPU_BASELINE_SECONDS = 10.0   # the oracle repeats its sample until this much CPU time has passed
+
+
 def cpu_baseline_decode(wl, inp, n_seq=8):
-    """The oracle, as is, on the first n_seq sequences of one input set."""
+    """The oracle, as is, on the first n_seq sequences of one input set: the
+    full step (page means, router scores, selection, attention) repeated until
+    CPU_BASELINE_SECONDS have passed."""
     import oracle.sparse_attn_oracle as O
     from threadpoolctl import threadpool_info
     P = wl.page_size
@@ -224,26 +232,36 @@ def cpu_baseline_decode(wl, inp, n_seq=8):
         bt[b, :len(pg)] = np.arange(off, off + len(pg))
         off += len(pg)
     q = inp["q"][:n_seq].float().cpu().numpy().astype(np.float64)
-    t0 = time.perf_counter()
-    npg = [O.n_pages_of(L, P) for L in lens]
-    if wl.scores == "gumbel":
-        scores = inp["scores"][:n_seq].cpu().numpy()
-    else:
-        mu = O.page_summary(kp, bt, lens, P, last_pages=1) if False else O.page_summary(kp, bt, lens, P)
-        scores = O.page_scores(q, mu, bt, lens, P, wl.n_kv_heads, wl.mode)
-    lists, counts, cc = O.select_pages(scores, npg, wl.sink_pages, wl.window_pages, wl.top_k, wl.critical_k)
     am = None if inp["ambient_mask"] is None else inp["ambient_mask"][:n_seq].cpu().numpy().astype(np.int64) & 0xffffffff
-    O.sparse_decode(q, kp, vp, bt, lens, P, lists, counts, wl.n_kv_heads, wl.mode, wl.sm_scale, cc, am,
-                    d_v=wl.d_v)
-    dt = time.perf_counter() - t0
+    npg = [O.n_pages_of(L, P) for L in lens]
+
+    def oracle_step():
+        if wl.scores == "gumbel":
+            scores = inp["scores"][:n_seq].cpu().numpy()
+        else:
+            mu = O.page_summary(kp, bt, lens, P)
+            scores = O.page_scores(q, mu, bt, lens, P, wl.n_kv_heads, wl.mode)
+        lists, counts, cc = O.select_pages(scores, npg, wl.sink_pages, wl.window_pages, wl.top_k, wl.critical_k)
+        O.sparse_decode(q, kp, vp, bt, lens, P, lists, counts, wl.n_kv_heads, wl.mode, wl.sm_scale, cc, am,
+                        d_v=wl.d_v)
+        return lists, counts
+
+    reps = 0
+    t0 = time.perf_counter()
+    while True:
+        lists, counts = oracle_step()
+        reps += 1
+        dt = time.perf_counter() - t0
+        if dt >= CPU_BASELINE_SECONDS:
+            break
     el = 2 if wl.dtype == "bf16" else 4
     per_tok = (wl.d_qk + (0 if wl.latent else wl.d_v)) * el
     nbytes = sum(min(P, int(lens[b]) - int(lp) * P) * per_tok
                  for b in range(n_seq) for s in range(wl.n_sel) for lp in lists[b, s, :counts[b, s]])
     threads = max([t.get("num_threads", 1) for t in threadpool_info()] + [1])
-    return dict(value=round(nbytes / dt / 1e9, 6), unit="GB/s", cores=threads, kind="oracle",
-                sample=f"{n_seq} of {wl.batch} sequences, full step incl. page means over all their pages "
-                       f"(numpy float64 oracle; {dt:.2f} s)", seconds=round(dt, 3))
+    return dict(value=round(reps * nbytes / dt / 1e9, 6), unit="GB/s", cores=threads, kind="oracle",
+                sample=f"{n_seq} of {wl.batch} sequences, full step incl. page means over all their pages, "
+                       f"{reps} repetitions (numpy float64 oracle; {dt:.2f} s)", seconds=round(dt, 3))
 
 
 def run_decode(args):
@@ -262,32 +280,32 @@ def run_decode(args):
     torch.cuda.synchronize()
     steps = []
     for inp, mu in sets:
-        graphs, res, dec = decode_step_fn(S, wl, inp, mu, splits)
-        steps.append((graphs, res, inp, dec))
-    timer = Timer()
+        graphs, res, dec, keep = decode_step_fn(S, wl, inp, mu, splits)
+        steps.append((graphs, res, inp, dec, keep))
 
     def step(i):
-        g, _, _, _ = steps[i % len(steps)]
-        timer.start("step")
-        g.replay()
-        timer.stop("step")
+        steps[i % len(steps)][0].replay()
 
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
-    timer.reset()
+    # one event pair around the whole timed region (a pair per step would add
+    # its own records between the graph launches)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
+    e0.record()
     for i in range(args.steps):
         step(i)
+    e1.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_per_step = 1000.0 * wall / args.steps
+    step_gpu_us = 1000.0 * e0.elapsed_time(e1) / args.steps
 
-    _, (lists, counts, ccounts), inp, _ = steps[0]
+    _, (lists, counts, ccounts), inp, _, _ = steps[0]
     # the dominant kernel alone: decode calls back to back, inputs rotating
     dec_b2b_us = time_back_to_back([st[3] for st in steps], 4 * len(steps))
     nbytes, uniq = selected_bytes(wl, inp, lists, counts, ccounts)
-    step_gpu_us = timer.avg_us("step")
     algo_bytes = uniq if wl.mode == "per_q_head" else nbytes
     achieved = algo_bytes / (dec_b2b_us * 1e-6) / 1e9
     value = nbytes / (ms_per_step * 1e-3) / 1e9
@@ -342,7 +360,8 @@ def prefill_flops(wl, table, counts):
 
 
 def cpu_baseline_prefill(wl, inp, table, counts):
-    """The oracle, as is, on the first and last Q-block of every head of KV head 0."""
+    """The oracle, as is, on the first and last Q-block of every head of KV head 0,
+    repeated until CPU_BASELINE_SECONDS have passed."""
     import oracle.sparse_attn_oracle as O
     from threadpoolctl import threadpool_info
     P = wl.page_size
@@ -357,17 +376,22 @@ def cpu_baseline_prefill(wl, inp, table, counts):
     phys = torch.as_tensor(bt[used].astype(np.int64), device=inp["k_pool"].device)
     kp[bt[used], 0] = inp["k_pool"][phys, 0].float().cpu().numpy()
     vp[bt[used], 0] = inp["v_pool"][phys, 0].float().cpu().numpy()
+    reps = 0
     t0 = time.perf_counter()
-    O.block_sparse_prefill(q[:, :wl.group], kp, vp, bt, int(inp["seq_lens"][0]), P, wl.q_start,
-                           T[:1], C[:1], 1, wl.sm_scale, rows=rows)
-    dt = time.perf_counter() - t0
+    while True:
+        O.block_sparse_prefill(q[:, :wl.group], kp, vp, bt, int(inp["seq_lens"][0]), P, wl.q_start,
+                               T[:1], C[:1], 1, wl.sm_scale, rows=rows)
+        reps += 1
+        dt = time.perf_counter() - t0
+        if dt >= CPU_BASELINE_SECONDS:
+            break
     pos = wl.q_start + np.array([i for i, _ in rows], dtype=np.int64)
     starts = used.astype(np.int64) * P
     vis = int(np.clip(pos[:, None] - starts[None, :] + 1, 0, P).sum())
     threads = max([t.get("num_threads", 1) for t in threadpool_info()] + [1])
-    return dict(value=round(4 * wl.d * vis / dt / 1e12, 6), unit="TFLOP/s", cores=threads, kind="oracle",
-                sample=f"{len(rows)} (row, head) pairs: first and last 64-row Q-block, all heads of KV head 0 "
-                       f"(numpy float64 oracle; {dt:.2f} s)", seconds=round(dt, 3))
+    return dict(value=round(reps * 4 * wl.d * vis / dt / 1e12, 6), unit="TFLOP/s", cores=threads, kind="oracle",
+                sample=f"{len(rows)} (row, head) pairs: first and last 64-row Q-block, all heads of KV head 0, "
+                       f"{reps} repetitions (numpy float64 oracle; {dt:.2f} s)", seconds=round(dt, 3))
 
 
 def run_prefill(args):

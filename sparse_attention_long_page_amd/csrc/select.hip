@@ -5,9 +5,10 @@
 //
 // One workgroup per (sequence, selection head).  Exact top-k by an MSB-first
 // radix select over order-preserving 32-bit keys held in LDS (4 passes of 8
-// bits, LDS histograms), then an index-ordered pass that takes the threshold
-// ties lowest-index-first and compacts the chosen pages into an ascending
-// list with workgroup prefix sums.  The result is a pure function of the fp32
+// bits, LDS histograms, one barrier per pass), then index-ordered passes over
+// per-thread ranges of consecutive pages that take the threshold ties
+// lowest-index-first and compact the chosen pages into an ascending list (one
+// workgroup prefix sum each).  The result is a pure function of the fp32
 // scores: same scores -> same list, bit for bit.
 #include "common.h"
 
@@ -24,8 +25,18 @@ __device__ __forceinline__ uint32_t score_key(float x) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-// Exclusive prefix sum over the workgroup (blockDim = kSelThreads), in thread
-// order.  Returns the exclusive prefix; *total gets the sum over all threads.
+// LDS working set of one selection: three pairs of 256-bin histograms used
+// round robin by consecutive radix passes (one barrier per pass; a pair
+// serves the two thresholds of a tiered list), and one per-wave partial-sum
+// array for each of the two workgroup scans.
+struct SelShared {
+  uint32_t hist[3][2][256];
+  uint32_t wsum[2][kSelThreads / 64];
+};
+
+// Exclusive prefix sum over the workgroup in thread order.  `wsum` serves this
+// one call only, so a single barrier suffices.  *total gets the sum over all
+// threads.
 __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* total, uint32_t* wsum) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   uint32_t x = v;
@@ -43,57 +54,88 @@ __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* total,
     if (w < wave) before += t;
     all += t;
   }
-  __syncthreads();
   *total = all;
   return before + x - v;
 }
 
-// k-th largest key among keys[0..n) (k >= 1): returns the key T and, in *need,
-// how many keys equal to T belong to the top k.
-__device__ uint32_t radix_select(const uint32_t* keys, int n, uint32_t k, uint32_t* need,
-                                 uint32_t* hist, uint32_t* bcast) {
-  uint32_t prefix = 0, pmask = 0, kk = k;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  for (int shift = 24; shift >= 0; shift -= 8) {
-    for (int i = threadIdx.x; i < 256; i += kSelThreads) hist[i] = 0;
-    __syncthreads();
-    for (int i = threadIdx.x; i < n; i += kSelThreads) {
-      const uint32_t key = keys[i];
-      if (key != 0u && (key & pmask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1u);
-    }
-    __syncthreads();
-    if (wave == 0) {
-      uint32_t c[4];
+// One radix digit of a k-th-largest search, found by every wave from the
+// 256-bin histogram h of the keys that match the search's prefix: the bin
+// holding the kk-th largest of them (returned), and in *kk its rank within
+// that bin.  Lane l holds bins 4l .. 4l+3; higher bins hold larger keys.
+__device__ __forceinline__ uint32_t find_digit(const uint32_t* h, uint32_t* kk) {
+  const int lane = threadIdx.x & 63;
+  uint32_t c[4];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) c[j] = hist[4 * lane + j];
-      const uint32_t mine = c[0] + c[1] + c[2] + c[3];
-      uint32_t suf = mine;                       // sum over lanes >= this one
+  for (int j = 0; j < 4; ++j) c[j] = h[4 * lane + j];
+  const uint32_t mine = c[0] + c[1] + c[2] + c[3];
+  uint32_t suf = mine;                           // sum over lanes >= this one
 #pragma unroll
-      for (int o = 1; o < 64; o <<= 1) {
-        const uint32_t y = __shfl_down(suf, o, 64);
-        if (lane + o < 64) suf += y;
-      }
-      const uint32_t above = suf - mine;         // keys in higher lanes' bins
-      if (suf >= kk && above < kk) {
-        uint32_t acc = above;
-        for (int j = 3; j >= 0; --j) {
-          if (acc + c[j] >= kk) {
-            bcast[0] = 4u * lane + j;
-            bcast[1] = kk - acc;
-            break;
-          }
-          acc += c[j];
-        }
-      }
-    }
-    __syncthreads();
-    prefix |= bcast[0] << shift;
-    pmask |= 255u << shift;
-    kk = bcast[1];
-    __syncthreads();
+  for (int o = 1; o < 64; o <<= 1) {
+    const uint32_t y = __shfl_down(suf, o, 64);
+    if (lane + o < 64) suf += y;
   }
-  *need = kk;
-  return prefix;
+  const uint32_t above = suf - mine;             // keys in higher lanes' bins
+  const bool here = suf >= *kk && above < *kk;   // exactly one lane
+  uint32_t bin = 0, rest = 0;
+  if (here) {
+    uint32_t acc = above;
+    for (int j = 3; j >= 0; --j) {
+      if (acc + c[j] >= *kk) {
+        bin = 4u * lane + j;
+        rest = *kk - acc;
+        break;
+      }
+      acc += c[j];
+    }
+  }
+  const int src = __builtin_ctzll(__ballot(here));
+  *kk = __shfl(rest, src, 64);
+  return __shfl(bin, src, 64);
+}
+
+// Thresholds of the kA-th and (when kB > 0) the kB-th largest of the nonzero
+// keys[0..n) (1 <= kA, kB <= their number), both in the same four MSB-first
+// passes of 8 bits.  Each returns the key T and, in need, how many keys equal
+// to T belong to the top k.  Pass p counts into hist[p % 3] (zeroed
+// beforehand, with a barrier since) and zeroes hist[(p + 1) % 3], which no
+// wave reads any more: its last readers finished before the previous pass's
+// barrier.  In pass 0 both searches share one histogram.
+__device__ void radix_select2(const uint32_t* keys, int n, uint32_t kA, uint32_t kB, uint32_t* TA, uint32_t* needA,
+                              uint32_t* TB, uint32_t* needB, SelShared& sh) {
+  uint32_t preA = 0, preB = 0, pmask = 0, kkA = kA, kkB = kB;
+  const bool two = kB > 0;
+  int pass = 0;
+  for (int shift = 24; shift >= 0; shift -= 8, ++pass) {
+    uint32_t* hA = sh.hist[pass % 3][0];
+    uint32_t* hB = pass == 0 ? hA : sh.hist[pass % 3][1];
+    uint32_t* hn = sh.hist[(pass + 1) % 3][0];
+    for (int i = threadIdx.x; i < 512; i += kSelThreads) hn[i] = 0u;   // both bins of the pair
+    const bool countB = two && pass > 0;
+    auto count = [&](uint32_t key) {
+      if (key == 0u) return;
+      const uint32_t bin = (key >> shift) & 255u;
+      if ((key & pmask) == preA) atomicAdd(&hA[bin], 1u);
+      if (countB && (key & pmask) == preB) atomicAdd(&hB[bin], 1u);
+    };
+    // long lists: 8 keys read before their atomics; then the rest one by one
+    const int n8 = n - n % (8 * kSelThreads);
+    for (int i0 = threadIdx.x; i0 < n8; i0 += 8 * kSelThreads) {
+      uint32_t kv[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) kv[j] = keys[i0 + j * kSelThreads];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) count(kv[j]);
+    }
+    for (int i = n8 + threadIdx.x; i < n; i += kSelThreads) count(keys[i]);
+    __syncthreads();
+    preA |= find_digit(hA, &kkA) << shift;
+    if (two) preB |= find_digit(hB, &kkB) << shift;
+    pmask |= 255u << shift;
+  }
+  *TA = preA;
+  *needA = kkA;
+  *TB = preB;
+  *needB = kkB;
 }
 
 // Forced pages and candidate counts of list (b, s).
@@ -113,53 +155,70 @@ __device__ __forceinline__ ListShape list_shape(const SelectParams& p, int b) {
 }
 
 // Select from keys[0..n) in LDS (0 = forced page, else score_key) and write
-// the list of (b, s).  Called by the whole workgroup after a barrier.
+// the list of (b, s).  Called by the whole workgroup after a barrier that
+// follows the keys' writes and the zeroing of the pair sh.hist[0].  Each thread owns
+// the consecutive keys [lo, hi), so ranking the threshold ties by index and
+// compacting the chosen pages in ascending order take one workgroup scan each.
 __device__ void select_from_keys(const SelectParams& p, const ListShape& L, int b, int s, uint32_t* keys,
-                                 uint32_t* hist, uint32_t* wsum, uint32_t* bcast) {
+                                 SelShared& sh) {
   const int sel = b * p.n_sel + s;
   const int n = L.n, sink_hi = L.sink_hi, win_lo = L.win_lo, n_forced = L.n_forced, k_eff = L.k_eff, k1 = L.k1;
   uint32_t T1 = 0xffffffffu, r1 = 0, T2 = 0xffffffffu, r2 = 0;
-  if (k_eff > 0) T2 = radix_select(keys, n, (uint32_t)k_eff, &r2, hist, bcast);
-  if (p.tiered && k1 > 0) T1 = radix_select(keys, n, (uint32_t)k1, &r1, hist, bcast);
+  if (k_eff > 0) {
+    const uint32_t kB = (p.tiered && k1 > 0) ? (uint32_t)k1 : 0u;
+    uint32_t TB = 0xffffffffu, rB = 0;
+    radix_select2(keys, n, (uint32_t)k_eff, kB, &T2, &r2, &TB, &rB, sh);
+    if (kB > 0) { T1 = TB; r1 = rB; }
+  }
   if (!p.tiered) { T1 = T2; r1 = r2; }
 
-  // pass 1: rank ties at the thresholds by index; replace keys with flags
-  // bit0 forced, bit1 in top-k1 (Critical), bit2 in top-k_eff
-  uint32_t run1 = 0, run2 = 0;
-  for (int base0 = 0; base0 < n; base0 += kSelThreads) {
-    const int i = base0 + threadIdx.x;
-    const uint32_t key = i < n ? keys[i] : 0u;
-    const uint32_t e1 = (key != 0u && key == T1) ? 1u : 0u;
-    const uint32_t e2 = (key != 0u && key == T2) ? 1u : 0u;
-    uint32_t tot;
-    const uint32_t ex = block_excl_scan(e1 | (e2 << 16), &tot, wsum);
-    const uint32_t rank1 = run1 + (ex & 0xffffu), rank2 = run2 + (ex >> 16);
+  const int m = (n + kSelThreads - 1) / kSelThreads;
+  const int lo = min(n, (int)threadIdx.x * m), hi = min(n, lo + m);
+
+  // ties at the thresholds before this thread's range (counts < 2^16: n <= 16384)
+  uint32_t t1 = 0, t2 = 0;
+  for (int i = lo; i < hi; ++i) {
+    const uint32_t key = keys[i];
+    t1 += (key != 0u && key == T1) ? 1u : 0u;
+    t2 += (key != 0u && key == T2) ? 1u : 0u;
+  }
+  uint32_t tot;
+  const uint32_t ex = block_excl_scan(t1 | (t2 << 16), &tot, sh.wsum[0]);
+
+  // flags: bit0 forced, bit1 in top-k1 (Critical), bit2 in top-k_eff; count
+  // this thread's entries of segment A (forced + Critical, or the whole
+  // untiered list) and segment B (Ambient)
+  uint32_t rank1 = ex & 0xffffu, rank2 = ex >> 16;
+  uint32_t ca = 0, cb = 0;
+  for (int i = lo; i < hi; ++i) {
+    const uint32_t key = keys[i];
+    const bool e1 = key != 0u && key == T1, e2 = key != 0u && key == T2;
     const bool top1 = key != 0u && (key > T1 || (e1 && rank1 < r1));
     const bool top2 = key != 0u && (key > T2 || (e2 && rank2 < r2));
-    const bool forced = i < n && (i < sink_hi || i >= win_lo);
-    if (i < n) keys[i] = (forced ? 1u : 0u) | (top1 ? 2u : 0u) | (top2 ? 4u : 0u);
-    run1 += tot & 0xffffu;
-    run2 += tot >> 16;
+    rank1 += e1 ? 1u : 0u;
+    rank2 += e2 ? 1u : 0u;
+    const bool forced = i < sink_hi || i >= win_lo;
+    const bool a = p.tiered ? (forced || top1) : (forced || top2);
+    const bool bb = p.tiered && top2 && !top1;
+    ca += a ? 1u : 0u;
+    cb += bb ? 1u : 0u;
+    keys[i] = (a ? 1u : 0u) | (bb ? 2u : 0u);
   }
-  __syncthreads();
+  const uint32_t ex2 = block_excl_scan(ca | (cb << 16), &tot, sh.wsum[1]);
 
-  // pass 2: ascending compaction; segment A (forced + Critical, or the whole
-  // untiered list), segment B (Ambient) after it
+  // ascending compaction of this thread's range
   int32_t* out = p.lists + (size_t)sel * p.list_stride;
   const int countA = n_forced + k1;
-  uint32_t runA = 0, runB = 0;
-  for (int base0 = 0; base0 < n; base0 += kSelThreads) {
-    const int i = base0 + threadIdx.x;
-    const uint32_t f = i < n ? keys[i] : 0u;
-    uint32_t a, bb;
-    if (p.tiered) { a = (f & 3u) ? 1u : 0u; bb = ((f & 4u) && !(f & 2u)) ? 1u : 0u; }
-    else { a = (f & 5u) ? 1u : 0u; bb = 0u; }
-    uint32_t tot;
-    const uint32_t ex = block_excl_scan(a | (bb << 16), &tot, wsum);
-    if (a) out[runA + (ex & 0xffffu)] = i;
-    if (bb) out[countA + runB + (ex >> 16)] = i;
-    runA += tot & 0xffffu;
-    runB += tot >> 16;
+  // (positions stay below n_forced + k_eff <= list_stride; the bound only
+  // keeps the stores inside the row should that ever fail)
+  const uint32_t stride = (uint32_t)p.list_stride;
+  uint32_t posA = ex2 & 0xffffu, posB = countA + (ex2 >> 16);
+  for (int i = lo; i < hi; ++i) {
+    const uint32_t f = keys[i];
+    if ((f & 1u) && posA < stride) out[posA] = i;
+    if ((f & 2u) && posB < stride) out[posB] = i;
+    posA += f & 1u;
+    posB += (f >> 1) & 1u;
   }
   if (threadIdx.x == 0) {
     p.counts[sel] = n_forced + k_eff;
@@ -169,18 +228,27 @@ __device__ void select_from_keys(const SelectParams& p, const ListShape& L, int 
 
 __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectParams p) {
   extern __shared__ uint32_t keys[];
-  __shared__ uint32_t hist[256];
-  __shared__ uint32_t wsum[kSelThreads / 64];
-  __shared__ uint32_t bcast[2];
+  __shared__ SelShared sh;
   const int s = blockIdx.x, b = blockIdx.y;
   const ListShape L = list_shape(p, b);
   const float* sc = p.scores + ((size_t)b * p.n_sel + s) * p.scores_stride;
-  for (int i = threadIdx.x; i < L.n; i += kSelThreads) {
-    const bool forced = i < L.sink_hi || i >= L.win_lo;
-    keys[i] = forced ? 0u : score_key(sc[i]);
+  for (int i = threadIdx.x; i < 512; i += kSelThreads) sh.hist[0][0][i] = 0u;
+  for (int i0 = threadIdx.x; i0 < L.n; i0 += 8 * kSelThreads) {
+    float v[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int i = i0 + j * kSelThreads;
+      v[j] = i < L.n ? sc[i] : 0.f;
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int i = i0 + j * kSelThreads;
+      const bool forced = i < L.sink_hi || i >= L.win_lo;
+      if (i < L.n) keys[i] = forced ? 0u : score_key(v[j]);
+    }
   }
   __syncthreads();
-  select_from_keys(p, L, b, s, keys, hist, wsum, bcast);
+  select_from_keys(p, L, b, s, keys, sh);
 }
 
 // Router scores and selection in one workgroup per list (used when there are
@@ -188,16 +256,16 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectParams p) {
 // scores 32 pages per round at d <= 128 (16 lanes per page, 4 pages per step,
 // the 8 steps' mean-row loads in flight together), writing order-preserving
 // keys into LDS.
-// The score arithmetic is the same as page_score_kernel's: float64 products
-// of the pooled query with the fp32 mean row, summed over 16 lanes in a fixed
-// butterfly, rounded once to fp32.
+// The score arithmetic is the same as page_score_kernel's: lane `sub` of a
+// page's 16 takes dims 64 i + 4 sub + 0..3 (each load instruction reads 256
+// contiguous bytes of the mean row), float64 products of the pooled query
+// with the fp32 mean row summed in that order, then over the 16 lanes in a
+// fixed butterfly, rounded once to fp32.
 template <typename T, int D>
 __global__ __launch_bounds__(kSelThreads) void score_select_kernel(ScoreParams sp, SelectParams p) {
   constexpr int PL = D / 16;
   extern __shared__ uint32_t keys[];
-  __shared__ uint32_t hist[256];
-  __shared__ uint32_t wsum[kSelThreads / 64];
-  __shared__ uint32_t bcast[2];
+  __shared__ SelShared sh;
   __shared__ double qbar[D];
   const int s = blockIdx.x, b = blockIdx.y;
   const ListShape L = list_shape(p, b);
@@ -215,6 +283,7 @@ __global__ __launch_bounds__(kSelThreads) void score_select_kernel(ScoreParams s
     }
     qbar[e] = v;
   }
+  for (int i = threadIdx.x; i < 512; i += kSelThreads) sh.hist[0][0][i] = 0u;
   __syncthreads();
   const int g = sp.per_q ? s / sp.G : s;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -229,21 +298,21 @@ __global__ __launch_bounds__(kSelThreads) void score_select_kernel(ScoreParams s
 #pragma unroll
     for (int it = 0; it < kSteps; ++it) {
       const int ph = __shfl(my_phys, it * 4 + slot, 64);
-      const float* m = sp.mu + ((size_t)max(ph, 0) * sp.Hkv + g) * D + sub * PL;
+      const float* m = sp.mu + ((size_t)max(ph, 0) * sp.Hkv + g) * D + 4 * sub;
 #pragma unroll
-      for (int i = 0; i < PL / 4; ++i) v[it][i] = ph >= 0 ? *reinterpret_cast<const f32x4*>(m + 4 * i) : f32x4{};
+      for (int i = 0; i < PL / 4; ++i) v[it][i] = ph >= 0 ? *reinterpret_cast<const f32x4*>(m + 64 * i) : f32x4{};
     }
 #pragma unroll
     for (int it = 0; it < kSteps; ++it) {
       const int lp = r0 + it * 4 + slot;
-      const double* qq = qbar + sub * PL;
+      const double* qq = qbar + 4 * sub;
       double acc = 0.0;
 #pragma unroll
       for (int i = 0; i < PL / 4; ++i) {
-        acc += qq[4 * i] * (double)v[it][i][0];
-        acc += qq[4 * i + 1] * (double)v[it][i][1];
-        acc += qq[4 * i + 2] * (double)v[it][i][2];
-        acc += qq[4 * i + 3] * (double)v[it][i][3];
+        acc += qq[64 * i] * (double)v[it][i][0];
+        acc += qq[64 * i + 1] * (double)v[it][i][1];
+        acc += qq[64 * i + 2] * (double)v[it][i][2];
+        acc += qq[64 * i + 3] * (double)v[it][i][3];
       }
 #pragma unroll
       for (int o = 8; o > 0; o >>= 1) acc += __shfl_xor(acc, o, 64);
@@ -258,7 +327,7 @@ __global__ __launch_bounds__(kSelThreads) void score_select_kernel(ScoreParams s
   if (sout)
     for (int lp = n + threadIdx.x; lp < sp.max_pages; lp += kSelThreads) sout[lp] = __builtin_nanf("");
   __syncthreads();
-  select_from_keys(p, L, b, s, keys, hist, wsum, bcast);
+  select_from_keys(p, L, b, s, keys, sh);
 }
 
 hipError_t launch_select(const SelectParams& p, int batch, int max_pages, hipStream_t s) {

@@ -111,20 +111,30 @@ __global__ __launch_bounds__(256) void pooled_q_kernel(ScoreParams p, double* qp
     double acc[VW];
 #pragma unroll
     for (int i = 0; i < VW; ++i) acc[i] = 0.0;
-#pragma unroll 4
-    for (int r = r0 + rs; r < r1; r += RS) {
-      int tt, h;
-      pooled_row(p, s, r, &tt, &h);
-      const u32x4 w = *reinterpret_cast<const u32x4*>(q + (((size_t)b * p.T + tt) * p.Hq + h) * p.d + cg * VW);
-      if constexpr (sizeof(T) == 2) {
+    // 8 rows' loads in flight, then added in row order
+    for (int rb = r0 + rs; rb < r1; rb += 8 * RS) {
+      u32x4 w[8];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          acc[2 * i] += (double)bf16_lo(w[i]);
-          acc[2 * i + 1] += (double)bf16_hi(w[i]);
+      for (int j = 0; j < 8; ++j) {
+        const int r = rb + j * RS;
+        int tt = 0, h = 0;
+        if (r < r1) pooled_row(p, s, r, &tt, &h);
+        w[j] = r < r1 ? *reinterpret_cast<const u32x4*>(q + (((size_t)b * p.T + tt) * p.Hq + h) * p.d + cg * VW)
+                      : u32x4{0u, 0u, 0u, 0u};
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        if (rb + j * RS >= r1) break;
+        if constexpr (sizeof(T) == 2) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            acc[2 * i] += (double)bf16_lo(w[j][i]);
+            acc[2 * i + 1] += (double)bf16_hi(w[j][i]);
+          }
+        } else {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) acc[i] += (double)__uint_as_float(w[j][i]);
         }
-      } else {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) acc[i] += (double)__uint_as_float(w[i]);
       }
     }
 #pragma unroll
@@ -142,6 +152,10 @@ __global__ __launch_bounds__(256) void pooled_q_kernel(ScoreParams p, double* qp
 // grid (page chunk of 64, n_sel, B), block 256.  The 64 pages' physical ids
 // are read first; then every wave issues the mean-row loads of its 16 pages
 // (4 pages of 16 lanes per step, all 4 steps in flight) before reducing.
+// Lane `sub` of a page's 16 takes dims 64 i + 4 sub + 0..3, so each load
+// instruction reads 256 contiguous bytes of the mean row; the float64
+// products are summed in that order, then over the 16 lanes in a fixed
+// butterfly, and rounded once to fp32.
 template <typename T, int D>
 __global__ __launch_bounds__(256) void page_score_kernel(ScoreParams p, const double* qpart) {
   constexpr int kPagesPerBlock = 64;
@@ -184,22 +198,22 @@ __global__ __launch_bounds__(256) void page_score_kernel(ScoreParams p, const do
 #pragma unroll
   for (int it = 0; it < 4; ++it) {
     const int ph = phys_s[wave * 16 + it * 4 + slot];
-    const float* m = p.mu + ((size_t)max(ph, 0) * p.Hkv + g) * D + sub * PL;
+    const float* m = p.mu + ((size_t)max(ph, 0) * p.Hkv + g) * D + 4 * sub;
 #pragma unroll
-    for (int i = 0; i < PL / 4; ++i) v[it][i] = ph >= 0 ? *reinterpret_cast<const f32x4*>(m + 4 * i) : f32x4{};
+    for (int i = 0; i < PL / 4; ++i) v[it][i] = ph >= 0 ? *reinterpret_cast<const f32x4*>(m + 64 * i) : f32x4{};
   }
   float* out = p.scores + ((size_t)b * p.n_sel + s) * p.max_pages;
 #pragma unroll
   for (int it = 0; it < 4; ++it) {
     const int lp = page0 + wave * 16 + it * 4 + slot;
-    const double* qq = qbar + sub * PL;
+    const double* qq = qbar + 4 * sub;
     double acc = 0.0;
 #pragma unroll
     for (int i = 0; i < PL / 4; ++i) {
-      acc += qq[4 * i] * (double)v[it][i][0];
-      acc += qq[4 * i + 1] * (double)v[it][i][1];
-      acc += qq[4 * i + 2] * (double)v[it][i][2];
-      acc += qq[4 * i + 3] * (double)v[it][i][3];
+      acc += qq[64 * i] * (double)v[it][i][0];
+      acc += qq[64 * i + 1] * (double)v[it][i][1];
+      acc += qq[64 * i + 2] * (double)v[it][i][2];
+      acc += qq[64 * i + 3] * (double)v[it][i][3];
     }
 #pragma unroll
     for (int o = 8; o > 0; o >>= 1) acc += __shfl_xor(acc, o, 64);

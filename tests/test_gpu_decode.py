@@ -112,6 +112,41 @@ def test_select_matches_oracle(name):
     assert rep.exact + rep.band_events == rep.units
 
 
+@pytest.mark.parametrize("tiered", [False, True])
+def test_select_long_lists_with_ties_exact(tiered):
+    """Selection on given scores is index work: it must equal the oracle's
+    lists exactly.  Lists of up to 9000 pages (several pages per thread of the
+    select workgroup), scores drawn from a few values (two of them adjacent
+    floats) plus NaN and both zeros, so the threshold key has thousands of
+    ties that must go to the lowest page indices."""
+    P, max_pages, H = 16, 9000, 3
+    lens = np.array([P * 9000, P * 5000 + 3, P * 513, P * 40 + 1], dtype=np.int32)
+    B = len(lens)
+    rng = np.random.default_rng(77)
+    vals = np.array([-1.5, -0.0, 0.0, 0.25, np.nextafter(np.float32(0.25), np.float32(1)), 2.0, np.nan],
+                    dtype=np.float32)
+    scores = vals[rng.integers(0, len(vals), size=(B, H, max_pages))]
+    sink, window, top_k = 2, 5, 2500
+    crit = 700 if tiered else None
+    kv = S.PagedKV(torch.zeros((4, 1, P, 64), dtype=torch.bfloat16, device=DEV),
+                   torch.zeros((4, 1, 64, P), dtype=torch.bfloat16, device=DEV),
+                   torch.zeros((B, max_pages), dtype=torch.int32, device=DEV), torch.from_numpy(lens).to(DEV))
+    lists, counts, cc = S.sa_select_pages(kv, n_q_heads=H, mode=S.SA_SEL_PER_Q_HEAD, sink_pages=sink,
+                                          window_pages=window, top_k=top_k,
+                                          scores=torch.from_numpy(scores).to(DEV), critical_k=crit)
+    torch.cuda.synchronize()
+    npg = [O.n_pages_of(int(L), P) for L in lens]
+    o_lists, o_counts, o_cc = O.select_pages(scores, npg, sink, window, top_k, crit)
+    g_lists, g_counts = npi(lists), npi(counts)
+    assert np.array_equal(g_counts, o_counts)
+    if tiered:
+        assert np.array_equal(npi(cc), o_cc)
+    for b in range(B):
+        for h in range(H):
+            n = int(o_counts[b, h])
+            assert np.array_equal(g_lists[b, h, :n], o_lists[b, h, :n]), (b, h)
+
+
 @pytest.mark.parametrize("name", DECODE_SMALL)
 @pytest.mark.parametrize("splits", [1, 2, 3, 0])
 def test_decode_matches_oracle(name, splits):
