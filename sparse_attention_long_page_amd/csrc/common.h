@@ -43,6 +43,25 @@ __device__ __forceinline__ double wave_sum_f64(double v) {
   return v;
 }
 
+// Reductions over the four 16-lane groups of a wave (lanes l, l^16, l^32,
+// l^48: the rows an MFMA 16x16 accumulator spreads over), by the gfx950 lane
+// swap instructions instead of LDS round trips.  Swapping a value with itself
+// leaves each lane holding its own and its partner's value (l^16, then l^32);
+// the pairing and order of operations match a butterfly over xor 16 then
+// xor 32, so the results are the same bits in all four lanes.
+__device__ __forceinline__ float max_over_row_groups(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float sum_over_row_groups(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
 // Number of valid tokens of logical page `lp` in a sequence of `len` tokens.
 __device__ __forceinline__ int page_valid(int len, int lp, int P) {
   int r = len - lp * P;

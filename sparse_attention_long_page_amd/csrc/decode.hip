@@ -188,8 +188,7 @@ __global__ __launch_bounds__(256, 2) void decode_bf16_kernel(DecodeParams p, con
         mraw = fmaxf(mraw, sacc[j4][i]);
       }
     }
-    mraw = fmaxf(mraw, __shfl_xor(mraw, 16, 64));
-    mraw = fmaxf(mraw, __shfl_xor(mraw, 32, 64));
+    mraw = max_over_row_groups(mraw);
     const float mloc = mraw == -INFINITY ? -INFINITY : mraw * p.scale_log2;
     const float m_new = fmaxf(m_run, mloc);
     const bool none = m_new == -INFINITY;
@@ -227,8 +226,7 @@ __global__ __launch_bounds__(256, 2) void decode_bf16_kernel(DecodeParams p, con
   }
 
   // combine the 4 waves
-  l_run += __shfl_xor(l_run, 16, 64);
-  l_run += __shfl_xor(l_run, 32, 64);
+  l_run = sum_over_row_groups(l_run);
   __shared__ float sm_m[4][16], sm_l[4][16];
   __shared__ float sm_o[4][16][D + 4];
   if (kg == 0) { sm_m[wave][col] = m_run; sm_l[wave][col] = l_run; }

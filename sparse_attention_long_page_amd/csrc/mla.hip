@@ -294,8 +294,7 @@ __global__ __launch_bounds__(256, 1) void mla_decode_kernel(DecodeParams p) {
               if (!(act[rt] && tok < nv)) sacc[j][rt][i] = -INFINITY;
               mraw = fmaxf(mraw, sacc[j][rt][i]);
             }
-          mraw = fmaxf(mraw, __shfl_xor(mraw, 16, 64));
-          mraw = fmaxf(mraw, __shfl_xor(mraw, 32, 64));
+          mraw = max_over_row_groups(mraw);
           const float mloc = mraw == -INFINITY ? -INFINITY : mraw * p.scale_log2;
           if (attempt == 1) {
             m_ref[rt] = fmaxf(m_ref[rt], mloc);
@@ -365,8 +364,7 @@ __global__ __launch_bounds__(256, 1) void mla_decode_kernel(DecodeParams p) {
 #pragma unroll
   for (int rt = 0; rt < 2; ++rt) {
     float l = l_run[rt];
-    l += __shfl_xor(l, 16, 64);
-    l += __shfl_xor(l, 32, 64);
+    l = sum_over_row_groups(l);
     const bool empty = m_ref[rt] == -INFINITY;
     const float inv = empty ? 0.f : 1.f / l;
     lse_row[rt] = empty ? -INFINITY : (m_ref[rt] + log2f(l)) * kLn2;

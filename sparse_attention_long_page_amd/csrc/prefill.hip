@@ -289,8 +289,7 @@ __global__ __launch_bounds__(128 * HW) void prefill_kernel(PrefillParams p) {
             }
             mraw = fmaxf(mraw, sacc[j4][rt][i]);
           }
-        mraw = fmaxf(mraw, __shfl_xor(mraw, 16, 64));
-        mraw = fmaxf(mraw, __shfl_xor(mraw, 32, 64));
+        mraw = max_over_row_groups(mraw);
         const float mloc = mraw == -INFINITY ? -INFINITY : mraw * p.scale_log2;
         // move the reference only when the row maximum outgrows it
         float mref = m_ref[rt];
@@ -359,8 +358,7 @@ __global__ __launch_bounds__(128 * HW) void prefill_kernel(PrefillParams p) {
 #pragma unroll
   for (int rt = 0; rt < kRT; ++rt) {
     float l = l_run[rt];
-    l += __shfl_xor(l, 16, 64);
-    l += __shfl_xor(l, 32, 64);
+    l = sum_over_row_groups(l);
     const int i = qw + 16 * rt + col;
     if (i >= p.q_len) continue;
     const bool empty = m_ref[rt] == -INFINITY;
