@@ -166,7 +166,10 @@ sa_status sa_select_pages(const sa_paged_kv* kv, int32_t batch,
  *   the scaled logits; an empty set gives o = 0 and lse = -inf.  sm_scale
  *   must be finite and positive (SA_ERR_INVALID_ARGUMENT otherwise).
  * Each list is cut into num_splits contiguous chunks (sizes differ by at most
- * one); chunk partials (o_s, lse_s) are combined by an LSE merge.
+ * one); chunk partials (o_s, lse_s) are combined by an LSE merge.  The
+ * workspace holds the partials: o_s in fp32, or in bf16 for a latent cache
+ * (each o_s is a normalised average, so bf16 adds at most 2^-9 of its
+ * magnitude before the merge), lse_s in fp32.
  *   q                 [batch][q_tokens][n_q_heads][d_qk]
  *   page_lists/counts as produced by sa_select_pages (logical page ids)
  *   ambient_head_mask [batch][max_pages][ceil(n_q_heads/32)] uint32 (tiered only)

@@ -109,10 +109,14 @@ int choose_splits(const sa_paged_kv* kv, int batch, int n_sel, int list_stride, 
   return std::max(1, std::min(s, 64));
 }
 
+// Split partials of o: bf16 for a latent cache (512-wide rows for 128+ heads
+// make fp32 partials the largest traffic of that path), fp32 otherwise.
+size_t partial_elem_bytes(const sa_paged_kv* kv) { return is_latent(kv) ? 2 : sizeof(float); }
+
 size_t decode_partials_bytes(const sa_paged_kv* kv, int batch, int q_tokens, int n_q_heads, int splits) {
   if (splits <= 1) return 0;
   const size_t rows = (size_t)batch * q_tokens * n_q_heads;
-  return align_up(rows * splits * kv->d_v * sizeof(float)) + align_up(rows * splits * sizeof(float));
+  return align_up(rows * splits * kv->d_v * partial_elem_bytes(kv)) + align_up(rows * splits * sizeof(float));
 }
 
 }  // namespace
@@ -337,7 +341,8 @@ sa_status sa_sparse_decode(const sa_paged_kv* kv, int32_t batch, const void* q, 
   if (splits > 1) {
     p.part_o = reinterpret_cast<float*>(workspace);
     p.part_lse = reinterpret_cast<float*>(reinterpret_cast<char*>(workspace) +
-                                          align_up(rows * splits * kv->d_v * sizeof(float)));
+                                          align_up(rows * splits * kv->d_v * partial_elem_bytes(kv)));
+    p.part_bf16 = is_latent(kv) ? 1 : 0;
   }
   p.B = batch;
   p.T = q_tokens;
@@ -367,6 +372,7 @@ sa_status sa_sparse_decode(const sa_paged_kv* kv, int32_t batch, const void* q, 
     mp.splits = splits;
     mp.d_v = kv->d_v;
     mp.out_fp32 = kv->dtype == SA_DTYPE_FP32;
+    mp.part_bf16 = p.part_bf16;
     e = sa::launch_merge(mp, stream);
     if (e != hipSuccess) return device_status(e, "merge launch");
   }

@@ -109,19 +109,20 @@ struct DecodeParams {
   const uint32_t* amask;     // [B][max_pages][mask_words] or null
   void* out;                 // [B][T][Hq][d_v]
   float* out_lse;            // [B][T][Hq] or null
-  float* part_o;             // [B][T][Hq][splits][d_v]
+  float* part_o;             // [B][T][Hq][splits][d_v], fp32 or (part_bf16) bf16
   float* part_lse;           // [B][T][Hq][splits]
+  int part_bf16;             // split partials of o stored as bf16 (latent path)
   int B, T, Hq, Hkv, G, n_sel, per_q, list_stride, max_pages, mask_words;
   int P, d_qk, d_v, splits;
   float scale_log2;          // sm_scale * log2(e)
 };
 
 struct MergeParams {
-  const float* part_o;
+  const float* part_o;       // fp32, or bf16 when part_bf16
   const float* part_lse;
   void* out;
   float* out_lse;
-  int rows, splits, d_v, out_fp32;
+  int rows, splits, d_v, out_fp32, part_bf16;
 };
 
 struct UnionParams {

@@ -352,8 +352,19 @@ __global__ __launch_bounds__(256) void decode_f32_kernel(DecodeParams p) {
 
 // ------------------------------------------------------------------- merge
 // One wave per query row: o = sum_s w_s o_s / sum_s w_s, w_s = exp(lse_s - max).
-// Lanes own 4 consecutive dims (16-byte loads); the loads of up to 8 splits
-// are issued before any is consumed.
+// Lanes own 4 consecutive dims (16-byte fp32 or 8-byte bf16 loads); the loads
+// of up to 8 splits are issued before any is consumed.
+template <bool BF16P>
+__device__ __forceinline__ f32x4 load_partial4(const float* po, size_t off) {
+  if constexpr (BF16P) {
+    const uint2 w = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint16_t*>(po) + off);
+    return f32x4{bf16_lo(w.x), bf16_hi(w.x), bf16_lo(w.y), bf16_hi(w.y)};
+  } else {
+    return *reinterpret_cast<const f32x4*>(po + off);
+  }
+}
+
+template <bool BF16P>
 __global__ __launch_bounds__(256) void lse_merge_kernel(MergeParams p) {
   const int lane = threadIdx.x & 63;
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -365,14 +376,15 @@ __global__ __launch_bounds__(256) void lse_merge_kernel(MergeParams p) {
   if (M != -INFINITY && lane < p.splits) w = __expf(mine - M);
   const float L = wave_sum(w);
   const float inv = M == -INFINITY ? 0.f : 1.f / L;
-  const float* po = p.part_o + (size_t)row * p.splits * p.d_v;
+  const float* po = p.part_o;
+  const size_t row_off = (size_t)row * p.splits * p.d_v;
   for (int d4 = lane; d4 < p.d_v / 4; d4 += 64) {
     f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
     for (int s0 = 0; s0 < p.splits; s0 += 8) {
       f32x4 v[8];
 #pragma unroll
       for (int j = 0; j < 8; ++j)
-        v[j] = s0 + j < p.splits ? *reinterpret_cast<const f32x4*>(po + (size_t)(s0 + j) * p.d_v + 4 * d4)
+        v[j] = s0 + j < p.splits ? load_partial4<BF16P>(po, row_off + (size_t)(s0 + j) * p.d_v + 4 * d4)
                                  : f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
@@ -397,7 +409,8 @@ __global__ __launch_bounds__(256) void lse_merge_kernel(MergeParams p) {
 }
 
 hipError_t launch_merge(const MergeParams& p, hipStream_t s) {
-  hipLaunchKernelGGL(lse_merge_kernel, dim3((p.rows + 3) / 4), dim3(256), 0, s, p);
+  if (p.part_bf16) hipLaunchKernelGGL(lse_merge_kernel<true>, dim3((p.rows + 3) / 4), dim3(256), 0, s, p);
+  else hipLaunchKernelGGL(lse_merge_kernel<false>, dim3((p.rows + 3) / 4), dim3(256), 0, s, p);
   return hipGetLastError();
 }
 

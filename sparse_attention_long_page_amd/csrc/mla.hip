@@ -127,13 +127,13 @@ __global__ __launch_bounds__(256, 1) void mla_decode_kernel(DecodeParams p) {
   bf16x8 qreg[2][kMKSteps];
 #pragma unroll
   for (int rt = 0; rt < 2; ++rt) {
-    // rows past the last head read row 0 and are zeroed (no branches)
+    // rows past the last head read row 0: their logits are masked in the
+    // softmax and their outputs never stored, so the loads need no select
+    // (a select would wait for each load before the page metadata is read)
     const size_t qrow = row_ok[rt] ? ((size_t)b * T + t_row[rt]) * p.Hq + h_row[rt] : 0;
 #pragma unroll
-    for (int kk = 0; kk < kMKSteps; ++kk) {
-      bf16x8 v = *reinterpret_cast<const bf16x8*>(qp + qrow * kMD + 8 * kg + 32 * kk);
-      qreg[rt][kk] = row_ok[rt] ? v : bf16x8{};
-    }
+    for (int kk = 0; kk < kMKSteps; ++kk)
+      qreg[rt][kk] = *reinterpret_cast<const bf16x8*>(qp + qrow * kMD + 8 * kg + 32 * kk);
   }
 
   f32x4 oacc[kMDTiles][2];
@@ -380,6 +380,17 @@ __global__ __launch_bounds__(256, 1) void mla_decode_kernel(DecodeParams p) {
         pk.x = (uint32_t)f32_to_bf16_bits(v[0]) | ((uint32_t)f32_to_bf16_bits(v[1]) << 16);
         pk.y = (uint32_t)f32_to_bf16_bits(v[2]) | ((uint32_t)f32_to_bf16_bits(v[3]) << 16);
         *reinterpret_cast<uint2*>(out + 16 * dt + 4 * kg) = pk;
+      }
+    } else if (p.part_bf16) {
+      uint16_t* po = reinterpret_cast<uint16_t*>(p.part_o) + (orow[rt] * p.splits + split) * kMDV;
+#pragma unroll
+      for (int dt = 0; dt < kMDTiles; ++dt) {
+        f32x4 v = oacc[dt][rt];
+        v[0] *= inv; v[1] *= inv; v[2] *= inv; v[3] *= inv;
+        uint2 pk;
+        pk.x = (uint32_t)f32_to_bf16_bits(v[0]) | ((uint32_t)f32_to_bf16_bits(v[1]) << 16);
+        pk.y = (uint32_t)f32_to_bf16_bits(v[2]) | ((uint32_t)f32_to_bf16_bits(v[3]) << 16);
+        *reinterpret_cast<uint2*>(po + 16 * dt + 4 * kg) = pk;
       }
     } else {
       float* po = p.part_o + (orow[rt] * p.splits + split) * kMDV;
