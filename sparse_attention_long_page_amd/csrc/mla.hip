@@ -46,6 +46,7 @@ constexpr int kMRS = kMRowChunks * 8;    // LDS row stride, bf16 elements (1168 
 constexpr int kMTile = kMP * kMRS;       // elements per staged page
 constexpr int kMInstr = kMP * kMRowChunks / 64;   // 73 wave-wide 16-byte DMA loads per page
 constexpr int kMKSteps = kMD / 32;       // 18
+constexpr int kMHalfInstr = 37;          // copy instructions covering rows 0-31 (37 * 64 >= 32 * 73)
 constexpr int kMDTiles = kMDV / 16;      // 32
 constexpr int kMetaWin = 256;            // pages of page metadata held in LDS
 constexpr float kMMargin = 64.0f;         // log2 units a logit may exceed its row's reference
@@ -147,10 +148,11 @@ __global__ __launch_bounds__(256, 1) void mla_decode_kernel(DecodeParams p) {
 
   // LDS-DMA copy of one page's K tile: wave-wide instruction i covers LDS
   // chunks [64 i, 64 i + 64); chunk c is row c / 73, 16-byte column c % 73
-  // (column 72 is row padding and re-reads column 0 of the row).
-  auto stage = [&](uint16_t* buf, int phys) {
+  // (column 72 is row padding and re-reads column 0 of the row).  Wave w
+  // issues the instructions i = w mod 4 of [i_lo, i_hi).
+  auto stage = [&](uint16_t* buf, int phys, int i_lo, int i_hi) {
     const uint16_t* src = kpool + (size_t)phys * p.Hkv * kMP * kMD;
-    for (int i = wave; i < kMInstr; i += 4) {
+    for (int i = i_lo + ((wave - i_lo) & 3); i < i_hi; i += 4) {
       const int c = 64 * i + lane;
       const int r = c / kMRowChunks, ch = c % kMRowChunks;
       const int sch = ch < kMRowChunks - 1 ? ch : 0;
@@ -210,7 +212,7 @@ __global__ __launch_bounds__(256, 1) void mla_decode_kernel(DecodeParams p) {
       __syncthreads();
     };
     load_meta(beg);
-    if (beg < end && m_nv[0] > 0) stage(sk0, m_phys[0]);
+    if (beg < end && m_nv[0] > 0) stage(sk0, m_phys[0], 0, kMInstr);
 
     // one page: compute from `cur` while the next page is copied into `nxt`
     auto page = [&](auto parity, int e) {
@@ -236,8 +238,15 @@ __global__ __launch_bounds__(256, 1) void mla_decode_kernel(DecodeParams p) {
           w0 = e + 1;
           load_meta(w0);
         }
-        if (m_nv[e + 1 - w0] > 0) stage(nxt, m_phys[e + 1 - w0]);
       }
+      // the next page's copy in two parts: rows 0-31 now, the rest between
+      // this page's two halves (issued at once, the copy stalls the wave on
+      // the memory pipeline for thousands of cycles)
+      const bool stage_next = e + 1 < end && m_nv[e + 1 - w0] > 0;
+      auto copy_rest = [&]() {
+        if (stage_next) stage(nxt, m_phys[e + 1 - w0], kMHalfInstr, kMInstr);
+      };
+      if (stage_next) stage(nxt, m_phys[e + 1 - w0], 0, kMHalfInstr);
       // which of this wave's rows attend the page
       bool act[2];
       bool any_row = false;
@@ -246,12 +255,13 @@ __global__ __launch_bounds__(256, 1) void mla_decode_kernel(DecodeParams p) {
         act[rt] = row_ok[rt] && ((word[rt] >> (h_row[rt] & 31)) & 1u);
         any_row |= __any(act[rt]) != 0;
       }
-      if (nv == 0 || !wave_rows || !any_row) return;
+      // a wave none of whose rows attend the page skips the work but still
+      // passes the copy point between the halves
+      const bool compute = nv > 0 && wave_rows && any_row;
 
       const uint16_t* K = cur;
-      constexpr int kAhead = 2;            // operand reads in flight ahead of use
-#pragma unroll
-      for (int half = 0; half < 2; ++half) {
+      constexpr int kAhead = 3;            // operand reads in flight ahead of use
+      auto half_page = [&](int half) {
         // S^T = K Q^T over tokens 32*half .. +32 (tiles j4 = 2*half, 2*half + 1)
         f32x4 sacc[2][2];
 #pragma unroll
@@ -316,7 +326,7 @@ __global__ __launch_bounds__(256, 1) void mla_decode_kernel(DecodeParams p) {
             }
           l_run[rt] += psum;
         }
-        if (!do_pv) continue;
+        if (!do_pv) return;
 
         // O^T += V^T P^T over the same 32 tokens.  k-slot 8*kg + 4*j + i of
         // this product is token tok_of(2*half + j, 4*kg + i), the S^T fragment
@@ -346,6 +356,11 @@ __global__ __launch_bounds__(256, 1) void mla_decode_kernel(DecodeParams p) {
                                                                    0, 0, 0);
           __builtin_amdgcn_sched_barrier(0);
         }
+      };
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        if (compute) half_page(half);
+        if (half == 0) copy_rest();
       }
     };
     for (int e = beg; e < end; e += 2) {
