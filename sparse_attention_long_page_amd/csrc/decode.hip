@@ -123,6 +123,24 @@ __global__ __launch_bounds__(256, 2) void decode_bf16_kernel(DecodeParams p, con
     }
   };
 
+  // K: A operand of tile j4, row m = col holds token
+  //   tau = 32*(j4/2) + 8*(m/4) + 4*(j4%2) + m%4
+  // The K loads of a wave's next chunk are issued as soon as this chunk's
+  // QK^T has consumed its K registers, so the vector-memory queue never runs
+  // dry while the chunk's softmax and PV compute.
+  bf16x8 kreg[4][KSTEPS];
+  auto load_k = [&](const int* ph, const int* nv) {
+#pragma unroll
+    for (int j4 = 0; j4 < 4; ++j4) {
+      const int tau = 32 * (j4 >> 1) + 8 * (col >> 2) + 4 * (j4 & 1) + (col & 3);
+      const int ent = tau / P, r = tau % P;
+      const int pg = nv[ent] > 0 ? ph[ent] : bt0;
+      const uint16_t* kb = kpool + (((size_t)pg * p.Hkv + g) * P + r) * D + 8 * kg;
+#pragma unroll
+      for (int kk = 0; kk < KSTEPS; ++kk) kreg[j4][kk] = *reinterpret_cast<const bf16x8*>(kb + 32 * kk);
+    }
+  };
+
   int phys[E], nval[E], lp_next[E];
   bool act[E];
   if (wave < nchunks) {
@@ -130,23 +148,17 @@ __global__ __launch_bounds__(256, 2) void decode_bf16_kernel(DecodeParams p, con
     load_lps(wave, lp0);
     resolve(wave, lp0, phys, nval, act);
     if (wave + 4 < nchunks) load_lps(wave + 4, lp_next);
+    load_k(phys, nval);
   }
-  for (int c = wave; c < nchunks; c += 4) {
+  // one chunk; `prefetch` (a compile-time constant in each instantiation)
+  // issues the next chunk's K loads.  The wave's last chunk is peeled off so
+  // that no chunk carries a branch around the prefetch: the wait-count pass
+  // would merge both paths and wait for the prefetch before PV.
+  auto chunk = [&](auto prefetch, int c) {
     // physical page of chunk entry j: the sequence's first page stands in for
     // entries with no valid token
     auto page_of = [&](int j) { return nval[j] > 0 ? phys[j] : bt0; };
 
-    // K: A operand of tile j4, row m = col holds token
-    //   tau = 32*(j4/2) + 8*(m/4) + 4*(j4%2) + m%4
-    bf16x8 kreg[4][KSTEPS];
-#pragma unroll
-    for (int j4 = 0; j4 < 4; ++j4) {
-      const int tau = 32 * (j4 >> 1) + 8 * (col >> 2) + 4 * (j4 & 1) + (col & 3);
-      const int ent = tau / P, r = tau % P;
-      const uint16_t* kb = kpool + (((size_t)page_of(ent) * p.Hkv + g) * P + r) * D + 8 * kg;
-#pragma unroll
-      for (int kk = 0; kk < KSTEPS; ++kk) kreg[j4][kk] = *reinterpret_cast<const bf16x8*>(kb + 32 * kk);
-    }
     // V^T: A operand of PV tile dt, k-step kp: dim 16*dt + col, tokens 32*kp + 8*kg + 0..7
     bf16x8 vreg[DTILES][2];
 #pragma unroll
@@ -172,6 +184,7 @@ __global__ __launch_bounds__(256, 2) void decode_bf16_kernel(DecodeParams p, con
       for (int kk = 0; kk < KSTEPS; ++kk)
         sacc[j4] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kreg[j4][kk], qreg[kk], sacc[j4], 0, 0, 0);
     }
+    if constexpr (decltype(prefetch)::value) load_k(nphys, nnval);
 
     // lane holds S^T[token 32*(j4/2) + 8*kg + 4*(j4%2) + i][row col]; the
     // row maximum is taken on the raw logits (the scale is positive), then
@@ -223,7 +236,10 @@ __global__ __launch_bounds__(256, 2) void decode_bf16_kernel(DecodeParams p, con
       act[j] = nact[j];
       lp_next[j] = lp_after[j];
     }
-  }
+  };
+  int c = wave;
+  for (; c + 4 < nchunks; c += 4) chunk(std::true_type{}, c);
+  if (c < nchunks) chunk(std::false_type{}, c);
 
   // combine the 4 waves
   l_run = sum_over_row_groups(l_run);
