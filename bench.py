@@ -81,7 +81,10 @@ def decode_step_fn(S, wl, inp, mu, splits):
     """One decode step as one HIP graph on the current stream: page summary of
     the newest page, selection, split-K decode and LSE merge.  Graph replay
     removes the host launch cost between kernels; every kernel still runs in
-    every replay.  A captured graph does not own the memory its kernels use,
+    every replay.  (Running the newest-page summary update on a second stream
+    beside the selection, which the library allows when a local window forces
+    that page, measured slower here: the fork and join cost more than the
+    overlap saves.)  A captured graph does not own the memory its kernels use,
     so the last value returned holds every buffer the graph touches; keep it
     as long as the graph."""
     kv = S.PagedKV(inp["k_pool"], inp["v_pool"], inp["block_table"], inp["seq_lens"], d_v=wl.d_v)
@@ -98,10 +101,10 @@ def decode_step_fn(S, wl, inp, mu, splits):
                                                                    splits)), dtype=torch.uint8, device=dev)
     out = torch.empty((wl.batch, wl.q_tokens, wl.n_q_heads, wl.d_v), dtype=inp["q"].dtype, device=dev)
     lse = torch.empty((wl.batch, wl.q_tokens, wl.n_q_heads), dtype=torch.float32, device=dev)
+    def summary():
+        S.sa_page_summary(kv, last_pages=1, out=mu)
 
     def select():
-        if mu is not None:
-            S.sa_page_summary(kv, last_pages=1, out=mu)
         S.sa_select_pages(kv, n_q_heads=wl.n_q_heads, mode=mode, sink_pages=wl.sink_pages,
                           window_pages=wl.window_pages, top_k=wl.top_k, q=inp["q"] if mu is not None else None,
                           page_summary=mu, scores=inp["scores"], critical_k=wl.critical_k, list_stride=stride,
@@ -112,35 +115,39 @@ def decode_step_fn(S, wl, inp, mu, splits):
                            critical_counts=ccounts, ambient_head_mask=inp["ambient_mask"], num_splits=splits,
                            out=out, out_lse=lse, workspace=dec_ws)
 
-    select()
-    decode()
+    def step():
+        if mu is not None:
+            summary()
+        select()
+        decode()
+
+    step()
     torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
-        select()
-        decode()
+        step()
     keep = (kv, inp, mu, lists, counts, ccounts, sel_ws, dec_ws, out, lse)
     return g, (lists, counts, ccounts), decode, keep
 
 
 def recorded_traffic(name):
-    """HBM bytes per launch of a kernel from the rocprofv3 FETCH_SIZE /
-    WRITE_SIZE counters recorded under profiles/ (scaled by the same counters
-    on a copy of known size), or None when the kernel's sources have changed
-    since the counters were taken."""
+    """HBM bytes of one call of the kernels a record under profiles/ names,
+    from their rocprofv3 FETCH_SIZE / WRITE_SIZE counters (KiB per dispatch,
+    scaled by what the same counters read for a copy of known size), or None
+    when the kernels' sources have changed since the counters were taken."""
     import hashlib
-    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles", name)
+    root = os.path.dirname(os.path.abspath(__file__))
+    path = os.path.join(root, "profiles", name)
     if not os.path.exists(path):
         return None
     rec = json.load(open(path))
     h = hashlib.sha256()
-    root = os.path.dirname(os.path.abspath(__file__))
     for src in rec["sources"]:
         h.update(open(os.path.join(root, src), "rb").read())
     if h.hexdigest() != rec["source_sha256"]:
         return None
-    return int(round(rec["fetch_size_kib_per_dispatch"] * 1024 * rec["fetch_scale"]
-                     + rec["write_size_kib_per_dispatch"] * 1024 * rec["write_scale"]))
+    return int(round(sum(k["fetch_size_kib_per_dispatch"] * 1024 * rec["fetch_scale"] +
+                         k["write_size_kib_per_dispatch"] * 1024 * rec["write_scale"] for k in rec["kernels"])))
 
 
 def time_back_to_back(calls, reps):
@@ -325,7 +332,7 @@ def run_decode(args):
         "selected_bytes": nbytes,
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": recorded_traffic(f"decode_bf16_{wl.name}_traffic.json"),
+                     "traffic": recorded_traffic(f"{'mla_decode' if wl.latent else 'sparse_decode'}_{wl.name}_traffic.json"),
                      "kernel": "sa_sparse_decode (decode kernel + split merge)", "algorithmic_bytes": algo_bytes,
                      "launch_us": round(dec_b2b_us, 2)},
     }
@@ -444,7 +451,8 @@ def run_prefill(args):
         "mask_density": round(float(inp["block_mask"].float().mean().item()), 5),
         "visible_pairs": visible,
         "roofline": {"bound": "mfma", "achieved": round(achieved, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
+                     "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
+                     "traffic": recorded_traffic(f"block_sparse_prefill_{wl.name}_traffic.json"),
                      "kernel": "sa_block_sparse_prefill (union + attention)", "algorithmic_flops": flops},
     }
     if not args.no_cpu_baseline:

@@ -250,6 +250,9 @@ sa_status sa_select_pages(const sa_paged_kv* kv, int32_t batch, const void* q, i
     p.block_table = kv->block_table;
     p.seq_lens = kv->seq_lens;
     p.scores = buf;
+    p.sink = sink_pages;
+    p.window = window_pages;
+    p.skip_forced = scores_out ? 0 : 1;
     p.B = batch;
     p.T = q_tokens;
     p.Hq = n_q_heads;

@@ -85,6 +85,8 @@ struct ScoreParams {
   float* scores;             // [B][n_sel][max_pages]
   int B, T, Hq, Hkv, G, n_sel, d, P, max_pages;
   int per_q;                 // 1: PER_Q_HEAD
+  int sink, window;          // forced pages: the first sink and the last window of a sequence
+  int skip_forced;           // forced pages' mean rows are not read (their scores are unused)
 };
 
 struct SelectParams {

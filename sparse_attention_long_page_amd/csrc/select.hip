@@ -293,7 +293,12 @@ __global__ __launch_bounds__(kSelThreads) void score_select_kernel(ScoreParams s
   constexpr int kWaves = kSelThreads / 64;
   constexpr int kSteps = D <= 128 ? 8 : 2;           // 4-page steps whose loads are in flight together
   for (int r0 = 4 * kSteps * wave; r0 < n; r0 += 4 * kSteps * kWaves) {
-    const int my_phys = (lane < 4 * kSteps && r0 + lane < n) ? bt[r0 + lane] : -1;
+    // forced pages' scores are not needed unless the caller asked for the
+    // scores: their mean rows are then not read at all (the newest page's row
+    // may be rewritten concurrently by a summary update on another stream)
+    const int lp_l = r0 + lane;
+    const bool need = lane < 4 * kSteps && lp_l < n && (sout || !(lp_l < L.sink_hi || lp_l >= L.win_lo));
+    const int my_phys = need ? bt[lp_l] : -1;
     f32x4 v[kSteps][PL / 4];
 #pragma unroll
     for (int it = 0; it < kSteps; ++it) {

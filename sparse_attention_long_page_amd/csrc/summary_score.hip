@@ -167,8 +167,11 @@ __global__ __launch_bounds__(256) void page_score_kernel(ScoreParams p, const do
   const int n = (len + p.P - 1) / p.P;
   const int page0 = blockIdx.x * kPagesPerBlock;
   if (threadIdx.x < kPagesPerBlock) {
+    // forced pages (first sink, last window) are scored only when the caller
+    // asked for the scores; otherwise their mean rows are not read
     const int lp = page0 + threadIdx.x;
-    phys_s[threadIdx.x] = lp < n ? p.block_table[(size_t)b * p.max_pages + lp] : -1;
+    const bool forced = lp < min(p.sink, n) || lp >= max(n - p.window, 0);
+    phys_s[threadIdx.x] = (lp < n && !(p.skip_forced && forced)) ? p.block_table[(size_t)b * p.max_pages + lp] : -1;
   }
   if (qpart) {
     const double* qp = qpart + ((size_t)b * p.n_sel + s) * kQChunks * D;

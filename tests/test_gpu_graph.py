@@ -7,7 +7,7 @@ import torch
 
 import sparse_attention_long_page_amd as S
 import workloads as W
-from test_gpu_decode import MODE, gpu_inputs, make_kv
+from test_gpu_decode import MANY_LISTS, MODE, gpu_inputs, make_kv
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -28,9 +28,10 @@ def _step_fns(wl, inp):
     out = torch.empty((wl.batch, wl.q_tokens, wl.n_q_heads, wl.d_v), dtype=inp["q"].dtype, device=DEV)
     lse = torch.empty((wl.batch, wl.q_tokens, wl.n_q_heads), dtype=torch.float32, device=DEV)
 
-    def step():
-        if mu is not None:
-            S.sa_page_summary(kv, last_pages=1, out=mu)
+    def summary():
+        S.sa_page_summary(kv, last_pages=1, out=mu)
+
+    def select_and_decode():
         S.sa_select_pages(kv, n_q_heads=wl.n_q_heads, mode=mode, sink_pages=wl.sink_pages,
                           window_pages=wl.window_pages, top_k=wl.top_k, q=inp["q"] if mu is not None else None,
                           page_summary=mu, scores=inp["scores"], critical_k=wl.critical_k, list_stride=stride,
@@ -39,7 +40,13 @@ def _step_fns(wl, inp):
                            ambient_head_mask=inp["ambient_mask"], num_splits=3, out=out, out_lse=lse,
                            workspace=dec_ws)
 
+    def step():
+        if mu is not None:
+            summary()
+        select_and_decode()
+
     results = [lists, counts, out, lse] + ([cc] if cc is not None else [])
+    step.parts = (summary, select_and_decode, mu)
     return step, results
 
 
@@ -108,3 +115,40 @@ def test_prefill_graph_replays_match_eager():
             n = int(counts[g_])
             assert torch.equal(table[g_, :n], eager[2][g_, :n]), f"replay {rep}: table {g_} differs"
         assert torch.equal(out, eager[0]) and torch.equal(lse, eager[1]), f"replay {rep} differs"
+
+
+@pytest.mark.parametrize("name", ["llama3_decode_small", "llama3_many_lists"])
+def test_summary_beside_selection_matches_serial(name):
+    """With a local window the newest page is forced and its summary takes no
+    part in the ranking; the selection does not read forced pages' summary
+    rows, so the newest-page summary update may run on a second stream beside
+    the selection and the decode.  Graph replays of that forked step equal the
+    serial eager step (fused score+select and separate kernels alike)."""
+    wl = {**W.SMALL, **MANY_LISTS}[name]
+    assert wl.window_pages >= 1 and wl.scores == "summary"
+    inp = gpu_inputs(W.make_decode_inputs(wl, "cpu", seed=43))
+    step, results = _step_fns(wl, inp)
+    summary, select_and_decode, mu = step.parts
+    step()
+    torch.cuda.synchronize()
+    eager = [r.clone() for r in results]
+    side = torch.cuda.Stream()
+
+    def forked():
+        cur = torch.cuda.current_stream()
+        side.wait_stream(cur)
+        with torch.cuda.stream(side):
+            summary()
+        select_and_decode()
+        cur.wait_stream(side)
+
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        forked()
+    for rep in range(4):
+        for r in results:
+            r.fill_(-7)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        _assert_same(results, eager, rep)
