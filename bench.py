@@ -79,7 +79,7 @@ class Timer:
 
 def decode_step_fn(S, wl, inp, mu, splits):
     """One decode step as one HIP graph on the current stream: page summary of
-    the newest page, selection, split-K decode and LSE merge.  Graph replay
+    the newest page and selection (one call), split-K decode and LSE merge.  Graph replay
     removes the host launch cost between kernels; every kernel still runs in
     every replay.  (Running the newest-page summary update on a second stream
     beside the selection, which the library allows when a local window forces
@@ -101,14 +101,13 @@ def decode_step_fn(S, wl, inp, mu, splits):
                                                                    splits)), dtype=torch.uint8, device=dev)
     out = torch.empty((wl.batch, wl.q_tokens, wl.n_q_heads, wl.d_v), dtype=inp["q"].dtype, device=dev)
     lse = torch.empty((wl.batch, wl.q_tokens, wl.n_q_heads), dtype=torch.float32, device=dev)
-    def summary():
-        S.sa_page_summary(kv, last_pages=1, out=mu)
-
     def select():
+        # the newest page's summary is recomputed inside the selection call
+        # (same bits as a separate sa_page_summary(last_pages=1) call)
         S.sa_select_pages(kv, n_q_heads=wl.n_q_heads, mode=mode, sink_pages=wl.sink_pages,
                           window_pages=wl.window_pages, top_k=wl.top_k, q=inp["q"] if mu is not None else None,
                           page_summary=mu, scores=inp["scores"], critical_k=wl.critical_k, list_stride=stride,
-                          workspace=sel_ws, out=(lists, counts, ccounts))
+                          workspace=sel_ws, out=(lists, counts, ccounts), refresh_newest_page=mu is not None)
 
     def decode():
         S.sa_sparse_decode(kv, inp["q"], lists, counts, mode=mode, sm_scale=wl.sm_scale,
@@ -116,8 +115,6 @@ def decode_step_fn(S, wl, inp, mu, splits):
                            out=out, out_lse=lse, workspace=dec_ws)
 
     def step():
-        if mu is not None:
-            summary()
         select()
         decode()
 

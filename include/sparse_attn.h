@@ -120,6 +120,10 @@ sa_status sa_page_summary(const sa_paged_kv* kv, int32_t batch, int32_t last_pag
  *           PER_Q_HEAD: head s alone, KV head s / group) of q, in float64.
  * With `scores` given, those values are used as-is instead (q and
  * page_summary may then be NULL).
+ * refresh_newest_page != 0 (router scores only, page_summary required):
+ * first recompute page_summary for each sequence's newest page, all KV heads,
+ * exactly as sa_page_summary(kv, batch, 1, page_summary) would (same bits),
+ * then score with it; one call replaces the per-step pair of calls.
  * Forced pages F = [0, sink_pages) u [n - window_pages, n), clipped to [0, n).
  * The other pages are ranked by (score descending, logical index ascending),
  * NaN last, -0 == +0; the first k = min(top_k, n - |F|) are selected.
@@ -128,7 +132,8 @@ sa_status sa_page_summary(const sa_paged_kv* kv, int32_t batch, int32_t last_pag
  *           Ambient  = ascending(the remaining selected); list = Critical
  *           then Ambient; critical_counts = |Critical|.
  *   q            [batch][q_tokens][n_q_heads][d_qk] (kv->dtype) or NULL
- *   page_summary [n_phys_pages][n_kv_heads][d_qk] fp32 or NULL
+ *   page_summary [n_phys_pages][n_kv_heads][d_qk] fp32 or NULL (written only
+ *                for the newest pages, and only with refresh_newest_page)
  *   scores       [batch][n_sel][scores_stride] fp32 or NULL, scores_stride >= max_pages
  *   page_lists   out [batch][n_sel][list_stride] int32 logical ids, entries
  *                past the count are left untouched;
@@ -145,7 +150,7 @@ size_t sa_select_pages_workspace_size(int32_t batch, int32_t n_sel, int32_t max_
 
 sa_status sa_select_pages(const sa_paged_kv* kv, int32_t batch,
                           const void* q, int32_t q_tokens, int32_t n_q_heads,
-                          const float* page_summary,
+                          float* page_summary, int32_t refresh_newest_page,
                           const float* scores, int32_t scores_stride,
                           sa_sel_mode mode,
                           int32_t sink_pages, int32_t window_pages, int32_t top_k,

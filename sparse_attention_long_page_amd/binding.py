@@ -68,7 +68,7 @@ def load_library(build_if_missing: bool = True) -> ctypes.CDLL:
     sig = {
         "sa_page_summary": (c_int, [P, c_int32, c_int32, P, P]),
         "sa_select_pages_workspace_size": (c_size_t, [c_int32, c_int32, c_int32]),
-        "sa_select_pages": (c_int, [P, c_int32, P, c_int32, c_int32, P, P, c_int32, c_int, c_int32, c_int32,
+        "sa_select_pages": (c_int, [P, c_int32, P, c_int32, c_int32, P, c_int32, P, c_int32, c_int, c_int32, c_int32,
                                     c_int32, c_int32, P, c_int32, P, P, P, P, c_size_t, P]),
         "sa_sparse_decode_workspace_size": (c_size_t, [P, c_int32, c_int32, c_int32, c_int32, c_int, c_int32]),
         "sa_sparse_decode": (c_int, [P, c_int32, P, c_int32, c_int32, P, P, c_int32, c_int, P, P, c_float,
@@ -160,8 +160,10 @@ def sa_select_pages(kv: PagedKV, *, n_q_heads: int, mode: int, sink_pages: int, 
                     q: Optional[torch.Tensor] = None, page_summary: Optional[torch.Tensor] = None,
                     scores: Optional[torch.Tensor] = None, critical_k: Optional[int] = None,
                     list_stride: Optional[int] = None, scores_out: Optional[torch.Tensor] = None,
-                    workspace: Optional[torch.Tensor] = None, out=None):
-    """Returns (page_lists [B][n_sel][list_stride] int32, page_counts, critical_counts or None)."""
+                    workspace: Optional[torch.Tensor] = None, out=None, refresh_newest_page: bool = False):
+    """Returns (page_lists [B][n_sel][list_stride] int32, page_counts, critical_counts or None).
+    refresh_newest_page: first rewrite page_summary for each sequence's newest page
+    (as sa_page_summary(kv, last_pages=1) would), then score with it."""
     B = kv.batch
     n_sel = kv.n_kv_heads if mode == SA_SEL_PER_KV_HEAD else n_q_heads
     if list_stride is None:
@@ -180,7 +182,8 @@ def sa_select_pages(kv: PagedKV, *, n_q_heads: int, mode: int, sink_pages: int, 
         workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=kv.device)
     ws_bytes = workspace.numel() if workspace is not None else 0
     _check(load_library().sa_select_pages(
-        kv.ref, B, _ptr(q), q_tokens, n_q_heads, _ptr(page_summary), _ptr(scores), scores_stride, mode,
+        kv.ref, B, _ptr(q), q_tokens, n_q_heads, _ptr(page_summary), 1 if refresh_newest_page else 0, _ptr(scores),
+        scores_stride, mode,
         sink_pages, window_pages, top_k, critical_k if critical_k is not None else 0, _ptr(lists),
         list_stride, _ptr(counts), _ptr(ccounts), _ptr(scores_out), _ptr(workspace), ws_bytes,
         _stream(kv.device)))

@@ -168,7 +168,7 @@ size_t sa_select_pages_workspace_size(int32_t batch, int32_t n_sel, int32_t max_
 }
 
 sa_status sa_select_pages(const sa_paged_kv* kv, int32_t batch, const void* q, int32_t q_tokens,
-                          int32_t n_q_heads, const float* page_summary, const float* scores,
+                          int32_t n_q_heads, float* page_summary, int32_t refresh_newest_page, const float* scores,
                           int32_t scores_stride, sa_sel_mode mode, int32_t sink_pages, int32_t window_pages,
                           int32_t top_k, int32_t critical_k, int32_t* page_lists, int32_t list_stride,
                           int32_t* page_counts, int32_t* critical_counts, float* scores_out, void* workspace,
@@ -191,6 +191,8 @@ sa_status sa_select_pages(const sa_paged_kv* kv, int32_t batch, const void* q, i
     return fail(SA_ERR_INVALID_ARGUMENT, "list_stride %d < min(max_pages, sink+window+top_k) = %ld", list_stride,
                 need_stride);
   const int n_sel = n_sel_of(kv, n_q_heads, mode);
+  if (refresh_newest_page && (scores || !page_summary))
+    return fail(SA_ERR_INVALID_ARGUMENT, "refresh_newest_page needs page_summary and router scores (no scores)");
   if (scores) {
     if (scores_stride < kv->max_pages)
       return fail(SA_ERR_INVALID_ARGUMENT, "scores_stride %d < max_pages %d", scores_stride, kv->max_pages);
@@ -237,8 +239,25 @@ sa_status sa_select_pages(const sa_paged_kv* kv, int32_t batch, const void* q, i
     p.P = kv->page_size;
     p.max_pages = kv->max_pages;
     p.per_q = mode == SA_SEL_PER_Q_HEAD;
+    p.refresh = refresh_newest_page ? 1 : 0;
+    p.k_pool = kv->k_pool;
+    p.mu_out = page_summary;
     return device_status(sa::launch_score_select(p, sp, batch, kv->dtype == SA_DTYPE_BF16, stream),
                          "score_select launch");
+  }
+  if (refresh_newest_page) {
+    sa::SummaryParams smp{};
+    smp.k_pool = kv->k_pool;
+    smp.block_table = kv->block_table;
+    smp.seq_lens = kv->seq_lens;
+    smp.mu = page_summary;
+    smp.n_kv = kv->n_kv_heads;
+    smp.P = kv->page_size;
+    smp.d = kv->d_qk;
+    smp.max_pages = kv->max_pages;
+    smp.last_pages = 1;
+    hipError_t e = sa::launch_page_summary(smp, batch, kv->dtype == SA_DTYPE_BF16, stream);
+    if (e != hipSuccess) return device_status(e, "page_summary launch");
   }
   if (!scores) {
     float* buf = scores_out ? scores_out : reinterpret_cast<float*>(workspace);

@@ -87,6 +87,9 @@ struct ScoreParams {
   int per_q;                 // 1: PER_Q_HEAD
   int sink, window;          // forced pages: the first sink and the last window of a sequence
   int skip_forced;           // forced pages' mean rows are not read (their scores are unused)
+  const void* k_pool;        // refresh: keys of the newest pages
+  float* mu_out;             // refresh: the summary rows rewritten (same array as mu)
+  int refresh;               // recompute each sequence's newest-page summary before scoring
 };
 
 struct SelectParams {

@@ -264,12 +264,48 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectParams p) {
 template <typename T, int D>
 __global__ __launch_bounds__(kSelThreads) void score_select_kernel(ScoreParams sp, SelectParams p) {
   constexpr int PL = D / 16;
+  // newest-page summary refresh: the thread partition of page_summary_kernel
+  // (thread (cg, ts): 16-byte column group cg, tokens ts, ts + TS, ...)
+  constexpr int VW = 16 / sizeof(T), CG = D / VW, TS = (256 / CG < 16) ? 256 / CG : 16;
   extern __shared__ uint32_t keys[];
   __shared__ SelShared sh;
   __shared__ double qbar[D];
+  __shared__ double rpart[TS * D];
+  __shared__ float fresh[D];
   const int s = blockIdx.x, b = blockIdx.y;
   const ListShape L = list_shape(p, b);
   const int n = L.n;
+  const int g = sp.per_q ? s / sp.G : s;
+  const int32_t* bt = sp.block_table + (size_t)b * sp.max_pages;
+  // With refresh, the newest page's mean row (KV head g) is recomputed here,
+  // summed in the same order as page_summary_kernel (same bits), written by
+  // one list per head, and used for this list's score of that page from LDS.
+  const bool refresh = sp.refresh && n > 0;
+  const int last_phys = refresh ? bt[n - 1] : 0;
+  const int last_nv = refresh ? page_valid(sp.seq_lens[b], n - 1, sp.P) : 0;
+  if (refresh && threadIdx.x < CG * TS) {
+    const int cg = threadIdx.x % CG, ts = threadIdx.x / CG;
+    const T* base = reinterpret_cast<const T*>(sp.k_pool) + (((size_t)last_phys * sp.Hkv + g) * sp.P) * D + cg * VW;
+    double acc[VW];
+#pragma unroll
+    for (int i = 0; i < VW; ++i) acc[i] = 0.0;
+#pragma unroll 4
+    for (int j = ts; j < last_nv; j += TS) {
+      const u32x4 w = *reinterpret_cast<const u32x4*>(base + (size_t)j * D);
+      if constexpr (sizeof(T) == 2) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          acc[2 * i] += (double)bf16_lo(w[i]);
+          acc[2 * i + 1] += (double)bf16_hi(w[i]);
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[i] += (double)__uint_as_float(w[i]);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < VW; ++i) rpart[ts * D + cg * VW + i] = acc[i];
+  }
   const T* q = reinterpret_cast<const T*>(sp.q);
   const int rows = sp.per_q ? sp.T : sp.T * sp.G;
   for (int e = threadIdx.x; e < D; e += kSelThreads) {
@@ -285,10 +321,20 @@ __global__ __launch_bounds__(kSelThreads) void score_select_kernel(ScoreParams s
   }
   for (int i = threadIdx.x; i < 512; i += kSelThreads) sh.hist[0][0][i] = 0u;
   __syncthreads();
-  const int g = sp.per_q ? s / sp.G : s;
+  if (refresh) {
+    const bool writer = !sp.per_q || s % sp.G == 0;
+    float* mrow = sp.mu_out + ((size_t)last_phys * sp.Hkv + g) * D;
+    for (int e = threadIdx.x; e < D; e += kSelThreads) {
+      double sum = 0.0;
+      for (int ts = 0; ts < TS; ++ts) sum += rpart[ts * D + e];
+      const float m = (float)(sum / (double)last_nv);
+      fresh[e] = m;
+      if (writer) mrow[e] = m;
+    }
+    __syncthreads();
+  }
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int sub = lane & 15, slot = lane >> 4;
-  const int32_t* bt = sp.block_table + (size_t)b * sp.max_pages;
   float* sout = sp.scores ? sp.scores + ((size_t)b * sp.n_sel + s) * sp.max_pages : nullptr;
   constexpr int kWaves = kSelThreads / 64;
   constexpr int kSteps = D <= 128 ? 8 : 2;           // 4-page steps whose loads are in flight together
@@ -297,7 +343,8 @@ __global__ __launch_bounds__(kSelThreads) void score_select_kernel(ScoreParams s
     // scores: their mean rows are then not read at all (the newest page's row
     // may be rewritten concurrently by a summary update on another stream)
     const int lp_l = r0 + lane;
-    const bool need = lane < 4 * kSteps && lp_l < n && (sout || !(lp_l < L.sink_hi || lp_l >= L.win_lo));
+    const bool need = lane < 4 * kSteps && lp_l < n && (sout || !(lp_l < L.sink_hi || lp_l >= L.win_lo)) &&
+                      !(refresh && lp_l == n - 1);    // the refreshed row comes from LDS
     const int my_phys = need ? bt[lp_l] : -1;
     f32x4 v[kSteps][PL / 4];
 #pragma unroll
@@ -310,6 +357,13 @@ __global__ __launch_bounds__(kSelThreads) void score_select_kernel(ScoreParams s
 #pragma unroll
     for (int it = 0; it < kSteps; ++it) {
       const int lp = r0 + it * 4 + slot;
+      if (refresh && lp == n - 1) {
+#pragma unroll
+        for (int i = 0; i < PL / 4; ++i) {
+          const float* f = fresh + 64 * i + 4 * sub;
+          v[it][i] = f32x4{f[0], f[1], f[2], f[3]};
+        }
+      }
       const double* qq = qbar + 4 * sub;
       double acc = 0.0;
 #pragma unroll

@@ -52,13 +52,13 @@ def kv(**over):
 
 
 def select(kvd, **over):
-    a = dict(batch=2, q=FAKE, q_tokens=1, n_q_heads=8, page_summary=FAKE, scores=None, scores_stride=0,
+    a = dict(batch=2, q=FAKE, q_tokens=1, n_q_heads=8, page_summary=FAKE, refresh=0, scores=None, scores_stride=0,
              mode=B.SA_SEL_PER_KV_HEAD, sink=1, window=2, top_k=4, critical_k=0, lists=FAKE, stride=7,
              counts=FAKE, ccounts=None, scores_out=None, ws=FAKE, ws_bytes=1 << 30)
     a.update(over)
     lib = S.load_library()
     return lib.sa_select_pages(ctypes.byref(kvd), a["batch"], a["q"], a["q_tokens"], a["n_q_heads"],
-                               a["page_summary"], a["scores"], a["scores_stride"], a["mode"], a["sink"],
+                               a["page_summary"], a["refresh"], a["scores"], a["scores_stride"], a["mode"], a["sink"],
                                a["window"], a["top_k"], a["critical_k"], a["lists"], a["stride"], a["counts"],
                                a["ccounts"], a["scores_out"], a["ws"], a["ws_bytes"], None)
 
@@ -103,6 +103,8 @@ SELECT_CASES = [
     ("bad mode", {}, dict(mode=5), INV),
     ("too many pages", dict(kv=dict(max_pages=20000)), {}, UNS),
     ("workspace too small", {}, dict(ws_bytes=16), WS),
+    ("refresh with given scores", {}, dict(refresh=1, scores=FAKE, scores_stride=32), INV),
+    ("refresh without summary", {}, dict(refresh=1, page_summary=None), INV),
 ]
 
 

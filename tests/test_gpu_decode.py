@@ -112,6 +112,43 @@ def test_select_matches_oracle(name):
     assert rep.exact + rep.band_events == rep.units
 
 
+@pytest.mark.parametrize("name", [n for n, w in SELECT_CASES.items() if w.scores == "summary"])
+def test_select_with_summary_refresh_matches_separate_calls(name):
+    """refresh_newest_page: the selection first rewrites each sequence's
+    newest-page summary (fused into the score+select kernel when there are
+    enough lists, a separate summary kernel otherwise).  Its summaries, scores
+    and lists equal those of sa_page_summary(last_pages=1) followed by a plain
+    selection, bit for bit; the newest pages' rows start out poisoned, so the
+    refresh must have written them."""
+    wl = SELECT_CASES[name]
+    cpu = W.make_decode_inputs(wl, "cpu", seed=5)
+    inp = gpu_inputs(cpu)
+    kv = make_kv(inp, wl)
+    mu_ref = S.sa_page_summary(kv)
+    bt, lens = npi(cpu["block_table"]), npi(cpu["seq_lens"])
+    newest = [int(bt[b, O.n_pages_of(int(L), wl.page_size) - 1]) for b, L in enumerate(lens) if L > 0]
+    mu_ref[newest] = float("nan")
+    mu_fused = mu_ref.clone()
+    args = dict(n_q_heads=wl.n_q_heads, mode=MODE[wl.mode], sink_pages=wl.sink_pages, window_pages=wl.window_pages,
+                top_k=wl.top_k, q=inp["q"], critical_k=wl.critical_k)
+    sc_ref = torch.empty((wl.batch, wl.n_sel, wl.max_pages), dtype=torch.float32, device=DEV)
+    sc_fused = torch.empty_like(sc_ref)
+    S.sa_page_summary(kv, last_pages=1, out=mu_ref)
+    l_ref, c_ref, cc_ref = S.sa_select_pages(kv, page_summary=mu_ref, scores_out=sc_ref, **args)
+    l_f, c_f, cc_f = S.sa_select_pages(kv, page_summary=mu_fused, scores_out=sc_fused, refresh_newest_page=True, **args)
+    torch.cuda.synchronize()
+    assert torch.equal(mu_fused.isnan(), mu_ref.isnan())
+    assert torch.equal(torch.nan_to_num(mu_fused, nan=0.0), torch.nan_to_num(mu_ref, nan=0.0))
+    assert not mu_ref[newest].isnan().any()
+    assert torch.equal(torch.nan_to_num(sc_fused, nan=0.0), torch.nan_to_num(sc_ref, nan=0.0))
+    assert torch.equal(c_f, c_ref)
+    if cc_ref is not None:
+        assert torch.equal(cc_f, cc_ref)
+    L1, L2, C = npi(l_f), npi(l_ref), npi(c_ref)
+    for idx in np.ndindex(*C.shape):
+        assert np.array_equal(L1[idx][:C[idx]], L2[idx][:C[idx]]), idx
+
+
 @pytest.mark.parametrize("tiered", [False, True])
 def test_select_long_lists_with_ties_exact(tiered):
     """Selection on given scores is index work: it must equal the oracle's
