@@ -36,7 +36,24 @@ namespace sa {
 // arguments: the kernel never writes them, so their wave-uniform reads compile
 // to scalar loads, which complete on their own counter and never wait behind
 // the K/V vector loads in flight.
-template <int D, int P, bool TIERED>
+// STAGED (d 128, per-KV-head lists): each wave copies its next 64-token
+// chunk (K rows and V^T rows, 32 KiB) into its own LDS area with non-temporal
+// load-to-LDS instructions of 1 KiB contiguous each, and reads the MFMA
+// operands from there.  Streaming reads whose instructions cover whole cache
+// lines run at ~6.1-6.4 TB/s on this HBM against ~5.4-6.0 TB/s for the
+// operand-shaped register loads (16 rows x 64 B per instruction), which
+// cannot use the non-temporal hint.  Every page of a per-KV-head list is read
+// by one workgroup only, so nothing is lost by not keeping it in L2.
+// LDS rows are XOR-swizzled so the operand reads are free of bank conflicts
+// (gfx950 16-byte reads: four cycles per 64 lanes, lanes of a cycle by
+// half-wave and the parity of lane bits 2..4, distinct 16-byte slots modulo
+// 256 bytes):
+//   K row r (256 B):   16-byte chunk c sits at slot c ^ (2 (r & 3) + 8 ((r >> 3) & 1))
+//   V^T row d (128 B): token chunk c sits at slot c ^ (d & 6)
+__device__ __forceinline__ int stg_kswz(int r) { return 2 * (r & 3) + 8 * ((r >> 3) & 1); }
+__device__ __forceinline__ int stg_vswz(int d) { return d & 6; }
+
+template <int D, int P, bool TIERED, bool STAGED>
 __global__ __launch_bounds__(256, 2) void decode_bf16_kernel(DecodeParams p, const int32_t* __restrict__ lists,
                                                             const int32_t* __restrict__ btab,
                                                             const int32_t* __restrict__ seq_lens,
@@ -129,6 +146,51 @@ __global__ __launch_bounds__(256, 2) void decode_bf16_kernel(DecodeParams p, con
   // QK^T has consumed its K registers, so the vector-memory queue never runs
   // dry while the chunk's softmax and PV compute.
   bf16x8 kreg[4][KSTEPS];
+  uint16_t* stage_buf = nullptr;        // this wave's 32 KiB staging area (STAGED)
+  if constexpr (STAGED) {
+    __shared__ __attribute__((aligned(16))) uint16_t stg[4 * 16384];
+    stage_buf = stg + wave * 16384;
+  }
+  // STAGED: copy of one chunk into the wave's staging area.  Wave-wide
+  // instruction i covers slots [64 i, 64 i + 64) of the K part (row s / 16,
+  // slot s % 16) and of the V^T part (row s / 8, slot s % 8).
+  auto stage_copy = [&](const int* ph, const int* nv) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int sl = 64 * i + lane, r = sl >> 4;
+      const int c = (sl & 15) ^ stg_kswz(r);
+      const int ent = r / P, rr = r % P;
+      const int pg = nv[ent] > 0 ? ph[ent] : bt0;
+      __builtin_amdgcn_global_load_lds(kpool + (((size_t)pg * p.Hkv + g) * P + rr) * D + 8 * c, stage_buf + 512 * i,
+                                       16, 0, 2 /* nt */);
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int sl = 64 * i + lane, d = sl >> 3;
+      const int c = (sl & 7) ^ stg_vswz(d);
+      const int t0 = 8 * c, ent = t0 / P, r0 = t0 % P;
+      const int pg = nv[ent] > 0 ? ph[ent] : bt0;
+      __builtin_amdgcn_global_load_lds(vpool + (((size_t)pg * p.Hkv + g) * D + d) * P + r0,
+                                       stage_buf + 8192 + 512 * i, 16, 0, 2 /* nt */);
+    }
+  };
+  // STAGED: the chunk's operands from the staging area (its copy complete)
+  auto read_staged = [&](bf16x8 (&vreg)[DTILES][2]) {
+#pragma unroll
+    for (int j4 = 0; j4 < 4; ++j4) {
+      const int tau = 32 * (j4 >> 1) + 8 * (col >> 2) + 4 * (j4 & 1) + (col & 3);
+#pragma unroll
+      for (int kk = 0; kk < KSTEPS; ++kk)
+        kreg[j4][kk] = *reinterpret_cast<const bf16x8*>(stage_buf + 8 * (16 * tau + ((kg + 4 * kk) ^ stg_kswz(tau))));
+    }
+#pragma unroll
+    for (int kp = 0; kp < 2; ++kp)
+#pragma unroll
+      for (int dt = 0; dt < DTILES; ++dt) {
+        const int d = 16 * dt + col;
+        vreg[dt][kp] = *reinterpret_cast<const bf16x8*>(stage_buf + 8192 + 8 * (8 * d + ((4 * kp + kg) ^ stg_vswz(d))));
+      }
+  };
   auto load_k = [&](const int* ph, const int* nv) {
 #pragma unroll
     for (int j4 = 0; j4 < 4; ++j4) {
@@ -148,7 +210,8 @@ __global__ __launch_bounds__(256, 2) void decode_bf16_kernel(DecodeParams p, con
     load_lps(wave, lp0);
     resolve(wave, lp0, phys, nval, act);
     if (wave + 4 < nchunks) load_lps(wave + 4, lp_next);
-    load_k(phys, nval);
+    if constexpr (STAGED) stage_copy(phys, nval);
+    else load_k(phys, nval);
   }
   // one chunk; `prefetch` (a compile-time constant in each instantiation)
   // issues the next chunk's K loads.  The wave's last chunk is peeled off so
@@ -161,13 +224,15 @@ __global__ __launch_bounds__(256, 2) void decode_bf16_kernel(DecodeParams p, con
 
     // V^T: A operand of PV tile dt, k-step kp: dim 16*dt + col, tokens 32*kp + 8*kg + 0..7
     bf16x8 vreg[DTILES][2];
+    if constexpr (!STAGED) {
 #pragma unroll
-    for (int kp = 0; kp < 2; ++kp) {
-      const int t0 = 32 * kp + 8 * kg;
-      const int ent = t0 / P, r0 = t0 % P;
-      const uint16_t* vb = vpool + (((size_t)page_of(ent) * p.Hkv + g) * D + col) * P + r0;
+      for (int kp = 0; kp < 2; ++kp) {
+        const int t0 = 32 * kp + 8 * kg;
+        const int ent = t0 / P, r0 = t0 % P;
+        const uint16_t* vb = vpool + (((size_t)page_of(ent) * p.Hkv + g) * D + col) * P + r0;
 #pragma unroll
-      for (int dt = 0; dt < DTILES; ++dt) vreg[dt][kp] = *reinterpret_cast<const bf16x8*>(vb + (size_t)16 * dt * P);
+        for (int dt = 0; dt < DTILES; ++dt) vreg[dt][kp] = *reinterpret_cast<const bf16x8*>(vb + (size_t)16 * dt * P);
+      }
     }
 
     // metadata of the next two chunks (scalar loads) while this one computes
@@ -175,6 +240,14 @@ __global__ __launch_bounds__(256, 2) void decode_bf16_kernel(DecodeParams p, con
     bool nact[E];
     if (c + 4 < nchunks) resolve(c + 4, lp_next, nphys, nnval, nact);
     if (c + 8 < nchunks) load_lps(c + 8, lp_after);
+    if constexpr (STAGED) {
+      // this chunk's copy has landed; take its operands, then reuse the
+      // staging area for the next chunk while this one computes
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      read_staged(vreg);
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      if constexpr (decltype(prefetch)::value) stage_copy(nphys, nnval);
+    }
 
     f32x4 sacc[4];
 #pragma unroll
@@ -184,7 +257,7 @@ __global__ __launch_bounds__(256, 2) void decode_bf16_kernel(DecodeParams p, con
       for (int kk = 0; kk < KSTEPS; ++kk)
         sacc[j4] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kreg[j4][kk], qreg[kk], sacc[j4], 0, 0, 0);
     }
-    if constexpr (decltype(prefetch)::value) load_k(nphys, nnval);
+    if constexpr (!STAGED && decltype(prefetch)::value) load_k(nphys, nnval);
 
     // lane holds S^T[token 32*(j4/2) + 8*kg + 4*(j4%2) + i][row col]; the
     // row maximum is taken on the raw logits (the scale is positive), then
@@ -244,7 +317,19 @@ __global__ __launch_bounds__(256, 2) void decode_bf16_kernel(DecodeParams p, con
   // combine the 4 waves
   l_run = sum_over_row_groups(l_run);
   __shared__ float sm_m[4][16], sm_l[4][16];
-  __shared__ float sm_o[4][16][D + 4];
+  float (*sm_o)[16][D + 4];              // [4][16][D + 4]
+  if constexpr (STAGED) {
+    // the staging areas are free once every wave has left the loop (its last
+    // operand reads waited for, no copy in flight after the peeled last
+    // chunk); the barrier keeps a fast wave's partial O out of an area
+    // another wave may still be reading
+    sm_o = reinterpret_cast<float (*)[16][D + 4]>(stage_buf - wave * 16384);
+    static_assert(4 * 16 * (D + 4) * sizeof(float) <= 4 * 16384 * sizeof(uint16_t), "partial O fits the staging areas");
+    __syncthreads();
+  } else {
+    __shared__ float sm_o_s[4][16][D + 4];
+    sm_o = sm_o_s;
+  }
   if (kg == 0) { sm_m[wave][col] = m_run; sm_l[wave][col] = l_run; }
 #pragma unroll
   for (int dt = 0; dt < DTILES; ++dt)
@@ -438,19 +523,27 @@ hipError_t launch_decode(const DecodeParams& p, int bf16, hipStream_t s) {
     else hipLaunchKernelGGL(decode_f32_kernel<128>, grid, block, 0, s, p);
     return hipGetLastError();
   }
-#define SA_DECODE_LAUNCH(D_, P_)                                                                        \
+#define SA_DECODE_LAUNCH(D_, P_, ST_)                                                                   \
   do {                                                                                                  \
     if (tiered)                                                                                         \
-      hipLaunchKernelGGL((decode_bf16_kernel<D_, P_, true>), grid, block, 0, s, p, p.lists, p.block_table, \
-                         p.seq_lens, p.counts);                                                         \
+      hipLaunchKernelGGL((decode_bf16_kernel<D_, P_, true, ST_>), grid, block, 0, s, p, p.lists,            \
+                         p.block_table, p.seq_lens, p.counts);                                          \
     else                                                                                                \
-      hipLaunchKernelGGL((decode_bf16_kernel<D_, P_, false>), grid, block, 0, s, p, p.lists, p.block_table, \
-                         p.seq_lens, p.counts);                                                         \
+      hipLaunchKernelGGL((decode_bf16_kernel<D_, P_, false, ST_>), grid, block, 0, s, p, p.lists,           \
+                         p.block_table, p.seq_lens, p.counts);                                          \
   } while (0)
-  if (p.d_qk == 64 && p.P == 16) SA_DECODE_LAUNCH(64, 16);
-  else if (p.d_qk == 64 && p.P == 64) SA_DECODE_LAUNCH(64, 64);
-  else if (p.d_qk == 128 && p.P == 16) SA_DECODE_LAUNCH(128, 16);
-  else SA_DECODE_LAUNCH(128, 64);
+  // staged operands for per-KV-head lists at d 128 (pages read by one
+  // workgroup only); register operands otherwise
+  const bool staged = !p.per_q;
+  if (p.d_qk == 64 && p.P == 16) SA_DECODE_LAUNCH(64, 16, false);
+  else if (p.d_qk == 64 && p.P == 64) SA_DECODE_LAUNCH(64, 64, false);
+  else if (p.d_qk == 128 && p.P == 16) {
+    if (staged) SA_DECODE_LAUNCH(128, 16, true);
+    else SA_DECODE_LAUNCH(128, 16, false);
+  } else {
+    if (staged) SA_DECODE_LAUNCH(128, 64, true);
+    else SA_DECODE_LAUNCH(128, 64, false);
+  }
 #undef SA_DECODE_LAUNCH
   return hipGetLastError();
 }
