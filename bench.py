@@ -9,9 +9,13 @@ One step = one decode layer's sparse-attention work for one batch:
   sa_page_summary(last_pages=1)  mean key of the page the newest token landed in
   sa_select_pages                router scores + sink/window/top-k lists
   sa_sparse_decode               split-K flash-decode over the lists (+ merge)
-Each step is replayed from one HIP graph captured once per input set, so the
-host's launch cost does not leave the GPU idle between kernels; every kernel
-runs in every step.  Inputs are
+The timed loop replays one HIP graph that holds one step per input set, run
+back to back as consecutive layers' attention runs inside a captured decode
+forward pass, so neither the host's launch cost nor a graph launch leaves the
+GPU idle between steps; every kernel runs in every step, and exactly --steps
+steps are timed (whole graphs, then single-step graphs for the remainder).
+The same steps replayed one graph per step are timed too
+(ms_per_step_single_step_graphs).  Inputs are
 resident in HBM before timing; steps rotate over 3 independently drawn input
 sets (4.2 GB each) so no step finds its pages in the 256 MB last-level cache
 left warm by the previous one.
@@ -124,7 +128,7 @@ def decode_step_fn(S, wl, inp, mu, splits):
     with torch.cuda.graph(g):
         step()
     keep = (kv, inp, mu, lists, counts, ccounts, sel_ws, dec_ws, out, lse)
-    return g, (lists, counts, ccounts), decode, keep
+    return g, (lists, counts, ccounts), decode, keep, step
 
 
 def recorded_traffic(name):
@@ -284,29 +288,44 @@ def run_decode(args):
     torch.cuda.synchronize()
     steps = []
     for inp, mu in sets:
-        graphs, res, dec, keep = decode_step_fn(S, wl, inp, mu, splits)
-        steps.append((graphs, res, inp, dec, keep))
-
-    def step(i):
-        steps[i % len(steps)][0].replay()
-
-    for i in range(args.warmup):
-        step(i)
+        graphs, res, dec, keep, step_call = decode_step_fn(S, wl, inp, mu, splits)
+        steps.append((graphs, res, inp, dec, keep, step_call))
+    # one graph with one step per input set, in set order
+    chain = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(chain):
+        for st in steps:
+            st[5]()
     torch.cuda.synchronize()
-    # one event pair around the whole timed region (a pair per step would add
-    # its own records between the graph launches)
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    t0 = time.perf_counter()
-    e0.record()
-    for i in range(args.steps):
-        step(i)
-    e1.record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms_per_step = 1000.0 * wall / args.steps
-    step_gpu_us = 1000.0 * e0.elapsed_time(e1) / args.steps
 
-    _, (lists, counts, ccounts), inp, _, _ = steps[0]
+    def run_steps(k, chained):
+        """k steps in set order: whole chain replays, then single-step graphs."""
+        done = 0
+        if chained:
+            while k - done >= len(steps):
+                chain.replay()
+                done += len(steps)
+        while done < k:
+            steps[done % len(steps)][0].replay()
+            done += 1
+
+    def timed(k, chained):
+        run_steps(args.warmup, chained)
+        torch.cuda.synchronize()
+        # one event pair around the whole timed region (a pair per step would
+        # add its own records between the graph launches)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0 = time.perf_counter()
+        e0.record()
+        run_steps(k, chained)
+        e1.record()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        return 1000.0 * wall / k, 1000.0 * e0.elapsed_time(e1) / k
+
+    single_ms, _ = timed(args.steps, False)
+    ms_per_step, step_gpu_us = timed(args.steps, True)
+
+    _, (lists, counts, ccounts), inp, _, _, _ = steps[0]
     # the dominant kernel alone: decode calls back to back, inputs rotating
     dec_b2b_us = time_back_to_back([st[3] for st in steps], 4 * len(steps))
     nbytes, uniq = selected_bytes(wl, inp, lists, counts, ccounts)
@@ -326,6 +345,7 @@ def run_decode(args):
         "us_per_layer": round(1000.0 * ms_per_step, 2),
         "pct_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
         "step_gpu_us": round(step_gpu_us, 2),
+        "ms_per_step_single_step_graphs": round(single_ms, 5),
         "selected_bytes": nbytes,
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),

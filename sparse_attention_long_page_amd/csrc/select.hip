@@ -29,22 +29,32 @@ __device__ __forceinline__ uint32_t score_key(float x) {
 // round robin by consecutive radix passes (one barrier per pass; a pair
 // serves the two thresholds of a tiered list), and one per-wave partial-sum
 // array for each of the two workgroup scans.
-struct SelShared {
+struct alignas(16) SelShared {
   uint32_t hist[3][2][256];
   uint32_t wsum[2][kSelThreads / 64];
 };
+
+// Inclusive prefix sum over the 64 lanes of a wave from DPP lane moves:
+// row shifts by 1, 2, 4, 8 (zero past the row start) sum each 16-lane row,
+// then the last lane of row 0 is added into row 1 and of row 2 into row 3
+// (row_bcast:15), and the last lane of row 1 into rows 2 and 3
+// (row_bcast:31).  No LDS round trip.
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x) {
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x111, 0xf, 0xf, true);    // row_shr:1
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x112, 0xf, 0xf, true);    // row_shr:2
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x114, 0xf, 0xf, true);    // row_shr:4
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x118, 0xf, 0xf, true);    // row_shr:8
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x142, 0xa, 0xf, false);   // row_bcast:15
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x143, 0xc, 0xf, false);   // row_bcast:31
+  return x;
+}
 
 // Exclusive prefix sum over the workgroup in thread order.  `wsum` serves this
 // one call only, so a single barrier suffices.  *total gets the sum over all
 // threads.
 __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* total, uint32_t* wsum) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  uint32_t x = v;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const uint32_t y = __shfl_up(x, o, 64);
-    if (lane >= o) x += y;
-  }
+  const uint32_t x = wave_incl_scan(v);
   if (lane == 63) wsum[wave] = x;
   __syncthreads();
   uint32_t before = 0, all = 0;
@@ -61,36 +71,33 @@ __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* total,
 // One radix digit of a k-th-largest search, found by every wave from the
 // 256-bin histogram h of the keys that match the search's prefix: the bin
 // holding the kk-th largest of them (returned), and in *kk its rank within
-// that bin.  Lane l holds bins 4l .. 4l+3; higher bins hold larger keys.
+// that bin.  Lane l holds bins 255 - 4l - j, j = 0..3 (higher bins hold
+// larger keys), so a prefix sum over the lanes counts the keys in this lane's
+// bins and all higher ones.
 __device__ __forceinline__ uint32_t find_digit(const uint32_t* h, uint32_t* kk) {
   const int lane = threadIdx.x & 63;
-  uint32_t c[4];
+  const u32x4 w = *reinterpret_cast<const u32x4*>(h + 252 - 4 * lane);
+  const uint32_t c[4] = {w[3], w[2], w[1], w[0]};
+  const uint32_t mine = (c[0] + c[1]) + (c[2] + c[3]);
+  const uint32_t incl = wave_incl_scan(mine);
+  const uint32_t above = incl - mine;            // keys in higher lanes' bins
+  const uint32_t k = *kk;
+  const bool here = incl >= k && above < k;      // exactly one lane
+  uint32_t bin = 0, rest = 0, acc = above;
+  bool found = false;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) c[j] = h[4 * lane + j];
-  const uint32_t mine = c[0] + c[1] + c[2] + c[3];
-  uint32_t suf = mine;                           // sum over lanes >= this one
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const uint32_t y = __shfl_down(suf, o, 64);
-    if (lane + o < 64) suf += y;
-  }
-  const uint32_t above = suf - mine;             // keys in higher lanes' bins
-  const bool here = suf >= *kk && above < *kk;   // exactly one lane
-  uint32_t bin = 0, rest = 0;
-  if (here) {
-    uint32_t acc = above;
-    for (int j = 3; j >= 0; --j) {
-      if (acc + c[j] >= *kk) {
-        bin = 4u * lane + j;
-        rest = *kk - acc;
-        break;
-      }
-      acc += c[j];
+  for (int j = 0; j < 4; ++j) {
+    const bool hit = !found && acc + c[j] >= k;
+    if (hit) {
+      bin = 255u - 4u * lane - j;
+      rest = k - acc;
     }
+    found |= hit;
+    acc += c[j];
   }
   const int src = __builtin_ctzll(__ballot(here));
-  *kk = __shfl(rest, src, 64);
-  return __shfl(bin, src, 64);
+  *kk = (uint32_t)__builtin_amdgcn_readlane((int)rest, src);
+  return (uint32_t)__builtin_amdgcn_readlane((int)bin, src);
 }
 
 // Thresholds of the kA-th and (when kB > 0) the kB-th largest of the nonzero

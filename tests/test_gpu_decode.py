@@ -184,6 +184,98 @@ def test_select_long_lists_with_ties_exact(tiered):
             assert np.array_equal(g_lists[b, h, :n], o_lists[b, h, :n]), (b, h)
 
 
+# list lengths (pages) on both sides of each selection-kernel width: keys in
+# registers for 1, 2 or 4 pages per thread (up to 512, 1024, 2048 pages), an
+# LDS radix select beyond
+PATH_EDGES = [1, 9, 64, 65, 511, 512, 513, 1024, 1025, 2047, 2048, 2049, 2600]
+
+
+@pytest.mark.parametrize("top_k,crit", [(41, None), (41, 8), (700, None), (700, 300), (0, None)])
+def test_select_list_sizes_across_paths_exact(top_k, crit):
+    """Given scores, every list length around the kernel's width switches must
+    give the oracle's lists exactly.  Head 0 draws from a few tied values (two
+    adjacent floats, NaN, both zeros), head 1 from a normal distribution."""
+    P, H = 16, 2
+    lens = np.array([P * n - (n % 5) for n in PATH_EDGES], dtype=np.int32)
+    B, max_pages = len(lens), max(PATH_EDGES)
+    rng = np.random.default_rng(91)
+    vals = np.array([-1.5, -0.0, 0.0, 0.25, np.nextafter(np.float32(0.25), np.float32(1)), 2.0, np.nan],
+                    dtype=np.float32)
+    scores = np.empty((B, H, max_pages), dtype=np.float32)
+    scores[:, 0] = vals[rng.integers(0, len(vals), size=(B, max_pages))]
+    scores[:, 1] = rng.standard_normal((B, max_pages)).astype(np.float32)
+    sink, window = 1, 8
+    kv = S.PagedKV(torch.zeros((4, 1, P, 64), dtype=torch.bfloat16, device=DEV),
+                   torch.zeros((4, 1, 64, P), dtype=torch.bfloat16, device=DEV),
+                   torch.zeros((B, max_pages), dtype=torch.int32, device=DEV), torch.from_numpy(lens).to(DEV))
+    lists, counts, cc = S.sa_select_pages(kv, n_q_heads=H, mode=S.SA_SEL_PER_Q_HEAD, sink_pages=sink,
+                                          window_pages=window, top_k=top_k,
+                                          scores=torch.from_numpy(scores).to(DEV), critical_k=crit)
+    torch.cuda.synchronize()
+    npg = [O.n_pages_of(int(L), P) for L in lens]
+    assert npg == PATH_EDGES
+    o_lists, o_counts, o_cc = O.select_pages(scores, npg, sink, window, top_k, crit)
+    g_lists, g_counts = npi(lists), npi(counts)
+    assert np.array_equal(g_counts, o_counts)
+    if crit is not None:
+        assert np.array_equal(npi(cc), o_cc)
+    for b in range(B):
+        for h in range(H):
+            n = int(o_counts[b, h])
+            assert np.array_equal(g_lists[b, h, :n], o_lists[b, h, :n]), (npg[b], h)
+
+
+@pytest.mark.parametrize("crit", [None, 8])
+def test_fused_score_select_long_lists(crit):
+    """Scoring fused with selection (128 lists, d 128) on lists of up to 2600
+    pages, covering each selection width.  The page summaries are given
+    (random fp32 rows), so the oracle needs no key pool.  Lists follow the
+    tie-band rule against the oracle's scores; the scores written out agree
+    to 1e-6 relative."""
+    P, Hkv, G, d = 16, 8, 4, 128
+    npg = PATH_EDGES[2:] + [40] * 5
+    B, max_pages = len(npg), max(npg)
+    lens = np.array([P * n - 3 for n in npg], dtype=np.int32)
+    n_phys = sum(npg) + 7
+    rng = np.random.default_rng(17)
+    bt = np.zeros((B, max_pages), dtype=np.int32)
+    perm = rng.permutation(n_phys).astype(np.int32)
+    off = 0
+    for b, n in enumerate(npg):
+        bt[b, :n] = perm[off:off + n]
+        off += n
+    mu = rng.standard_normal((n_phys, Hkv, d)).astype(np.float32)
+    q = torch.from_numpy(rng.standard_normal((B, 1, Hkv * G, d)).astype(np.float32)).to(torch.bfloat16)
+    kv = S.PagedKV(torch.empty((n_phys, Hkv, P, d), dtype=torch.bfloat16, device=DEV),
+                   torch.empty((n_phys, Hkv, d, P), dtype=torch.bfloat16, device=DEV),
+                   torch.from_numpy(bt).to(DEV), torch.from_numpy(lens).to(DEV))
+    sink, window, top_k = 1, 8, 41
+    scores_out = torch.empty((B, Hkv, max_pages), dtype=torch.float32, device=DEV)
+    lists, counts, cc = S.sa_select_pages(kv, n_q_heads=Hkv * G, mode=S.SA_SEL_PER_KV_HEAD, sink_pages=sink,
+                                          window_pages=window, top_k=top_k, q=q.to(DEV),
+                                          page_summary=torch.from_numpy(mu).to(DEV), critical_k=crit,
+                                          scores_out=scores_out)
+    # the same selection without scores written out (the forced pages' rows are then not read)
+    l2, c2, cc2 = S.sa_select_pages(kv, n_q_heads=Hkv * G, mode=S.SA_SEL_PER_KV_HEAD, sink_pages=sink,
+                                    window_pages=window, top_k=top_k, q=q.to(DEV),
+                                    page_summary=torch.from_numpy(mu).to(DEV), critical_k=crit)
+    torch.cuda.synchronize()
+    o_scores = O.page_scores(q.float().numpy().astype(np.float64), mu, bt, lens, P, Hkv, "per_kv_head")
+    g = scores_out.cpu().numpy()
+    assert np.array_equal(np.isnan(g), np.isnan(o_scores))
+    fin = ~np.isnan(g)
+    rel = np.abs(g[fin].astype(np.float64) - o_scores[fin]) / np.maximum(1.0, np.abs(o_scores[fin]))
+    assert rel.max() <= 1e-6, rel.max()
+    rep = check_page_lists(npi(lists), npi(counts), None if cc is None else npi(cc), o_scores, npg,
+                           sink, window, top_k, crit)
+    assert not rep.failures, rep.failures[:5]
+    assert rep.exact + rep.band_events == rep.units
+    assert torch.equal(c2, counts)
+    C, L1, L2 = npi(counts), npi(lists), npi(l2)
+    for idx in np.ndindex(*C.shape):
+        assert np.array_equal(L1[idx][:C[idx]], L2[idx][:C[idx]]), idx
+
+
 @pytest.mark.parametrize("name", DECODE_SMALL)
 @pytest.mark.parametrize("splits", [1, 2, 3, 0])
 def test_decode_matches_oracle(name, splits):
