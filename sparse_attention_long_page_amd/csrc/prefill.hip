@@ -143,6 +143,9 @@ __device__ __forceinline__ int ptok(int j4, int m) {
 // dim d.  With these, both the K and the V^T reads are free of conflicts.
 __device__ __forceinline__ int vsw(int d) { return 4 * (((d >> 2) ^ (d >> 3)) & 1); }
 
+// a value every lane of the wave holds, moved to a scalar register
+__device__ __forceinline__ int wave_uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
+
 template <int V>
 struct Stage {
   static constexpr int value = V;
@@ -217,28 +220,37 @@ __global__ __launch_bounds__(128 * HW) void prefill_kernel(PrefillParams p) {
   }
 
   // LDS-DMA copy of table entry t into a stage: wave-wide load i covers stage
-  // chunks [64 i, 64 i + 64).  K slots copy straight; V^T slot c of row d
-  // receives token-chunk c ^ vsw(d) (an involution); pad slots re-read chunk 0
-  // of their row.  Every wave issues exactly NI loads (the
-  // last real load is repeated to fill), so the wait below can count them.
+  // chunks [64 i, 64 i + 64); loads 0-16 hold the K tile, 17-34 the V^T tile.
+  // K slots copy straight; V^T slot c of row d receives token-chunk
+  // c ^ vsw(d) (an involution); pad slots re-read chunk 0 of their row.  Every
+  // wave issues exactly NI loads (the last real load is repeated to fill), so
+  // the wait below can count them.  Each lane's element offset within the
+  // (page, head) tile is fixed per load and computed once; per block only the
+  // tile's base address (scalar) changes.
+  static_assert(kKChunks % 64 == 0, "loads hold K or V^T chunks only");
+  constexpr int kKInstr = kKChunks / 64;
+  int lane_off[NI];
+#pragma unroll
+  for (int j = 0; j < NI; ++j) {
+    const int i = min(wave + NW * j, kStageInstr - 1);
+    const int c = 64 * i + lane;
+    if (c < kKChunks) {
+      const int r = c / (kKRow / 8), slot = c % (kKRow / 8);
+      lane_off[j] = r * kPD + 8 * (slot < 16 ? slot : 0);
+    } else {
+      const int cv = c - kKChunks;
+      const int r = cv / (kVRow / 8), slot = cv % (kVRow / 8);
+      lane_off[j] = r * kPP + 8 * (slot < 8 ? (slot ^ vsw(r)) : 0);
+    }
+  }
   auto stage_copy = [&](uint16_t* st, int t) {
-    const int kb = kb_s[t];
-    const int phys = ph_s[t];
-    const uint16_t* kb_base = kpool + ((size_t)phys * p.Hkv + g) * kPP * kPD;
-    const uint16_t* vb_base = vpool + ((size_t)phys * p.Hkv + g) * kPD * kPP;
+    const int phys = wave_uniform(ph_s[t]);
+    const size_t tile = ((size_t)phys * p.Hkv + g) * kPP * kPD;     // same size for K and V^T tiles
 #pragma unroll
     for (int j = 0; j < NI; ++j) {
       const int i = min(wave + NW * j, kStageInstr - 1);
-      const int c = 64 * i + lane;
-      const uint16_t* src;
-      if (c < kKChunks) {
-        const int r = c / (kKRow / 8), slot = c % (kKRow / 8);
-        src = kb_base + r * kPD + 8 * (slot < 16 ? slot : 0);
-      } else {
-        const int cv = c - kKChunks;
-        const int r = cv / (kVRow / 8), slot = cv % (kVRow / 8);
-        src = vb_base + r * kPP + 8 * (slot < 8 ? (slot ^ vsw(r)) : 0);
-      }
+      const uint16_t* base = (i < kKInstr ? kpool : vpool) + tile;
+      const uint16_t* src = base + lane_off[j];
       __builtin_amdgcn_global_load_lds(src, st + i * 512, 16, 0, 0);
     }
   };
@@ -267,12 +279,13 @@ __global__ __launch_bounds__(128 * HW) void prefill_kernel(PrefillParams p) {
       for (int j4 = 0; j4 < 4; ++j4)
 #pragma unroll
         for (int rt = 0; rt < kRT; ++rt) sacc[j4][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      // k-steps outer: the eight accumulators of a k-step are independent,
+      // so an MFMA never waits on the one just issued
 #pragma unroll
-      for (int j4 = 0; j4 < 4; ++j4) {
-        const int tau = ptok(j4, col);
+      for (int kk = 0; kk < 4; ++kk) {
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
-          const bf16x8 a = *reinterpret_cast<const bf16x8*>(K + tau * kKRow + 8 * (kk + 4 * kg));
+        for (int j4 = 0; j4 < 4; ++j4) {
+          const bf16x8 a = *reinterpret_cast<const bf16x8*>(K + ptok(j4, col) * kKRow + 8 * (kk + 4 * kg));
 #pragma unroll
           for (int rt = 0; rt < kRT; ++rt)
             sacc[j4][rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qreg[rt][kk], sacc[j4][rt], 0, 0, 0);

@@ -171,3 +171,19 @@ def test_workspace_sizes():
     expect = ((rows * 4 * 128 * 4 + 255) // 256) * 256 + ((rows * 4 * 4 + 255) // 256) * 256
     assert lib.sa_sparse_decode_workspace_size(ctypes.byref(k), 2, 1, 8, 7, 0, 4) == expect
     assert lib.sa_sparse_decode_workspace_size(ctypes.byref(k), 2, 1, 8, 7, 0, 1) == 0
+
+
+def test_library_has_no_undefined_kernel_symbols():
+    """Every kernel launch stub and helper of the library is defined in it: a
+    kernel template whose host-side instantiation failed leaves its launch stub
+    undefined, which only shows when the library is loaded with lazy binding
+    off or the launch runs."""
+    import shutil
+    import subprocess
+    nm = shutil.which("nm")
+    if nm is None:
+        pytest.skip("nm not available")
+    lib = S.load_library()
+    out = subprocess.run([nm, "-D", "--undefined-only", lib._name], capture_output=True, text=True, check=True).stdout
+    missing = [line.split()[-1] for line in out.splitlines() if line.split() and line.split()[-1].startswith("_ZN2sa")]
+    assert not missing, missing
