@@ -163,8 +163,9 @@ sa_status sa_page_summary(const sa_paged_kv* kv, int32_t batch, int32_t last_pag
 size_t sa_select_pages_workspace_size(int32_t batch, int32_t n_sel, int32_t max_pages) {
   if (batch <= 0 || n_sel <= 0 || max_pages <= 0) return 0;
   // router scores + float64 pooled-query partials (8 row chunks, d_qk <= 576)
+  // + one arrival counter per list
   return align_up((size_t)batch * n_sel * max_pages * sizeof(float)) +
-         align_up((size_t)batch * n_sel * 8 * 576 * sizeof(double));
+         align_up((size_t)batch * n_sel * 8 * 576 * sizeof(double)) + align_up((size_t)batch * n_sel * sizeof(uint32_t));
 }
 
 sa_status sa_select_pages(const sa_paged_kv* kv, int32_t batch, const void* q, int32_t q_tokens,
@@ -218,10 +219,8 @@ sa_status sa_select_pages(const sa_paged_kv* kv, int32_t batch, const void* q, i
   sp.critical_k = critical_k;
   sp.tiered = critical_counts != nullptr;
 
-  const float* sc = scores;
-  int stride = scores_stride;
   const int pooled_rows = mode == SA_SEL_PER_KV_HEAD ? q_tokens * (n_q_heads / kv->n_kv_heads) : q_tokens;
-  if (!scores && batch * n_sel >= 128 && pooled_rows <= 32) {
+  if (!scores && batch * n_sel >= 128 && pooled_rows <= sa::kScoreInlineRows) {
     // enough lists to fill the GPU: score and select in one workgroup per list
     sa::ScoreParams p{};
     p.q = q;
@@ -245,24 +244,15 @@ sa_status sa_select_pages(const sa_paged_kv* kv, int32_t batch, const void* q, i
     return device_status(sa::launch_score_select(p, sp, batch, kv->dtype == SA_DTYPE_BF16, stream),
                          "score_select launch");
   }
-  if (refresh_newest_page) {
-    sa::SummaryParams smp{};
-    smp.k_pool = kv->k_pool;
-    smp.block_table = kv->block_table;
-    smp.seq_lens = kv->seq_lens;
-    smp.mu = page_summary;
-    smp.n_kv = kv->n_kv_heads;
-    smp.P = kv->page_size;
-    smp.d = kv->d_qk;
-    smp.max_pages = kv->max_pages;
-    smp.last_pages = 1;
-    hipError_t e = sa::launch_page_summary(smp, batch, kv->dtype == SA_DTYPE_BF16, stream);
-    if (e != hipSuccess) return device_status(e, "page_summary launch");
-  }
   if (!scores) {
+    // too few lists for one workgroup each: a prep kernel (pooled query,
+    // newest-page summaries, arrival counters), then scoring over blocks of
+    // pages whose last workgroup per list selects
     float* buf = scores_out ? scores_out : reinterpret_cast<float*>(workspace);
-    double* qbar = reinterpret_cast<double*>(reinterpret_cast<char*>(workspace) +
-                                             align_up((size_t)batch * n_sel * kv->max_pages * sizeof(float)));
+    char* ws = reinterpret_cast<char*>(workspace);
+    const size_t sc_bytes = align_up((size_t)batch * n_sel * kv->max_pages * sizeof(float));
+    double* qbar = reinterpret_cast<double*>(ws + sc_bytes);
+    uint32_t* arrivals = reinterpret_cast<uint32_t*>(ws + sc_bytes + align_up((size_t)batch * n_sel * 8 * 576 * sizeof(double)));
     sa::ScoreParams p{};
     p.q = q;
     p.mu = page_summary;
@@ -282,13 +272,25 @@ sa_status sa_select_pages(const sa_paged_kv* kv, int32_t batch, const void* q, i
     p.P = kv->page_size;
     p.max_pages = kv->max_pages;
     p.per_q = mode == SA_SEL_PER_Q_HEAD;
-    hipError_t e = sa::launch_page_scores_ws(p, kv->dtype == SA_DTYPE_BF16, qbar, stream);
-    if (e != hipSuccess) return device_status(e, "page_scores launch");
-    sc = buf;
-    stride = kv->max_pages;
+    sa::SummaryParams smp{};
+    smp.k_pool = kv->k_pool;
+    smp.block_table = kv->block_table;
+    smp.seq_lens = kv->seq_lens;
+    smp.mu = page_summary;
+    smp.n_kv = kv->n_kv_heads;
+    smp.P = kv->page_size;
+    smp.d = kv->d_qk;
+    smp.max_pages = kv->max_pages;
+    smp.last_pages = 1;
+    const bool bf16 = kv->dtype == SA_DTYPE_BF16;
+    hipError_t e = sa::launch_select_prep(smp, p, bf16, refresh_newest_page != 0, qbar, arrivals, stream);
+    if (e != hipSuccess) return device_status(e, "select prep launch");
+    const bool pooled = pooled_rows > sa::kScoreInlineRows;
+    return device_status(sa::launch_score_lastsel(p, sp, bf16, pooled ? qbar : nullptr, arrivals, stream),
+                         "score/select launch");
   }
-  sp.scores = sc;
-  sp.scores_stride = stride;
+  sp.scores = scores;
+  sp.scores_stride = scores_stride;
   return device_status(sa::launch_select(sp, batch, kv->max_pages, stream), "select launch");
 }
 

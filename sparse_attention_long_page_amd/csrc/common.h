@@ -69,6 +69,12 @@ __device__ __forceinline__ int page_valid(int len, int lp, int P) {
 }
 
 // ---------------------------------------------------------------- launch params
+// Pooled queries of more than kScoreInlineRows rows are summed by a kernel of
+// their own in kQChunks row chunks (float64 partials) before scoring; fewer
+// rows are summed inside the scoring kernel.
+constexpr int kQChunks = 8;
+constexpr int kScoreInlineRows = 32;
+
 struct SummaryParams {
   const void* k_pool;
   const int32_t* block_table;
@@ -154,9 +160,12 @@ struct PrefillParams {
 
 // ------------------------------------------------------------- launchers
 hipError_t launch_page_summary(const SummaryParams& p, int batch, int bf16, hipStream_t s);
-hipError_t launch_page_scores_ws(const ScoreParams& p, int bf16, double* qbar_ws, hipStream_t s);
 hipError_t launch_select(const SelectParams& p, int batch, int max_pages, hipStream_t s);
 hipError_t launch_score_select(const ScoreParams& sp, const SelectParams& p, int batch, int bf16, hipStream_t s);
+hipError_t launch_select_prep(const SummaryParams& smp, const ScoreParams& sp, int bf16, bool refresh, double* qpart,
+                              uint32_t* arrivals, hipStream_t s);
+hipError_t launch_score_lastsel(const ScoreParams& sp, const SelectParams& p, int bf16, const double* qpart,
+                                uint32_t* arrivals, hipStream_t s);
 hipError_t launch_decode(const DecodeParams& p, int bf16, hipStream_t s);
 hipError_t launch_merge(const MergeParams& p, hipStream_t s);
 hipError_t launch_mla_decode(const DecodeParams& p, hipStream_t s);

@@ -396,6 +396,133 @@ __global__ __launch_bounds__(kSelThreads) void score_select_kernel(ScoreParams s
   select_from_keys(p, L, b, s, keys, sh);
 }
 
+// Router scores and selection of long lists on few selection heads (too few
+// lists to fill the GPU with one workgroup each): grid (block of 64 pages,
+// selection head, sequence), 512 threads.  Each workgroup scores its pages
+// with the arithmetic of the fused kernel (lane `sub` of a page's 16 takes
+// dims 64 i + 4 sub + 0..3, float64 products summed in that order, then over
+// the 16 lanes in a fixed butterfly, rounded once to fp32) into the list's
+// score row; the last workgroup of the list to finish, counted on the list's
+// arrival counter (cleared by the prep kernel), selects from the whole row.
+// A forced page's mean row is read only when the caller asked for the scores.
+template <typename T, int D>
+__global__ __launch_bounds__(kSelThreads) void score_lastsel_kernel(ScoreParams sp, SelectParams p,
+                                                                    const double* qpart, uint32_t* arrivals) {
+  constexpr int kWaves = kSelThreads / 64;
+  constexpr int kSteps = 2;                          // 4-page steps per wave
+  constexpr int kPages = 4 * kSteps * kWaves;
+  constexpr int PL = D / 16;
+  extern __shared__ uint32_t keys[];
+  __shared__ SelShared sh;
+  __shared__ double qbar[D];
+  __shared__ int phys_s[kPages];
+  __shared__ int last_s;
+  const int s = blockIdx.y, b = blockIdx.z;
+  const ListShape L = list_shape(p, b);
+  const int n = L.n;
+  const int page0 = blockIdx.x * kPages;
+  const int g = sp.per_q ? s / sp.G : s;
+  if (threadIdx.x < kPages) {
+    const int lp = page0 + threadIdx.x;
+    const bool forced = lp < L.sink_hi || lp >= L.win_lo;
+    phys_s[threadIdx.x] = (lp < n && !(sp.skip_forced && forced)) ? sp.block_table[(size_t)b * sp.max_pages + lp] : -1;
+  }
+  // pooled query: the row-chunk partials in chunk order, or the rows in order
+  if (qpart) {
+    const double* qp = qpart + ((size_t)b * sp.n_sel + s) * kQChunks * D;
+    for (int e = threadIdx.x; e < D; e += kSelThreads) {
+      double v = 0.0;
+#pragma unroll
+      for (int c = 0; c < kQChunks; ++c) v += qp[(size_t)c * D + e];
+      qbar[e] = v;
+    }
+  } else {
+    const T* q = reinterpret_cast<const T*>(sp.q);
+    const int rows = sp.per_q ? sp.T : sp.T * sp.G;
+    for (int e = threadIdx.x; e < D; e += kSelThreads) {
+      double v = 0.0;
+      for (int r = 0; r < rows; ++r) {
+        int t, h;
+        if (sp.per_q) { t = r; h = s; } else { t = r / sp.G; h = s * sp.G + r % sp.G; }
+        const size_t i = (((size_t)b * sp.T + t) * sp.Hq + h) * D + e;
+        if constexpr (sizeof(T) == 2) v += (double)bf16_bits_to_f32(q[i]);
+        else v += (double)q[i];
+      }
+      qbar[e] = v;
+    }
+  }
+  __syncthreads();
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int sub = lane & 15, slot = lane >> 4;
+  f32x4 v[kSteps][PL / 4];
+#pragma unroll
+  for (int it = 0; it < kSteps; ++it) {
+    const int ph = phys_s[wave * 4 * kSteps + it * 4 + slot];
+    const float* m = sp.mu + ((size_t)max(ph, 0) * sp.Hkv + g) * D + 4 * sub;
+#pragma unroll
+    for (int i = 0; i < PL / 4; ++i) v[it][i] = ph >= 0 ? *reinterpret_cast<const f32x4*>(m + 64 * i) : f32x4{};
+  }
+  float* out = sp.scores + ((size_t)b * sp.n_sel + s) * sp.max_pages;
+#pragma unroll
+  for (int it = 0; it < kSteps; ++it) {
+    const int lp = page0 + wave * 4 * kSteps + it * 4 + slot;
+    const double* qq = qbar + 4 * sub;
+    double acc = 0.0;
+#pragma unroll
+    for (int i = 0; i < PL / 4; ++i) {
+      acc += qq[64 * i] * (double)v[it][i][0];
+      acc += qq[64 * i + 1] * (double)v[it][i][1];
+      acc += qq[64 * i + 2] * (double)v[it][i][2];
+      acc += qq[64 * i + 3] * (double)v[it][i][3];
+    }
+#pragma unroll
+    for (int o = 8; o > 0; o >>= 1) acc += __shfl_xor(acc, o, 64);
+    // (device-coherent stores: the list's last workgroup, possibly on
+    // another XCD, reads them back)
+    if (sub == 0 && lp < sp.max_pages)
+      __hip_atomic_store(&out[lp], lp < n ? (float)acc : __builtin_nanf(""), __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
+  }
+  // The list's last workgroup selects.  Every workgroup's score stores are
+  // acknowledged (written at the device's coherence point) before it counts
+  // itself on the list's counter; the one that counts last reads all the
+  // scores back with device-coherent loads.  (A device-scope fence would
+  // write back and invalidate the whole L2 of the XCD instead.)
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  if (threadIdx.x == 0)
+    last_s = __hip_atomic_fetch_add(&arrivals[(size_t)b * sp.n_sel + s], 1u, __ATOMIC_RELAXED,
+                                    __HIP_MEMORY_SCOPE_AGENT) == gridDim.x - 1;
+  __syncthreads();
+  if (!last_s) return;
+  for (int i = threadIdx.x; i < 512; i += kSelThreads) sh.hist[0][0][i] = 0u;
+  for (int i = threadIdx.x; i < n; i += kSelThreads) {
+    const bool forced = i < L.sink_hi || i >= L.win_lo;
+    keys[i] = forced ? 0u : score_key(__hip_atomic_load(&out[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+  }
+  __syncthreads();
+  select_from_keys(p, L, b, s, keys, sh);
+}
+
+hipError_t launch_score_lastsel(const ScoreParams& sp, const SelectParams& p, int bf16, const double* qpart,
+                                uint32_t* arrivals, hipStream_t s) {
+  constexpr int kPages = 8 * (kSelThreads / 64);
+  dim3 grid((sp.max_pages + kPages - 1) / kPages, p.n_sel, sp.B);
+  const size_t lds = (size_t)sp.max_pages * sizeof(uint32_t);
+#define SA_LS_LAUNCH(T_, D_) \
+  hipLaunchKernelGGL((score_lastsel_kernel<T_, D_>), grid, dim3(kSelThreads), lds, s, sp, p, qpart, arrivals)
+  if (bf16) {
+    if (sp.d == 64) SA_LS_LAUNCH(uint16_t, 64);
+    else if (sp.d == 128) SA_LS_LAUNCH(uint16_t, 128);
+    else SA_LS_LAUNCH(uint16_t, 576);
+  } else {
+    if (sp.d == 64) SA_LS_LAUNCH(float, 64);
+    else SA_LS_LAUNCH(float, 128);
+  }
+#undef SA_LS_LAUNCH
+  return hipGetLastError();
+}
+
 hipError_t launch_select(const SelectParams& p, int batch, int max_pages, hipStream_t s) {
   dim3 grid(p.n_sel, batch);
   hipLaunchKernelGGL(select_kernel, grid, dim3(kSelThreads), (size_t)max_pages * sizeof(uint32_t), s, p);

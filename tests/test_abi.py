@@ -163,8 +163,9 @@ def test_prefill_rejects(name, kvo, argo, status):
 
 def test_workspace_sizes():
     lib = S.load_library()
-    # select: fp32 scores [B][n_sel][max_pages] + fp64 pooled queries, 256-aligned pieces
-    assert lib.sa_select_pages_workspace_size(2, 3, 100) == 2560 + 2 * 3 * 8 * 576 * 8
+    # select: fp32 scores [B][n_sel][max_pages] + fp64 pooled queries + one arrival
+    # counter per list, 256-aligned pieces
+    assert lib.sa_select_pages_workspace_size(2, 3, 100) == 2560 + 2 * 3 * 8 * 576 * 8 + 256
     k = kv()
     # decode with an explicit split count: fp32 partials o [rows][splits][d_v] + lse [rows][splits]
     rows = 2 * 1 * 8

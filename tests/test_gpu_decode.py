@@ -225,14 +225,23 @@ def test_select_list_sizes_across_paths_exact(top_k, crit):
             assert np.array_equal(g_lists[b, h, :n], o_lists[b, h, :n]), (npg[b], h)
 
 
+# (KV heads, group size, query tokens): 128 lists scored and selected one
+# workgroup each; 16 lists scored over blocks of pages whose last workgroup
+# selects, with the pooled query summed inline (4 rows) or by the prep kernel
+# in row chunks (64 rows)
+LONG_LIST_SHAPES = [(8, 4, 1), (1, 4, 1), (1, 32, 2)]
+
+
 @pytest.mark.parametrize("crit", [None, 8])
-def test_fused_score_select_long_lists(crit):
-    """Scoring fused with selection (128 lists, d 128) on lists of up to 2600
-    pages, covering each selection width.  The page summaries are given
-    (random fp32 rows), so the oracle needs no key pool.  Lists follow the
-    tie-band rule against the oracle's scores; the scores written out agree
-    to 1e-6 relative."""
-    P, Hkv, G, d = 16, 8, 4, 128
+@pytest.mark.parametrize("shape", LONG_LIST_SHAPES, ids=["128_lists", "16_lists", "16_lists_pooled"])
+def test_score_select_long_lists(crit, shape):
+    """Router scores and selection on lists of up to 2600 pages, covering each
+    selection width.  The page summaries are given (random fp32 rows), so the
+    oracle needs no key pool.  Lists follow the tie-band rule against the
+    oracle's scores; the scores written out agree to 1e-6 relative, and the
+    same call without scores written out gives the same lists."""
+    Hkv, G, T = shape
+    P, d = 16, 128
     npg = PATH_EDGES[2:] + [40] * 5
     B, max_pages = len(npg), max(npg)
     lens = np.array([P * n - 3 for n in npg], dtype=np.int32)
@@ -245,7 +254,7 @@ def test_fused_score_select_long_lists(crit):
         bt[b, :n] = perm[off:off + n]
         off += n
     mu = rng.standard_normal((n_phys, Hkv, d)).astype(np.float32)
-    q = torch.from_numpy(rng.standard_normal((B, 1, Hkv * G, d)).astype(np.float32)).to(torch.bfloat16)
+    q = torch.from_numpy(rng.standard_normal((B, T, Hkv * G, d)).astype(np.float32)).to(torch.bfloat16)
     kv = S.PagedKV(torch.empty((n_phys, Hkv, P, d), dtype=torch.bfloat16, device=DEV),
                    torch.empty((n_phys, Hkv, d, P), dtype=torch.bfloat16, device=DEV),
                    torch.from_numpy(bt).to(DEV), torch.from_numpy(lens).to(DEV))
