@@ -297,24 +297,34 @@ __global__ __launch_bounds__(128 * HW) void prefill_kernel(PrefillParams p) {
       // then p = 2^(s * scale_log2 - m) is one FMA and one v_exp_f32
       // (results below 2^-126 flush to zero: their weight relative to the
       // row maximum is below 2^-126).
+      // causal and sequence-end masks, only on blocks that cross a row (the
+      // empty volatile asm keeps this a branch: if-converted, the masking
+      // would run as per-element compares and selects on every block)
       const bool full = (tok0 + kPP - 1 <= wpos_lo) && (tok0 + kPP <= seq_len);
+      if (!full) {
+        asm volatile("" ::: "memory");
+#pragma unroll
+        for (int rt = 0; rt < kRT; ++rt) {
+          const int row_pos = wpos_lo + 16 * rt + col;
+#pragma unroll
+          for (int j4 = 0; j4 < 4; ++j4)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const int j = tok0 + ptok(j4, 4 * kg + i);
+              if (j > row_pos || j >= seq_len) sacc[j4][rt][i] = -INFINITY;
+            }
+        }
+      }
       bf16x8 pb[kRT][2];
       float alpha[kRT];
       bool need_rescale = false;
 #pragma unroll
       for (int rt = 0; rt < kRT; ++rt) {
-        const int row_pos = wpos_lo + 16 * rt + col;
         float mraw = -INFINITY;
 #pragma unroll
         for (int j4 = 0; j4 < 4; ++j4)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            if (!full) {
-              const int j = tok0 + ptok(j4, 4 * kg + i);
-              if (j > row_pos || j >= seq_len) sacc[j4][rt][i] = -INFINITY;
-            }
-            mraw = fmaxf(mraw, sacc[j4][rt][i]);
-          }
+          for (int i = 0; i < 4; ++i) mraw = fmaxf(mraw, sacc[j4][rt][i]);
         mraw = max_over_row_groups(mraw);
         const float mloc = mraw == -INFINITY ? -INFINITY : mraw * p.scale_log2;
         // move the reference only when the row maximum outgrows it
