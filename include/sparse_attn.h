@@ -203,6 +203,35 @@ sa_status sa_sparse_decode(const sa_paged_kv* kv, int32_t batch,
                            void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* ------------------------------------------------------------------------
+ * sa_select_decode -- the decode step's two calls in one launch: page
+ * selection with router scores ([UAE] "The Product", "Content-Dependent
+ * Dynamic Routing") and sparse decode over the selected pages ([UAE] "Key
+ * Design Decisions" 3), for per-KV-head, untiered lists.
+ *
+ * Writes exactly what these two calls write, bit for bit:
+ *   sa_select_pages(kv, batch, q, q_tokens, n_q_heads, page_summary,
+ *                   refresh_newest_page, NULL, 0, SA_SEL_PER_KV_HEAD,
+ *                   sink_pages, window_pages, top_k, 0, page_lists,
+ *                   list_stride, page_counts, NULL, NULL, ...)
+ *   sa_sparse_decode(kv, batch, q, q_tokens, n_q_heads, page_lists,
+ *                    page_counts, list_stride, SA_SEL_PER_KV_HEAD, NULL, NULL,
+ *                    sm_scale, 1, out, out_lse, ...)
+ * One workgroup per (sequence, KV head) selects its list and decodes it
+ * without waiting for the other lists' selections; no workspace is needed.
+ * Arguments are those of the two calls.  Supported: bf16, a V pool, d_qk ==
+ * d_v == 128, page_size 64, q_tokens * group <= 16, and max_pages +
+ * list_stride small enough for the keys and the list to sit in LDS (about
+ * 2,000 entries); anything else returns SA_ERR_UNSUPPORTED (use the two
+ * calls).  Validation and errors as for the two calls.
+ * ---------------------------------------------------------------------- */
+sa_status sa_select_decode(const sa_paged_kv* kv, int32_t batch,
+                           const void* q, int32_t q_tokens, int32_t n_q_heads,
+                           float* page_summary, int32_t refresh_newest_page,
+                           int32_t sink_pages, int32_t window_pages, int32_t top_k,
+                           int32_t* page_lists, int32_t list_stride, int32_t* page_counts,
+                           float sm_scale, void* out, float* out_lse, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
  * sa_block_sparse_prefill -- chunked-prefill attention with a 2D block mask
  * turned into GQA-union KV block tables ([CA]; [UAE] block-sparse prefill).
  *

@@ -5,7 +5,7 @@ include/sparse_attn.h); ``binding`` marshals torch tensors into its calls.
 """
 from .binding import (PagedKV, SparseAttnError, load_library, library_path, sa_page_summary,
                       sa_select_pages, sa_select_pages_workspace_size, sa_sparse_decode,
-                      sa_sparse_decode_workspace_size, sa_block_sparse_prefill,
+                      sa_sparse_decode_workspace_size, sa_select_decode, sa_block_sparse_prefill,
                       sa_block_sparse_prefill_workspace_size, sa_version, SA_SEL_PER_KV_HEAD,
                       SA_SEL_PER_Q_HEAD, SA_DTYPE_BF16, SA_DTYPE_FP32, SA_OK, SA_ERR_INVALID_ARGUMENT,
                       SA_ERR_UNSUPPORTED, SA_ERR_WORKSPACE_TOO_SMALL, SA_ERR_DEVICE, EXPORTED)

@@ -29,7 +29,7 @@ SA_SEL_PER_Q_HEAD = 1
 
 EXPORTED = [
     "sa_page_summary", "sa_select_pages_workspace_size", "sa_select_pages",
-    "sa_sparse_decode_workspace_size", "sa_sparse_decode",
+    "sa_sparse_decode_workspace_size", "sa_sparse_decode", "sa_select_decode",
     "sa_block_sparse_prefill_workspace_size", "sa_block_sparse_prefill",
     "sa_status_string", "sa_last_error_message", "sa_version",
 ]
@@ -73,6 +73,8 @@ def load_library(build_if_missing: bool = True) -> ctypes.CDLL:
         "sa_sparse_decode_workspace_size": (c_size_t, [P, c_int32, c_int32, c_int32, c_int32, c_int, c_int32]),
         "sa_sparse_decode": (c_int, [P, c_int32, P, c_int32, c_int32, P, P, c_int32, c_int, P, P, c_float,
                                      c_int32, P, P, P, c_size_t, P]),
+        "sa_select_decode": (c_int, [P, c_int32, P, c_int32, c_int32, P, c_int32, c_int32, c_int32, c_int32, P,
+                                     c_int32, P, c_float, P, P, P]),
         "sa_block_sparse_prefill_workspace_size": (c_size_t, [P, c_int32, c_int32, c_int32]),
         "sa_block_sparse_prefill": (c_int, [P, c_int32, P, c_int32, c_int32, c_int32, P, c_int32, c_int32, P, P,
                                             c_float, P, P, P, c_size_t, P]),
@@ -216,6 +218,27 @@ def sa_sparse_decode(kv: PagedKV, q: torch.Tensor, page_lists: torch.Tensor, pag
         _ptr(critical_counts), _ptr(ambient_head_mask), float(sm_scale), num_splits, _ptr(out), _ptr(out_lse),
         _ptr(workspace), workspace.numel(), _stream(kv.device)))
     return out, out_lse
+
+
+def sa_select_decode(kv: PagedKV, q: torch.Tensor, page_summary: torch.Tensor, *, sink_pages: int,
+                     window_pages: int, top_k: int, sm_scale: float, refresh_newest_page: bool = False,
+                     list_stride: Optional[int] = None, out=None, want_lse: bool = True):
+    """Selection and decode of per-KV-head lists in one call.  Returns (page_lists
+    [B][Hkv][list_stride] int32, page_counts [B][Hkv], out [B][T][Hq][d_v], lse or None)."""
+    B, T, Hq, _ = q.shape
+    if list_stride is None:
+        list_stride = max(1, min(kv.max_pages, sink_pages + window_pages + top_k))
+    if out is None:
+        lists = torch.full((B, kv.n_kv_heads, list_stride), -1, dtype=torch.int32, device=kv.device)
+        counts = torch.zeros((B, kv.n_kv_heads), dtype=torch.int32, device=kv.device)
+        o = torch.empty((B, T, Hq, kv.d_v), dtype=kv.dtype, device=kv.device)
+        lse = torch.empty((B, T, Hq), dtype=torch.float32, device=kv.device) if want_lse else None
+    else:
+        lists, counts, o, lse = out
+    _check(load_library().sa_select_decode(
+        kv.ref, B, _ptr(q), T, Hq, _ptr(page_summary), 1 if refresh_newest_page else 0, sink_pages, window_pages,
+        top_k, _ptr(lists), list_stride, _ptr(counts), float(sm_scale), _ptr(o), _ptr(lse), _stream(kv.device)))
+    return lists, counts, o, lse
 
 
 def sa_block_sparse_prefill_workspace_size(kv: PagedKV, q_len: int, n_q_heads: int, n_kv_blocks: int) -> int:

@@ -22,7 +22,8 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libsparse_attn.so")
 ARCH = "gfx950"
 
-SOURCES = ["api.cpp", "summary_score.hip", "select.hip", "decode.hip", "mla.hip", "prefill.hip"]
+SOURCES = ["api.cpp", "summary_score.hip", "select.hip", "decode.hip", "mla.hip", "prefill.hip",
+           "select_decode.hip"]
 
 CFLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-fPIC", "-std=c++17", "-Wall", "-Wno-unused-function",

@@ -403,6 +403,98 @@ sa_status sa_sparse_decode(const sa_paged_kv* kv, int32_t batch, const void* q, 
   return ok();
 }
 
+// ---------------------------------------------------------- select + decode
+sa_status sa_select_decode(const sa_paged_kv* kv, int32_t batch, const void* q, int32_t q_tokens,
+                           int32_t n_q_heads, float* page_summary, int32_t refresh_newest_page, int32_t sink_pages,
+                           int32_t window_pages, int32_t top_k, int32_t* page_lists, int32_t list_stride,
+                           int32_t* page_counts, float sm_scale, void* out, float* out_lse, hipStream_t stream) {
+  sa_status st = check_kv(kv, true);
+  if (st != SA_OK) return st;
+  st = check_decode_shape(kv, batch, q_tokens, n_q_heads, SA_SEL_PER_KV_HEAD);
+  if (st != SA_OK) return st;
+  if (kv->dtype != SA_DTYPE_BF16 || is_latent(kv) || kv->d_qk != 128 || kv->page_size != 64)
+    return fail(SA_ERR_UNSUPPORTED, "select+decode needs bf16, a V pool, d 128 and page_size 64");
+  if (q_tokens * (n_q_heads / kv->n_kv_heads) > sa::kScoreInlineRows)
+    return fail(SA_ERR_UNSUPPORTED, "select+decode pools at most %d query rows", sa::kScoreInlineRows);
+  if (!q || !page_summary || !page_lists || !page_counts || !out)
+    return fail(SA_ERR_INVALID_ARGUMENT, "q, page_summary, page_lists, page_counts and out must be set");
+  if (sink_pages < 0 || window_pages < 0 || top_k < 0)
+    return fail(SA_ERR_INVALID_ARGUMENT, "sink_pages, window_pages and top_k must be >= 0");
+  const long need_stride = std::min<long>(kv->max_pages, (long)sink_pages + window_pages + top_k);
+  if (list_stride < need_stride || list_stride <= 0)
+    return fail(SA_ERR_INVALID_ARGUMENT, "list_stride %d < min(max_pages, sink+window+top_k) = %ld", list_stride,
+                need_stride);
+  if (!std::isfinite(sm_scale) || !(sm_scale > 0.f))
+    return fail(SA_ERR_INVALID_ARGUMENT, "sm_scale must be finite and positive");
+  // the keys and the list sit in LDS beside the decode's 128 KiB of staging
+  const size_t lds_max = sa::select_decode_lds_limit();
+  if (sa::select_decode_lds_bytes(kv->max_pages, list_stride) > lds_max)
+    return fail(SA_ERR_UNSUPPORTED, "select+decode holds max_pages + list_stride <= %zu entries in LDS",
+                lds_max / sizeof(uint32_t));
+  const int n_sel = kv->n_kv_heads;
+
+  sa::ScoreParams sp{};
+  sp.q = q;
+  sp.mu = page_summary;
+  sp.block_table = kv->block_table;
+  sp.seq_lens = kv->seq_lens;
+  sp.scores = nullptr;
+  sp.B = batch;
+  sp.T = q_tokens;
+  sp.Hq = n_q_heads;
+  sp.Hkv = kv->n_kv_heads;
+  sp.G = n_q_heads / kv->n_kv_heads;
+  sp.n_sel = n_sel;
+  sp.d = kv->d_qk;
+  sp.P = kv->page_size;
+  sp.max_pages = kv->max_pages;
+  sp.per_q = 0;
+  sp.refresh = refresh_newest_page ? 1 : 0;
+  sp.k_pool = kv->k_pool;
+  sp.mu_out = page_summary;
+
+  sa::SelectParams p{};
+  p.seq_lens = kv->seq_lens;
+  p.lists = page_lists;
+  p.counts = page_counts;
+  p.ccounts = nullptr;
+  p.n_sel = n_sel;
+  p.P = kv->page_size;
+  p.list_stride = list_stride;
+  p.sink = sink_pages;
+  p.window = window_pages;
+  p.top_k = top_k;
+  p.critical_k = 0;
+  p.tiered = 0;
+
+  sa::DecodeParams dp{};
+  dp.q = q;
+  dp.k_pool = kv->k_pool;
+  dp.v_pool = kv->v_pool;
+  dp.block_table = kv->block_table;
+  dp.seq_lens = kv->seq_lens;
+  dp.lists = page_lists;
+  dp.counts = page_counts;
+  dp.out = out;
+  dp.out_lse = out_lse;
+  dp.B = batch;
+  dp.T = q_tokens;
+  dp.Hq = n_q_heads;
+  dp.Hkv = kv->n_kv_heads;
+  dp.G = n_q_heads / kv->n_kv_heads;
+  dp.n_sel = n_sel;
+  dp.per_q = 0;
+  dp.list_stride = list_stride;
+  dp.max_pages = kv->max_pages;
+  dp.mask_words = (n_q_heads + 31) / 32;
+  dp.P = kv->page_size;
+  dp.d_qk = kv->d_qk;
+  dp.d_v = kv->d_v;
+  dp.splits = 1;
+  dp.scale_log2 = sm_scale * sa::kLog2e;
+  return device_status(sa::launch_select_decode(sp, p, dp, batch, stream), "select+decode launch");
+}
+
 // ------------------------------------------------------------------ prefill
 size_t sa_block_sparse_prefill_workspace_size(const sa_paged_kv* kv, int32_t q_len, int32_t n_q_heads,
                                               int32_t n_kv_blocks) {

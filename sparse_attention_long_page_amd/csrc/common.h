@@ -162,6 +162,10 @@ struct PrefillParams {
 hipError_t launch_page_summary(const SummaryParams& p, int batch, int bf16, hipStream_t s);
 hipError_t launch_select(const SelectParams& p, int batch, int max_pages, hipStream_t s);
 hipError_t launch_score_select(const ScoreParams& sp, const SelectParams& p, int batch, int bf16, hipStream_t s);
+size_t select_decode_lds_bytes(int max_pages, int list_stride);
+size_t select_decode_lds_limit();
+hipError_t launch_select_decode(const ScoreParams& sp, const SelectParams& p, const DecodeParams& dp, int batch,
+                                hipStream_t s);
 hipError_t launch_select_prep(const SummaryParams& smp, const ScoreParams& sp, int bf16, bool refresh, double* qpart,
                               uint32_t* arrivals, hipStream_t s);
 hipError_t launch_score_lastsel(const ScoreParams& sp, const SelectParams& p, int bf16, const double* qpart,

@@ -161,6 +161,38 @@ def test_prefill_rejects(name, kvo, argo, status):
     assert st == status, S.load_library().sa_last_error_message()
 
 
+def select_decode(kvd, **over):
+    a = dict(batch=2, q=FAKE, q_tokens=1, n_q_heads=8, page_summary=FAKE, refresh=0, sink=1, window=2, top_k=4,
+             lists=FAKE, stride=7, counts=FAKE, scale=0.1, out=FAKE, lse=None)
+    a.update(over)
+    lib = S.load_library()
+    return lib.sa_select_decode(ctypes.byref(kvd), a["batch"], a["q"], a["q_tokens"], a["n_q_heads"],
+                                a["page_summary"], a["refresh"], a["sink"], a["window"], a["top_k"], a["lists"],
+                                a["stride"], a["counts"], a["scale"], a["out"], a["lse"], None)
+
+
+SELECT_DECODE_CASES = [
+    ("fp32", dict(kv=dict(dtype=B.SA_DTYPE_FP32)), {}, UNS),
+    ("d 64", dict(kv=dict(d_qk=64, d_v=64)), {}, UNS),
+    ("page 16", dict(kv=dict(page_size=16)), {}, UNS),
+    ("latent", dict(kv=dict(v_pool=None, d_qk=576, d_v=512, n_kv_heads=1)), dict(n_q_heads=16), UNS),
+    ("rows exceed tile", {}, dict(q_tokens=5), UNS),
+    ("no summary", {}, dict(page_summary=None), INV),
+    ("no lists", {}, dict(lists=None), INV),
+    ("short stride", {}, dict(stride=6), INV),
+    ("negative top_k", {}, dict(top_k=-1), INV),
+    ("zero scale", {}, dict(scale=0.0), INV),
+    ("heads not multiple", {}, dict(n_q_heads=7), INV),
+]
+
+
+@pytest.mark.parametrize("name,kvo,argo,status", SELECT_DECODE_CASES, ids=[c[0] for c in SELECT_DECODE_CASES])
+def test_select_decode_rejects(name, kvo, argo, status):
+    st = select_decode(kv(**kvo.get("kv", {})), **argo)
+    assert st == status, S.load_library().sa_last_error_message()
+    assert S.load_library().sa_last_error_message()
+
+
 def test_workspace_sizes():
     lib = S.load_library()
     # select: fp32 scores [B][n_sel][max_pages] + fp64 pooled queries + one arrival

@@ -426,3 +426,69 @@ def test_full_size_llama3_decode_32k_sampled():
 def test_full_size_token_head_decode_128k_sampled():
     (mx, mean, lse_err), rep = _full_size_check(W.TOKEN_HEAD_DECODE_128K, seed=12, n_sample=2)
     print(f"max_abs {mx:.3e} mean_abs {mean:.3e} lse {lse_err:.3e} band events {rep.band_events}/{rep.units}")
+
+
+def _select_then_decode(kv, inp, wl, mu, refresh):
+    """The two calls sa_select_decode stands for (one decode split)."""
+    lists, counts, _ = S.sa_select_pages(kv, n_q_heads=wl.n_q_heads, mode=S.SA_SEL_PER_KV_HEAD,
+                                         sink_pages=wl.sink_pages, window_pages=wl.window_pages, top_k=wl.top_k,
+                                         q=inp["q"], page_summary=mu, refresh_newest_page=refresh)
+    out, lse = S.sa_sparse_decode(kv, inp["q"], lists, counts, mode=S.SA_SEL_PER_KV_HEAD, sm_scale=wl.sm_scale,
+                                  num_splits=1)
+    return lists, counts, out, lse
+
+
+def _assert_same_step(a, b):
+    (l1, c1, o1, s1), (l2, c2, o2, s2) = a, b
+    assert torch.equal(c1, c2)
+    L1, L2, C = npi(l1), npi(l2), npi(c1)
+    for idx in np.ndindex(*C.shape):
+        assert np.array_equal(L1[idx][:C[idx]], L2[idx][:C[idx]]), idx
+    assert torch.equal(o1, o2)
+    assert torch.equal(s1, s2)
+
+
+@pytest.mark.parametrize("refresh", [False, True])
+@pytest.mark.parametrize("name", ["llama3_decode_small", "llama3_many_lists"])
+def test_select_decode_equals_select_then_decode(name, refresh):
+    """sa_select_decode writes exactly what sa_select_pages followed by a
+    one-split sa_sparse_decode write: lists, counts, output and lse bit for bit
+    (and, with refresh, the newest pages' summaries); the small case is also
+    checked against the oracle."""
+    wl = SELECT_CASES[name]
+    cpu = W.make_decode_inputs(wl, "cpu", seed=13)
+    inp = gpu_inputs(cpu)
+    kv = make_kv(inp, wl)
+    mu_a = S.sa_page_summary(kv)
+    mu_b = mu_a.clone()
+    ref = _select_then_decode(kv, inp, wl, mu_a, refresh)
+    got = S.sa_select_decode(kv, inp["q"], mu_b, sink_pages=wl.sink_pages, window_pages=wl.window_pages,
+                             top_k=wl.top_k, sm_scale=wl.sm_scale, refresh_newest_page=refresh)
+    torch.cuda.synchronize()
+    _assert_same_step(got, ref)
+    assert torch.equal(torch.nan_to_num(mu_a, nan=0.0), torch.nan_to_num(mu_b, nan=0.0))
+    if name == "llama3_decode_small":
+        _, o_scores, o_lists, o_counts, _, npg = oracle_chain(cpu, wl)
+        rep = check_page_lists(npi(got[0]), npi(got[1]), None, o_scores, npg, wl.sink_pages, wl.window_pages,
+                               wl.top_k, None)
+        assert not rep.failures, rep.failures[:5]
+        assert rep.exact == rep.units
+        ref_o, ref_l = O.sparse_decode(np64(cpu["q"]), np64(cpu["k_pool"]), np64(cpu["v_pool"]),
+                                       npi(cpu["block_table"]), npi(cpu["seq_lens"]), wl.page_size, o_lists,
+                                       o_counts, wl.n_kv_heads, wl.mode, wl.sm_scale)
+        compare_outputs(got[2], got[3], ref_o, ref_l)
+
+
+def test_full_size_llama3_select_decode_equals_two_calls():
+    """At the Llama-3 32K shape, in the decode step's form (newest-page refresh)."""
+    wl = W.LLAMA3_DECODE_32K
+    inp = W.make_decode_inputs(wl, DEV, seed=14)
+    kv = make_kv(inp, wl)
+    mu_a = S.sa_page_summary(kv)
+    mu_b = mu_a.clone()
+    ref = _select_then_decode(kv, inp, wl, mu_a, True)
+    got = S.sa_select_decode(kv, inp["q"], mu_b, sink_pages=wl.sink_pages, window_pages=wl.window_pages,
+                             top_k=wl.top_k, sm_scale=wl.sm_scale, refresh_newest_page=True)
+    torch.cuda.synchronize()
+    _assert_same_step(got, ref)
+    assert torch.equal(mu_a, mu_b)
