@@ -54,6 +54,9 @@ def parse():
     ap.add_argument("--sets", type=int, default=3, help="independent input sets rotated over")
     ap.add_argument("--splits", type=int, default=-1, help="decode splits (-1: workload default)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--two-calls", action="store_true",
+                    help="run the decode step as sa_select_pages + sa_sparse_decode even where one "
+                         "sa_select_decode call can")
     return ap.parse_args()
 
 
@@ -81,11 +84,21 @@ class Timer:
         self.pairs = {}
 
 
-def decode_step_fn(S, wl, inp, mu, splits):
+def fused_path(wl, splits):
+    """True when one sa_select_decode call can run the step: per-KV-head lists
+    scored from page summaries, untiered, a bf16 cache of d 128 in pages of 64,
+    one split (the library's own choice when every CU holds one list, as for
+    the Llama-3-8B batch of 32 x 8 lists)."""
+    return (wl.mode == "per_kv_head" and wl.scores == "summary" and not wl.tiered and not wl.latent
+            and wl.d_qk == 128 and wl.d_v == 128 and wl.page_size == 64 and wl.dtype == "bf16" and splits in (0, 1))
+
+
+def decode_step_fn(S, wl, inp, mu, splits, fused=False):
     """One decode step as one HIP graph on the current stream: page summary of
     the newest page and selection (one call), split-K decode and LSE merge.  Graph replay
     removes the host launch cost between kernels; every kernel still runs in
-    every replay.  (Running the newest-page summary update on a second stream
+    every replay.  With `fused` the step is one sa_select_decode call (same
+    lists and outputs, bit for bit, as the two calls).  (Running the newest-page summary update on a second stream
     beside the selection, which the library allows when a local window forces
     that page, measured slower here: the fork and join cost more than the
     overlap saves.)  A captured graph does not own the memory its kernels use,
@@ -118,9 +131,17 @@ def decode_step_fn(S, wl, inp, mu, splits):
                            critical_counts=ccounts, ambient_head_mask=inp["ambient_mask"], num_splits=splits,
                            out=out, out_lse=lse, workspace=dec_ws)
 
+    def select_decode():
+        S.sa_select_decode(kv, inp["q"], mu, sink_pages=wl.sink_pages, window_pages=wl.window_pages,
+                           top_k=wl.top_k, sm_scale=wl.sm_scale, refresh_newest_page=True, list_stride=stride,
+                           out=(lists, counts, out, lse))
+
     def step():
-        select()
-        decode()
+        if fused:
+            select_decode()
+        else:
+            select()
+            decode()
 
     step()
     torch.cuda.synchronize()
@@ -128,7 +149,7 @@ def decode_step_fn(S, wl, inp, mu, splits):
     with torch.cuda.graph(g):
         step()
     keep = (kv, inp, mu, lists, counts, ccounts, sel_ws, dec_ws, out, lse)
-    return g, (lists, counts, ccounts), decode, keep, step
+    return g, (lists, counts, ccounts), (step if fused else decode), decode, keep, step
 
 
 def recorded_traffic(name):
@@ -192,6 +213,31 @@ def selected_bytes(wl, inp, lists, counts, ccounts):
                     pages.update(int(x) for x in L[b, s, :C[b, s]])
                 uniq += sum(min(P, int(lens[b]) - p * P) for p in pages) * per_tok
     return total, (uniq if wl.mode == "per_q_head" else total)
+
+
+def fused_bytes(wl, inp, lists, counts, kv_bytes):
+    """Algorithmic bytes of one sa_select_decode call: the selected pages' K and
+    V (`kv_bytes`, valid tokens), the fp32 mean-key rows of the pages it scores
+    (every page but the forced sink and local-window ones), the newest page's
+    keys and its new mean-key row (its summary is recomputed), the query rows,
+    and what it writes (o, lse, the lists and their counts)."""
+    P, D = wl.page_size, wl.d_qk
+    G = wl.n_q_heads // wl.n_kv_heads
+    lens = inp["seq_lens"].cpu().numpy()
+    C = counts.cpu().numpy()
+    total = kv_bytes
+    for b in range(wl.batch):
+        L = int(lens[b])
+        n = (L + P - 1) // P
+        if n == 0:
+            continue
+        sink_hi = min(wl.sink_pages, n)
+        win_lo = max(n - wl.window_pages, 0)
+        scored = n - (sink_hi + max(0, n - max(win_lo, sink_hi)))
+        last_nv = L - (n - 1) * P
+        per_list = scored * D * 4 + last_nv * D * 2 + D * 4 + wl.q_tokens * G * (2 * D * 2 + 4) + 4
+        total += wl.n_kv_heads * per_list + 4 * int(C[b].sum())
+    return int(total)
 
 
 def tiered_flops(wl, inp, lists, counts, ccounts):
@@ -286,10 +332,11 @@ def run_decode(args):
             mu = S.sa_page_summary(kv)       # amortised: built once per filled page
         sets.append((inp, mu))
     torch.cuda.synchronize()
+    fused = fused_path(wl, splits) and not args.two_calls
     steps = []
     for inp, mu in sets:
-        graphs, res, dec, keep, step_call = decode_step_fn(S, wl, inp, mu, splits)
-        steps.append((graphs, res, inp, dec, keep, step_call))
+        graphs, res, dom, dec, keep, step_call = decode_step_fn(S, wl, inp, mu, splits, fused)
+        steps.append((graphs, res, inp, dom, keep, step_call, dec))
     # one graph with one step per input set, in set order
     chain = torch.cuda.CUDAGraph()
     with torch.cuda.graph(chain):
@@ -325,13 +372,22 @@ def run_decode(args):
     single_ms, _ = timed(args.steps, False)
     ms_per_step, step_gpu_us = timed(args.steps, True)
 
-    _, (lists, counts, ccounts), inp, _, _, _ = steps[0]
-    # the dominant kernel alone: decode calls back to back, inputs rotating
+    _, (lists, counts, ccounts), inp, _, _, _, _ = steps[0]
+    # the dominant kernel alone (the decode, or the fused selection + decode):
+    # its calls back to back, inputs rotating
     dec_b2b_us = time_back_to_back([st[3] for st in steps], 4 * len(steps))
     nbytes, uniq = selected_bytes(wl, inp, lists, counts, ccounts)
     algo_bytes = uniq if wl.mode == "per_q_head" else nbytes
+    if fused:
+        algo_bytes = fused_bytes(wl, inp, lists, counts, nbytes)
     achieved = algo_bytes / (dec_b2b_us * 1e-6) / 1e9
     value = nbytes / (ms_per_step * 1e-3) / 1e9
+    if fused:
+        tag, kernel = "select_decode", "sa_select_decode (scoring, selection and decode in one kernel)"
+    elif wl.latent:
+        tag, kernel = "mla_decode", "sa_sparse_decode (latent tiered + split merge)"
+    else:
+        tag, kernel = "sparse_decode", "sa_sparse_decode (decode kernel + split merge)"
     res = {
         "metric": "sparse-decode selected-KV GB/s (% of HBM peak) + us/layer at 32K ctx, 90% sparsity",
         "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
@@ -341,7 +397,8 @@ def run_decode(args):
                    "kv_heads": wl.n_kv_heads, "head_dim": wl.d_qk, "page_size": wl.page_size,
                    "sink_pages": wl.sink_pages, "window_pages": wl.window_pages, "top_k": wl.top_k,
                    "kept_tokens_per_head": int(counts.float().mean().item() * wl.page_size),
-                   "splits": splits, "input_sets": args.sets},
+                   "splits": splits, "input_sets": args.sets,
+                   "step_calls": ["sa_select_decode"] if fused else ["sa_select_pages", "sa_sparse_decode"]},
         "us_per_layer": round(1000.0 * ms_per_step, 2),
         "pct_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
         "step_gpu_us": round(step_gpu_us, 2),
@@ -349,10 +406,18 @@ def run_decode(args):
         "selected_bytes": nbytes,
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": recorded_traffic(f"{'mla_decode' if wl.latent else 'sparse_decode'}_{wl.name}_traffic.json"),
-                     "kernel": "sa_sparse_decode (decode kernel + split merge)", "algorithmic_bytes": algo_bytes,
+                     "traffic": recorded_traffic(f"{tag}_{wl.name}_traffic.json"),
+                     "kernel": kernel, "algorithmic_bytes": algo_bytes,
                      "launch_us": round(dec_b2b_us, 2)},
     }
+    if fused:
+        # the decode kernel alone, on the lists the fused calls wrote
+        d_us = time_back_to_back([st[6] for st in steps], 4 * len(steps))
+        d_gbs = nbytes / (d_us * 1e-6) / 1e9
+        res["roofline_decode_only"] = {"bound": "hbm", "achieved": round(d_gbs, 1), "peak": HBM_PEAK_GBS,
+                                       "unit": "GB/s", "frac": round(d_gbs / HBM_PEAK_GBS, 4),
+                                       "kernel": "sa_sparse_decode on the same lists", "algorithmic_bytes": nbytes,
+                                       "launch_us": round(d_us, 2)}
     if wl.mode == "per_q_head":
         res["pair_counted_bytes"] = nbytes
     if wl.latent:

@@ -152,3 +152,41 @@ def test_summary_beside_selection_matches_serial(name):
         g.replay()
         torch.cuda.synchronize()
         _assert_same(results, eager, rep)
+
+
+@pytest.mark.parametrize("name", ["llama3_decode_small", "llama3_many_lists"])
+def test_select_decode_graph_replays_match_eager(name):
+    """The fused selection + decode call (newest-page summary recomputed inside)
+    captured in a graph: every replay, with the outputs poisoned and unrelated
+    eager work between replays, equals the eager call."""
+    wl = {**W.SMALL, **MANY_LISTS}[name]
+    inp = gpu_inputs(W.make_decode_inputs(wl, "cpu", seed=44))
+    kv = make_kv(inp, wl)
+    mu = S.sa_page_summary(kv)
+    stride = wl.list_stride
+    lists = torch.full((wl.batch, wl.n_sel, stride), -1, dtype=torch.int32, device=DEV)
+    counts = torch.zeros((wl.batch, wl.n_sel), dtype=torch.int32, device=DEV)
+    out = torch.empty((wl.batch, wl.q_tokens, wl.n_q_heads, wl.d_v), dtype=inp["q"].dtype, device=DEV)
+    lse = torch.empty((wl.batch, wl.q_tokens, wl.n_q_heads), dtype=torch.float32, device=DEV)
+    results = [lists, counts, out, lse]
+
+    def step():
+        S.sa_select_decode(kv, inp["q"], mu, sink_pages=wl.sink_pages, window_pages=wl.window_pages,
+                           top_k=wl.top_k, sm_scale=wl.sm_scale, refresh_newest_page=True, list_stride=stride,
+                           out=(lists, counts, out, lse))
+
+    step()
+    torch.cuda.synchronize()
+    eager = [r.clone() for r in results]
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for rep in range(4):
+        for r in results:
+            r.fill_(-7)
+        other = torch.randn(1 << 20, device=DEV).sum()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.isfinite(other)
+        _assert_same(results, eager, rep)
