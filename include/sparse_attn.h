@@ -142,9 +142,11 @@ sa_status sa_page_summary(const sa_paged_kv* kv, int32_t batch, int32_t last_pag
  *   scores_out   optional out [batch][n_sel][max_pages] fp32 router scores (NaN
  *                past each sequence's last page); ignored when scores given
  * n_sel = n_kv_heads (PER_KV_HEAD) or n_q_heads (PER_Q_HEAD).  max_pages <= 16384.
- * Unless scores_out is given, the page_summary rows of forced pages are not
- * read, so a summary update of forced pages (e.g. the newest page inside the
- * local window) may run concurrently with this call on another stream.
+ * Unless scores_out is given, the page_summary rows of forced pages take no
+ * part in the call (they are read only when no page of the sequence is
+ * scored, and then ignored), so a summary update of forced pages (e.g. the
+ * newest page inside the local window) may run concurrently with this call on
+ * another stream.
  * ---------------------------------------------------------------------- */
 size_t sa_select_pages_workspace_size(int32_t batch, int32_t n_sel, int32_t max_pages);
 

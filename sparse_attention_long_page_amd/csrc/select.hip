@@ -133,8 +133,7 @@ __global__ __launch_bounds__(kSelThreads) void score_lastsel_kernel(ScoreParams 
       acc += qq[64 * i + 2] * (double)v[it][i][2];
       acc += qq[64 * i + 3] * (double)v[it][i][3];
     }
-#pragma unroll
-    for (int o = 8; o > 0; o >>= 1) acc += __shfl_xor(acc, o, 64);
+    acc = row16_sum(acc);
     // (device-coherent stores: the list's last workgroup, possibly on
     // another XCD, reads them back)
     if (sub == 0 && lp < sp.max_pages)

@@ -41,6 +41,26 @@ __device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x) {
   return x;
 }
 
+// Sum of a double over the 16 lanes of each DPP row, rotating the row by 8,
+// 4, 2 and 1 lanes (no LDS round trip).  The first lane of the row adds the
+// same values in the same order as an xor butterfly over 8, 4, 2, 1 (for every
+// lane it depends on, rotating by k reaches lane ^ k), so its result has the
+// same bits; the other lanes hold the sum in another order.
+template <int CTRL>
+__device__ __forceinline__ double dpp_f64(double x) {
+  const unsigned long long v = (unsigned long long)__double_as_longlong(x);
+  const unsigned lo = (unsigned)__builtin_amdgcn_update_dpp(0, (int)(unsigned)v, CTRL, 0xf, 0xf, false);
+  const unsigned hi = (unsigned)__builtin_amdgcn_update_dpp(0, (int)(unsigned)(v >> 32), CTRL, 0xf, 0xf, false);
+  return __longlong_as_double((long long)(((unsigned long long)hi << 32) | lo));
+}
+__device__ __forceinline__ double row16_sum(double x) {
+  x += dpp_f64<0x128>(x);   // row_ror:8
+  x += dpp_f64<0x124>(x);   // row_ror:4
+  x += dpp_f64<0x122>(x);   // row_ror:2
+  x += dpp_f64<0x121>(x);   // row_ror:1
+  return x;
+}
+
 // Exclusive prefix sum over the workgroup in thread order.  `wsum` serves this
 // one call only, so a single barrier suffices.  *total gets the sum over all
 // threads.
@@ -227,15 +247,27 @@ __device__ inline void select_from_keys(const SelectParams& p, const ListShape& 
 
 // Router scores of list (b, s) into order-preserving keys in LDS, by one
 // workgroup of kSelThreads threads (the selection follows after a barrier;
-// the zeroing of sh.hist[0] it needs is done here).  The pooled query sits in LDS; each wave
-// scores 32 pages per round at d <= 128 (16 lanes per page, 4 pages per step,
-// the 8 steps' mean-row loads in flight together), writing order-preserving
-// keys into LDS.
-// The score arithmetic is the same as page_score_kernel's: lane `sub` of a
+// the zeroing of sh.hist[0] it needs is done here).  The pooled query sits in
+// LDS.  Each wave scores 4 pages per step with 16 lanes per page; at d <= 128
+// a round is 16 steps, so the 8 waves cover 512 pages per round.
+// The score arithmetic is the same as score_lastsel_kernel's: lane `sub` of a
 // page's 16 takes dims 64 i + 4 sub + 0..3 (each load instruction reads 256
 // contiguous bytes of the mean row), float64 products of the pooled query
 // with the fp32 mean row summed in that order, then over the 16 lanes in a
-// fixed butterfly, rounded once to fp32.
+// fixed butterfly (row16_sum), rounded once to fp32.
+// Memory round trips: the block-table entries of the first round, the
+// newest page's keys and the query rows are loaded together; the first
+// round's mean rows are issued as soon as the block-table entries arrive,
+// while the pooled query and the refreshed mean are summed.  Every load is
+// unconditional, from a clamped valid index: rows past the query rows and
+// tokens past the newest page's valid ones add +0.0 (exact: the float64 sums
+// start at +0.0 and never become -0.0), and a lane whose page is forced, past
+// the sequence or refreshed re-reads the mean row of the nearest page the list
+// does score, and does not use it.  Forced pages' rows are thus read only
+// when the scores are written out, or when the list scores no page at all
+// (page 0's row is then read and ignored).  (A load under a per-lane
+// condition makes the compiler wait for it at once, and a wait after a branch
+// waits for every load of either path.)
 // newest-page summary refresh: the thread partition of page_summary_kernel
 // (thread (cg, ts): 16-byte column group cg, tokens ts, ts + TS, ...); the
 // refresh needs TS * D doubles of LDS
@@ -249,54 +281,136 @@ __device__ __forceinline__ void score_keys_body(const ScoreParams& sp, const Sel
                                                 int b, int s, uint32_t* keys, SelShared& sh, double* rpart) {
   constexpr int PL = D / 16;
   constexpr int VW = 16 / sizeof(T), CG = D / VW, TS = refresh_ts<T, D>();
+  constexpr int kWaves = kSelThreads / 64;
+  constexpr int kSteps = D <= 128 ? 16 : 2;           // 4-page steps whose loads are in flight together
+  constexpr int kRound = 4 * kSteps * kWaves;         // pages per round
+  constexpr int kQPer = (D + kSelThreads - 1) / kSelThreads;   // pooled-query dims per thread
+  constexpr int kQRows = 8;                            // query rows loaded together
   __shared__ double qbar[D];
   __shared__ float fresh[D];
   const int n = L.n;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int sub = lane & 15, slot = lane >> 4;
+  float* sout = sp.scores ? sp.scores + ((size_t)b * sp.n_sel + s) * sp.max_pages : nullptr;
+  for (int i = threadIdx.x; i < 512; i += kSelThreads) sh.hist[0][0][i] = 0u;
+  if (sout)
+    for (int lp = n + threadIdx.x; lp < sp.max_pages; lp += kSelThreads) sout[lp] = __builtin_nanf("");
+  if (n == 0) return;                                   // nothing to score (uniform)
   const int g = sp.per_q ? s / sp.G : s;
   const int32_t* bt = sp.block_table + (size_t)b * sp.max_pages;
+  const float* mu_g = sp.mu + (size_t)g * D + 4 * sub;
+  const size_t mu_page = (size_t)sp.Hkv * D;
+  // this lane's page in a round: round base + 4 kSteps wave + lane (lanes
+  // past 4 kSteps carry no page)
+  const int lane_pg = 4 * kSteps * wave + min(lane, 4 * kSteps - 1);
+  const bool refresh = sp.refresh != 0;
+  // the pages whose mean rows this list uses: all with the scores written
+  // out, else those not forced; the refreshed newest page's row comes from LDS
+  const int rd_lo = sout ? 0 : L.sink_hi;
+  const int rd_hi = min(sout ? n : L.win_lo, refresh ? n - 1 : n);
+  auto row_page = [&](int lp) __attribute__((always_inline)) {
+    return rd_lo < rd_hi ? min(max(lp, rd_lo), rd_hi - 1) : 0;
+  };
+
+  // (1) block-table entries of the first round
+  const int phys0 = bt[row_page(lane_pg)];
+
+  // (2) the newest page's keys (refresh) and the query rows
   // With refresh, the newest page's mean row (KV head g) is recomputed here,
   // summed in the same order as page_summary_kernel (same bits), written by
   // one list per head, and used for this list's score of that page from LDS.
-  const bool refresh = sp.refresh && n > 0;
-  const int last_phys = refresh ? bt[n - 1] : 0;
-  const int last_nv = refresh ? page_valid(sp.seq_lens[b], n - 1, sp.P) : 0;
-  if (refresh && threadIdx.x < CG * TS) {
-    const int cg = threadIdx.x % CG, ts = threadIdx.x / CG;
-    const T* base = reinterpret_cast<const T*>(sp.k_pool) + (((size_t)last_phys * sp.Hkv + g) * sp.P) * D + cg * VW;
-    double acc[VW];
+  const int last_phys = bt[n - 1];
+  const int last_nv = page_valid(sp.seq_lens[b], n - 1, sp.P);
+  const int rcg = (threadIdx.x & 255) % CG, rts = min((threadIdx.x & 255) / CG, TS - 1);
+  constexpr int kTokMax = 4;                            // tokens per thread per refresh chunk
+  u32x4 rw[kTokMax];
+  const T* rbase = reinterpret_cast<const T*>(sp.k_pool) + (((size_t)last_phys * sp.Hkv + g) * sp.P) * D + rcg * VW;
+  if (refresh) {
 #pragma unroll
-    for (int i = 0; i < VW; ++i) acc[i] = 0.0;
-#pragma unroll 4
-    for (int j = ts; j < last_nv; j += TS) {
-      const u32x4 w = *reinterpret_cast<const u32x4*>(base + (size_t)j * D);
-      if constexpr (sizeof(T) == 2) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          acc[2 * i] += (double)bf16_lo(w[i]);
-          acc[2 * i + 1] += (double)bf16_hi(w[i]);
-        }
-      } else {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) acc[i] += (double)__uint_as_float(w[i]);
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < VW; ++i) rpart[ts * D + cg * VW + i] = acc[i];
+    for (int j = 0; j < kTokMax; ++j)
+      rw[j] = *reinterpret_cast<const u32x4*>(rbase + (size_t)min(rts + j * TS, last_nv - 1) * D);
   }
   const T* q = reinterpret_cast<const T*>(sp.q);
   const int rows = sp.per_q ? sp.T : sp.T * sp.G;
-  for (int e = threadIdx.x; e < D; e += kSelThreads) {
-    double v = 0.0;
-    for (int r = 0; r < rows; ++r) {
-      int t, h;
-      if (sp.per_q) { t = r; h = s; } else { t = r / sp.G; h = s * sp.G + r % sp.G; }
-      const size_t i = (((size_t)b * sp.T + t) * sp.Hq + h) * D + e;
-      if constexpr (sizeof(T) == 2) v += (double)bf16_bits_to_f32(q[i]);
-      else v += (double)q[i];
+  auto q_index = [&](int r, int e) __attribute__((always_inline)) {
+    int t, h;
+    if (sp.per_q) { t = r; h = s; } else { t = r / sp.G; h = s * sp.G + r % sp.G; }
+    return (((size_t)b * sp.T + t) * sp.Hq + h) * D + e;
+  };
+  float qv[kQPer][kQRows];
+#pragma unroll
+  for (int k = 0; k < kQPer; ++k) {
+    const int e = min((int)threadIdx.x + k * kSelThreads, D - 1);
+#pragma unroll
+    for (int r = 0; r < kQRows; ++r) {
+      const size_t i = q_index(min(r, rows - 1), e);
+      if constexpr (sizeof(T) == 2) qv[k][r] = bf16_bits_to_f32(q[i]);
+      else qv[k][r] = q[i];
     }
-    qbar[e] = v;
   }
-  for (int i = threadIdx.x; i < 512; i += kSelThreads) sh.hist[0][0][i] = 0u;
+
+  // (3) mean rows of the first round
+  f32x4 v[kSteps][PL / 4];
+  auto load_round = [&](int phys) __attribute__((always_inline)) {
+#pragma unroll
+    for (int it = 0; it < kSteps; ++it) {
+      const int ph = __shfl(phys, it * 4 + slot, 64);
+      const float* m = mu_g + (size_t)ph * mu_page;
+#pragma unroll
+      for (int i = 0; i < PL / 4; ++i) v[it][i] = *reinterpret_cast<const f32x4*>(m + 64 * i);
+    }
+  };
+  load_round(phys0);
+
+  // pooled query (rows in order; rows past `rows` add +0.0) and refresh partials
+#pragma unroll
+  for (int k = 0; k < kQPer; ++k) {
+    const int e = threadIdx.x + k * kSelThreads;
+    double acc = 0.0;
+#pragma unroll
+    for (int r = 0; r < kQRows; ++r) acc += r < rows ? (double)qv[k][r] : 0.0;
+    for (int r0 = kQRows; r0 < rows; r0 += kQRows) {     // more rows than one batch
+      float w[kQRows];
+#pragma unroll
+      for (int r = 0; r < kQRows; ++r) {
+        const size_t i = q_index(min(r0 + r, rows - 1), min(e, D - 1));
+        if constexpr (sizeof(T) == 2) w[r] = bf16_bits_to_f32(q[i]);
+        else w[r] = q[i];
+      }
+#pragma unroll
+      for (int r = 0; r < kQRows; ++r) acc += r0 + r < rows ? (double)w[r] : 0.0;
+    }
+    if (e < D) qbar[e] = acc;
+  }
+  if (refresh) {
+    double acc[VW];
+#pragma unroll
+    for (int i = 0; i < VW; ++i) acc[i] = 0.0;
+    for (int j0 = 0; j0 * TS < last_nv; j0 += kTokMax) {
+      if (j0 > 0) {                                     // pages of more than kTokMax * TS tokens
+#pragma unroll
+        for (int j = 0; j < kTokMax; ++j)
+          rw[j] = *reinterpret_cast<const u32x4*>(rbase + (size_t)min(rts + (j0 + j) * TS, last_nv - 1) * D);
+      }
+#pragma unroll
+      for (int j = 0; j < kTokMax; ++j) {
+        const bool ok = rts + (j0 + j) * TS < last_nv;
+        if constexpr (sizeof(T) == 2) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            acc[2 * i] += ok ? (double)bf16_lo(rw[j][i]) : 0.0;
+            acc[2 * i + 1] += ok ? (double)bf16_hi(rw[j][i]) : 0.0;
+          }
+        } else {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) acc[i] += ok ? (double)__uint_as_float(rw[j][i]) : 0.0;
+        }
+      }
+    }
+    if (threadIdx.x < CG * TS)
+#pragma unroll
+      for (int i = 0; i < VW; ++i) rpart[rts * D + rcg * VW + i] = acc[i];
+  }
   __syncthreads();
   if (refresh) {
     const bool writer = !sp.per_q || s % sp.G == 0;
@@ -310,31 +424,16 @@ __device__ __forceinline__ void score_keys_body(const ScoreParams& sp, const Sel
     }
     __syncthreads();
   }
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int sub = lane & 15, slot = lane >> 4;
-  float* sout = sp.scores ? sp.scores + ((size_t)b * sp.n_sel + s) * sp.max_pages : nullptr;
-  constexpr int kWaves = kSelThreads / 64;
-  constexpr int kSteps = D <= 128 ? 8 : 2;           // 4-page steps whose loads are in flight together
-  for (int r0 = 4 * kSteps * wave; r0 < n; r0 += 4 * kSteps * kWaves) {
-    // forced pages' scores are not needed unless the caller asked for the
-    // scores: their mean rows are then not read at all (the newest page's row
-    // may be rewritten concurrently by a summary update on another stream)
-    const int lp_l = r0 + lane;
-    const bool need = lane < 4 * kSteps && lp_l < n && (sout || !(lp_l < L.sink_hi || lp_l >= L.win_lo)) &&
-                      !(refresh && lp_l == n - 1);    // the refreshed row comes from LDS
-    const int my_phys = need ? bt[lp_l] : -1;
-    f32x4 v[kSteps][PL / 4];
-#pragma unroll
-    for (int it = 0; it < kSteps; ++it) {
-      const int ph = __shfl(my_phys, it * 4 + slot, 64);
-      const float* m = sp.mu + ((size_t)max(ph, 0) * sp.Hkv + g) * D + 4 * sub;
-#pragma unroll
-      for (int i = 0; i < PL / 4; ++i) v[it][i] = ph >= 0 ? *reinterpret_cast<const f32x4*>(m + 64 * i) : f32x4{};
-    }
+
+  // (4) scores of each round; the next round's block-table entries and mean
+  // rows are loaded after this round's scores
+  for (int base = 0; base < n; base += kRound) {
+    if (base > 0) load_round(bt[row_page(base + lane_pg)]);
+    const int r0 = base + 4 * kSteps * wave;
 #pragma unroll
     for (int it = 0; it < kSteps; ++it) {
       const int lp = r0 + it * 4 + slot;
-      if (refresh && lp == n - 1) {
+      if (refresh && lp == n - 1) {                     // the refreshed row comes from LDS
 #pragma unroll
         for (int i = 0; i < PL / 4; ++i) {
           const float* f = fresh + 64 * i + 4 * sub;
@@ -350,8 +449,7 @@ __device__ __forceinline__ void score_keys_body(const ScoreParams& sp, const Sel
         acc += qq[64 * i + 2] * (double)v[it][i][2];
         acc += qq[64 * i + 3] * (double)v[it][i][3];
       }
-#pragma unroll
-      for (int o = 8; o > 0; o >>= 1) acc += __shfl_xor(acc, o, 64);
+      acc = row16_sum(acc);
       if (sub == 0 && lp < n) {
         const float sc = (float)acc;
         const bool forced = lp < L.sink_hi || lp >= L.win_lo;
@@ -360,8 +458,6 @@ __device__ __forceinline__ void score_keys_body(const ScoreParams& sp, const Sel
       }
     }
   }
-  if (sout)
-    for (int lp = n + threadIdx.x; lp < sp.max_pages; lp += kSelThreads) sout[lp] = __builtin_nanf("");
 }
 
 }  // namespace sa

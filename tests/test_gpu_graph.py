@@ -120,8 +120,8 @@ def test_prefill_graph_replays_match_eager():
 @pytest.mark.parametrize("name", ["llama3_decode_small", "llama3_many_lists"])
 def test_summary_beside_selection_matches_serial(name):
     """With a local window the newest page is forced and its summary takes no
-    part in the ranking; the selection does not read forced pages' summary
-    rows, so the newest-page summary update may run on a second stream beside
+    part in the ranking; forced pages' summary rows take no part in the
+    selection, so the newest-page summary update may run on a second stream beside
     the selection and the decode.  Graph replays of that forked step equal the
     serial eager step (fused score+select and separate kernels alike)."""
     wl = {**W.SMALL, **MANY_LISTS}[name]
