@@ -123,7 +123,7 @@ def compare_outputs(gpu_out, gpu_lse, ref_out, ref_lse, fp32=False, rows_mask=No
             gl, rl = gl[rows_mask], rl[rows_mask]
         both_inf = np.isneginf(gl) & np.isneginf(rl)
         assert np.array_equal(np.isneginf(gl), np.isneginf(rl)), "lse -inf pattern differs"
-        d = np.abs(np.where(both_inf, 0.0, gl - rl))
+        d = np.abs(np.where(both_inf, 0.0, gl) - np.where(both_inf, 0.0, rl))
         lse_err = float(d.max()) if d.size else 0.0
     if fp32:
         assert max_abs <= FP32_MAX_ABS, f"fp32 max abs err {max_abs}"

@@ -83,6 +83,11 @@ MANY_LISTS = {
     "llama3_many_lists": W.SMALL["llama3_decode_small"].replace(
         name="llama3_many_lists", batch=17, n_q_heads=32, n_kv_heads=8,
         seq_lens=tuple(64 * (9 + 3 * i) + (i * 13) % 64 for i in range(17))),
+    # 128 lists (one workgroup each scores and selects) over sequences with no
+    # page, one page, only forced pages and a single candidate
+    "short_many_lists": W.SMALL["llama3_decode_small"].replace(
+        name="short_many_lists", batch=16, n_q_heads=32, n_kv_heads=8,
+        seq_lens=(0, 1, 64, 65, 64 * 3, 64 * 3 + 5, 64 * 9 + 1, 64 * 20, 0, 2, 63, 128, 129, 64 * 4, 64 * 5 + 3, 7)),
     "per_q_summary_many_lists": W.SMALL["token_head_decode_small"].replace(
         name="per_q_summary_many_lists", batch=4, n_q_heads=32, n_kv_heads=8, scores="summary",
         context=16 * 90 + 7, top_k=12, sink_pages=1, window_pages=3, num_splits=2),
@@ -492,3 +497,39 @@ def test_full_size_llama3_select_decode_equals_two_calls():
     torch.cuda.synchronize()
     _assert_same_step(got, ref)
     assert torch.equal(mu_a, mu_b)
+
+
+# empty sequence, one page (1 and 64 tokens), two pages, every page forced
+# (3 pages = sink 1 + window 2), one candidate past the forced pages, 10 pages
+SHORT_LENS = (0, 1, 64, 65, 64 * 3, 64 * 3 + 5, 64 * 9 + 1)
+
+
+@pytest.mark.parametrize("refresh", [False, True])
+def test_select_decode_short_and_empty_sequences(refresh):
+    """Sequences with no page, one page, only forced pages, or one candidate:
+    the fused call writes exactly what the two calls write, and the oracle's
+    lists and attention (an empty sequence: empty list, o = 0, lse = -inf)."""
+    wl = W.SMALL["llama3_decode_small"].replace(batch=len(SHORT_LENS), seq_lens=SHORT_LENS)
+    cpu = W.make_decode_inputs(wl, "cpu", seed=21)
+    inp = gpu_inputs(cpu)
+    kv = make_kv(inp, wl)
+    mu_a = S.sa_page_summary(kv)
+    mu_b = mu_a.clone()
+    ref = _select_then_decode(kv, inp, wl, mu_a, refresh)
+    got = S.sa_select_decode(kv, inp["q"], mu_b, sink_pages=wl.sink_pages, window_pages=wl.window_pages,
+                             top_k=wl.top_k, sm_scale=wl.sm_scale, refresh_newest_page=refresh)
+    torch.cuda.synchronize()
+    _assert_same_step(got, ref)
+    assert torch.equal(torch.nan_to_num(mu_a, nan=0.0), torch.nan_to_num(mu_b, nan=0.0))
+    _, o_scores, o_lists, o_counts, _, npg = oracle_chain(cpu, wl)
+    assert npg == [0, 1, 1, 2, 3, 4, 10]
+    g_lists, g_counts = npi(got[0]), npi(got[1])
+    assert np.array_equal(g_counts, o_counts)
+    for b in range(wl.batch):
+        for s in range(wl.n_sel):
+            assert np.array_equal(g_lists[b, s, :g_counts[b, s]], o_lists[b, s, :o_counts[b, s]]), (b, s)
+    ref_o, ref_l = O.sparse_decode(np64(cpu["q"]), np64(cpu["k_pool"]), np64(cpu["v_pool"]),
+                                   npi(cpu["block_table"]), npi(cpu["seq_lens"]), wl.page_size, o_lists,
+                                   o_counts, wl.n_kv_heads, wl.mode, wl.sm_scale)
+    compare_outputs(got[2], got[3], ref_o, ref_l)
+    assert (got[2][0].float() == 0).all() and torch.isneginf(got[3][0]).all()
