@@ -16,7 +16,7 @@
 namespace sa {
 
 __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectParams p) {
-  extern __shared__ uint32_t keys[];
+  extern __shared__ __attribute__((aligned(16))) uint32_t keys[];
   __shared__ SelShared sh;
   const int s = blockIdx.x, b = blockIdx.y;
   const ListShape L = list_shape(p, b);
@@ -44,7 +44,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectParams p) {
 // enough lists to fill the GPU).
 template <typename T, int D>
 __global__ __launch_bounds__(kSelThreads) void score_select_kernel(ScoreParams sp, SelectParams p) {
-  extern __shared__ uint32_t keys[];
+  extern __shared__ __attribute__((aligned(16))) uint32_t keys[];
   __shared__ SelShared sh;
   __shared__ double rpart[refresh_ts<T, D>() * D];
   const int s = blockIdx.x, b = blockIdx.y;
@@ -70,7 +70,7 @@ __global__ __launch_bounds__(kSelThreads) void score_lastsel_kernel(ScoreParams 
   constexpr int kSteps = 2;                          // 4-page steps per wave
   constexpr int kPages = 4 * kSteps * kWaves;
   constexpr int PL = D / 16;
-  extern __shared__ uint32_t keys[];
+  extern __shared__ __attribute__((aligned(16))) uint32_t keys[];
   __shared__ SelShared sh;
   __shared__ double qbar[D];
   __shared__ int phys_s[kPages];

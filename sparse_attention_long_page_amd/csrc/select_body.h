@@ -195,49 +195,102 @@ __device__ inline void select_from_keys(const SelectParams& p, const ListShape& 
   const int m = (n + kSelThreads - 1) / kSelThreads;
   const int lo = min(n, (int)threadIdx.x * m), hi = min(n, lo + m);
 
-  // ties at the thresholds before this thread's range (counts < 2^16: n <= 16384)
-  uint32_t t1 = 0, t2 = 0;
-  for (int i = lo; i < hi; ++i) {
-    const uint32_t key = keys[i];
-    t1 += (key != 0u && key == T1) ? 1u : 0u;
-    t2 += (key != 0u && key == T2) ? 1u : 0u;
-  }
-  uint32_t tot;
-  const uint32_t ex = block_excl_scan(t1 | (t2 << 16), &tot, sh.wsum[0]);
-
-  // flags: bit0 forced, bit1 in top-k1 (Critical), bit2 in top-k_eff; count
-  // this thread's entries of segment A (forced + Critical, or the whole
-  // untiered list) and segment B (Ambient)
-  uint32_t rank1 = ex & 0xffffu, rank2 = ex >> 16;
-  uint32_t ca = 0, cb = 0;
-  for (int i = lo; i < hi; ++i) {
-    const uint32_t key = keys[i];
-    const bool e1 = key != 0u && key == T1, e2 = key != 0u && key == T2;
-    const bool top1 = key != 0u && (key > T1 || (e1 && rank1 < r1));
-    const bool top2 = key != 0u && (key > T2 || (e2 && rank2 < r2));
-    rank1 += e1 ? 1u : 0u;
-    rank2 += e2 ? 1u : 0u;
-    const bool forced = i < sink_hi || i >= win_lo;
-    const bool a = p.tiered ? (forced || top1) : (forced || top2);
-    const bool bb = p.tiered && top2 && !top1;
-    ca += a ? 1u : 0u;
-    cb += bb ? 1u : 0u;
-    keys[i] = (a ? 1u : 0u) | (bb ? 2u : 0u);
-  }
-  const uint32_t ex2 = block_excl_scan(ca | (cb << 16), &tot, sh.wsum[1]);
-
-  // ascending compaction of this thread's range
   const int countA = n_forced + k1;
   // (positions stay below n_forced + k_eff <= list_stride; the bound only
   // keeps the stores inside the row should that ever fail)
   const uint32_t stride = (uint32_t)p.list_stride;
-  uint32_t posA = ex2 & 0xffffu, posB = countA + (ex2 >> 16);
-  for (int i = lo; i < hi; ++i) {
-    const uint32_t f = keys[i];
-    if ((f & 1u) && posA < stride) out[posA] = i;
-    if ((f & 2u) && posB < stride) out[posB] = i;
-    posA += f & 1u;
-    posB += (f >> 1) & 1u;
+  uint32_t tot;
+  // Ranges of 4 to 16 keys made of whole 16-byte groups (e.g. 8,192 pages on
+  // 512 threads): each thread reads its keys once, 16 bytes at a time, and
+  // keeps them and their flags in registers.  (Threads' ranges sit 64 bytes
+  // apart, so single-word reads of them conflict 16-way in the LDS banks,
+  // 16-byte reads 4-way.)  Same ranks, flags and order as the loops below.
+  if ((m & 3) == 0 && m <= 16 && (n & 3) == 0 && (reinterpret_cast<uintptr_t>(keys) & 15u) == 0) {
+    const int cnt = hi - lo;
+    uint32_t kr[16];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      u32x4 w = u32x4{0u, 0u, 0u, 0u};
+      if (4 * q < cnt) w = *reinterpret_cast<const u32x4*>(keys + lo + 4 * q);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) kr[4 * q + e] = w[e];
+    }
+    uint32_t t1 = 0, t2 = 0;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const uint32_t key = j < cnt ? kr[j] : 0u;
+      t1 += (key != 0u && key == T1) ? 1u : 0u;
+      t2 += (key != 0u && key == T2) ? 1u : 0u;
+    }
+    const uint32_t ex = block_excl_scan(t1 | (t2 << 16), &tot, sh.wsum[0]);
+    uint32_t rank1 = ex & 0xffffu, rank2 = ex >> 16;
+    uint32_t ca = 0, cb = 0, fl = 0;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const uint32_t key = j < cnt ? kr[j] : 0u;
+      const bool e1 = key != 0u && key == T1, e2 = key != 0u && key == T2;
+      const bool top1 = key != 0u && (key > T1 || (e1 && rank1 < r1));
+      const bool top2 = key != 0u && (key > T2 || (e2 && rank2 < r2));
+      rank1 += e1 ? 1u : 0u;
+      rank2 += e2 ? 1u : 0u;
+      const int i = lo + j;
+      const bool forced = j < cnt && (i < sink_hi || i >= win_lo);
+      const bool fa = p.tiered ? (forced || top1) : (forced || top2);
+      const bool fb = p.tiered && top2 && !top1;
+      ca += fa ? 1u : 0u;
+      cb += fb ? 1u : 0u;
+      fl |= ((fa ? 1u : 0u) | (fb ? 2u : 0u)) << (2 * j);
+    }
+    const uint32_t ex2 = block_excl_scan(ca | (cb << 16), &tot, sh.wsum[1]);
+    uint32_t posA = ex2 & 0xffffu, posB = countA + (ex2 >> 16);
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const uint32_t f = (fl >> (2 * j)) & 3u;
+      if ((f & 1u) && posA < stride) out[posA] = lo + j;
+      if ((f & 2u) && posB < stride) out[posB] = lo + j;
+      posA += f & 1u;
+      posB += (f >> 1) & 1u;
+    }
+  } else {
+    // ties at the thresholds before this thread's range (counts < 2^16: n <= 16384)
+    uint32_t t1 = 0, t2 = 0;
+    for (int i = lo; i < hi; ++i) {
+      const uint32_t key = keys[i];
+      t1 += (key != 0u && key == T1) ? 1u : 0u;
+      t2 += (key != 0u && key == T2) ? 1u : 0u;
+    }
+    const uint32_t ex = block_excl_scan(t1 | (t2 << 16), &tot, sh.wsum[0]);
+
+    // flags: bit0 forced, bit1 in top-k1 (Critical), bit2 in top-k_eff; count
+    // this thread's entries of segment A (forced + Critical, or the whole
+    // untiered list) and segment B (Ambient)
+    uint32_t rank1 = ex & 0xffffu, rank2 = ex >> 16;
+    uint32_t ca = 0, cb = 0;
+    for (int i = lo; i < hi; ++i) {
+      const uint32_t key = keys[i];
+      const bool e1 = key != 0u && key == T1, e2 = key != 0u && key == T2;
+      const bool top1 = key != 0u && (key > T1 || (e1 && rank1 < r1));
+      const bool top2 = key != 0u && (key > T2 || (e2 && rank2 < r2));
+      rank1 += e1 ? 1u : 0u;
+      rank2 += e2 ? 1u : 0u;
+      const bool forced = i < sink_hi || i >= win_lo;
+      const bool a = p.tiered ? (forced || top1) : (forced || top2);
+      const bool bb = p.tiered && top2 && !top1;
+      ca += a ? 1u : 0u;
+      cb += bb ? 1u : 0u;
+      keys[i] = (a ? 1u : 0u) | (bb ? 2u : 0u);
+    }
+    const uint32_t ex2 = block_excl_scan(ca | (cb << 16), &tot, sh.wsum[1]);
+
+    // ascending compaction of this thread's range
+    uint32_t posA = ex2 & 0xffffu, posB = countA + (ex2 >> 16);
+    for (int i = lo; i < hi; ++i) {
+      const uint32_t f = keys[i];
+      if ((f & 1u) && posA < stride) out[posA] = i;
+      if ((f & 2u) && posB < stride) out[posB] = i;
+      posA += f & 1u;
+      posB += (f >> 1) & 1u;
+    }
   }
   if (threadIdx.x == 0) {
     p.counts[sel] = n_forced + k_eff;

@@ -24,7 +24,7 @@ __global__ __launch_bounds__(kSelThreads, 1) void select_decode_kernel(ScorePara
                                                                        DecodeParams p,
                                                                        const int32_t* __restrict__ btab,
                                                                        const int32_t* __restrict__ seq_lens) {
-  extern __shared__ uint32_t keys[];            // [max_pages] keys, then the list [list_stride]
+  extern __shared__ __attribute__((aligned(16))) uint32_t keys[];   // [max_pages] keys, then the list [list_stride]
   __shared__ SelShared sh;
   __shared__ double rpart[refresh_ts<uint16_t, D>() * D];
   const int s = blockIdx.x, b = blockIdx.y;

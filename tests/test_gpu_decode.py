@@ -198,11 +198,13 @@ PATH_EDGES = [1, 9, 64, 65, 511, 512, 513, 1024, 1025, 2047, 2048, 2049, 2600]
 @pytest.mark.parametrize("top_k,crit", [(41, None), (41, 8), (700, None), (700, 300), (0, None)])
 def test_select_list_sizes_across_paths_exact(top_k, crit):
     """Given scores, every list length around the kernel's width switches must
-    give the oracle's lists exactly.  Head 0 draws from a few tied values (two
+    give the oracle's lists exactly (4,096 and 8,192 pages: 8 and 16 keys per
+    thread, read in 16-byte groups).  Head 0 draws from a few tied values (two
     adjacent floats, NaN, both zeros), head 1 from a normal distribution."""
     P, H = 16, 2
-    lens = np.array([P * n - (n % 5) for n in PATH_EDGES], dtype=np.int32)
-    B, max_pages = len(lens), max(PATH_EDGES)
+    edges = PATH_EDGES + [4096, 8192]
+    lens = np.array([P * n - (n % 5) for n in edges], dtype=np.int32)
+    B, max_pages = len(lens), max(edges)
     rng = np.random.default_rng(91)
     vals = np.array([-1.5, -0.0, 0.0, 0.25, np.nextafter(np.float32(0.25), np.float32(1)), 2.0, np.nan],
                     dtype=np.float32)
@@ -218,7 +220,7 @@ def test_select_list_sizes_across_paths_exact(top_k, crit):
                                           scores=torch.from_numpy(scores).to(DEV), critical_k=crit)
     torch.cuda.synchronize()
     npg = [O.n_pages_of(int(L), P) for L in lens]
-    assert npg == PATH_EDGES
+    assert npg == edges
     o_lists, o_counts, o_cc = O.select_pages(scores, npg, sink, window, top_k, crit)
     g_lists, g_counts = npi(lists), npi(counts)
     assert np.array_equal(g_counts, o_counts)
