@@ -177,17 +177,20 @@ __global__ __launch_bounds__(256) void lse_merge_kernel(MergeParams p) {
   for (int d4 = lane; d4 < p.d_v / 4; d4 += 64) {
     f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
     for (int s0 = 0; s0 < p.splits; s0 += 8) {
+      // all 8 loads in flight together: each is unconditional (a split past
+      // the last re-reads the last one), and a split that takes no part adds
+      // +0.0, which leaves acc unchanged (it starts at +0.0 and never becomes
+      // -0.0); an empty split's partial, whatever it holds, is never used
       f32x4 v[8];
 #pragma unroll
       for (int j = 0; j < 8; ++j)
-        v[j] = s0 + j < p.splits ? load_partial4<BF16P>(po, row_off + (size_t)(s0 + j) * p.d_v + 4 * d4)
-                                 : f32x4{0.f, 0.f, 0.f, 0.f};
+        v[j] = load_partial4<BF16P>(po, row_off + (size_t)min(s0 + j, p.splits - 1) * p.d_v + 4 * d4);
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         const float ws = __shfl(w, (s0 + j) & 63, 64);
-        if (s0 + j < p.splits && ws != 0.f) {
-          acc[0] += ws * v[j][0]; acc[1] += ws * v[j][1]; acc[2] += ws * v[j][2]; acc[3] += ws * v[j][3];
-        }
+        const bool use = s0 + j < p.splits && ws != 0.f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[e] += use ? ws * v[j][e] : 0.f;
       }
     }
     const size_t o = (size_t)row * p.d_v + 4 * d4;
