@@ -196,17 +196,23 @@ __global__ __launch_bounds__(256, 1) void mla_decode_kernel(DecodeParams p) {
       for (int i = threadIdx.x; i < kMetaWin && first + i < end; i += 256) {
         const int e = first + i;
         const int lp = list[e];
+        // the block-table entry and the mask words are loaded together,
+        // unconditionally (lp is a page of the sequence, the word index is
+        // clamped), and chosen afterwards: a load under a condition would be
+        // waited for before the next one is issued
+        const int ph = btab[lp];
+        uint32_t wd[4] = {0xffffffffu, 0xffffffffu, 0xffffffffu, 0xffffffffu};
+        if (p.ccounts) {
+          const uint32_t* mrow = p.amask + ((size_t)b * p.max_pages + lp) * p.mask_words;
+#pragma unroll
+          for (int k = 0; k < 4; ++k) wd[k] = mrow[min(word0 + k, p.mask_words - 1)];
+        }
         const int nv = page_valid(seq_len, lp, kMP);
         m_nv[i] = nv;
-        m_phys[i] = nv > 0 ? btab[lp] : 0;
+        m_phys[i] = nv > 0 ? ph : 0;
         const bool ambient = p.ccounts && e >= cc;
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          const int widx = word0 + k;
-          m_word[i][k] = (ambient && widx < p.mask_words)
-                             ? p.amask[((size_t)b * p.max_pages + lp) * p.mask_words + widx]
-                             : 0xffffffffu;
-        }
+        for (int k = 0; k < 4; ++k) m_word[i][k] = (ambient && word0 + k < p.mask_words) ? wd[k] : 0xffffffffu;
       }
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       __syncthreads();
