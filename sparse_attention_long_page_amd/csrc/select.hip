@@ -95,16 +95,25 @@ __global__ __launch_bounds__(kSelThreads) void score_lastsel_kernel(ScoreParams 
       qbar[e] = v;
     }
   } else {
+    // rows 8 at a time, all 8 loads in flight (rows past the end re-read the
+    // last one and add +0.0: the sum starts at +0.0 and never becomes -0.0)
     const T* q = reinterpret_cast<const T*>(sp.q);
     const int rows = sp.per_q ? sp.T : sp.T * sp.G;
     for (int e = threadIdx.x; e < D; e += kSelThreads) {
       double v = 0.0;
-      for (int r = 0; r < rows; ++r) {
-        int t, h;
-        if (sp.per_q) { t = r; h = s; } else { t = r / sp.G; h = s * sp.G + r % sp.G; }
-        const size_t i = (((size_t)b * sp.T + t) * sp.Hq + h) * D + e;
-        if constexpr (sizeof(T) == 2) v += (double)bf16_bits_to_f32(q[i]);
-        else v += (double)q[i];
+      for (int r0 = 0; r0 < rows; r0 += 8) {
+        float w[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int r = min(r0 + j, rows - 1);
+          int t, h;
+          if (sp.per_q) { t = r; h = s; } else { t = r / sp.G; h = s * sp.G + r % sp.G; }
+          const size_t i = (((size_t)b * sp.T + t) * sp.Hq + h) * D + e;
+          if constexpr (sizeof(T) == 2) w[j] = bf16_bits_to_f32(q[i]);
+          else w[j] = q[i];
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j) v += r0 + j < rows ? (double)w[j] : 0.0;
       }
       qbar[e] = v;
     }
@@ -112,13 +121,28 @@ __global__ __launch_bounds__(kSelThreads) void score_lastsel_kernel(ScoreParams 
   __syncthreads();
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int sub = lane & 15, slot = lane >> 4;
+  // A lane whose page needs no row (forced without scores written out, or
+  // past the sequence) reads the row of the block's first page that needs
+  // one, so every load is unconditional (a load under a per-lane condition is
+  // waited for before the next is issued); its score lands only where it is
+  // not used (a forced page's key is 0, a page past the end gets NaN).  A
+  // block with no such page reads nothing.
+  int safe = -1;
+  for (int j = 0; j < kPages && safe < 0; ++j) safe = phys_s[j];
   f32x4 v[kSteps][PL / 4];
+  if (safe >= 0) {
 #pragma unroll
-  for (int it = 0; it < kSteps; ++it) {
-    const int ph = phys_s[wave * 4 * kSteps + it * 4 + slot];
-    const float* m = sp.mu + ((size_t)max(ph, 0) * sp.Hkv + g) * D + 4 * sub;
+    for (int it = 0; it < kSteps; ++it) {
+      const int ph = phys_s[wave * 4 * kSteps + it * 4 + slot];
+      const float* m = sp.mu + ((size_t)(ph >= 0 ? ph : safe) * sp.Hkv + g) * D + 4 * sub;
 #pragma unroll
-    for (int i = 0; i < PL / 4; ++i) v[it][i] = ph >= 0 ? *reinterpret_cast<const f32x4*>(m + 64 * i) : f32x4{};
+      for (int i = 0; i < PL / 4; ++i) v[it][i] = *reinterpret_cast<const f32x4*>(m + 64 * i);
+    }
+  } else {
+#pragma unroll
+    for (int it = 0; it < kSteps; ++it)
+#pragma unroll
+      for (int i = 0; i < PL / 4; ++i) v[it][i] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
   float* out = sp.scores + ((size_t)b * sp.n_sel + s) * sp.max_pages;
 #pragma unroll
@@ -153,9 +177,19 @@ __global__ __launch_bounds__(kSelThreads) void score_lastsel_kernel(ScoreParams 
   __syncthreads();
   if (!last_s) return;
   for (int i = threadIdx.x; i < 512; i += kSelThreads) sh.hist[0][0][i] = 0u;
-  for (int i = threadIdx.x; i < n; i += kSelThreads) {
-    const bool forced = i < L.sink_hi || i >= L.win_lo;
-    keys[i] = forced ? 0u : score_key(__hip_atomic_load(&out[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+  // 8 scores per thread in flight, loaded before any is used (indices past
+  // the end re-read the last score)
+  for (int i0 = threadIdx.x; i0 < n; i0 += 8 * kSelThreads) {
+    float x[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      x[j] = __hip_atomic_load(&out[min(i0 + j * kSelThreads, n - 1)], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int i = i0 + j * kSelThreads;
+      const bool forced = i < L.sink_hi || i >= L.win_lo;
+      if (i < n) keys[i] = forced ? 0u : score_key(x[j]);
+    }
   }
   __syncthreads();
   select_from_keys(p, L, b, s, keys, sh, p.lists + ((size_t)b * p.n_sel + s) * p.list_stride);
