@@ -223,8 +223,9 @@ sa_status sa_sparse_decode(const sa_paged_kv* kv, int32_t batch,
  * Arguments are those of the two calls.  Supported: bf16, a V pool, d_qk ==
  * d_v == 128, page_size 64, q_tokens * group <= 16, and max_pages +
  * list_stride small enough for the keys and the list to sit in LDS (about
- * 2,000 entries); anything else returns SA_ERR_UNSUPPORTED (use the two
- * calls).  Validation and errors as for the two calls.
+ * 6,000 entries: 128K tokens of pages of 64 fit); anything else returns
+ * SA_ERR_UNSUPPORTED (use the two calls).  Validation and errors as for the
+ * two calls.
  * ---------------------------------------------------------------------- */
 sa_status sa_select_decode(const sa_paged_kv* kv, int32_t batch,
                            const void* q, int32_t q_tokens, int32_t n_q_heads,

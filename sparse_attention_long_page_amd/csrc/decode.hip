@@ -56,6 +56,8 @@ __global__ __launch_bounds__(256, 2) void decode_bf16_kernel(DecodeParams p, con
   const int count = counts[sel];
   const int32_t* list = lists + (size_t)sel * p.list_stride;
   const int cc = TIERED ? p.ccounts[sel] : count;
+  __shared__ __attribute__((aligned(16))) uint16_t stg[STAGED ? 4 * 16384 : 8];
+  uint16_t* const stg_area = stg;
 #include "decode_body.inc"
 }
 

@@ -26,7 +26,11 @@ __global__ __launch_bounds__(kSelThreads, 1) void select_decode_kernel(ScorePara
                                                                        const int32_t* __restrict__ seq_lens) {
   extern __shared__ __attribute__((aligned(16))) uint32_t keys[];   // [max_pages] keys, then the list [list_stride]
   __shared__ SelShared sh;
-  __shared__ double rpart[refresh_ts<uint16_t, D>() * D];
+  // the decode's staging areas; before the decode they hold the newest
+  // page's summary partials (refresh), which are dead once the scores are in
+  __shared__ __attribute__((aligned(16))) uint16_t stg[4 * 16384];
+  static_assert(refresh_ts<uint16_t, D>() * D * sizeof(double) <= sizeof(stg), "refresh partials fit");
+  double* rpart = reinterpret_cast<double*>(stg);
   const int s = blockIdx.x, b = blockIdx.y;
   const ListShape L = list_shape(sel, b);
   score_keys_body<uint16_t, D>(sp, sel, L, b, s, keys, sh, rpart);
@@ -50,6 +54,7 @@ __global__ __launch_bounds__(kSelThreads, 1) void select_decode_kernel(ScorePara
     const int g = p.per_q ? s / p.G : s;
     const int R = p.per_q ? p.T : p.T * p.G;
     const int cc = count;
+    uint16_t* const stg_area = stg;
 #include "decode_body.inc"
   }
 }

@@ -535,3 +535,36 @@ def test_select_decode_short_and_empty_sequences(refresh):
                                    o_counts, wl.n_kv_heads, wl.mode, wl.sm_scale)
     compare_outputs(got[2], got[3], ref_o, ref_l)
     assert (got[2][0].float() == 0).all() and torch.isneginf(got[3][0]).all()
+
+
+def test_select_decode_128k_context_equals_two_calls():
+    """A 128K context (2,048 pages per list) through the fused call: the keys
+    and the list fit the LDS beside the staging areas, and the result equals
+    the two calls bit for bit, with the newest-page refresh."""
+    wl = W.LLAMA3_DECODE_32K.replace(name="llama3_decode_128k_two", batch=2, context=131072)
+    inp = W.make_decode_inputs(wl, DEV, seed=15)
+    kv = make_kv(inp, wl)
+    assert kv.max_pages >= 2048
+    mu_a = S.sa_page_summary(kv)
+    mu_b = mu_a.clone()
+    ref = _select_then_decode(kv, inp, wl, mu_a, True)
+    got = S.sa_select_decode(kv, inp["q"], mu_b, sink_pages=wl.sink_pages, window_pages=wl.window_pages,
+                             top_k=wl.top_k, sm_scale=wl.sm_scale, refresh_newest_page=True)
+    torch.cuda.synchronize()
+    _assert_same_step(got, ref)
+    assert torch.equal(mu_a, mu_b)
+
+
+def test_select_decode_rejects_lists_beyond_lds():
+    """max_pages + list_stride past what the LDS holds beside the staging
+    areas: the call fails with SA_ERR_UNSUPPORTED and launches nothing."""
+    wl = W.SMALL["llama3_decode_small"]
+    inp = gpu_inputs(W.make_decode_inputs(wl, "cpu", seed=16))
+    bt = torch.zeros((wl.batch, 8192), dtype=torch.int32, device=DEV)
+    bt[:, :inp["block_table"].shape[1]] = inp["block_table"]
+    kv = S.PagedKV(inp["k_pool"], inp["v_pool"], bt, inp["seq_lens"])
+    mu = S.sa_page_summary(kv)
+    with pytest.raises(S.SparseAttnError) as e:
+        S.sa_select_decode(kv, inp["q"], mu, sink_pages=wl.sink_pages, window_pages=wl.window_pages,
+                           top_k=wl.top_k, sm_scale=wl.sm_scale)
+    assert e.value.status == S.SA_ERR_UNSUPPORTED and "LDS" in str(e.value)
