@@ -86,7 +86,7 @@ __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* total,
 // that bin.  Lane l holds bins 255 - 4l - j, j = 0..3 (higher bins hold
 // larger keys), so a prefix sum over the lanes counts the keys in this lane's
 // bins and all higher ones.
-__device__ __forceinline__ uint32_t find_digit(const uint32_t* h, uint32_t* kk) {
+__device__ __forceinline__ uint32_t find_digit(const uint32_t* h, uint32_t* kk, uint32_t* in_bin) {
   const int lane = threadIdx.x & 63;
   const u32x4 w = *reinterpret_cast<const u32x4*>(h + 252 - 4 * lane);
   const uint32_t c[4] = {w[3], w[2], w[1], w[0]};
@@ -95,7 +95,7 @@ __device__ __forceinline__ uint32_t find_digit(const uint32_t* h, uint32_t* kk) 
   const uint32_t above = incl - mine;            // keys in higher lanes' bins
   const uint32_t k = *kk;
   const bool here = incl >= k && above < k;      // exactly one lane
-  uint32_t bin = 0, rest = 0, acc = above;
+  uint32_t bin = 0, rest = 0, cnt = 0, acc = above;
   bool found = false;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
@@ -103,12 +103,14 @@ __device__ __forceinline__ uint32_t find_digit(const uint32_t* h, uint32_t* kk) 
     if (hit) {
       bin = 255u - 4u * lane - j;
       rest = k - acc;
+      cnt = c[j];
     }
     found |= hit;
     acc += c[j];
   }
   const int src = __builtin_ctzll(__ballot(here));
   *kk = (uint32_t)__builtin_amdgcn_readlane((int)rest, src);
+  *in_bin = (uint32_t)__builtin_amdgcn_readlane((int)cnt, src);
   return (uint32_t)__builtin_amdgcn_readlane((int)bin, src);
 }
 
@@ -147,9 +149,23 @@ __device__ inline void radix_select2(const uint32_t* keys, int n, uint32_t kA, u
     }
     for (int i = n8 + threadIdx.x; i < n; i += kSelThreads) count(keys[i]);
     __syncthreads();
-    preA |= find_digit(hA, &kkA) << shift;
-    if (two) preB |= find_digit(hB, &kkB) << shift;
+    uint32_t cntA = 0, cntB = 0;
+    preA |= find_digit(hA, &kkA, &cntA) << shift;
+    if (two) preB |= find_digit(hB, &kkB, &cntB) << shift;
     pmask |= 255u << shift;
+    // Every key of the chosen bin is needed (and the bin's lowest key is not
+    // 0): the top k are exactly the keys >= that lowest key, so the
+    // threshold is the key just below it, with no ties taken; the remaining
+    // passes are skipped.  (Uniform: the counts come from one lane.)
+    const bool doneA = kkA == cntA && preA != 0u;
+    const bool doneB = !two || (kkB == cntB && preB != 0u);
+    if (shift > 0 && doneA && doneB) {
+      *TA = preA - 1u;
+      *needA = 0u;
+      *TB = two ? preB - 1u : preB;
+      *needB = two ? 0u : kkB;
+      return;
+    }
   }
   *TA = preA;
   *needA = kkA;
