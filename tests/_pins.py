@@ -423,6 +423,56 @@ def check_decode_split_merge():
             assert abs(ml - ref_l[0, 0, h]) < 1e-12
 
 
+def check_decode_latent_sdpa():
+    """Latent cache (no V pool): V is the first d_v dims of each cached row, K the whole row.
+
+    The rope tail of every row is large and distinct, so reading V from any other
+    dims (or K from only the first d_v) moves the output far beyond the tolerance.
+    Checked against torch float64 SDPA on explicitly built V = K[..., :d_v], for
+    Critical-only lists and for tiered lists with a mixed Ambient head mask.
+    """
+    rng = np.random.default_rng(16)
+    B, T, Hq, P, dl, dr = 2, 2, 4, 4, 8, 4
+    d = dl + dr
+    lens = (22, 15)
+    L = max(lens)
+    q = rng.standard_normal((B, T, Hq, d))
+    K = rng.standard_normal((B, 1, L, d))
+    K[..., dl:] = 5.0 + 3.0 * np.arange(dr) + rng.standard_normal((B, 1, L, dr))
+    kp, _, bt = scatter_to_pool(K, K[..., :dl], P, rng, extra_pages=2)
+    scale = 0.2
+    sets = [[{0, 2, 5}], [{1, 3}]]
+    lists, counts = _lists_from(sets, bt.shape[1])
+    lens_a = np.array(lens)
+    # Critical only: every head of the single latent head attends the whole list
+    out, lse = O.sparse_decode(q, kp, None, bt, lens_a, P, lists, counts, 1, O.PER_KV_HEAD, scale, d_v=dl)
+    assert out.shape == (B, T, Hq, dl)
+    for b in range(B):
+        Lb = lens[b]
+        allowed = np.array([(j // P) in sets[b][0] for j in range(Lb)])[None, :].repeat(T, 0)
+        Kd = K[b, 0, :Lb]
+        Vd = np.array(Kd[:, :dl])
+        for h in range(Hq):
+            eo, el = sdpa(q[b, :, h], Kd, Vd, scale, allowed)
+            assert np.allclose(out[b, :, h], eo, atol=1e-12, rtol=1e-10), (b, h)
+            assert np.allclose(lse[b, :, h], el, atol=1e-12, rtol=1e-10), (b, h)
+    # tiered: the first listed page is Critical, the rest Ambient under a mixed head mask
+    cc = np.ones((B, 1), dtype=np.int32)
+    mixed = rng.integers(0, 1 << Hq, size=(B, bt.shape[1], 1)).astype(np.int64)
+    to, tl = O.sparse_decode(q, kp, None, bt, lens_a, P, lists, counts, 1, O.PER_KV_HEAD, scale, cc, mixed,
+                             d_v=dl)
+    for b in range(B):
+        Lb = lens[b]
+        ordered = sorted(sets[b][0])
+        Kd = K[b, 0, :Lb]
+        Vd = np.array(Kd[:, :dl])
+        for h in range(Hq):
+            seen = {ordered[0]} | {p for p in ordered[1:] if (int(mixed[b, p, 0]) >> h) & 1}
+            allowed = np.array([(j // P) in seen for j in range(Lb)])[None, :].repeat(T, 0)
+            eo, el = sdpa(q[b, :, h], Kd, Vd, scale, allowed)
+            assert np.allclose(to[b, :, h], eo, atol=1e-12) and np.allclose(tl[b, :, h], el, atol=1e-12), (b, h)
+
+
 # ------------------------------------------------------------------- a6-a7
 def check_union_bruteforce():
     rng = np.random.default_rng(13)
@@ -516,7 +566,7 @@ ALL_CHECKS = [
     check_select_bruteforce, check_select_golden,
     check_decode_select_all_sdpa, check_decode_masked_sdpa, check_decode_golden,
     check_decode_closed_forms, check_decode_large_logits, check_decode_pool_permutation,
-    check_decode_modes_and_tiers, check_decode_split_merge,
+    check_decode_modes_and_tiers, check_decode_split_merge, check_decode_latent_sdpa,
     check_union_bruteforce, check_union_golden,
     check_prefill_causal_sdpa, check_prefill_masked_sdpa,
 ]

@@ -45,6 +45,22 @@ def _v_not_transposed(k_pool, v_pool, block_table, b, g, pages, seq_len, page_si
                         page_size, d_v)
 
 
+def _latent_v_from_tail(k_pool, v_pool, block_table, b, g, pages, seq_len, page_size, d_v):
+    """Latent cache: take V from the last d_v dims of the row (rope dims included)."""
+    K, V = _orig_gather(k_pool, v_pool, block_table, b, g, pages, seq_len, page_size, d_v)
+    if v_pool is None and K is not None:
+        V = K[:, -d_v:]
+    return K, V
+
+
+def _latent_k_head_only(k_pool, v_pool, block_table, b, g, pages, seq_len, page_size, d_v):
+    """Latent cache: score against the first d_v dims only (rope dims dropped from K)."""
+    K, V = _orig_gather(k_pool, v_pool, block_table, b, g, pages, seq_len, page_size, d_v)
+    if v_pool is None and K is not None:
+        K = np.concatenate([K[:, :d_v], np.zeros_like(K[:, d_v:])], axis=1)
+    return K, V
+
+
 def _logical_as_physical(k_pool, v_pool, block_table, b, g, pages, seq_len, page_size, d_v):
     ident = np.tile(np.arange(block_table.shape[1], dtype=np.int32), (block_table.shape[0], 1))
     return _orig_gather(k_pool, v_pool, ident, b, g, pages, seq_len, page_size, d_v)
@@ -87,6 +103,8 @@ MUTANTS = {
     "no_max_shift": ("softmax_attend", _no_max_shift),
     "v_read_untransposed": ("gather_tokens", _v_not_transposed),
     "logical_page_as_physical": ("gather_tokens", _logical_as_physical),
+    "latent_v_from_tail": ("gather_tokens", _latent_v_from_tail),
+    "latent_k_drops_rope": ("gather_tokens", _latent_k_head_only),
     "ties_to_highest_index": ("rank_candidates", _highest_index_ties),
     "window_off_by_one": ("forced_pages", _window_off_by_one),
     "union_skips_group_heads": ("gqa_union_block_table", _union_first_head_only),
