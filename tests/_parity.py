@@ -47,6 +47,9 @@ def _band_ok(sel, cand, scores, k, band):
     """sel: chosen candidate set of size k; checks the tie-band rule, returns (ok, msg)."""
     if len(sel) != k:
         return False, f"selected {len(sel)} != {k}"
+    stray = set(sel) - set(cand)
+    if stray:
+        return False, f"selected pages {sorted(stray)[:8]} are not candidates"
     if k == 0:
         return True, ""
     ranked = O.rank_candidates(scores, cand)
@@ -92,6 +95,9 @@ def check_page_lists(lists, counts, ccounts, oracle_scores, n_pages, sink, windo
                 seg = [got[:cc], got[cc:]]
             if any(x != sorted(x) for x in seg) or len(set(got)) != len(got):
                 rep.failures.append(f"(b={b}, s={s}) list not ascending/unique: {got}")
+                continue
+            if any(p < 0 or p >= n for p in got):
+                rep.failures.append(f"(b={b}, s={s}) page id outside [0, {n}): {got}")
                 continue
             if not fset.issubset(set(seg[0])):
                 rep.failures.append(f"(b={b}, s={s}) forced pages missing")

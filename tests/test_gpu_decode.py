@@ -92,6 +92,21 @@ MANY_LISTS = {
         name="per_q_summary_many_lists", batch=4, n_q_heads=32, n_kv_heads=8, scores="summary",
         context=16 * 90 + 7, top_k=12, sink_pages=1, window_pages=3, num_splits=2),
 }
+# the one-workgroup-per-list scoring kernel at the other head dims and dtypes
+MANY_LISTS.update({
+    "bf16_d64_many_lists": W.SMALL["bf16_d64_p16_kv_small"].replace(
+        name="bf16_d64_many_lists", batch=32, n_q_heads=16, n_kv_heads=4,
+        seq_lens=tuple(16 * (5 + 7 * i) + (i * 5) % 16 for i in range(32))),
+    "fp32_d64_many_lists": W.SMALL["fp32_d64_p16_q_small"].replace(
+        name="fp32_d64_many_lists", batch=32, seq_lens=tuple(16 * (4 + 3 * i) + i % 16 for i in range(32))),
+    "fp32_d128_many_lists": W.SMALL["fp32_d128_p64_kv_small"].replace(
+        name="fp32_d128_many_lists", batch=64, n_q_heads=8, n_kv_heads=2,
+        seq_lens=tuple(64 * (4 + i % 13) + (i * 11) % 64 for i in range(64))),
+    # 128 sequences over one latent head: 576-d scores, tiered lists
+    "latent_many_lists": W.SMALL["mla_tiered_decode_small"].replace(
+        name="latent_many_lists", batch=128, n_q_heads=16, ambient_heads=4, context=0, top_k=4, critical_k=2,
+        seq_lens=tuple(64 * (1 + i % 9) + (i * 7) % 64 for i in range(128))),
+})
 SELECT_CASES = {**{n: W.SMALL[n] for n in DECODE_SMALL}, **MANY_LISTS}
 
 
@@ -407,22 +422,12 @@ def _full_size_check(wl, seed, n_sample):
     rep = check_page_lists(g_lists, g_counts, g_cc, o_scores, npg, wl.sink_pages, wl.window_pages, wl.top_k,
                            wl.critical_k)
     assert not rep.failures, rep.failures[:5]
-    # attention checked on the oracle's own lists where they equal the GPU's (all units when no band event)
-    o_lists, o_counts, o_cc = O.select_pages(o_scores, npg, wl.sink_pages, wl.window_pages, wl.top_k,
-                                             wl.critical_k)
-    same = np.array([[np.array_equal(g_lists[i, s, :g_counts[i, s]], o_lists[i, s, :o_counts[i, s]])
-                      for s in range(wl.n_sel)] for i in range(len(picks))])
+    # attention: the oracle runs on the GPU's own (accepted) lists, so a tolerated
+    # tie swap is never counted as an attention error and every row is compared
     amask = None if inp["ambient_mask"] is None else npi(inp["ambient_mask"])[picks].astype(np.int64) & 0xffffffff
-    ref_o, ref_l = O.sparse_decode(np64(inp["q"])[picks], kp, vp, bt, lens, wl.page_size, o_lists, o_counts,
-                                   wl.n_kv_heads, wl.mode, wl.sm_scale, o_cc, amask, d_v=wl.d_v)
-    G = wl.group
-    rows_ok = np.zeros(ref_l.shape, dtype=bool)
-    for i in range(len(picks)):
-        for h in range(wl.n_q_heads):
-            s = h // G if wl.mode == "per_kv_head" else h
-            rows_ok[i, :, h] = same[i, s]
-    assert rows_ok.mean() > 0.9
-    return compare_outputs(out[picks], lse[picks], ref_o, ref_l, rows_mask=rows_ok), rep
+    ref_o, ref_l = O.sparse_decode(np64(inp["q"])[picks], kp, vp, bt, lens, wl.page_size, g_lists, g_counts,
+                                   wl.n_kv_heads, wl.mode, wl.sm_scale, g_cc, amask, d_v=wl.d_v)
+    return compare_outputs(out[picks], lse[picks], ref_o, ref_l), rep
 
 
 def test_full_size_llama3_decode_32k_sampled():

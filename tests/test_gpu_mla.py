@@ -54,6 +54,9 @@ CASES = {
     "t1": SMALL.replace(q_tokens=1, n_q_heads=64, ambient_heads=16),
     # four query tokens share each head's tile and Ambient bit
     "t4": SMALL.replace(q_tokens=4, n_q_heads=32, ambient_heads=5),
+    # eight and sixteen query tokens per head (one head's rows fill half or all of a 16-row tile)
+    "t8": SMALL.replace(q_tokens=8, n_q_heads=32, ambient_heads=9),
+    "t16": SMALL.replace(q_tokens=16, n_q_heads=8, ambient_heads=3),
     # 144 heads: a second workgroup row group with only part of its rows valid
     "h144": SMALL.replace(n_q_heads=144, ambient_heads=40, batch=1),
     # no Ambient head at all for some pages' heads; no tiers beyond Critical

@@ -113,19 +113,19 @@ def test_prefill_pool_permutation_invariant_and_deterministic():
 
 def test_full_size_chunked_prefill_128k_sampled():
     """Full-size chunk (2048 queries at 126976 over 129024 KV tokens, 32/8 heads):
-    block tables bit-exact; attention on a seeded sample of (query, head) rows
-    that always includes the first and last Q-block."""
+    block tables bit-exact; attention on every row of the first and last
+    Q-block for all heads, plus 256 seeded random (query, head) rows."""
     wl = W.CHUNKED_PREFILL_128K
     inp = W.make_prefill_inputs(wl, DEV, seed=31)
     out, lse, table, counts = run_gpu(inp, wl)
     tab, cnt = check_tables(table, counts, inp["block_mask"].cpu(), wl.n_kv_heads)
     rng = np.random.default_rng(31)
     rows = set()
+    # every row of the first and the last Q-block, for every head
     for h in range(wl.n_q_heads):
-        for i in (0, 63, wl.q_len - 64, wl.q_len - 1):
-            if h % 4 == i % 4:
-                rows.add((i, h))
-    for i, h in zip(rng.integers(0, wl.q_len, 48), rng.integers(0, wl.n_q_heads, 48)):
+        for i in list(range(0, wl.block_q)) + list(range(wl.q_len - wl.block_q, wl.q_len)):
+            rows.add((i, h))
+    for i, h in zip(rng.integers(0, wl.q_len, 256), rng.integers(0, wl.n_q_heads, 256)):
         rows.add((int(i), int(h)))
     rows = sorted(rows)
     cpu = {k: v.cpu() for k, v in inp.items()}

@@ -186,6 +186,28 @@ SMALL = {
     "mla_tiered_decode_small": MLA_TIERED_DECODE_64K.replace(
         name="mla_tiered_decode_small", batch=2, n_q_heads=32, context=64 * 30 + 5,
         top_k=10, critical_k=3, ambient_heads=8),
+    # every other shape the decode side dispatches: head dim 64 in bf16 at both
+    # page sizes and both selection modes, the staged per-KV-head path on pages
+    # of 16, per-query-head lists on pages of 64, and fp32 caches at d 128
+    "bf16_d64_p16_kv_small": LLAMA3_DECODE_32K.replace(
+        name="bf16_d64_p16_kv_small", batch=2, n_q_heads=8, n_kv_heads=2, d_qk=64, d_v=64, page_size=16,
+        context=0, seq_lens=(16 * 70 + 5, 16 * 33), top_k=9, sink_pages=1, window_pages=3, plant_fraction=0.0,
+        extra_pool_pages=3),
+    "bf16_d64_p64_q_small": LLAMA3_DECODE_32K.replace(
+        name="bf16_d64_p64_q_small", batch=2, n_q_heads=4, n_kv_heads=2, d_qk=64, d_v=64, mode="per_q_head",
+        context=0, seq_lens=(64 * 25 + 7, 64 * 12), top_k=6, sink_pages=1, window_pages=2, plant_fraction=0.0),
+    "bf16_d128_p16_kv_small": LLAMA3_DECODE_32K.replace(
+        name="bf16_d128_p16_kv_small", batch=2, n_q_heads=8, n_kv_heads=2, page_size=16, context=0,
+        seq_lens=(16 * 150 + 9, 16 * 77), top_k=20, sink_pages=1, window_pages=4, plant_fraction=0.0),
+    "bf16_d128_p64_q_small": LLAMA3_DECODE_32K.replace(
+        name="bf16_d128_p64_q_small", batch=2, n_q_heads=4, n_kv_heads=2, mode="per_q_head", context=0,
+        seq_lens=(64 * 30 + 3, 64 * 17), top_k=8, sink_pages=1, window_pages=2, plant_fraction=0.0),
+    "fp32_d128_p64_kv_small": TINY_DECODE.replace(
+        name="fp32_d128_p64_kv_small", batch=2, d_qk=128, d_v=128, page_size=64, context=0,
+        seq_lens=(64 * 20 + 1, 64 * 11), top_k=5, sink_pages=1, window_pages=2),
+    "fp32_d64_p16_q_small": TINY_DECODE.replace(
+        name="fp32_d64_p16_q_small", batch=2, n_q_heads=4, n_kv_heads=2, mode="per_q_head", context=0,
+        seq_lens=(16 * 50 + 3, 16 * 31), top_k=7, sink_pages=1, window_pages=3),
     "chunked_prefill_small": CHUNKED_PREFILL_128K.replace(
         name="chunked_prefill_small", n_q_heads=8, n_kv_heads=2, q_len=200, q_start=1000,
         random_fraction=0.3, extra_pool_pages=3),
