@@ -205,6 +205,34 @@ sa_status sa_sparse_decode(const sa_paged_kv* kv, int32_t batch,
                            void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* ------------------------------------------------------------------------
+ * sa_sparse_decode_noalloc -- sa_sparse_decode for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc): the same arguments, kernels and results
+ * bit for bit, without `workspace`.  The split partials live in a static
+ * device array of SA_NOALLOC_SCRATCH_BYTES inside the library, one copy per
+ * GPU, held from the library's load until the process ends; its address is
+ * looked up once per device, on the first call that needs it with that
+ * device current.  The call allocates nothing (no hipMalloc, hipFree or
+ * allocating library routine).
+ *  - `stream` must belong to the current device.
+ *  - A call whose partials need more than SA_NOALLOC_SCRATCH_BYTES (the size
+ *    sa_sparse_decode_workspace_size reports for the same arguments) returns
+ *    SA_ERR_WORKSPACE_TOO_SMALL and launches nothing; fewer splits need less.
+ *  - Every call on one GPU shares that GPU's array and leaves its partials
+ *    there.  Calls that overlap on one GPU (other streams, or other threads
+ *    without ordering) race on it: the caller must order them.
+ * ---------------------------------------------------------------------- */
+#define SA_NOALLOC_SCRATCH_BYTES (64u << 20)
+
+sa_status sa_sparse_decode_noalloc(const sa_paged_kv* kv, int32_t batch,
+                                   const void* q, int32_t q_tokens, int32_t n_q_heads,
+                                   const int32_t* page_lists, const int32_t* page_counts,
+                                   int32_t list_stride, sa_sel_mode mode,
+                                   const int32_t* critical_counts, const uint32_t* ambient_head_mask,
+                                   float sm_scale, int32_t num_splits,
+                                   void* out, float* out_lse, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
  * sa_select_decode -- the decode step's two calls in one launch: page
  * selection with router scores ([UAE] "The Product", "Content-Dependent
  * Dynamic Routing") and sparse decode over the selected pages ([UAE] "Key

@@ -26,10 +26,11 @@ SA_DTYPE_BF16 = 0
 SA_DTYPE_FP32 = 1
 SA_SEL_PER_KV_HEAD = 0
 SA_SEL_PER_Q_HEAD = 1
+SA_NOALLOC_SCRATCH_BYTES = 64 << 20
 
 EXPORTED = [
     "sa_page_summary", "sa_select_pages_workspace_size", "sa_select_pages",
-    "sa_sparse_decode_workspace_size", "sa_sparse_decode", "sa_select_decode",
+    "sa_sparse_decode_workspace_size", "sa_sparse_decode", "sa_sparse_decode_noalloc", "sa_select_decode",
     "sa_block_sparse_prefill_workspace_size", "sa_block_sparse_prefill",
     "sa_status_string", "sa_last_error_message", "sa_version",
 ]
@@ -73,6 +74,8 @@ def load_library(build_if_missing: bool = True) -> ctypes.CDLL:
         "sa_sparse_decode_workspace_size": (c_size_t, [P, c_int32, c_int32, c_int32, c_int32, c_int, c_int32]),
         "sa_sparse_decode": (c_int, [P, c_int32, P, c_int32, c_int32, P, P, c_int32, c_int, P, P, c_float,
                                      c_int32, P, P, P, c_size_t, P]),
+        "sa_sparse_decode_noalloc": (c_int, [P, c_int32, P, c_int32, c_int32, P, P, c_int32, c_int, P, P, c_float,
+                                             c_int32, P, P, P]),
         "sa_select_decode": (c_int, [P, c_int32, P, c_int32, c_int32, P, c_int32, c_int32, c_int32, c_int32, P,
                                      c_int32, P, c_float, P, P, P]),
         "sa_block_sparse_prefill_workspace_size": (c_size_t, [P, c_int32, c_int32, c_int32]),
@@ -217,6 +220,29 @@ def sa_sparse_decode(kv: PagedKV, q: torch.Tensor, page_lists: torch.Tensor, pag
         kv.ref, B, _ptr(q), T, Hq, _ptr(page_lists), _ptr(page_counts), list_stride, mode,
         _ptr(critical_counts), _ptr(ambient_head_mask), float(sm_scale), num_splits, _ptr(out), _ptr(out_lse),
         _ptr(workspace), workspace.numel(), _stream(kv.device)))
+    return out, out_lse
+
+
+def sa_sparse_decode_noalloc(kv: PagedKV, q: torch.Tensor, page_lists: torch.Tensor, page_counts: torch.Tensor,
+                             *, mode: int, sm_scale: float, critical_counts: Optional[torch.Tensor] = None,
+                             ambient_head_mask: Optional[torch.Tensor] = None, num_splits: int = 0,
+                             out: Optional[torch.Tensor] = None, out_lse: Optional[torch.Tensor] = None,
+                             want_lse: bool = True):
+    """sa_sparse_decode with the split partials in the library's static scratch (no workspace).
+
+    Returns (out, lse).  Outputs the caller does not pass are allocated here by
+    torch; the library call itself allocates nothing.
+    """
+    B, T, Hq, _ = q.shape
+    list_stride = page_lists.shape[-1]
+    if out is None:
+        out = torch.empty((B, T, Hq, kv.d_v), dtype=kv.dtype, device=kv.device)
+    if out_lse is None and want_lse:
+        out_lse = torch.empty((B, T, Hq), dtype=torch.float32, device=kv.device)
+    _check(load_library().sa_sparse_decode_noalloc(
+        kv.ref, B, _ptr(q), T, Hq, _ptr(page_lists), _ptr(page_counts), list_stride, mode,
+        _ptr(critical_counts), _ptr(ambient_head_mask), float(sm_scale), num_splits, _ptr(out), _ptr(out_lse),
+        _stream(kv.device)))
     return out, out_lse
 
 

@@ -9,6 +9,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
 
 #include "../../include/sparse_attn.h"
@@ -326,11 +327,13 @@ size_t sa_sparse_decode_workspace_size(const sa_paged_kv* kv, int32_t batch, int
   return decode_partials_bytes(kv, batch, q_tokens, n_q_heads, splits);
 }
 
-sa_status sa_sparse_decode(const sa_paged_kv* kv, int32_t batch, const void* q, int32_t q_tokens,
-                           int32_t n_q_heads, const int32_t* page_lists, const int32_t* page_counts,
-                           int32_t list_stride, sa_sel_mode mode, const int32_t* critical_counts,
-                           const uint32_t* ambient_head_mask, float sm_scale, int32_t num_splits, void* out,
-                           float* out_lse, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+// Host validation of a decode call; on success `splits` and the workspace
+// bytes it needs are set.  Touches no device memory.
+static sa_status decode_validate(const sa_paged_kv* kv, int32_t batch, const void* q, int32_t q_tokens,
+                                 int32_t n_q_heads, const int32_t* page_lists, const int32_t* page_counts,
+                                 int32_t list_stride, sa_sel_mode mode, const int32_t* critical_counts,
+                                 const uint32_t* ambient_head_mask, float sm_scale, int32_t num_splits, void* out,
+                                 int* splits_out, size_t* need_out) {
   sa_status st = check_kv(kv, true);
   if (st != SA_OK) return st;
   st = check_decode_shape(kv, batch, q_tokens, n_q_heads, mode);
@@ -345,10 +348,18 @@ sa_status sa_sparse_decode(const sa_paged_kv* kv, int32_t batch, const void* q, 
   if (num_splits < 0 || num_splits > 64) return fail(SA_ERR_INVALID_ARGUMENT, "num_splits must be in 0..64");
   const int n_sel = n_sel_of(kv, n_q_heads, mode);
   const int splits = num_splits > 0 ? num_splits : choose_splits(kv, batch, n_sel, list_stride, q_tokens, n_q_heads);
-  const size_t need = decode_partials_bytes(kv, batch, q_tokens, n_q_heads, splits);
-  if (workspace_bytes < need || (need && !workspace))
-    return fail(SA_ERR_WORKSPACE_TOO_SMALL, "workspace %zu < %zu bytes", workspace_bytes, need);
+  *splits_out = splits;
+  *need_out = decode_partials_bytes(kv, batch, q_tokens, n_q_heads, splits);
+  return SA_OK;
+}
 
+// Launches of a validated decode call; `workspace` holds at least the bytes
+// decode_validate reported.
+static sa_status decode_launch(const sa_paged_kv* kv, int32_t batch, const void* q, int32_t q_tokens,
+                               int32_t n_q_heads, const int32_t* page_lists, const int32_t* page_counts,
+                               int32_t list_stride, sa_sel_mode mode, const int32_t* critical_counts,
+                               const uint32_t* ambient_head_mask, float sm_scale, int splits, void* out,
+                               float* out_lse, void* workspace, hipStream_t stream) {
   sa::DecodeParams p{};
   p.q = q;
   p.k_pool = kv->k_pool;
@@ -373,7 +384,7 @@ sa_status sa_sparse_decode(const sa_paged_kv* kv, int32_t batch, const void* q, 
   p.Hq = n_q_heads;
   p.Hkv = kv->n_kv_heads;
   p.G = n_q_heads / kv->n_kv_heads;
-  p.n_sel = n_sel;
+  p.n_sel = n_sel_of(kv, n_q_heads, mode);
   p.per_q = mode == SA_SEL_PER_Q_HEAD;
   p.list_stride = list_stride;
   p.max_pages = kv->max_pages;
@@ -401,6 +412,73 @@ sa_status sa_sparse_decode(const sa_paged_kv* kv, int32_t batch, const void* q, 
     if (e != hipSuccess) return device_status(e, "merge launch");
   }
   return ok();
+}
+
+sa_status sa_sparse_decode(const sa_paged_kv* kv, int32_t batch, const void* q, int32_t q_tokens,
+                           int32_t n_q_heads, const int32_t* page_lists, const int32_t* page_counts,
+                           int32_t list_stride, sa_sel_mode mode, const int32_t* critical_counts,
+                           const uint32_t* ambient_head_mask, float sm_scale, int32_t num_splits, void* out,
+                           float* out_lse, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  int splits = 1;
+  size_t need = 0;
+  sa_status st = decode_validate(kv, batch, q, q_tokens, n_q_heads, page_lists, page_counts, list_stride, mode,
+                                 critical_counts, ambient_head_mask, sm_scale, num_splits, out, &splits, &need);
+  if (st != SA_OK) return st;
+  if (workspace_bytes < need || (need && !workspace))
+    return fail(SA_ERR_WORKSPACE_TOO_SMALL, "workspace %zu < %zu bytes", workspace_bytes, need);
+  return decode_launch(kv, batch, q, q_tokens, n_q_heads, page_lists, page_counts, list_stride, mode,
+                       critical_counts, ambient_head_mask, sm_scale, splits, out, out_lse, workspace, stream);
+}
+
+// ------------------------------------------------- decode without allocation
+// Split partials of sa_sparse_decode_noalloc live in this file-scope device
+// array.  Its name is a host-side stand-in in host code: the device address of
+// each GPU's copy comes from hipGetSymbolAddress (taken once per device, with
+// that device current) and only that address is ever handed to a kernel.
+__device__ __align__(256) unsigned char scratch[SA_NOALLOC_SCRATCH_BYTES];
+
+static constexpr int kMaxScratchDevices = 256;
+static std::mutex g_scratch_mu;
+static void* g_scratch_dev[kMaxScratchDevices];   // device address of `scratch`, per device
+
+static sa_status scratch_for_current_device(void** ptr) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return device_status(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxScratchDevices) return fail(SA_ERR_UNSUPPORTED, "device ordinal %d out of range", dev);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_dev[dev]) {
+    void* addr = nullptr;
+    e = hipGetSymbolAddress(&addr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return device_status(e, "hipGetSymbolAddress(scratch)");
+    if (!addr) return fail(SA_ERR_DEVICE, "hipGetSymbolAddress(scratch) returned NULL");
+    g_scratch_dev[dev] = addr;
+  }
+  *ptr = g_scratch_dev[dev];
+  return SA_OK;
+}
+
+sa_status sa_sparse_decode_noalloc(const sa_paged_kv* kv, int32_t batch, const void* q, int32_t q_tokens,
+                                   int32_t n_q_heads, const int32_t* page_lists, const int32_t* page_counts,
+                                   int32_t list_stride, sa_sel_mode mode, const int32_t* critical_counts,
+                                   const uint32_t* ambient_head_mask, float sm_scale, int32_t num_splits,
+                                   void* out, float* out_lse, hipStream_t stream) {
+  int splits = 1;
+  size_t need = 0;
+  sa_status st = decode_validate(kv, batch, q, q_tokens, n_q_heads, page_lists, page_counts, list_stride, mode,
+                                 critical_counts, ambient_head_mask, sm_scale, num_splits, out, &splits, &need);
+  if (st != SA_OK) return st;
+  if (need > (size_t)SA_NOALLOC_SCRATCH_BYTES)
+    return fail(SA_ERR_WORKSPACE_TOO_SMALL,
+                "%d splits need %zu bytes of partials; the static scratch holds %zu (use fewer splits, or "
+                "sa_sparse_decode with a workspace)", splits, need, (size_t)SA_NOALLOC_SCRATCH_BYTES);
+  void* ws = nullptr;
+  if (need) {
+    st = scratch_for_current_device(&ws);
+    if (st != SA_OK) return st;
+  }
+  return decode_launch(kv, batch, q, q_tokens, n_q_heads, page_lists, page_counts, list_stride, mode,
+                       critical_counts, ambient_head_mask, sm_scale, splits, out, out_lse, ws, stream);
 }
 
 // ---------------------------------------------------------- select + decode

@@ -220,3 +220,43 @@ def test_library_has_no_undefined_kernel_symbols():
     out = subprocess.run([nm, "-D", "--undefined-only", lib._name], capture_output=True, text=True, check=True).stdout
     missing = [line.split()[-1] for line in out.splitlines() if line.split() and line.split()[-1].startswith("_ZN2sa")]
     assert not missing, missing
+
+
+def noalloc(kvd, **over):
+    a = dict(batch=2, q=FAKE, q_tokens=1, n_q_heads=8, lists=FAKE, counts=FAKE, stride=7,
+             mode=B.SA_SEL_PER_KV_HEAD, ccounts=None, amask=None, scale=0.1, splits=1, out=FAKE, lse=None)
+    a.update(over)
+    lib = S.load_library()
+    return lib.sa_sparse_decode_noalloc(ctypes.byref(kvd), a["batch"], a["q"], a["q_tokens"], a["n_q_heads"],
+                                        a["lists"], a["counts"], a["stride"], a["mode"], a["ccounts"], a["amask"],
+                                        a["scale"], a["splits"], a["out"], a["lse"], None)
+
+
+NOALLOC_CASES = [
+    ("rows exceed tile", {}, dict(q_tokens=5), UNS),
+    ("splits out of range", {}, dict(splits=65), INV),
+    ("nan scale", {}, dict(scale=float("nan")), INV),
+    ("missing out", {}, dict(out=None), INV),
+    # 4096 sequences x 32 heads x 32 splits x 128 fp32 dims = 2 GiB of partials
+    ("partials beyond the static scratch", dict(kv=dict(n_kv_heads=8)), dict(batch=4096, n_q_heads=32, splits=32),
+     WS),
+]
+
+
+@pytest.mark.parametrize("name,kvo,argo,status", NOALLOC_CASES, ids=[c[0] for c in NOALLOC_CASES])
+def test_decode_noalloc_rejects(name, kvo, argo, status):
+    """Host-side rejections of the allocation-free decode, before any device
+    call: the same argument checks as sa_sparse_decode, and partials larger
+    than the library's static scratch."""
+    st = noalloc(kv(**kvo.get("kv", {})), **argo)
+    assert st == status, S.load_library().sa_last_error_message()
+    msg = S.load_library().sa_last_error_message().decode()
+    assert msg
+    if status == WS:
+        assert str(B.SA_NOALLOC_SCRATCH_BYTES) in msg
+
+
+def test_noalloc_scratch_limit_matches_header():
+    src = open(HEADER).read()
+    m = re.search(r"#define SA_NOALLOC_SCRATCH_BYTES \((\d+)u << (\d+)\)", src)
+    assert m and int(m.group(1)) << int(m.group(2)) == B.SA_NOALLOC_SCRATCH_BYTES
