@@ -36,8 +36,9 @@
  *    launched.  On error the call returns a non-SA_OK status, enqueues
  *    nothing, writes no output, records a message for sa_last_error_message()
  *    (thread-local) and never aborts.  A launch failure returns SA_ERR_DEVICE.
- *    Device data (page ids, list entries, lengths) is trusted: out-of-range
- *    page ids are undefined behaviour.
+ *    Device data (page ids, list entries, lengths, given scores) is trusted:
+ *    out-of-range page ids are undefined behaviour, unless debug validation
+ *    is on (sa_set_debug_validate below).
  *  - Layout of the paged KV cache (sa_paged_kv), all row-major:
  *      k_pool      [n_phys_pages][n_kv_heads][page_size][d_qk]   (token-major page)
  *      v_pool      [n_phys_pages][n_kv_heads][d_v][page_size]    (page-transposed,
@@ -67,7 +68,8 @@ typedef enum {
   SA_ERR_INVALID_ARGUMENT = 1,
   SA_ERR_UNSUPPORTED = 2,
   SA_ERR_WORKSPACE_TOO_SMALL = 3,
-  SA_ERR_DEVICE = 4
+  SA_ERR_DEVICE = 4,
+  SA_ERR_DATA = 5                /* debug validation found invalid device data */
 } sa_status;
 
 typedef enum { SA_DTYPE_BF16 = 0, SA_DTYPE_FP32 = 1 } sa_dtype;
@@ -291,6 +293,30 @@ sa_status sa_block_sparse_prefill(const sa_paged_kv* kv, int32_t seq,
                                   int32_t* block_table_out, int32_t* block_counts_out,
                                   float sm_scale, void* out, float* out_lse,
                                   void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * sa_set_debug_validate -- opt-in device-side checks of the index data every
+ * call trusts, for callers that must not trust it (the "raise a clear error"
+ * convention of the TileSparse README, "Quick start"; [UAE] "Key Design
+ * Decisions": the cache is read through page tables).
+ *
+ * With validation on, each call first runs check kernels on its stream that
+ * read the device arrays it is about to trust, within their declared shapes,
+ * and never dereference the values they check:
+ *   seq_lens[b] in [0, max_pages * page_size] (all calls, seq for prefill);
+ *   block_table[b][lp] in [0, n_phys_pages) for the sequence's pages (all
+ *     calls that read pages or page summaries);
+ *   page_counts in [0, list_stride], list entries in [0, n_pages(b)),
+ *     critical_counts in [0, page_counts] (decode);
+ *   given scores finite over each sequence's pages (selection).
+ * The call then waits for the checks (it synchronises `stream`, so it cannot
+ * be captured into a graph) and, on the first violation found, returns
+ * SA_ERR_DATA with a message naming the entry, enqueues nothing more and
+ * writes no output.  Off by default; the environment variable
+ * SA_DEBUG_VALIDATE (any value but "0") turns it on at the first call.
+ * Returns the previous setting (0 or 1).  Process-wide.
+ * ---------------------------------------------------------------------- */
+int sa_set_debug_validate(int on);
 
 /* ------------------------------------------------------------------------ utilities */
 const char* sa_status_string(sa_status s);

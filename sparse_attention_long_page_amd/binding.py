@@ -22,6 +22,7 @@ SA_ERR_INVALID_ARGUMENT = 1
 SA_ERR_UNSUPPORTED = 2
 SA_ERR_WORKSPACE_TOO_SMALL = 3
 SA_ERR_DEVICE = 4
+SA_ERR_DATA = 5
 SA_DTYPE_BF16 = 0
 SA_DTYPE_FP32 = 1
 SA_SEL_PER_KV_HEAD = 0
@@ -31,7 +32,7 @@ SA_NOALLOC_SCRATCH_BYTES = 64 << 20
 EXPORTED = [
     "sa_page_summary", "sa_select_pages_workspace_size", "sa_select_pages",
     "sa_sparse_decode_workspace_size", "sa_sparse_decode", "sa_sparse_decode_noalloc", "sa_select_decode",
-    "sa_block_sparse_prefill_workspace_size", "sa_block_sparse_prefill",
+    "sa_block_sparse_prefill_workspace_size", "sa_block_sparse_prefill", "sa_set_debug_validate",
     "sa_status_string", "sa_last_error_message", "sa_version",
 ]
 
@@ -81,6 +82,7 @@ def load_library(build_if_missing: bool = True) -> ctypes.CDLL:
         "sa_block_sparse_prefill_workspace_size": (c_size_t, [P, c_int32, c_int32, c_int32]),
         "sa_block_sparse_prefill": (c_int, [P, c_int32, P, c_int32, c_int32, c_int32, P, c_int32, c_int32, P, P,
                                             c_float, P, P, P, c_size_t, P]),
+        "sa_set_debug_validate": (c_int, [c_int]),
         "sa_status_string": (ctypes.c_char_p, [c_int]),
         "sa_last_error_message": (ctypes.c_char_p, []),
         "sa_version": (c_int, []),
@@ -294,6 +296,11 @@ def sa_block_sparse_prefill(kv: PagedKV, seq: int, q: torch.Tensor, q_start: int
         _ptr(block_counts_out), float(sm_scale), _ptr(out), _ptr(out_lse), _ptr(workspace), workspace.numel(),
         _stream(kv.device)))
     return out, out_lse, block_table_out, block_counts_out
+
+
+def sa_set_debug_validate(on: bool) -> bool:
+    """Turn the library's device-side data checks on or off; returns the previous setting."""
+    return bool(load_library().sa_set_debug_validate(1 if on else 0))
 
 
 def sa_version() -> int:

@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
+#include <cstdlib>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -120,9 +122,93 @@ size_t decode_partials_bytes(const sa_paged_kv* kv, int batch, int q_tokens, int
   return align_up(rows * splits * kv->d_v * partial_elem_bytes(kv)) + align_up(rows * splits * sizeof(float));
 }
 
+// Debug validation: off unless SA_DEBUG_VALIDATE is set in the environment
+// (to anything but "0") or sa_set_debug_validate(1) was called.
+std::atomic<int> g_validate{-1};   // -1: environment not read yet
+
+bool validate_on() {
+  int v = g_validate.load(std::memory_order_relaxed);
+  if (v < 0) {
+    const char* env = std::getenv("SA_DEBUG_VALIDATE");
+    int want = (env && *env && std::strcmp(env, "0") != 0) ? 1 : 0;
+    int expected = -1;
+    g_validate.compare_exchange_strong(expected, want);
+    v = g_validate.load(std::memory_order_relaxed);
+  }
+  return v != 0;
+}
+
+// Runs the device checks of one call on its stream, then waits for them and
+// turns the first violation into SA_ERR_DATA.  Nothing else is enqueued in
+// between, so a call that fails here launches none of its own kernels.
+struct Validator {
+  hipStream_t stream;
+  uint32_t* res = nullptr;
+  hipError_t err = hipSuccess;
+
+  explicit Validator(hipStream_t s) : stream(s) {
+    err = sa::validate_result_ptr(&res);
+    if (err == hipSuccess) err = sa::launch_validate_clear(res, stream);
+  }
+  void kv(const sa_paged_kv* kv, int seq0, int batch, bool block_table = true) {
+    if (err != hipSuccess) return;
+    sa::ValidateKV v{block_table ? kv->block_table : nullptr, kv->seq_lens, seq0, kv->max_pages, kv->page_size,
+                     kv->n_phys_pages};
+    err = sa::launch_validate_kv(v, batch, res, stream);
+  }
+  void lists(const sa_paged_kv* kv, int batch, int n_sel, const int32_t* lists, const int32_t* counts,
+             const int32_t* ccounts, int stride) {
+    if (err != hipSuccess) return;
+    sa::ValidateLists v{lists, counts, ccounts, kv->seq_lens, n_sel, stride, kv->page_size};
+    err = sa::launch_validate_lists(v, batch, res, stream);
+  }
+  void scores(const sa_paged_kv* kv, int batch, int n_sel, const float* scores, int stride) {
+    if (err != hipSuccess) return;
+    sa::ValidateScores v{scores, kv->seq_lens, n_sel, stride, kv->page_size, kv->max_pages};
+    err = sa::launch_validate_scores(v, batch, res, stream);
+  }
+  sa_status finish(const sa_paged_kv* kv, int list_stride) {
+    uint32_t h[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    if (err == hipSuccess) err = hipMemcpyAsync(h, res, sizeof(h), hipMemcpyDeviceToHost, stream);
+    if (err == hipSuccess) err = hipStreamSynchronize(stream);
+    if (err != hipSuccess) return device_status(err, "debug validation");
+    const int v = (int)h[4];
+    switch (h[0]) {
+      case 0: return SA_OK;
+      case sa::kValSeqLen:
+        return fail(SA_ERR_DATA, "seq_lens[%u] = %d outside [0, max_pages * page_size = %ld]", h[1], v,
+                    (long)kv->max_pages * kv->page_size);
+      case sa::kValBlockTable:
+        return fail(SA_ERR_DATA, "block_table[%u][%u] = %d outside [0, n_phys_pages = %d)", h[1], h[2], v,
+                    kv->n_phys_pages);
+      case sa::kValCount:
+        return fail(SA_ERR_DATA, "page_counts[%u][%u] = %d outside [0, list_stride = %d]", h[1], h[2], v,
+                    list_stride);
+      case sa::kValListEntry:
+        return fail(SA_ERR_DATA, "page_lists[%u][%u][%u] = %d is not a page of sequence %u", h[1], h[2], h[3], v,
+                    h[1]);
+      case sa::kValCriticalCount:
+        return fail(SA_ERR_DATA, "critical_counts[%u][%u] = %d outside [0, page_counts[%u][%u]]", h[1], h[2], v,
+                    h[1], h[2]);
+      case sa::kValScore: {
+        float x;
+        std::memcpy(&x, &h[4], sizeof(x));
+        return fail(SA_ERR_DATA, "scores[%u][%u][%u] = %g is not finite", h[1], h[2], h[3], (double)x);
+      }
+    }
+    return fail(SA_ERR_DATA, "debug validation reported code %u", h[0]);
+  }
+};
+
 }  // namespace
 
 extern "C" {
+
+int sa_set_debug_validate(int on) {
+  const int prev = validate_on() ? 1 : 0;
+  g_validate.store(on ? 1 : 0, std::memory_order_relaxed);
+  return prev;
+}
 
 const char* sa_status_string(sa_status s) {
   switch (s) {
@@ -131,6 +217,7 @@ const char* sa_status_string(sa_status s) {
     case SA_ERR_UNSUPPORTED: return "SA_ERR_UNSUPPORTED";
     case SA_ERR_WORKSPACE_TOO_SMALL: return "SA_ERR_WORKSPACE_TOO_SMALL";
     case SA_ERR_DEVICE: return "SA_ERR_DEVICE";
+    case SA_ERR_DATA: return "SA_ERR_DATA";
   }
   return "SA_ERR_UNKNOWN";
 }
@@ -157,6 +244,12 @@ sa_status sa_page_summary(const sa_paged_kv* kv, int32_t batch, int32_t last_pag
   p.d = kv->d_qk;
   p.max_pages = kv->max_pages;
   p.last_pages = std::min(last_pages, kv->max_pages);
+  if (validate_on()) {
+    Validator v(stream);
+    v.kv(kv, 0, batch);
+    st = v.finish(kv, 0);
+    if (st != SA_OK) return st;
+  }
   return device_status(sa::launch_page_summary(p, batch, kv->dtype == SA_DTYPE_BF16, stream), "page_summary launch");
 }
 
@@ -219,6 +312,14 @@ sa_status sa_select_pages(const sa_paged_kv* kv, int32_t batch, const void* q, i
   sp.top_k = top_k;
   sp.critical_k = critical_k;
   sp.tiered = critical_counts != nullptr;
+
+  if (validate_on()) {
+    Validator v(stream);
+    v.kv(kv, 0, batch, scores == nullptr);   // given scores: the block table is not read
+    if (scores) v.scores(kv, batch, n_sel, scores, scores_stride);
+    st = v.finish(kv, list_stride);
+    if (st != SA_OK) return st;
+  }
 
   const int pooled_rows = mode == SA_SEL_PER_KV_HEAD ? q_tokens * (n_q_heads / kv->n_kv_heads) : q_tokens;
   if (!scores && batch * n_sel >= 128 && pooled_rows <= sa::kScoreInlineRows) {
@@ -311,6 +412,7 @@ static sa_status check_decode_shape(const sa_paged_kv* kv, int32_t batch, int32_
     if (16 % q_tokens != 0)
       return fail(SA_ERR_UNSUPPORTED, "latent decode needs q_tokens in {1, 2, 4, 8, 16}, got %d", q_tokens);
     if (kv->page_size != 64) return fail(SA_ERR_UNSUPPORTED, "latent decode needs page_size 64");
+    if (n_q_heads > 256) return fail(SA_ERR_UNSUPPORTED, "latent decode supports up to 256 query heads");
   } else if (kv->dtype == SA_DTYPE_BF16) {
     const int rows = mode == SA_SEL_PER_KV_HEAD ? q_tokens * G : q_tokens;
     if (rows > 16)
@@ -351,6 +453,18 @@ static sa_status decode_validate(const sa_paged_kv* kv, int32_t batch, const voi
   *splits_out = splits;
   *need_out = decode_partials_bytes(kv, batch, q_tokens, n_q_heads, splits);
   return SA_OK;
+}
+
+// Debug validation of a decode call's device data (lengths, block table,
+// counts, list entries, critical counts).
+static sa_status decode_check_device(const sa_paged_kv* kv, int32_t batch, int32_t n_q_heads, sa_sel_mode mode,
+                                     const int32_t* page_lists, const int32_t* page_counts, int32_t list_stride,
+                                     const int32_t* critical_counts, hipStream_t stream) {
+  if (!validate_on()) return SA_OK;
+  Validator v(stream);
+  v.kv(kv, 0, batch);
+  v.lists(kv, batch, n_sel_of(kv, n_q_heads, mode), page_lists, page_counts, critical_counts, list_stride);
+  return v.finish(kv, list_stride);
 }
 
 // Launches of a validated decode call; `workspace` holds at least the bytes
@@ -426,6 +540,8 @@ sa_status sa_sparse_decode(const sa_paged_kv* kv, int32_t batch, const void* q, 
   if (st != SA_OK) return st;
   if (workspace_bytes < need || (need && !workspace))
     return fail(SA_ERR_WORKSPACE_TOO_SMALL, "workspace %zu < %zu bytes", workspace_bytes, need);
+  st = decode_check_device(kv, batch, n_q_heads, mode, page_lists, page_counts, list_stride, critical_counts, stream);
+  if (st != SA_OK) return st;
   return decode_launch(kv, batch, q, q_tokens, n_q_heads, page_lists, page_counts, list_stride, mode,
                        critical_counts, ambient_head_mask, sm_scale, splits, out, out_lse, workspace, stream);
 }
@@ -472,6 +588,8 @@ sa_status sa_sparse_decode_noalloc(const sa_paged_kv* kv, int32_t batch, const v
     return fail(SA_ERR_WORKSPACE_TOO_SMALL,
                 "%d splits need %zu bytes of partials; the static scratch holds %zu (use fewer splits, or "
                 "sa_sparse_decode with a workspace)", splits, need, (size_t)SA_NOALLOC_SCRATCH_BYTES);
+  st = decode_check_device(kv, batch, n_q_heads, mode, page_lists, page_counts, list_stride, critical_counts, stream);
+  if (st != SA_OK) return st;
   void* ws = nullptr;
   if (need) {
     st = scratch_for_current_device(&ws);
@@ -570,6 +688,12 @@ sa_status sa_select_decode(const sa_paged_kv* kv, int32_t batch, const void* q, 
   dp.d_v = kv->d_v;
   dp.splits = 1;
   dp.scale_log2 = sm_scale * sa::kLog2e;
+  if (validate_on()) {
+    Validator v(stream);
+    v.kv(kv, 0, batch);
+    st = v.finish(kv, list_stride);
+    if (st != SA_OK) return st;
+  }
   return device_status(sa::launch_select_decode(sp, p, dp, batch, stream), "select+decode launch");
 }
 
@@ -607,6 +731,13 @@ sa_status sa_block_sparse_prefill(const sa_paged_kv* kv, int32_t seq, const void
     return fail(SA_ERR_INVALID_ARGUMENT, "sm_scale must be finite and positive");
   const int G = n_q_heads / kv->n_kv_heads;
   if (G > 8) return fail(SA_ERR_UNSUPPORTED, "prefill supports up to 8 query heads per KV head");
+
+  if (validate_on()) {
+    Validator v(stream);
+    v.kv(kv, seq, 1);
+    st = v.finish(kv, 0);
+    if (st != SA_OK) return st;
+  }
 
   sa::UnionParams up{};
   up.mask = block_mask;

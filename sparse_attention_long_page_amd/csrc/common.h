@@ -62,6 +62,16 @@ __device__ __forceinline__ float sum_over_row_groups(float x) {
   return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
+// Word 3 of a raw buffer resource on gfx950 (32-bit data format, no swizzle,
+// offsets bounds-checked against the record count).
+constexpr uint32_t kBufferRsrcWord3 = 0x00020000u;
+
+// A shared-memory pointer as the LDS address-space pointer that the
+// buffer-load-to-LDS builtins take.
+__device__ __forceinline__ __attribute__((address_space(3))) void* lds_ptr(const void* p) {
+  return (__attribute__((address_space(3))) void*)(const_cast<void*>(p));
+}
+
 // Number of valid tokens of logical page `lp` in a sequence of `len` tokens.
 __device__ __forceinline__ int page_valid(int len, int lp, int P) {
   int r = len - lp * P;
@@ -170,6 +180,39 @@ hipError_t launch_select_prep(const SummaryParams& smp, const ScoreParams& sp, i
                               uint32_t* arrivals, hipStream_t s);
 hipError_t launch_score_lastsel(const ScoreParams& sp, const SelectParams& p, int bf16, const double* qpart,
                                 uint32_t* arrivals, hipStream_t s);
+// Device-side data checks (debug validation mode).  Violation codes:
+constexpr uint32_t kValSeqLen = 1;         // seq_lens[b] outside [0, max_pages * page_size]
+constexpr uint32_t kValBlockTable = 2;     // block_table[b][lp] outside [0, n_phys_pages)
+constexpr uint32_t kValCount = 3;          // page_counts[b][s] outside [0, list_stride]
+constexpr uint32_t kValListEntry = 4;      // page_lists[b][s][e] outside [0, n_pages(b))
+constexpr uint32_t kValCriticalCount = 5;  // critical_counts[b][s] outside [0, page_counts[b][s]]
+constexpr uint32_t kValScore = 6;          // a given score that is not finite
+
+struct ValidateKV {
+  const int32_t* block_table;  // null: only the lengths are checked
+  const int32_t* seq_lens;
+  int seq0, max_pages, P, n_phys;
+};
+
+struct ValidateLists {
+  const int32_t* lists;
+  const int32_t* counts;
+  const int32_t* ccounts;    // or null
+  const int32_t* seq_lens;
+  int n_sel, stride, P;
+};
+
+struct ValidateScores {
+  const float* scores;
+  const int32_t* seq_lens;
+  int n_sel, stride, P, max_pages;
+};
+
+hipError_t validate_result_ptr(uint32_t** ptr);
+hipError_t launch_validate_clear(uint32_t* res, hipStream_t s);
+hipError_t launch_validate_kv(const ValidateKV& v, int batch, uint32_t* res, hipStream_t s);
+hipError_t launch_validate_lists(const ValidateLists& v, int batch, uint32_t* res, hipStream_t s);
+hipError_t launch_validate_scores(const ValidateScores& v, int batch, uint32_t* res, hipStream_t s);
 hipError_t launch_decode(const DecodeParams& p, int bf16, hipStream_t s);
 hipError_t launch_merge(const MergeParams& p, hipStream_t s);
 hipError_t launch_mla_decode(const DecodeParams& p, hipStream_t s);

@@ -12,10 +12,18 @@
 // first 512 dims of the same row; pages of 64 tokens; rows = (head, token).
 //
 // Design (bf16 in, fp32 accumulate):
-//  * workgroup = (sequence, group of 128 query rows, split of the page list),
-//    4 waves of 32 rows (two 16-row MFMA column tiles) each; a row tile holds
-//    16/T heads x T query tokens, so both MTP tokens of a head share a tile
-//    and the head's Ambient bit;
+//  * workgroup = (sequence, row group, split of the page list), 4 waves of two
+//    16-row MFMA column tiles each; a tile holds 16/T heads x T query tokens,
+//    so the MTP tokens of a head share a tile and the head's Ambient bit;
+//  * a split takes a contiguous chunk of the Critical segment and a contiguous
+//    chunk of the Ambient segment of the list (chunk sizes differ by at most
+//    one), so every split holds a few Ambient pages;
+//  * the Ambient tier saves compute: every workgroup of a (sequence, split)
+//    ranks the sequence's heads by their membership pattern over the split's
+//    Ambient pages (heads attending the same pages become neighbours), and
+//    deals the ranked heads out in tiles; a tile computes an Ambient page only
+//    if one of its heads attends it, so each Ambient page runs on few tiles
+//    instead of on every tile with a member head somewhere;
 //  * each page's 64 x 576 K tile is copied once into LDS by the LDS-DMA path
 //    (global_load_lds_dwordx4, no registers), double-buffered: the copy of the
 //    next page runs while the current one is computed; rows are padded to
@@ -23,17 +31,18 @@
 //    spread over the banks;
 //  * S^T = K Q^T on v_mfma_f32_16x16x32_bf16 with Q^T resident in registers
 //    (576 dims x 32 rows); the S^T fragments are the P^T operand of the PV
-//    product directly; V^T operands (8 tokens of one dim) are gathered from
-//    the token-major tile with 2-byte LDS reads;
-//  * rows whose head is not in an Ambient page's head set see that page as
-//    masked (-inf); a page none of the wave's rows attends is skipped;
+//    product directly; V^T operands (8 tokens of one dim) come from the
+//    token-major tile with transposing LDS reads;
+//  * rows of an active tile whose head is not in an Ambient page's head set
+//    see that page as masked (-inf);
 //  * softmax in base 2 against a per-row reference maximum fixed at the first
 //    page the row attends; the accumulators are never rescaled (a rescale of
 //    256 accumulation registers per wave would cost as much VALU time as the
 //    page's MFMAs).  Logits may exceed the reference by up to 2^64 before a
 //    workgroup falls back to an exact-maximum pass and a recompute;
-//  * fp32 partials (o_s, lse_s) per split go to the workspace and are merged
-//    by the LSE-merge kernel; with one split the output is written directly.
+//  * bf16 partials (o_s) and fp32 lse_s per split go to the workspace and are
+//    merged by the LSE-merge kernel; with one split the output is written
+//    directly.
 #include "common.h"
 
 namespace sa {
@@ -48,7 +57,8 @@ constexpr int kMInstr = kMP * kMRowChunks / 64;   // 73 wave-wide 16-byte DMA lo
 constexpr int kMKSteps = kMD / 32;       // 18
 constexpr int kMHalfInstr = 37;          // copy instructions covering rows 0-31 (37 * 64 >= 32 * 73)
 constexpr int kMDTiles = kMDV / 16;      // 32
-constexpr int kMetaWin = 256;            // pages of page metadata held in LDS
+constexpr int kMetaWin = 128;            // pages of page metadata held in LDS
+constexpr int kMaxMaskWords = 8;         // Ambient head-mask words per page (n_q_heads <= 256)
 constexpr float kMMargin = 64.0f;         // log2 units a logit may exceed its row's reference
 
 // Token of row m (0..15) of the 16-token MFMA tile j4 of a page.  Rows
@@ -73,21 +83,32 @@ __device__ __forceinline__ lds_v4i16* lds_v4(const uint16_t* p) {
   return (lds_v4i16*)(const_cast<uint16_t*>(p));
 }
 
+// Chunk s of [0, n) cut into S contiguous chunks whose sizes differ by at most one.
+__device__ __forceinline__ void split_chunk(int n, int S, int s, int& lo, int& hi) {
+  const int base = n / S, extra = n % S;
+  lo = s * base + min(s, extra);
+  hi = lo + base + (s < extra ? 1 : 0);
+}
+
 __global__ __launch_bounds__(256, 1) void mla_decode_kernel(DecodeParams p) {
   // two page buffers as distinct LDS objects, so the wait-count pass can
   // tell an LDS-DMA into one from reads of the other
   __shared__ __attribute__((aligned(16))) uint16_t sk0[kMTile];
   __shared__ __attribute__((aligned(16))) uint16_t sk1[kMTile];
   // metadata of a window of the split's pages: physical page, valid tokens,
-  // and the Ambient head-mask words covering this workgroup's heads
+  // and the page's Ambient head-mask words (all ones for a Critical page)
   __shared__ int m_phys[kMetaWin], m_nv[kMetaWin];
-  __shared__ uint32_t m_word[kMetaWin][4];
+  __shared__ uint32_t m_word[kMetaWin][kMaxMaskWords];
+  // heads ranked by their Ambient membership pattern over the split
+  __shared__ __attribute__((aligned(16))) uint32_t h_key[256];
+  __shared__ uint16_t h_rank[256];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform per wave
   const int col = lane & 15, kg = lane >> 4;
   const int T = p.T;
-  const int heads_per_wg = 128 / T, heads_per_tile = 16 / T;
-  const int n_rg = (p.Hq + heads_per_wg - 1) / heads_per_wg;
+  const int hpt = 16 / T;                                // heads per 16-row tile
+  const int n_tiles = (p.Hq + hpt - 1) / hpt;
+  const int n_rg = (n_tiles + 7) / 8;                    // 8 tiles per workgroup
 
   // XCD-aware order: consecutive logical ids (the row groups of one
   // (sequence, split), which stream the same pages) share an XCD and its L2.
@@ -100,28 +121,121 @@ __global__ __launch_bounds__(256, 1) void mla_decode_kernel(DecodeParams p) {
 
   const int sel = b;                       // one latent KV head: one list per sequence
   const int count = p.counts[sel];
-  const int cc = p.ccounts ? p.ccounts[sel] : count;
+  const int cc = p.ccounts ? min(p.ccounts[sel], count) : count;
   const int32_t* list = p.lists + (size_t)sel * p.list_stride;
   const int32_t* btab = p.block_table + (size_t)b * p.max_pages;
-  const int sbase = count / p.splits, sextra = count % p.splits;
-  const int beg = split * sbase + min(split, sextra);
-  const int end = beg + sbase + (split < sextra ? 1 : 0);
+  // this split's pages: chunk `split` of the Critical segment, then chunk
+  // `split` of the Ambient segment
+  int cb, ce, ab, ae;
+  split_chunk(cc, p.splits, split, cb, ce);
+  split_chunk(count - cc, p.splits, split, ab, ae);
+  ab += cc;
+  ae += cc;
+  const int n_crit = ce - cb;
+  const int n_pg = n_crit + (ae - ab);
   const int seq_len = p.seq_lens[b];
 
-  // this lane's query row in each of the wave's two row tiles; a tile's
-  // 16/T heads lie in one 32-bit word of the Ambient head mask
-  int h_row[2], t_row[2], tile_word[2];
+  const uint16_t* kpool = reinterpret_cast<const uint16_t*>(p.k_pool);
+
+  // The copies are buffer loads to LDS over a resource spanning the page
+  // (lanes past it would read 0): as buffer instructions they count on the
+  // vector-memory counter only, so the compiler keeps its partial waits on
+  // the LDS reads of the page being computed while a copy is in flight (with
+  // the global-load form it waits for every LDS read at once).
+  auto stage = [&](uint16_t* buf, int phys, int i_lo, int i_hi) {
+    const uint16_t* src = kpool + (size_t)phys * p.Hkv * kMP * kMD;
+    const __amdgpu_buffer_rsrc_t rsrc =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(src), 0, kMP * kMD * 2, kBufferRsrcWord3);
+    for (int i = i_lo + ((wave - i_lo) & 3); i < i_hi; i += 4) {
+      const int c = 64 * i + lane;
+      const int r = c / kMRowChunks, ch = c % kMRowChunks;
+      const int sch = ch < kMRowChunks - 1 ? ch : 0;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, lds_ptr(buf + i * 512), 16, (r * kMD + 8 * sch) * 2, 0, 0, 0);
+    }
+  };
+
+  // page metadata for pages [w0, w0 + kMetaWin) of the split, read into LDS
+  // while no page copy is in flight (global loads complete in issue order)
+  int w0 = 0;
+  auto load_meta = [&](int first) {
+    for (int i = threadIdx.x; i < kMetaWin && first + i < n_pg; i += 256) {
+      const int k = first + i;
+      const int e = k < n_crit ? cb + k : ab + (k - n_crit);
+      const int lp = list[e];
+      // the block-table entry and the mask words are loaded together,
+      // unconditionally (lp is a page of the sequence, the word index is
+      // clamped), and chosen afterwards: a load under a condition would be
+      // waited for before the next one is issued
+      const int ph = btab[lp];
+      uint32_t wd[kMaxMaskWords];
+#pragma unroll
+      for (int j = 0; j < kMaxMaskWords; ++j) wd[j] = 0xffffffffu;
+      if (p.ccounts) {
+        const uint32_t* mrow = p.amask + ((size_t)b * p.max_pages + lp) * p.mask_words;
+#pragma unroll
+        for (int j = 0; j < kMaxMaskWords; ++j) wd[j] = mrow[min(j, p.mask_words - 1)];
+      }
+      const int nv = page_valid(seq_len, lp, kMP);
+      m_nv[i] = nv;
+      m_phys[i] = nv > 0 ? ph : 0;
+      const bool ambient = k >= n_crit;
+#pragma unroll
+      for (int j = 0; j < kMaxMaskWords; ++j) m_word[i][j] = ambient ? wd[j] : 0xffffffffu;
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+  };
+  load_meta(0);
+
+  // Rank the heads: key bit j = the head attends Ambient page j of the split
+  // (first 32 held in the first window); ranked by (key, head index), so the
+  // ranking is the same in every workgroup of the (sequence, split).  Slots
+  // past the last head hold the largest key and never count.
+  const bool ranked = p.ccounts != nullptr;
+  if (ranked) {
+    const int na = min(min(n_pg - n_crit, 32), kMetaWin - n_crit);
+    for (int h = threadIdx.x; h < 256; h += 256) {
+      uint32_t key = 0xffffffffu;
+      if (h < p.Hq) {
+        key = 0;
+        for (int j = 0; j < na; ++j) key |= ((m_word[n_crit + j][h >> 5] >> (h & 31)) & 1u) << j;
+      }
+      h_key[h] = key;
+    }
+    __syncthreads();
+    const uint4* keys4 = reinterpret_cast<const uint4*>(h_key);
+    const int n4 = (p.Hq + 3) >> 2;
+    for (int h = threadIdx.x; h < p.Hq; h += 256) {
+      const uint32_t kh = h_key[h];
+      int r = 0;
+#pragma unroll 8
+      for (int i = 0; i < n4; ++i) {
+        const uint4 v = keys4[i];
+        const int hb = 4 * i;
+        r += (v.x < kh || (v.x == kh && hb < h)) ? 1 : 0;
+        r += (v.y < kh || (v.y == kh && hb + 1 < h)) ? 1 : 0;
+        r += (v.z < kh || (v.z == kh && hb + 2 < h)) ? 1 : 0;
+        r += (v.w < kh || (v.w == kh && hb + 3 < h)) ? 1 : 0;
+      }
+      h_rank[r] = (uint16_t)h;
+    }
+    __syncthreads();
+  }
+
+  // This lane's query row in each of the wave's two row tiles.  Ranked tile
+  // t (heads of ranks t*hpt ..) goes to row group, wave and slot in a snake
+  // order, so every wave gets a mix of rarely and often attending tiles.
+  int h_row[2], t_row[2];
   bool row_ok[2];
 #pragma unroll
   for (int rt = 0; rt < 2; ++rt) {
-    const int tile_h0 = rg * heads_per_wg + wave * 2 * heads_per_tile + rt * heads_per_tile;
-    tile_word[rt] = tile_h0 >> 5;
-    h_row[rt] = tile_h0 + col / T;
+    const int j = rt * 4 + (rt ? 3 - wave : wave);
+    const int t = j * n_rg + ((j & 1) ? n_rg - 1 - rg : rg);
+    const int pos = t * hpt + col / T;
+    row_ok[rt] = t < n_tiles && pos < p.Hq;
+    h_row[rt] = row_ok[rt] ? (ranked ? (int)h_rank[pos] : pos) : 0;
     t_row[rt] = col % T;
-    row_ok[rt] = h_row[rt] < p.Hq;
   }
-  const bool wave_rows = rg * heads_per_wg + wave * 2 * heads_per_tile < p.Hq;   // uniform
-  const int word0 = (rg * heads_per_wg) >> 5;      // the workgroup's heads span words word0 .. word0+3
 
   // Q^T operand, resident: tile rt, k-step kk -> row col, dims 8*kg + 32*kk .. +8
   const uint16_t* qp = reinterpret_cast<const uint16_t*>(p.q);
@@ -144,22 +258,10 @@ __global__ __launch_bounds__(256, 1) void mla_decode_kernel(DecodeParams p) {
     for (int rt = 0; rt < 2; ++rt) oacc[dt][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m_ref[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.f, 0.f};
 
-  const uint16_t* kpool = reinterpret_cast<const uint16_t*>(p.k_pool);
-
   // LDS-DMA copy of one page's K tile: wave-wide instruction i covers LDS
   // chunks [64 i, 64 i + 64); chunk c is row c / 73, 16-byte column c % 73
   // (column 72 is row padding and re-reads column 0 of the row).  Wave w
   // issues the instructions i = w mod 4 of [i_lo, i_hi).
-  auto stage = [&](uint16_t* buf, int phys, int i_lo, int i_hi) {
-    const uint16_t* src = kpool + (size_t)phys * p.Hkv * kMP * kMD;
-    for (int i = i_lo + ((wave - i_lo) & 3); i < i_hi; i += 4) {
-      const int c = 64 * i + lane;
-      const int r = c / kMRowChunks, ch = c % kMRowChunks;
-      const int sch = ch < kMRowChunks - 1 ? ch : 0;
-      __builtin_amdgcn_global_load_lds(src + (size_t)r * kMD + 8 * sch, buf + i * 512, 16, 0, 0);
-    }
-  };
-
   // Pass structure.  Attempt 0 sets each row's reference maximum from the
   // first page it attends and never moves it: later logits may exceed it by
   // up to 2^64 (exp2 stays finite in fp32), so the accumulators are never
@@ -168,10 +270,10 @@ __global__ __launch_bounds__(256, 1) void mla_decode_kernel(DecodeParams p) {
   // recomputes with that fixed reference.  Inputs with ordinary logit ranges
   // take attempt 0 only.
   //
-  // Within a page, every global load the page needs (list entry, block
-  // table, head-mask words) is issued and consumed before the next page's
-  // LDS-DMA is issued: completions are counted in issue order, so a wait for
-  // a later load would also wait for the whole copy.
+  // Within a page, every global load the page needs is issued and consumed
+  // before the next page's LDS-DMA is issued: completions are counted in
+  // issue order, so a wait for a later load would also wait for the whole
+  // copy.  The page metadata comes from LDS.
   bool overflow = false;
   for (int attempt = 0; attempt < 3; ++attempt) {
     if (attempt == 1) {
@@ -187,49 +289,26 @@ __global__ __launch_bounds__(256, 1) void mla_decode_kernel(DecodeParams p) {
       for (int rt = 0; rt < 2; ++rt) l_run[rt] = 0.f;
     }
     const bool do_pv = attempt != 1;
-
-    // metadata of the page being computed (cur_*) and of the next one
-    // page metadata for pages [w0, w0 + kMetaWin) of the split, read into LDS
-    // while no page copy is in flight (global loads complete in issue order)
-    int w0 = beg;
-    auto load_meta = [&](int first) {
-      for (int i = threadIdx.x; i < kMetaWin && first + i < end; i += 256) {
-        const int e = first + i;
-        const int lp = list[e];
-        // the block-table entry and the mask words are loaded together,
-        // unconditionally (lp is a page of the sequence, the word index is
-        // clamped), and chosen afterwards: a load under a condition would be
-        // waited for before the next one is issued
-        const int ph = btab[lp];
-        uint32_t wd[4] = {0xffffffffu, 0xffffffffu, 0xffffffffu, 0xffffffffu};
-        if (p.ccounts) {
-          const uint32_t* mrow = p.amask + ((size_t)b * p.max_pages + lp) * p.mask_words;
-#pragma unroll
-          for (int k = 0; k < 4; ++k) wd[k] = mrow[min(word0 + k, p.mask_words - 1)];
-        }
-        const int nv = page_valid(seq_len, lp, kMP);
-        m_nv[i] = nv;
-        m_phys[i] = nv > 0 ? ph : 0;
-        const bool ambient = p.ccounts && e >= cc;
-#pragma unroll
-        for (int k = 0; k < 4; ++k) m_word[i][k] = (ambient && word0 + k < p.mask_words) ? wd[k] : 0xffffffffu;
-      }
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    if (attempt > 0 && w0 != 0) {
       __syncthreads();
-    };
-    load_meta(beg);
-    if (beg < end && m_nv[0] > 0) stage(sk0, m_phys[0], 0, kMInstr);
+      w0 = 0;
+      load_meta(0);
+    }
+    if (n_pg > 0 && m_nv[0] > 0) stage(sk0, m_phys[0], 0, kMInstr);
 
     // one page: compute from `cur` while the next page is copied into `nxt`
-    auto page = [&](auto parity, int e) {
+    auto page = [&](auto parity, int k) {
       uint16_t* cur = parity.value ? sk1 : sk0;
       uint16_t* nxt = parity.value ? sk0 : sk1;
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       __syncthreads();
-      const int nv = m_nv[e - w0];
-      uint32_t word[2];
+      const int nv = m_nv[k - w0];
+      bool act[2];
 #pragma unroll
-      for (int rt = 0; rt < 2; ++rt) word[rt] = m_word[e - w0][tile_word[rt] - word0];
+      for (int rt = 0; rt < 2; ++rt) {
+        const uint32_t word = m_word[k - w0][h_row[rt] >> 5];
+        act[rt] = row_ok[rt] && ((word >> (h_row[rt] & 31)) & 1u);
+      }
       if (nv > 0 && nv < kMP) {
         // tokens past the sequence end: zero their rows (V operand must be finite)
         for (int idx = threadIdx.x; idx < (kMP - nv) * 72; idx += 256) {
@@ -238,42 +317,30 @@ __global__ __launch_bounds__(256, 1) void mla_decode_kernel(DecodeParams p) {
         }
         __syncthreads();
       }
-      if (e + 1 < end) {
-        if (e + 1 - w0 == kMetaWin) {           // next window (long splits only)
-          __syncthreads();
-          w0 = e + 1;
-          load_meta(w0);
-        }
+      if (k + 1 < n_pg && k + 1 - w0 == kMetaWin) {   // next window (long splits only)
+        __syncthreads();
+        w0 = k + 1;
+        load_meta(w0);
       }
       // the next page's copy in two parts: rows 0-31 now, the rest between
       // this page's two halves (issued at once, the copy stalls the wave on
       // the memory pipeline for thousands of cycles)
-      const bool stage_next = e + 1 < end && m_nv[e + 1 - w0] > 0;
+      const bool stage_next = k + 1 < n_pg && m_nv[k + 1 - w0] > 0;
       auto copy_rest = [&]() {
-        if (stage_next) stage(nxt, m_phys[e + 1 - w0], kMHalfInstr, kMInstr);
+        if (stage_next) stage(nxt, m_phys[k + 1 - w0], kMHalfInstr, kMInstr);
       };
-      if (stage_next) stage(nxt, m_phys[e + 1 - w0], 0, kMHalfInstr);
-      // which of this wave's rows attend the page
-      bool act[2];
-      bool any_row = false;
-#pragma unroll
-      for (int rt = 0; rt < 2; ++rt) {
-        act[rt] = row_ok[rt] && ((word[rt] >> (h_row[rt] & 31)) & 1u);
-        any_row |= __any(act[rt]) != 0;
-      }
-      // a wave none of whose rows attend the page skips the work but still
-      // passes the copy point between the halves
-      const bool compute = nv > 0 && wave_rows && any_row;
+      if (stage_next) stage(nxt, m_phys[k + 1 - w0], 0, kMHalfInstr);
+      // tiles of this wave with a row that attends the page (wave-uniform)
+      const int tmask = nv > 0 ? ((__any(act[0]) ? 1 : 0) | (__any(act[1]) ? 2 : 0)) : 0;
 
       const uint16_t* K = cur;
-      constexpr int kAhead = 3;            // operand reads in flight ahead of use
-      auto half_page = [&](int half) {
-        // S^T = K Q^T over tokens 32*half .. +32 (tiles j4 = 2*half, 2*half + 1)
-        f32x4 sacc[2][2];
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-#pragma unroll
-          for (int rt = 0; rt < 2; ++rt) sacc[j][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      constexpr int kAhead = 5;            // operand reads in flight ahead of use
+      // One row tile over half a page: S^T = K Q^T over tokens 32*half .. +32
+      // (MFMA tiles j4 = 2*half, 2*half + 1), softmax, O^T += V^T P^T.  A tile
+      // none of whose rows attends the page is skipped entirely.
+      auto tile_half = [&](auto rtc, int half) {
+        constexpr int rt = decltype(rtc)::value;
+        f32x4 sacc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
         constexpr int nsq = 2 * kMKSteps;
         // A row m of tile j4 is token tok_of(j4, m): the 8 lanes of one LDS
         // pass read 8 rows with distinct (row mod 8), i.e. distinct banks.
@@ -287,52 +354,45 @@ __global__ __launch_bounds__(256, 1) void mla_decode_kernel(DecodeParams p) {
 #pragma unroll
         for (int step = 0; step < nsq; ++step) {
           if (step + kAhead < nsq) ka[(step + kAhead) % (kAhead + 1)] = kload(step + kAhead);
-#pragma unroll
-          for (int rt = 0; rt < 2; ++rt)
-            sacc[step & 1][rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[step % (kAhead + 1)],
-                                                                         qreg[rt][step >> 1], sacc[step & 1][rt],
-                                                                         0, 0, 0);
+          sacc[step & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[step % (kAhead + 1)], qreg[rt][step >> 1],
+                                                                   sacc[step & 1], 0, 0, 0);
           __builtin_amdgcn_sched_barrier(0);
         }
 
-        // softmax: lane holds S^T[token tok_of(2*half + j, 4*kg + i)][row col]
-        bf16x8 pb[2];
+        // softmax: lane holds S^T[token tok_of(2*half + j, 4*kg + i)][row col].
+        // Row maximum on the raw logits (the scale is positive); then
+        // p = 2^(s * scale_log2 - m) is one FMA and one v_exp_f32.
+        float mraw = -INFINITY;
 #pragma unroll
-        for (int rt = 0; rt < 2; ++rt) {
-          // row maximum on the raw logits (the scale is positive); then
-          // p = 2^(s * scale_log2 - m) is one FMA and one v_exp_f32
-          float mraw = -INFINITY;
+        for (int j = 0; j < 2; ++j)
 #pragma unroll
-          for (int j = 0; j < 2; ++j)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const int tok = tok_of(2 * half + j, 4 * kg + i);
-              if (!(act[rt] && tok < nv)) sacc[j][rt][i] = -INFINITY;
-              mraw = fmaxf(mraw, sacc[j][rt][i]);
-            }
-          mraw = max_over_row_groups(mraw);
-          const float mloc = mraw == -INFINITY ? -INFINITY : mraw * p.scale_log2;
-          if (attempt == 1) {
-            m_ref[rt] = fmaxf(m_ref[rt], mloc);
-            continue;
+          for (int i = 0; i < 4; ++i) {
+            const int tok = tok_of(2 * half + j, 4 * kg + i);
+            if (!(act[rt] && tok < nv)) sacc[j][i] = -INFINITY;
+            mraw = fmaxf(mraw, sacc[j][i]);
           }
-          if (attempt == 0) {
-            if (m_ref[rt] == -INFINITY) m_ref[rt] = mloc;
-            else if (mloc > m_ref[rt] + kMMargin) overflow = true;
-          }
-          const float msub = m_ref[rt] == -INFINITY ? 0.f : m_ref[rt];
-          float psum = 0.f;
-#pragma unroll
-          for (int j = 0; j < 2; ++j)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[j][rt][i], p.scale_log2, -msub));
-              psum += pv;
-              pb[rt][4 * j + i] = (__bf16)pv;
-            }
-          l_run[rt] += psum;
+        mraw = max_over_row_groups(mraw);
+        const float mloc = mraw == -INFINITY ? -INFINITY : mraw * p.scale_log2;
+        if (attempt == 1) {
+          m_ref[rt] = fmaxf(m_ref[rt], mloc);
+          return;
         }
-        if (!do_pv) return;
+        if (attempt == 0) {
+          if (m_ref[rt] == -INFINITY) m_ref[rt] = mloc;
+          else if (mloc > m_ref[rt] + kMMargin) overflow = true;
+        }
+        const float msub = m_ref[rt] == -INFINITY ? 0.f : m_ref[rt];
+        float psum = 0.f;
+        bf16x8 pb;
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[j][i], p.scale_log2, -msub));
+            psum += pv;
+            pb[4 * j + i] = (__bf16)pv;
+          }
+        l_run[rt] += psum;
 
         // O^T += V^T P^T over the same 32 tokens.  k-slot 8*kg + 4*j + i of
         // this product is token tok_of(2*half + j, 4*kg + i), the S^T fragment
@@ -356,22 +416,22 @@ __global__ __launch_bounds__(256, 1) void mla_decode_kernel(DecodeParams p) {
 #pragma unroll
         for (int dt = 0; dt < kMDTiles; ++dt) {
           if (dt + kAhead < kMDTiles) va[(dt + kAhead) % (kAhead + 1)] = vload(dt + kAhead);
-#pragma unroll
-          for (int rt = 0; rt < 2; ++rt)
-            oacc[dt][rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[dt % (kAhead + 1)], pb[rt], oacc[dt][rt],
-                                                                   0, 0, 0);
+          oacc[dt][rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[dt % (kAhead + 1)], pb, oacc[dt][rt], 0, 0, 0);
           __builtin_amdgcn_sched_barrier(0);
         }
       };
-#pragma unroll
-      for (int half = 0; half < 2; ++half) {
-        if (compute) half_page(half);
-        if (half == 0) copy_rest();
-      }
+      const bool on0 = (tmask & 1) != 0, on1 = (tmask & 2) != 0;   // wave-uniform
+      // a wave with no active tile skips the work but still passes the copy
+      // point between the halves
+      if (on0) tile_half(std::integral_constant<int, 0>{}, 0);
+      if (on1) tile_half(std::integral_constant<int, 1>{}, 0);
+      copy_rest();
+      if (on0) tile_half(std::integral_constant<int, 0>{}, 1);
+      if (on1) tile_half(std::integral_constant<int, 1>{}, 1);
     };
-    for (int e = beg; e < end; e += 2) {
-      page(Parity<0>{}, e);
-      if (e + 1 < end) page(Parity<1>{}, e + 1);
+    for (int k = 0; k < n_pg; k += 2) {
+      page(Parity<0>{}, k);
+      if (k + 1 < n_pg) page(Parity<1>{}, k + 1);
     }
     // every wave has finished reading the last staged page before a new
     // attempt restages buffer 0
@@ -442,8 +502,8 @@ __global__ __launch_bounds__(256, 1) void mla_decode_kernel(DecodeParams p) {
 }
 
 hipError_t launch_mla_decode(const DecodeParams& p, hipStream_t s) {
-  const int heads_per_wg = 128 / p.T;
-  const int n_rg = (p.Hq + heads_per_wg - 1) / heads_per_wg;
+  const int hpt = 16 / p.T;
+  const int n_rg = ((p.Hq + hpt - 1) / hpt + 7) / 8;
   const dim3 grid(p.B * n_rg * p.splits), block(256);
   hipLaunchKernelGGL(mla_decode_kernel, grid, block, 0, s, p);
   return hipGetLastError();

@@ -38,6 +38,7 @@ def test_status_strings_and_version():
     lib = S.load_library()
     assert lib.sa_status_string(0) == b"SA_OK"
     assert lib.sa_status_string(3) == b"SA_ERR_WORKSPACE_TOO_SMALL"
+    assert lib.sa_status_string(5) == b"SA_ERR_DATA"
     assert S.sa_version() >= 100
 
 
@@ -260,3 +261,15 @@ def test_noalloc_scratch_limit_matches_header():
     src = open(HEADER).read()
     m = re.search(r"#define SA_NOALLOC_SCRATCH_BYTES \((\d+)u << (\d+)\)", src)
     assert m and int(m.group(1)) << int(m.group(2)) == B.SA_NOALLOC_SCRATCH_BYTES
+
+
+def test_debug_validate_toggle():
+    """The switch returns the previous setting; it starts off unless the
+    environment turned it on."""
+    import os
+    lib = S.load_library()
+    first = lib.sa_set_debug_validate(1)
+    env = os.environ.get("SA_DEBUG_VALIDATE", "")
+    assert first == (1 if env not in ("", "0") else 0)
+    assert lib.sa_set_debug_validate(0) == 1
+    assert lib.sa_set_debug_validate(first) == 0
