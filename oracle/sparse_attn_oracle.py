@@ -374,3 +374,63 @@ def block_sparse_prefill(q, k_pool, v_pool, block_table_row, seq_len, page_size,
             with np.errstate(divide="ignore"):
                 lse[qi, h] = np.where(empty, -np.inf, m_safe + np.log(L_safe))
     return out, lse
+
+
+# ------------------------------------------------------------- prefill mask
+def prefill_block_mask(q, mu, block_table_row, seq_len, page_size, q_start, block_q, n_kv_blocks,
+                       n_kv_heads, sm_scale, top_k=None, max_gap=None):
+    """2D block mask for a prefill chunk by block-level pattern discovery.
+
+    Sources: the block-sparse prefill brief on the Paperraft page ("instantaneous
+    pattern discovery, max-based dynamic thresholding"), the router score form of
+    [UAE] "Content-Dependent Dynamic Routing" (pooled query against the block's
+    mean key) and the mask structure the CompactAttention abstract feeds to its
+    Q-block / intra-group union ([CA]).
+
+    For query head h and Q-block qb (queries i in [qb*block_q, min((qb+1)*block_q, q_len))):
+      qbar = mean over the Q-block's queries of q[i, h, :]   (float64)
+      n    = number of KV blocks holding a token at or before the block's last
+             position q_start + i_last (and below seq_len): the causal blocks
+      s[kb] = fp32( sm_scale * sum_d qbar[d] * mu[phys(kb), g(h), d] ),  kb < n
+      forced = {0} u [kb_lo, n), kb_lo = block of the first query's position
+               (the sink block and the diagonal blocks)
+      chosen (top-k mode)     = the first min(top_k, |C|) candidates C = causal
+                                minus forced, by (score desc, index asc)
+      chosen (threshold mode) = {c in C : s[c] >= max_{kb < n} s[kb] - max_gap}
+      mask[h, qb, kb] = 1 for kb in forced u chosen, else 0.
+    Exactly one of top_k / max_gap is given.  Returns (mask uint8
+    [Hq][nqb][n_kv_blocks], scores fp32 [Hq][nqb][n_kv_blocks] with NaN past
+    the causal blocks).
+    """
+    assert (top_k is None) != (max_gap is None)
+    q_len, Hq, d = q.shape
+    G = Hq // n_kv_heads
+    P = page_size
+    nqb = (q_len + block_q - 1) // block_q
+    n_seq_pages = n_pages_of(seq_len, P)
+    mask = np.zeros((Hq, nqb, n_kv_blocks), dtype=np.uint8)
+    scores = np.full((Hq, nqb, n_kv_blocks), np.nan, dtype=np.float32)
+    for h in range(Hq):
+        g = h // G
+        for qb in range(nqb):
+            i0, i1 = qb * block_q, min((qb + 1) * block_q, q_len)
+            qbar = np.asarray(q[i0:i1, h, :], dtype=np.float64).sum(axis=0) / (i1 - i0)
+            n = min((q_start + i1 - 1) // P + 1, n_seq_pages, n_kv_blocks)
+            if n <= 0:
+                continue
+            kb_lo = min((q_start + i0) // P, n - 1)
+            for kb in range(n):
+                m = np.asarray(mu[int(block_table_row[kb]), g], dtype=np.float64)
+                scores[h, qb, kb] = np.float32(sm_scale * np.dot(qbar, m))
+            forced = {0} | set(range(kb_lo, n))
+            cand = [kb for kb in range(n) if kb not in forced]
+            if top_k is not None:
+                chosen = rank_candidates(scores[h, qb], cand)[:max(0, min(top_k, len(cand)))]
+            else:
+                row = scores[h, qb, :n]
+                top = np.float32(np.max(row))
+                thr = np.float32(top - np.float32(max_gap))
+                chosen = [kb for kb in cand if row[kb] >= thr]
+            for kb in forced | set(chosen):
+                mask[h, qb, kb] = 1
+    return mask, scores

@@ -560,6 +560,106 @@ def check_prefill_masked_sdpa():
         assert (out[empty, h] == 0).all() and np.isneginf(lse[empty, h]).all()
 
 
+# ------------------------------------------------------------ prefill mask
+def _brute_mask(q, K_dense, scale, P, q_start, bq, nkb, n_kv, seq_len, top_k, max_gap):
+    """Pure-Python reference for the block mask on a dense per-group key array K_dense[g][L][d]."""
+    q_len, Hq, d = q.shape
+    G = Hq // n_kv
+    nqb = (q_len + bq - 1) // bq
+    out = np.zeros((Hq, nqb, nkb), dtype=np.uint8)
+    n_seq = (seq_len + P - 1) // P
+    for h in range(Hq):
+        g = h // G
+        for qb in range(nqb):
+            rows = list(range(qb * bq, min((qb + 1) * bq, q_len)))
+            qbar = [math.fsum(float(q[i, h, e]) for i in rows) / len(rows) for e in range(d)]
+            last = q_start + rows[-1]
+            n = min(last // P + 1, n_seq, nkb)
+            kb_lo = min((q_start + rows[0]) // P, n - 1)
+            sc = []
+            for kb in range(n):
+                toks = [j for j in range(kb * P, (kb + 1) * P) if j < seq_len]
+                mean_k = [math.fsum(float(K_dense[g, j, e]) for j in toks) / len(toks) for e in range(d)]
+                sc.append(float(np.float32(scale * math.fsum(qbar[e] * mean_k[e] for e in range(d)))))
+            forced = set([0]) | set(range(kb_lo, n))
+            cand = [kb for kb in range(n) if kb not in forced]
+            if top_k is not None:
+                chosen = sorted(cand, key=lambda kb: (-sc[kb], kb))[:min(top_k, len(cand))]
+            else:
+                thr = float(np.float32(np.float32(max(sc)) - np.float32(max_gap)))
+                chosen = [kb for kb in cand if sc[kb] >= thr]
+            for kb in forced | set(chosen):
+                out[h, qb, kb] = 1
+    return out
+
+
+def _mask_case(rng, integer):
+    Hq, Hkv, P, d, bq = 4, 2, 4, 6, 4
+    q_len, q_start = 10, 13
+    L = q_start + q_len
+    if integer:
+        q = rng.integers(-3, 4, size=(q_len, Hq, d)).astype(np.float64)
+        K = rng.integers(-4, 5, size=(1, Hkv, L, d)).astype(np.float64)
+    else:
+        q = rng.standard_normal((q_len, Hq, d))
+        K = rng.standard_normal((1, Hkv, L, d))
+    kp, _, bt = scatter_to_pool(K, K, P, rng, extra_pages=2)
+    mu = O.page_summary(kp, bt, np.array([L]), P)
+    return q, K[0], kp, bt[0], mu, Hkv, P, bq, q_start, L
+
+
+def check_mask_bruteforce():
+    """Integer-valued inputs make every mean and score exact, so exact score
+    ties occur and must go to the lowest block index; real-valued inputs check
+    the threshold mode."""
+    rng = np.random.default_rng(17)
+    for trial in range(6):
+        integer = trial % 2 == 0
+        q, Kd, kp, bt, mu, Hkv, P, bq, q_start, L = _mask_case(rng, integer)
+        nkb = (L + P - 1) // P
+        scale = 0.5
+        for mode in ({"top_k": 0}, {"top_k": 1}, {"top_k": 2}, {"top_k": 50}, {"max_gap": 0.0},
+                     {"max_gap": 1.5}, {"max_gap": float("inf")}):
+            got, sc = O.prefill_block_mask(q, mu, bt, L, P, q_start, bq, nkb, Hkv, scale, **mode)
+            exp = _brute_mask(q, Kd, scale, P, q_start, bq, nkb, Hkv, L, mode.get("top_k"), mode.get("max_gap"))
+            assert np.array_equal(got, exp), (trial, mode)
+
+
+def check_mask_invariants():
+    rng = np.random.default_rng(18)
+    q, Kd, kp, bt, mu, Hkv, P, bq, q_start, L = _mask_case(rng, False)
+    nkb = (L + P - 1) // P
+    q_len, Hq, _ = q.shape
+    nqb = (q_len + bq - 1) // bq
+    none, _ = O.prefill_block_mask(q, mu, bt, L, P, q_start, bq, nkb, Hkv, 0.3, top_k=0)
+    every, _ = O.prefill_block_mask(q, mu, bt, L, P, q_start, bq, nkb, Hkv, 0.3, top_k=10 ** 6)
+    gap_inf, _ = O.prefill_block_mask(q, mu, bt, L, P, q_start, bq, nkb, Hkv, 0.3, max_gap=float("inf"))
+    assert np.array_equal(every, gap_inf)
+    for qb in range(nqb):
+        first, last = q_start + qb * bq, q_start + min((qb + 1) * bq, q_len) - 1
+        causal = np.zeros(nkb, dtype=np.uint8)
+        causal[:last // P + 1] = 1
+        forced = np.zeros(nkb, dtype=np.uint8)
+        forced[0] = 1
+        forced[first // P:last // P + 1] = 1
+        for h in range(Hq):
+            assert np.array_equal(none[h, qb], forced), (h, qb)      # top_k = 0: sink + diagonal only
+            assert np.array_equal(every[h, qb], causal), (h, qb)     # everything causal, nothing beyond
+
+
+def check_mask_union_keeps_selection():
+    """The union block tables built from a produced mask keep every block it selects."""
+    rng = np.random.default_rng(19)
+    q, Kd, kp, bt, mu, Hkv, P, bq, q_start, L = _mask_case(rng, False)
+    nkb = (L + P - 1) // P
+    mask, _ = O.prefill_block_mask(q, mu, bt, L, P, q_start, bq, nkb, Hkv, 0.3, top_k=1)
+    tables, counts = O.gqa_union_block_table(mask, Hkv)
+    G = q.shape[1] // Hkv
+    for h in range(q.shape[1]):
+        kept = set(int(x) for x in tables[h // G, :counts[h // G]])
+        assert set(np.flatnonzero(mask[h].any(axis=0)).tolist()) <= kept
+
+
 ALL_CHECKS = [
     check_summary_constant_pages, check_summary_bruteforce,
     check_scores_exact_integers, check_scores_linearity_and_unfactored,
@@ -569,4 +669,5 @@ ALL_CHECKS = [
     check_decode_modes_and_tiers, check_decode_split_merge, check_decode_latent_sdpa,
     check_union_bruteforce, check_union_golden,
     check_prefill_causal_sdpa, check_prefill_masked_sdpa,
+    check_mask_bruteforce, check_mask_invariants, check_mask_union_keeps_selection,
 ]

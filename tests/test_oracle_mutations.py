@@ -19,6 +19,7 @@ _orig_union = O.gqa_union_block_table
 _orig_summary = O.page_summary
 _orig_sel_heads = O.selection_heads
 _orig_row_pages = O.row_pages
+_orig_mask = O.prefill_block_mask
 
 
 def _no_scale(qrow, K, V, sm_scale, d_v):
@@ -98,7 +99,40 @@ def _ambient_ignores_mask(b, s, h, page_lists, page_counts, critical_counts, amb
     return _orig_row_pages(b, s, h, page_lists, page_counts, None, None)
 
 
+def _mask_sum_not_mean(q, mu, bt, seq_len, P, q_start, bq, nkb, n_kv, scale, top_k=None, max_gap=None):
+    """Pool the Q-block's queries by their sum instead of their mean."""
+    qs = np.array(q, dtype=np.float64)
+    for qb in range(0, qs.shape[0], bq):
+        qs[qb:qb + bq] *= min(bq, qs.shape[0] - qb)
+    return _orig_mask(qs, mu, bt, seq_len, P, q_start, bq, nkb, n_kv, scale, top_k=top_k, max_gap=max_gap)
+
+
+def _mask_no_diagonal(q, mu, bt, seq_len, P, q_start, bq, nkb, n_kv, scale, top_k=None, max_gap=None):
+    """Forget to force the diagonal block of each Q-block."""
+    m, sc = _orig_mask(q, mu, bt, seq_len, P, q_start, bq, nkb, n_kv, scale, top_k=top_k, max_gap=max_gap)
+    m = m.copy()
+    for qb in range(m.shape[1]):
+        last = q_start + min((qb + 1) * bq, q.shape[0]) - 1
+        if last // P > 0:
+            m[:, qb, last // P] = 0
+    return m, sc
+
+
+def _mask_one_past_causal(q, mu, bt, seq_len, P, q_start, bq, nkb, n_kv, scale, top_k=None, max_gap=None):
+    """Let each Q-block also keep the block just past its last query."""
+    m, sc = _orig_mask(q, mu, bt, seq_len, P, q_start, bq, nkb, n_kv, scale, top_k=top_k, max_gap=max_gap)
+    m = m.copy()
+    for qb in range(m.shape[1]):
+        nxt = (q_start + min((qb + 1) * bq, q.shape[0]) - 1) // P + 1
+        if nxt < nkb:
+            m[:, qb, nxt] = 1
+    return m, sc
+
+
 MUTANTS = {
+    "mask_sum_not_mean": ("prefill_block_mask", _mask_sum_not_mean),
+    "mask_no_diagonal": ("prefill_block_mask", _mask_no_diagonal),
+    "mask_one_past_causal": ("prefill_block_mask", _mask_one_past_causal),
     "no_softmax_scale": ("softmax_attend", _no_scale),
     "no_max_shift": ("softmax_attend", _no_max_shift),
     "v_read_untransposed": ("gather_tokens", _v_not_transposed),
