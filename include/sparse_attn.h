@@ -265,6 +265,36 @@ sa_status sa_select_decode(const sa_paged_kv* kv, int32_t batch,
                            float sm_scale, void* out, float* out_lse, hipStream_t stream);
 
 /* ------------------------------------------------------------------------
+ * sa_prefill_block_mask -- the 2D block mask of a prefill chunk by
+ * block-level pattern discovery (block-sparse prefill brief on the Paperraft
+ * page: instantaneous pattern discovery, max-based dynamic thresholding;
+ * score form of the [UAE] router, "Content-Dependent Dynamic Routing"; the
+ * mask feeds the [CA] Q-block / intra-group union of sa_block_sparse_prefill).
+ *
+ * For query head h and Q-block qb (queries [qb*block_q, min(+block_q, q_len))):
+ *   qbar   = mean of the Q-block's query rows of head h (float64)
+ *   n      = KV blocks holding a token at or before the Q-block's last
+ *            position q_start + i_last and below seq_lens[seq] (causal blocks)
+ *   s[kb]  = fp32(sm_scale * sum_d qbar[d] * page_summary[phys(kb)][g(h)][d]),  kb < n
+ *   forced = block 0 and the diagonal blocks [block of q_start + i_first, n)
+ *   top_k >= 0: keep the top_k other causal blocks by (score desc, index asc)
+ *   top_k <  0: keep the other causal blocks with s >= fp32(max_kb<n s[kb] - max_gap)
+ *   block_mask_out[h][qb][kb] = 1 for forced and kept blocks, else 0.
+ *   q            [q_len][n_q_heads][d_qk] (kv->dtype)
+ *   page_summary [n_phys_pages][n_kv_heads][d_qk] fp32 (sa_page_summary)
+ *   block_mask_out out [n_q_heads][ceil(q_len/block_q)][n_kv_blocks] uint8
+ * Needs a V-pool cache (d 64 or 128), at most 8 query heads per KV head,
+ * n_kv_blocks covering q_start + q_len and <= max_pages, and
+ * (group + 2) * n_kv_blocks * 4 bytes <= 144 KiB (e.g. 4 heads per KV head
+ * and 4,096 blocks).  max_gap >= 0 (may be +inf) in threshold mode.
+ * ---------------------------------------------------------------------- */
+sa_status sa_prefill_block_mask(const sa_paged_kv* kv, int32_t seq,
+                                const void* q, int32_t q_len, int32_t q_start, int32_t n_q_heads,
+                                const float* page_summary, int32_t block_q, int32_t n_kv_blocks,
+                                float sm_scale, int32_t top_k, float max_gap,
+                                uint8_t* block_mask_out, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
  * sa_block_sparse_prefill -- chunked-prefill attention with a 2D block mask
  * turned into GQA-union KV block tables ([CA]; [UAE] block-sparse prefill).
  *

@@ -32,7 +32,8 @@ SA_NOALLOC_SCRATCH_BYTES = 64 << 20
 EXPORTED = [
     "sa_page_summary", "sa_select_pages_workspace_size", "sa_select_pages",
     "sa_sparse_decode_workspace_size", "sa_sparse_decode", "sa_sparse_decode_noalloc", "sa_select_decode",
-    "sa_block_sparse_prefill_workspace_size", "sa_block_sparse_prefill", "sa_set_debug_validate",
+    "sa_block_sparse_prefill_workspace_size", "sa_block_sparse_prefill", "sa_prefill_block_mask",
+    "sa_set_debug_validate",
     "sa_status_string", "sa_last_error_message", "sa_version",
 ]
 
@@ -82,6 +83,8 @@ def load_library(build_if_missing: bool = True) -> ctypes.CDLL:
         "sa_block_sparse_prefill_workspace_size": (c_size_t, [P, c_int32, c_int32, c_int32]),
         "sa_block_sparse_prefill": (c_int, [P, c_int32, P, c_int32, c_int32, c_int32, P, c_int32, c_int32, P, P,
                                             c_float, P, P, P, c_size_t, P]),
+        "sa_prefill_block_mask": (c_int, [P, c_int32, P, c_int32, c_int32, c_int32, P, c_int32, c_int32, c_float,
+                                          c_int32, c_float, P, P]),
         "sa_set_debug_validate": (c_int, [c_int]),
         "sa_status_string": (ctypes.c_char_p, [c_int]),
         "sa_last_error_message": (ctypes.c_char_p, []),
@@ -296,6 +299,26 @@ def sa_block_sparse_prefill(kv: PagedKV, seq: int, q: torch.Tensor, q_start: int
         _ptr(block_counts_out), float(sm_scale), _ptr(out), _ptr(out_lse), _ptr(workspace), workspace.numel(),
         _stream(kv.device)))
     return out, out_lse, block_table_out, block_counts_out
+
+
+def sa_prefill_block_mask(kv: PagedKV, seq: int, q: torch.Tensor, q_start: int, page_summary: torch.Tensor,
+                          block_q: int, sm_scale: float, *, top_k: Optional[int] = None,
+                          max_gap: Optional[float] = None, n_kv_blocks: Optional[int] = None,
+                          out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Returns the uint8 block mask [Hq][ceil(q_len/block_q)][n_kv_blocks]; give exactly one of top_k / max_gap."""
+    if (top_k is None) == (max_gap is None):
+        raise ValueError("give exactly one of top_k and max_gap")
+    q_len, Hq, _ = q.shape
+    if n_kv_blocks is None:
+        n_kv_blocks = (q_start + q_len + kv.page_size - 1) // kv.page_size
+    nqb = (q_len + block_q - 1) // block_q
+    if out is None:
+        out = torch.empty((Hq, nqb, n_kv_blocks), dtype=torch.uint8, device=kv.device)
+    _check(load_library().sa_prefill_block_mask(
+        kv.ref, seq, _ptr(q), q_len, q_start, Hq, _ptr(page_summary), block_q, n_kv_blocks, float(sm_scale),
+        -1 if top_k is None else int(top_k), float("inf") if max_gap is None else float(max_gap), _ptr(out),
+        _stream(kv.device)))
+    return out
 
 
 def sa_set_debug_validate(on: bool) -> bool:

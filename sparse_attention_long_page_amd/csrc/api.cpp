@@ -226,6 +226,61 @@ const char* sa_last_error_message(void) { return g_last_error.c_str(); }
 
 int sa_version(void) { return 100; }   // 0.1.0
 
+// --------------------------------------------------------- prefill block mask
+sa_status sa_prefill_block_mask(const sa_paged_kv* kv, int32_t seq, const void* q, int32_t q_len, int32_t q_start,
+                                int32_t n_q_heads, const float* page_summary, int32_t block_q, int32_t n_kv_blocks,
+                                float sm_scale, int32_t top_k, float max_gap, uint8_t* block_mask_out,
+                                hipStream_t stream) {
+  sa_status st = check_kv(kv, false);
+  if (st != SA_OK) return st;
+  if (is_latent(kv)) return fail(SA_ERR_UNSUPPORTED, "the block mask needs a V-pool cache (d 64 or 128)");
+  if (seq < 0) return fail(SA_ERR_INVALID_ARGUMENT, "seq must be >= 0");
+  if (!q || !page_summary || !block_mask_out)
+    return fail(SA_ERR_INVALID_ARGUMENT, "q, page_summary and block_mask_out must be set");
+  if (q_len <= 0 || q_start < 0 || block_q <= 0)
+    return fail(SA_ERR_INVALID_ARGUMENT, "q_len and block_q must be positive, q_start >= 0");
+  if (n_q_heads <= 0 || n_q_heads % kv->n_kv_heads != 0)
+    return fail(SA_ERR_INVALID_ARGUMENT, "n_q_heads must be a positive multiple of n_kv_heads");
+  const int G = n_q_heads / kv->n_kv_heads;
+  if (G > 8) return fail(SA_ERR_UNSUPPORTED, "the block mask supports up to 8 query heads per KV head");
+  const long need_blocks = ((long)q_start + q_len + kv->page_size - 1) / kv->page_size;
+  if (n_kv_blocks < need_blocks || n_kv_blocks > kv->max_pages)
+    return fail(SA_ERR_INVALID_ARGUMENT, "n_kv_blocks %d must cover q_start+q_len (%ld) and be <= max_pages %d",
+                n_kv_blocks, need_blocks, kv->max_pages);
+  if (sa::block_mask_lds_bytes(G, n_kv_blocks) > 144 * 1024)
+    return fail(SA_ERR_UNSUPPORTED, "%d heads per KV head x %d KV blocks of scores exceed the LDS budget", G,
+                n_kv_blocks);
+  if (!std::isfinite(sm_scale) || !(sm_scale > 0.f))
+    return fail(SA_ERR_INVALID_ARGUMENT, "sm_scale must be finite and positive");
+  if (top_k < 0 && !(max_gap >= 0.f))
+    return fail(SA_ERR_INVALID_ARGUMENT, "threshold mode (top_k < 0) needs max_gap >= 0 (+inf allowed)");
+  if (validate_on()) {
+    Validator v(stream);
+    v.kv(kv, seq, 1);
+    st = v.finish(kv, 0);
+    if (st != SA_OK) return st;
+  }
+  sa::MaskParams mp{};
+  mp.q = q;
+  mp.mu = page_summary;
+  mp.bt_row = kv->block_table + (size_t)seq * kv->max_pages;
+  mp.seq_len = kv->seq_lens + seq;
+  mp.mask = block_mask_out;
+  mp.q_len = q_len;
+  mp.q_start = q_start;
+  mp.Hq = n_q_heads;
+  mp.Hkv = kv->n_kv_heads;
+  mp.G = G;
+  mp.P = kv->page_size;
+  mp.block_q = block_q;
+  mp.nqb = (q_len + block_q - 1) / block_q;
+  mp.nkb = n_kv_blocks;
+  mp.top_k = top_k < 0 ? -1 : top_k;
+  mp.sm_scale = sm_scale;
+  mp.max_gap = top_k < 0 ? max_gap : 0.f;
+  return device_status(sa::launch_block_mask(mp, kv->dtype == SA_DTYPE_BF16, kv->d_qk, stream), "block mask launch");
+}
+
 // ------------------------------------------------------------------ summary
 sa_status sa_page_summary(const sa_paged_kv* kv, int32_t batch, int32_t last_pages, float* page_summary,
                           hipStream_t stream) {

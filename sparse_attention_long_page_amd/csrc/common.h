@@ -180,6 +180,18 @@ hipError_t launch_select_prep(const SummaryParams& smp, const ScoreParams& sp, i
                               uint32_t* arrivals, hipStream_t s);
 hipError_t launch_score_lastsel(const ScoreParams& sp, const SelectParams& p, int bf16, const double* qpart,
                                 uint32_t* arrivals, hipStream_t s);
+struct MaskParams {
+  const void* q;             // [q_len][Hq][d]
+  const float* mu;           // page summaries [n_phys][Hkv][d]
+  const int32_t* bt_row;     // block_table row of the sequence
+  const int32_t* seq_len;    // pointer to seq_lens[seq]
+  uint8_t* mask;             // out [Hq][nqb][nkb]
+  int q_len, q_start, Hq, Hkv, G, P, block_q, nqb, nkb, top_k;
+  float sm_scale, max_gap;   // top_k < 0: keep candidates with score >= max - max_gap
+};
+size_t block_mask_lds_bytes(int G, int nkb);
+hipError_t launch_block_mask(const MaskParams& mp, int bf16, int d, hipStream_t s);
+
 // Device-side data checks (debug validation mode).  Violation codes:
 constexpr uint32_t kValSeqLen = 1;         // seq_lens[b] outside [0, max_pages * page_size]
 constexpr uint32_t kValBlockTable = 2;     // block_table[b][lp] outside [0, n_phys_pages)
