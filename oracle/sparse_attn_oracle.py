@@ -434,3 +434,34 @@ def prefill_block_mask(q, mu, block_table_row, seq_len, page_size, q_start, bloc
             for kb in forced | set(chosen):
                 mask[h, qb, kb] = 1
     return mask, scores
+
+
+# -------------------------------------------------------------- FP8 pages
+def fp8_e4m3_to_float(codes: np.ndarray) -> np.ndarray:
+    """Value of each OCP FP8 E4M3 byte (1 sign bit, 4 exponent bits with bias 7,
+    3 mantissa bits; exponent 0 is subnormal, m * 2^-9; S.1111.111 is NaN; no
+    infinities), as float64.
+
+    Source: the quantized KV cache named in "Universal Attention Engine", "Key
+    Design Decisions" 2 (cache format paged, block-sparse, quantized) and
+    "Milestones" (Phase 3: quantized KV cache support), and the FP8 regime of
+    the block-sparse prefill brief; the byte encoding is the OCP 8-bit floating
+    point E4M3 format.
+    """
+    c = np.asarray(codes, dtype=np.int64)
+    sign = np.where((c >> 7) & 1, -1.0, 1.0)
+    e = (c >> 3) & 0xF
+    m = (c & 0x7).astype(np.float64)
+    normal = sign * (1.0 + m / 8.0) * np.exp2(e.astype(np.float64) - 7.0)
+    sub = sign * m * 2.0 ** -9
+    out = np.where(e == 0, sub, normal)
+    return np.where((c & 0x7F) == 0x7F, np.nan, out)
+
+
+def dequantize_pages(pool_u8: np.ndarray, scale: np.ndarray) -> np.ndarray:
+    """Dequantised pool: every element of page (phys, g) is its FP8 value times
+    the page's scale scale[phys, g] (one scale per page and KV head for K and
+    one for V, applied when the page is loaded).  pool_u8 [n_phys][Hkv][...]."""
+    vals = fp8_e4m3_to_float(pool_u8)
+    s = np.asarray(scale, dtype=np.float64).reshape(scale.shape + (1,) * (pool_u8.ndim - 2))
+    return vals * s

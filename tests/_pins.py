@@ -660,6 +660,61 @@ def check_mask_union_keeps_selection():
         assert set(np.flatnonzero(mask[h].any(axis=0)).tolist()) <= kept
 
 
+# ------------------------------------------------------------------ FP8
+def check_fp8_decoding():
+    """Every E4M3 byte against torch's float8_e4m3fn (an independent
+    implementation of the OCP format), plus hand-derived values."""
+    codes = np.arange(256, dtype=np.uint8)
+    got = O.fp8_e4m3_to_float(codes)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan) and nan.sum() == 2
+    assert np.array_equal(got[~nan], ref[~nan])
+    hand = {0x00: 0.0, 0x38: 1.0, 0x40: 2.0, 0x3C: 1.5, 0x7E: 448.0, 0x08: 2.0 ** -6, 0x01: 2.0 ** -9,
+            0x07: 7 * 2.0 ** -9, 0xC0: -2.0, 0xB8: -1.0, 0x80: -0.0}
+    for c, v in hand.items():
+        assert got[c] == v and np.signbit(got[c]) == np.signbit(v), (hex(c), got[c], v)
+
+
+def check_fp8_decode_sdpa():
+    """Decode over FP8 pages with per-page scales: the oracle's dequantised
+    pools give torch float64 SDPA on the dense values dequantised with torch's
+    own FP8 conversion."""
+    rng = np.random.default_rng(20)
+    B, T, Hq, Hkv, P, d = 2, 1, 4, 2, 4, 8
+    lens = (14, 9)
+    L = max(lens)
+    npg = (L + P - 1) // P
+    n_phys = B * npg + 1
+    kq = rng.integers(0, 256, size=(n_phys, Hkv, P, d)).astype(np.uint8)
+    vq = rng.integers(0, 256, size=(n_phys, Hkv, d, P)).astype(np.uint8)
+    kq[(kq & 0x7F) == 0x7F] = 0x30          # no NaN codes
+    vq[(vq & 0x7F) == 0x7F] = 0x30
+    ks = rng.uniform(0.001, 0.02, size=(n_phys, Hkv)).astype(np.float32)
+    vs = rng.uniform(0.1, 2.0, size=(n_phys, Hkv)).astype(np.float32)
+    perm = rng.permutation(n_phys)
+    bt = np.full((B, npg), -1, dtype=np.int32)
+    for b in range(B):
+        bt[b] = perm[b * npg:(b + 1) * npg]
+    q = rng.standard_normal((B, T, Hq, d))
+    kd = O.dequantize_pages(kq, ks)
+    vd = O.dequantize_pages(vq, vs)
+    sets = [[{0, 2}, {1, 3}], [{0, 1, 2}, {2}]]
+    lists, counts = _lists_from(sets, npg)
+    out, lse = O.sparse_decode(q, kd, vd, bt, np.array(lens), P, lists, counts, Hkv, O.PER_KV_HEAD, 0.35)
+    tk = torch.from_numpy(kq).view(torch.float8_e4m3fn).to(torch.float64).numpy() * ks[:, :, None, None]
+    tv = torch.from_numpy(vq).view(torch.float8_e4m3fn).to(torch.float64).numpy() * vs[:, :, None, None]
+    G = Hq // Hkv
+    for b in range(B):
+        for h in range(Hq):
+            g = h // G
+            toks = [(lp, r) for lp in sorted(sets[b][g]) for r in range(P) if lp * P + r < lens[b]]
+            K = np.stack([tk[bt[b, lp], g, r] for lp, r in toks])
+            V = np.stack([tv[bt[b, lp], g, :, r] for lp, r in toks])
+            eo, el = sdpa(q[b, :, h], K, V, 0.35, np.ones((T, len(toks)), bool))
+            assert np.allclose(out[b, :, h], eo, atol=1e-12) and np.allclose(lse[b, :, h], el, atol=1e-12), (b, h)
+
+
 ALL_CHECKS = [
     check_summary_constant_pages, check_summary_bruteforce,
     check_scores_exact_integers, check_scores_linearity_and_unfactored,
@@ -670,4 +725,5 @@ ALL_CHECKS = [
     check_union_bruteforce, check_union_golden,
     check_prefill_causal_sdpa, check_prefill_masked_sdpa,
     check_mask_bruteforce, check_mask_invariants, check_mask_union_keeps_selection,
+    check_fp8_decoding, check_fp8_decode_sdpa,
 ]

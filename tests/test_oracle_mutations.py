@@ -20,6 +20,8 @@ _orig_summary = O.page_summary
 _orig_sel_heads = O.selection_heads
 _orig_row_pages = O.row_pages
 _orig_mask = O.prefill_block_mask
+_orig_fp8 = O.fp8_e4m3_to_float
+_orig_deq = O.dequantize_pages
 
 
 def _no_scale(qrow, K, V, sm_scale, d_v):
@@ -129,7 +131,26 @@ def _mask_one_past_causal(q, mu, bt, seq_len, P, q_start, bq, nkb, n_kv, scale, 
     return m, sc
 
 
+def _fp8_bias_8(codes):
+    """Decode E4M3 with exponent bias 8 (the FNUZ variant's bias)."""
+    return _orig_fp8(codes) / 2.0
+
+
+def _fp8_no_subnormals(codes):
+    """Flush exponent-0 codes to zero."""
+    c = np.asarray(codes, dtype=np.int64)
+    v = _orig_fp8(codes)
+    return np.where(((c >> 3) & 0xF) == 0, 0.0 * v, v)
+
+
+def _deq_scale_ignored(pool, scale):
+    return _orig_deq(pool, np.ones_like(scale))
+
+
 MUTANTS = {
+    "fp8_bias_8": ("fp8_e4m3_to_float", _fp8_bias_8),
+    "fp8_no_subnormals": ("fp8_e4m3_to_float", _fp8_no_subnormals),
+    "fp8_page_scale_ignored": ("dequantize_pages", _deq_scale_ignored),
     "mask_sum_not_mean": ("prefill_block_mask", _mask_sum_not_mean),
     "mask_no_diagonal": ("prefill_block_mask", _mask_no_diagonal),
     "mask_one_past_causal": ("prefill_block_mask", _mask_one_past_causal),
