@@ -49,8 +49,8 @@
  *                  sequence b holds tokens [p*page_size, min((p+1)*page_size, len))
  *  - Supported shapes: page_size 16 or 64; (d_qk, d_v) = (64, 64) or (128, 128)
  *    with a V pool, (576, 512) without one; dtype bf16, or fp32 for the decode
- *    side (summary, select, decode) at d 64/128.  Anything else returns
- *    SA_ERR_UNSUPPORTED.
+ *    side (summary, select, decode) at d 64/128, or FP8 E4M3 pages (see
+ *    sa_dtype) at d 128.  Anything else returns SA_ERR_UNSUPPORTED.
  */
 #ifndef SPARSE_ATTN_H_
 #define SPARSE_ATTN_H_
@@ -72,7 +72,14 @@ typedef enum {
   SA_ERR_DATA = 5                /* debug validation found invalid device data */
 } sa_status;
 
-typedef enum { SA_DTYPE_BF16 = 0, SA_DTYPE_FP32 = 1 } sa_dtype;
+/* SA_DTYPE_FP8_E4M3: k_pool and v_pool hold OCP FP8 E4M3 bytes, with one
+ * fp32 scale per (physical page, KV head) for K (k_scale) and one for V
+ * (v_scale): an element's value is its E4M3 value times its page's scale
+ * ([UAE] "Key Design Decisions" 2 and "Milestones" Phase 3: quantized KV
+ * cache).  Queries and outputs are then bf16.  Supported by sa_page_summary,
+ * sa_select_pages (without refresh_newest_page), sa_prefill_block_mask and
+ * sa_sparse_decode, at d_qk == d_v == 128 with a V pool. */
+typedef enum { SA_DTYPE_BF16 = 0, SA_DTYPE_FP32 = 1, SA_DTYPE_FP8_E4M3 = 2 } sa_dtype;
 
 /* Selection granularity.  PER_KV_HEAD: one list per KV head, scored with the
  * query summed over the head's query group (GQA) and query tokens.
@@ -91,7 +98,9 @@ typedef struct {
   int32_t d_qk;
   int32_t d_v;
   int32_t max_pages;             /* row stride of block_table */
-  sa_dtype dtype;                /* element type of q, k_pool, v_pool and outputs */
+  sa_dtype dtype;                /* element type of q, k_pool, v_pool and outputs (FP8: of the pools) */
+  const float* k_scale;          /* FP8 only: [n_phys_pages][n_kv_heads] K scales (else NULL) */
+  const float* v_scale;          /* FP8 only: [n_phys_pages][n_kv_heads] V scales (else NULL) */
 } sa_paged_kv;
 
 /* ------------------------------------------------------------------------

@@ -25,6 +25,7 @@ SA_ERR_DEVICE = 4
 SA_ERR_DATA = 5
 SA_DTYPE_BF16 = 0
 SA_DTYPE_FP32 = 1
+SA_DTYPE_FP8_E4M3 = 2
 SA_SEL_PER_KV_HEAD = 0
 SA_SEL_PER_Q_HEAD = 1
 SA_NOALLOC_SCRATCH_BYTES = 64 << 20
@@ -42,7 +43,7 @@ class sa_paged_kv(ctypes.Structure):
     _fields_ = [("k_pool", c_void_p), ("v_pool", c_void_p), ("block_table", c_void_p),
                 ("seq_lens", c_void_p), ("n_phys_pages", c_int32), ("n_kv_heads", c_int32),
                 ("page_size", c_int32), ("d_qk", c_int32), ("d_v", c_int32), ("max_pages", c_int32),
-                ("dtype", c_int)]
+                ("dtype", c_int), ("k_scale", c_void_p), ("v_scale", c_void_p)]
 
 
 class SparseAttnError(RuntimeError):
@@ -121,15 +122,20 @@ def _dtype_code(t: torch.Tensor) -> int:
         return SA_DTYPE_BF16
     if t.dtype == torch.float32:
         return SA_DTYPE_FP32
+    if t.dtype in (torch.uint8, torch.float8_e4m3fn):
+        return SA_DTYPE_FP8_E4M3
     raise TypeError(f"unsupported dtype {t.dtype}")
 
 
 class PagedKV:
-    """Holds the paged cache tensors and the matching C descriptor."""
+    """Holds the paged cache tensors and the matching C descriptor.  FP8 pools
+    (uint8 or float8_e4m3fn E4M3 bytes) come with k_scale / v_scale
+    [n_phys][n_kv_heads] fp32; queries and outputs are then bf16."""
 
     def __init__(self, k_pool: torch.Tensor, v_pool: Optional[torch.Tensor], block_table: torch.Tensor,
-                 seq_lens: torch.Tensor, d_v: Optional[int] = None):
-        for t in (k_pool, v_pool, block_table, seq_lens):
+                 seq_lens: torch.Tensor, d_v: Optional[int] = None, k_scale: Optional[torch.Tensor] = None,
+                 v_scale: Optional[torch.Tensor] = None):
+        for t in (k_pool, v_pool, block_table, seq_lens, k_scale, v_scale):
             if t is not None and not t.is_contiguous():
                 raise ValueError("paged cache tensors must be contiguous")
         if block_table.dtype != torch.int32 or seq_lens.dtype != torch.int32:
@@ -140,14 +146,20 @@ class PagedKV:
             d_v = v_pool.shape[2]
         elif d_v is None:
             d_v = 512
+        code = _dtype_code(k_pool)
+        if code == SA_DTYPE_FP8_E4M3 and (k_scale is None or v_scale is None):
+            raise ValueError("FP8 pools need k_scale and v_scale")
+        self.k_scale, self.v_scale = k_scale, v_scale
         self.c = sa_paged_kv(k_pool.data_ptr(), None if v_pool is None else v_pool.data_ptr(),
                              block_table.data_ptr(), seq_lens.data_ptr(), n_phys, n_kv, P, d_qk, d_v,
-                             block_table.shape[1], _dtype_code(k_pool))
+                             block_table.shape[1], code,
+                             None if k_scale is None else k_scale.data_ptr(),
+                             None if v_scale is None else v_scale.data_ptr())
         self.batch = block_table.shape[0]
         self.n_kv_heads, self.page_size, self.d_qk, self.d_v = n_kv, P, d_qk, d_v
         self.max_pages = block_table.shape[1]
         self.device = k_pool.device
-        self.dtype = k_pool.dtype
+        self.dtype = torch.bfloat16 if code == SA_DTYPE_FP8_E4M3 else k_pool.dtype   # of queries and outputs
 
     @property
     def ref(self):

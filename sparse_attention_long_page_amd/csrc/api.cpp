@@ -67,8 +67,13 @@ sa_status check_kv(const sa_paged_kv* kv, bool need_pools) {
   if (need_pools && !kv->k_pool) return fail(SA_ERR_INVALID_ARGUMENT, "k_pool is NULL");
   if (kv->n_phys_pages <= 0 || kv->n_kv_heads <= 0 || kv->max_pages <= 0)
     return fail(SA_ERR_INVALID_ARGUMENT, "n_phys_pages/n_kv_heads/max_pages must be positive");
-  if (kv->dtype != SA_DTYPE_BF16 && kv->dtype != SA_DTYPE_FP32)
+  if (kv->dtype != SA_DTYPE_BF16 && kv->dtype != SA_DTYPE_FP32 && kv->dtype != SA_DTYPE_FP8_E4M3)
     return fail(SA_ERR_INVALID_ARGUMENT, "unknown dtype %d", (int)kv->dtype);
+  if (kv->dtype == SA_DTYPE_FP8_E4M3) {
+    if (!kv->v_pool || kv->d_qk != 128 || kv->d_v != 128)
+      return fail(SA_ERR_UNSUPPORTED, "FP8 pages need a V pool and d_qk == d_v == 128");
+    if (!kv->k_scale || !kv->v_scale) return fail(SA_ERR_INVALID_ARGUMENT, "FP8 pages need k_scale and v_scale");
+  }
   if (kv->page_size != 16 && kv->page_size != 64)
     return fail(SA_ERR_UNSUPPORTED, "page_size %d unsupported (16 or 64)", kv->page_size);
   const bool latent = kv->v_pool == nullptr;
@@ -278,7 +283,7 @@ sa_status sa_prefill_block_mask(const sa_paged_kv* kv, int32_t seq, const void* 
   mp.top_k = top_k < 0 ? -1 : top_k;
   mp.sm_scale = sm_scale;
   mp.max_gap = top_k < 0 ? max_gap : 0.f;
-  return device_status(sa::launch_block_mask(mp, kv->dtype == SA_DTYPE_BF16, kv->d_qk, stream), "block mask launch");
+  return device_status(sa::launch_block_mask(mp, kv->dtype != SA_DTYPE_FP32, kv->d_qk, stream), "block mask launch");
 }
 
 // ------------------------------------------------------------------ summary
@@ -305,6 +310,7 @@ sa_status sa_page_summary(const sa_paged_kv* kv, int32_t batch, int32_t last_pag
     st = v.finish(kv, 0);
     if (st != SA_OK) return st;
   }
+  p.k_scale = kv->dtype == SA_DTYPE_FP8_E4M3 ? kv->k_scale : nullptr;
   return device_status(sa::launch_page_summary(p, batch, kv->dtype == SA_DTYPE_BF16, stream), "page_summary launch");
 }
 
@@ -341,6 +347,8 @@ sa_status sa_select_pages(const sa_paged_kv* kv, int32_t batch, const void* q, i
     return fail(SA_ERR_INVALID_ARGUMENT, "list_stride %d < min(max_pages, sink+window+top_k) = %ld", list_stride,
                 need_stride);
   const int n_sel = n_sel_of(kv, n_q_heads, mode);
+  if (refresh_newest_page && kv->dtype == SA_DTYPE_FP8_E4M3)
+    return fail(SA_ERR_UNSUPPORTED, "refresh_newest_page is not supported for FP8 pages (use sa_page_summary)");
   if (refresh_newest_page && (scores || !page_summary))
     return fail(SA_ERR_INVALID_ARGUMENT, "refresh_newest_page needs page_summary and router scores (no scores)");
   if (scores) {
@@ -398,7 +406,7 @@ sa_status sa_select_pages(const sa_paged_kv* kv, int32_t batch, const void* q, i
     p.refresh = refresh_newest_page ? 1 : 0;
     p.k_pool = kv->k_pool;
     p.mu_out = page_summary;
-    return device_status(sa::launch_score_select(p, sp, batch, kv->dtype == SA_DTYPE_BF16, stream),
+    return device_status(sa::launch_score_select(p, sp, batch, kv->dtype != SA_DTYPE_FP32, stream),
                          "score_select launch");
   }
   if (!scores) {
@@ -439,7 +447,7 @@ sa_status sa_select_pages(const sa_paged_kv* kv, int32_t batch, const void* q, i
     smp.d = kv->d_qk;
     smp.max_pages = kv->max_pages;
     smp.last_pages = 1;
-    const bool bf16 = kv->dtype == SA_DTYPE_BF16;
+    const bool bf16 = kv->dtype != SA_DTYPE_FP32;   // the query's type (bf16 for FP8 pages)
     hipError_t e = sa::launch_select_prep(smp, p, bf16, refresh_newest_page != 0, qbar, arrivals, stream);
     if (e != hipSuccess) return device_status(e, "select prep launch");
     const bool pooled = pooled_rows > sa::kScoreInlineRows;
@@ -468,7 +476,7 @@ static sa_status check_decode_shape(const sa_paged_kv* kv, int32_t batch, int32_
       return fail(SA_ERR_UNSUPPORTED, "latent decode needs q_tokens in {1, 2, 4, 8, 16}, got %d", q_tokens);
     if (kv->page_size != 64) return fail(SA_ERR_UNSUPPORTED, "latent decode needs page_size 64");
     if (n_q_heads > 256) return fail(SA_ERR_UNSUPPORTED, "latent decode supports up to 256 query heads");
-  } else if (kv->dtype == SA_DTYPE_BF16) {
+  } else if (kv->dtype != SA_DTYPE_FP32) {
     const int rows = mode == SA_SEL_PER_KV_HEAD ? q_tokens * G : q_tokens;
     if (rows > 16)
       return fail(SA_ERR_UNSUPPORTED, "%d query rows share a KV head; the bf16 decode tile holds 16", rows);
@@ -563,8 +571,11 @@ static sa_status decode_launch(const sa_paged_kv* kv, int32_t batch, const void*
   p.d_v = kv->d_v;
   p.splits = splits;
   p.scale_log2 = sm_scale * sa::kLog2e;
+  p.fp8 = kv->dtype == SA_DTYPE_FP8_E4M3 ? 1 : 0;
+  p.k_scale = kv->k_scale;
+  p.v_scale = kv->v_scale;
   hipError_t e = is_latent(kv) ? sa::launch_mla_decode(p, stream)
-                               : sa::launch_decode(p, kv->dtype == SA_DTYPE_BF16, stream);
+                               : sa::launch_decode(p, kv->dtype != SA_DTYPE_FP32, stream);
   if (e != hipSuccess) return device_status(e, "decode launch");
   if (splits > 1) {
     sa::MergeParams mp{};

@@ -91,6 +91,7 @@ struct SummaryParams {
   const int32_t* seq_lens;
   float* mu;
   int n_kv, P, d, max_pages, last_pages;
+  const float* k_scale;      // FP8 pages: [n_phys][n_kv] scales (null otherwise)
 };
 
 struct ScoreParams {
@@ -136,6 +137,9 @@ struct DecodeParams {
   int B, T, Hq, Hkv, G, n_sel, per_q, list_stride, max_pages, mask_words;
   int P, d_qk, d_v, splits;
   float scale_log2;          // sm_scale * log2(e)
+  int fp8;                   // K/V pools hold OCP E4M3 bytes with per-(page, KV head) scales
+  const float* k_scale;      // [n_phys][Hkv] (fp8 only)
+  const float* v_scale;
 };
 
 struct MergeParams {

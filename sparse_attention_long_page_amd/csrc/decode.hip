@@ -33,7 +33,7 @@
 namespace sa {
 
 // ---------------------------------------------------------------- bf16 / MFMA
-template <int D, int P, bool TIERED, bool STAGED>
+template <int D, int P, bool TIERED, bool STAGED, bool FP8>
 __global__ __launch_bounds__(256, 2) void decode_bf16_kernel(DecodeParams p, const int32_t* __restrict__ lists,
                                                             const int32_t* __restrict__ btab,
                                                             const int32_t* __restrict__ seq_lens,
@@ -223,15 +223,22 @@ hipError_t launch_decode(const DecodeParams& p, int bf16, hipStream_t s) {
     else hipLaunchKernelGGL(decode_f32_kernel<128>, grid, block, 0, s, p);
     return hipGetLastError();
   }
-#define SA_DECODE_LAUNCH(D_, P_, ST_)                                                                   \
+#define SA_DECODE_LAUNCH3(D_, P_, ST_, F8_)                                                             \
   do {                                                                                                  \
     if (tiered)                                                                                         \
-      hipLaunchKernelGGL((decode_bf16_kernel<D_, P_, true, ST_>), grid, block, 0, s, p, p.lists,            \
+      hipLaunchKernelGGL((decode_bf16_kernel<D_, P_, true, ST_, F8_>), grid, block, 0, s, p, p.lists,       \
                          p.block_table, p.seq_lens, p.counts);                                          \
     else                                                                                                \
-      hipLaunchKernelGGL((decode_bf16_kernel<D_, P_, false, ST_>), grid, block, 0, s, p, p.lists,           \
+      hipLaunchKernelGGL((decode_bf16_kernel<D_, P_, false, ST_, F8_>), grid, block, 0, s, p, p.lists,      \
                          p.block_table, p.seq_lens, p.counts);                                          \
   } while (0)
+#define SA_DECODE_LAUNCH(D_, P_, ST_) SA_DECODE_LAUNCH3(D_, P_, ST_, false)
+  if (p.fp8) {
+    // FP8 pages: register operands (d 128)
+    if (p.P == 16) SA_DECODE_LAUNCH3(128, 16, false, true);
+    else SA_DECODE_LAUNCH3(128, 64, false, true);
+    return hipGetLastError();
+  }
   // staged operands for per-KV-head lists at d 128 (pages read by one
   // workgroup only); register operands otherwise
   const bool staged = !p.per_q;
@@ -245,6 +252,7 @@ hipError_t launch_decode(const DecodeParams& p, int bf16, hipStream_t s) {
     else SA_DECODE_LAUNCH(128, 64, false);
   }
 #undef SA_DECODE_LAUNCH
+#undef SA_DECODE_LAUNCH3
   return hipGetLastError();
 }
 

@@ -43,7 +43,7 @@ __global__ __launch_bounds__(kSelThreads, 1) void select_decode_kernel(ScorePara
   for (int i = threadIdx.x; i < count; i += kSelThreads) lrow[i] = list[i];
   if (threadIdx.x >= 256) return;
   {
-    constexpr bool TIERED = false, STAGED = true;
+    constexpr bool TIERED = false, STAGED = true, FP8 = false;
     constexpr int KSTEPS = D / 32;
     constexpr int DTILES = D / 16;
     constexpr int E = 64 / P;

@@ -46,7 +46,19 @@ __device__ __forceinline__ void summary_page(const SummaryParams& p, int g, int 
 #pragma unroll
       for (int i = 0; i < R; ++i) {
         const uint32_t keep = ts + i * TS < nv ? 0xffffffffu : 0u;
-        if constexpr (sizeof(T) == 2) {
+        if constexpr (sizeof(T) == 1) {
+          // OCP E4M3 bytes -> exact values (via bf16); the page scale is applied to the sum
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            const uint32_t v = w[i][c] & keep;
+            const uint32_t lo = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v, 1.0f, false));
+            const uint32_t hi = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v, 1.0f, true));
+            acc[4 * c] += (double)bf16_lo(lo);
+            acc[4 * c + 1] += (double)bf16_hi(lo);
+            acc[4 * c + 2] += (double)bf16_lo(hi);
+            acc[4 * c + 3] += (double)bf16_hi(hi);
+          }
+        } else if constexpr (sizeof(T) == 2) {
 #pragma unroll
           for (int c = 0; c < 4; ++c) {
             acc[2 * c] += (double)bf16_lo(w[i][c] & keep);
@@ -66,10 +78,13 @@ __device__ __forceinline__ void summary_page(const SummaryParams& p, int g, int 
   }
   __syncthreads();
   float* out = p.mu + ((size_t)phys * p.n_kv + g) * p.d;
+  // FP8: sum of the page's values times its scale (both exact in float64:
+  // E4M3 values carry 4 significant bits, the scale 24)
+  const double scale = sizeof(T) == 1 ? (double)p.k_scale[(size_t)phys * p.n_kv + g] : 1.0;
   for (int e = t; e < p.d; e += 256) {
     double sum = 0.0;
     for (int ts = 0; ts < TS; ++ts) sum += part[ts * p.d + e];
-    out[e] = (float)(sum / (double)nv);
+    out[e] = (float)(sum * scale / (double)nv);
   }
 }
 
@@ -88,7 +103,9 @@ __global__ __launch_bounds__(256) void page_summary_kernel(SummaryParams p) {
 hipError_t launch_page_summary(const SummaryParams& p, int batch, int bf16, hipStream_t s) {
   const int slots = p.last_pages > 0 ? p.last_pages : p.max_pages;
   dim3 grid(p.n_kv, slots, batch);
-  if (bf16)
+  if (p.k_scale)
+    hipLaunchKernelGGL((page_summary_kernel<uint8_t, 16>), grid, dim3(256), 0, s, p);
+  else if (bf16)
     hipLaunchKernelGGL((page_summary_kernel<uint16_t, 8>), grid, dim3(256), 0, s, p);
   else
     hipLaunchKernelGGL((page_summary_kernel<float, 4>), grid, dim3(256), 0, s, p);

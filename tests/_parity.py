@@ -141,6 +141,16 @@ def compare_outputs(gpu_out, gpu_lse, ref_out, ref_lse, fp32=False, rows_mask=No
     return max_abs, mean_abs, lse_err
 
 
+def oracle_pools(inp):
+    """The K and V pools as the oracle reads them: float64 values, dequantised
+    (E4M3 value times the page's scale) for FP8 pages."""
+    if inp.get("k_scale") is not None:
+        k = O.dequantize_pages(npi(inp["k_pool"]), npi(inp["k_scale"]))
+        v = None if inp["v_pool"] is None else O.dequantize_pages(npi(inp["v_pool"]), npi(inp["v_scale"]))
+        return k, v
+    return np64(inp["k_pool"]), (None if inp["v_pool"] is None else np64(inp["v_pool"]))
+
+
 def sub_pool(inp, b_idx):
     """Host copy of the pages of sequences ``b_idx`` with a compact block table (harness plumbing)."""
     bt = inp["block_table"]
@@ -152,8 +162,10 @@ def sub_pool(inp, b_idx):
         pages.append(bt[b, :n].long())
         rows.append(n)
     allp = torch.cat(pages)
-    kp = np64(inp["k_pool"][allp])
-    vp = np64(inp["v_pool"][allp]) if inp["v_pool"] is not None else None
+    sub = {"k_pool": inp["k_pool"][allp], "v_pool": None if inp["v_pool"] is None else inp["v_pool"][allp],
+           "k_scale": None if inp.get("k_scale") is None else inp["k_scale"][allp],
+           "v_scale": None if inp.get("v_scale") is None else inp["v_scale"][allp]}
+    kp, vp = oracle_pools(sub)
     maxn = bt.shape[1]
     nbt = np.full((len(b_idx), maxn), -1, dtype=np.int32)
     off = 0

@@ -9,7 +9,7 @@ import torch
 import oracle.sparse_attn_oracle as O
 import sparse_attention_long_page_amd as S
 import workloads as W
-from _parity import check_page_lists, compare_outputs, np64, npi, sub_pool
+from _parity import check_page_lists, compare_outputs, np64, npi, oracle_pools, sub_pool
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -22,7 +22,8 @@ def gpu_inputs(cpu):
 
 
 def make_kv(inp, wl):
-    return S.PagedKV(inp["k_pool"], inp["v_pool"], inp["block_table"], inp["seq_lens"], d_v=wl.d_v)
+    return S.PagedKV(inp["k_pool"], inp["v_pool"], inp["block_table"], inp["seq_lens"], d_v=wl.d_v,
+                     k_scale=inp.get("k_scale"), v_scale=inp.get("v_scale"))
 
 
 def oracle_chain(cpu, wl):
@@ -33,7 +34,7 @@ def oracle_chain(cpu, wl):
     if wl.scores == "gumbel":
         scores = npi(cpu["scores"])
     else:
-        mu = O.page_summary(np64(cpu["k_pool"]), bt, lens, wl.page_size)
+        mu = O.page_summary(oracle_pools(cpu)[0], bt, lens, wl.page_size)
         scores = O.page_scores(np64(cpu["q"]), mu, bt, lens, wl.page_size, wl.n_kv_heads, wl.mode)
     lists, counts, cc = O.select_pages(scores, npg, wl.sink_pages, wl.window_pages, wl.top_k, wl.critical_k)
     return mu, scores, lists, counts, cc, npg
@@ -58,7 +59,7 @@ def test_page_summary_matches_oracle(name):
     inp = gpu_inputs(cpu)
     mu_gpu = S.sa_page_summary(make_kv(inp, wl))
     torch.cuda.synchronize()
-    mu_ref = O.page_summary(np64(cpu["k_pool"]), npi(cpu["block_table"]), npi(cpu["seq_lens"]), wl.page_size)
+    mu_ref = O.page_summary(oracle_pools(cpu)[0], npi(cpu["block_table"]), npi(cpu["seq_lens"]), wl.page_size)
     got = mu_gpu.cpu().numpy()
     ref_pages = ~np.isnan(mu_ref[:, 0, 0])
     assert np.isnan(got[~ref_pages]).all(), "pages outside every sequence must stay untouched"
@@ -132,7 +133,7 @@ def test_select_matches_oracle(name):
     assert rep.exact + rep.band_events == rep.units
 
 
-@pytest.mark.parametrize("name", [n for n, w in SELECT_CASES.items() if w.scores == "summary"])
+@pytest.mark.parametrize("name", [n for n, w in SELECT_CASES.items() if w.scores == "summary" and w.dtype != "fp8"])
 def test_select_with_summary_refresh_matches_separate_calls(name):
     """refresh_newest_page: the selection first rewrites each sequence's
     newest-page summary (fused into the score+select kernel when there are
@@ -320,7 +321,7 @@ def test_decode_matches_oracle(name, splits):
     out, lse = S.sa_sparse_decode(kv, inp["q"], lists, counts, mode=MODE[wl.mode], sm_scale=wl.sm_scale,
                                   num_splits=splits)
     torch.cuda.synchronize()
-    ref_o, ref_l = O.sparse_decode(np64(cpu["q"]), np64(cpu["k_pool"]), np64(cpu["v_pool"]),
+    ref_o, ref_l = O.sparse_decode(np64(cpu["q"]), *oracle_pools(cpu),
                                    npi(cpu["block_table"]), npi(cpu["seq_lens"]), wl.page_size, o_lists,
                                    o_counts, wl.n_kv_heads, wl.mode, wl.sm_scale)
     compare_outputs(out, lse, ref_o, ref_l, fp32=wl.dtype == "fp32")
@@ -347,7 +348,7 @@ def test_tiered_small_heads_matches_oracle(name):
                                   critical_counts=torch.from_numpy(o_cc).to(DEV), ambient_head_mask=amask,
                                   num_splits=2)
     torch.cuda.synchronize()
-    ref_o, ref_l = O.sparse_decode(np64(cpu["q"]), np64(cpu["k_pool"]), np64(cpu["v_pool"]),
+    ref_o, ref_l = O.sparse_decode(np64(cpu["q"]), *oracle_pools(cpu),
                                    npi(cpu["block_table"]), npi(cpu["seq_lens"]), wl.page_size, o_lists,
                                    o_counts, wl.n_kv_heads, wl.mode, wl.sm_scale, o_cc,
                                    npi(cpu["ambient_mask"]).astype(np.int64) & 0xffffffff)
@@ -435,6 +436,12 @@ def test_full_size_llama3_decode_32k_sampled():
     print(f"max_abs {mx:.3e} mean_abs {mean:.3e} lse {lse_err:.3e} band events {rep.band_events}/{rep.units}")
 
 
+def test_full_size_llama3_decode_32k_fp8_sampled():
+    """The Llama-3 32K layer over FP8 pages with per-page scales."""
+    (mx, mean, lse_err), rep = _full_size_check(W.LLAMA3_DECODE_32K_FP8, seed=17, n_sample=4)
+    print(f"max_abs {mx:.3e} mean_abs {mean:.3e} lse {lse_err:.3e} band events {rep.band_events}/{rep.units}")
+
+
 def test_full_size_token_head_decode_128k_sampled():
     (mx, mean, lse_err), rep = _full_size_check(W.TOKEN_HEAD_DECODE_128K, seed=12, n_sample=2)
     print(f"max_abs {mx:.3e} mean_abs {mean:.3e} lse {lse_err:.3e} band events {rep.band_events}/{rep.units}")
@@ -485,7 +492,7 @@ def test_select_decode_equals_select_then_decode(name, refresh):
                                wl.top_k, None)
         assert not rep.failures, rep.failures[:5]
         assert rep.exact == rep.units
-        ref_o, ref_l = O.sparse_decode(np64(cpu["q"]), np64(cpu["k_pool"]), np64(cpu["v_pool"]),
+        ref_o, ref_l = O.sparse_decode(np64(cpu["q"]), *oracle_pools(cpu),
                                        npi(cpu["block_table"]), npi(cpu["seq_lens"]), wl.page_size, o_lists,
                                        o_counts, wl.n_kv_heads, wl.mode, wl.sm_scale)
         compare_outputs(got[2], got[3], ref_o, ref_l)
@@ -535,7 +542,7 @@ def test_select_decode_short_and_empty_sequences(refresh):
     for b in range(wl.batch):
         for s in range(wl.n_sel):
             assert np.array_equal(g_lists[b, s, :g_counts[b, s]], o_lists[b, s, :o_counts[b, s]]), (b, s)
-    ref_o, ref_l = O.sparse_decode(np64(cpu["q"]), np64(cpu["k_pool"]), np64(cpu["v_pool"]),
+    ref_o, ref_l = O.sparse_decode(np64(cpu["q"]), *oracle_pools(cpu),
                                    npi(cpu["block_table"]), npi(cpu["seq_lens"]), wl.page_size, o_lists,
                                    o_counts, wl.n_kv_heads, wl.mode, wl.sm_scale)
     compare_outputs(got[2], got[3], ref_o, ref_l)

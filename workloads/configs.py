@@ -47,7 +47,7 @@ class DecodeWorkload:
     n_kv_heads: int
     d_qk: int
     d_v: int
-    dtype: str                 # "bf16" | "fp32"
+    dtype: str                 # "bf16" | "fp32" | "fp8" (E4M3 K/V pages with per-page scales, bf16 q)
     context: int               # tokens per sequence (unless seq_lens given)
     page_size: int
     mode: str                  # "per_kv_head" | "per_q_head"
@@ -168,8 +168,11 @@ MLA_TIERED_DECODE_64K = DecodeWorkload(
     d_v=512, dtype="bf16", context=65536, page_size=64, mode="per_kv_head",
     sink_pages=0, window_pages=0, top_k=40, critical_k=8, ambient_heads=32, latent=True)
 
+# the Llama-3-8B decode layer over FP8 K/V pages (one scale per page and KV head)
+LLAMA3_DECODE_32K_FP8 = LLAMA3_DECODE_32K.replace(name="llama3_8b_decode_32k_fp8", dtype="fp8")
+
 FULL = {w.name: w for w in (TINY_DECODE, LLAMA3_DECODE_32K, TOKEN_HEAD_DECODE_128K,
-                             CHUNKED_PREFILL_128K, MLA_TIERED_DECODE_64K)}
+                             CHUNKED_PREFILL_128K, MLA_TIERED_DECODE_64K, LLAMA3_DECODE_32K_FP8)}
 
 # ---------------------------------------------------------- parity variants
 # Same structure as the full-size cases, sized so the oracle finishes in
@@ -208,6 +211,13 @@ SMALL = {
     "fp32_d64_p16_q_small": TINY_DECODE.replace(
         name="fp32_d64_p16_q_small", batch=2, n_q_heads=4, n_kv_heads=2, mode="per_q_head", context=0,
         seq_lens=(16 * 50 + 3, 16 * 31), top_k=7, sink_pages=1, window_pages=3),
+    # FP8 K/V pages: per-KV-head lists on pages of 64, per-query-head lists on pages of 16
+    "fp8_d128_p64_kv_small": LLAMA3_DECODE_32K.replace(
+        name="fp8_d128_p64_kv_small", dtype="fp8", batch=3, n_q_heads=8, n_kv_heads=2, context=0,
+        seq_lens=(64 * 37 + 13, 64 * 20, 64 * 9 + 1), top_k=7, sink_pages=1, window_pages=2, extra_pool_pages=5),
+    "fp8_d128_p16_q_small": TOKEN_HEAD_DECODE_128K.replace(
+        name="fp8_d128_p16_q_small", dtype="fp8", batch=2, n_q_heads=8, n_kv_heads=2, context=16 * 301,
+        top_k=30, num_splits=4),
     "chunked_prefill_small": CHUNKED_PREFILL_128K.replace(
         name="chunked_prefill_small", n_q_heads=8, n_kv_heads=2, q_len=200, q_start=1000,
         random_fraction=0.3, extra_pool_pages=3),

@@ -7,8 +7,10 @@ method's arithmetic (no page means, scores, selection or attention), so the
 HIP path and the oracle can both consume its output without sharing code.
 
 Layouts (the library's interface):
-  q            [batch][q_tokens][n_q_heads][d_qk]
+  q            [batch][q_tokens][n_q_heads][d_qk]  (bf16 for an fp8 cache)
   k_pool       [n_phys_pages][n_kv_heads][page_size][d_qk]   token-major page
+               (fp8: OCP E4M3 bytes, with k_scale / v_scale [n_phys][n_kv_heads]
+               fp32, one per page and KV head; None otherwise)
   v_pool       [n_phys_pages][n_kv_heads][d_v][page_size]    page-transposed
   block_table  [batch][max_pages] int32, logical page -> physical page, -1 unused
   seq_lens     [batch] int32
@@ -31,7 +33,19 @@ import torch
 
 from .configs import DecodeWorkload, PrefillWorkload
 
-_DT = {"bf16": torch.bfloat16, "fp32": torch.float32}
+_DT = {"bf16": torch.bfloat16, "fp32": torch.float32, "fp8": torch.bfloat16}   # fp8: the query stays bf16
+FP8_MAX = 448.0   # largest finite OCP E4M3 value
+
+
+def _quantize_pages(x: torch.Tensor):
+    """fp32 pages [n_phys][Hkv][...] -> (OCP E4M3 bytes as uint8, fp32 scale
+    [n_phys][Hkv]): one scale per page and KV head, amax / 448, so each page's
+    largest magnitude maps to the largest finite code (a cache writer's
+    quantisation; the values are then what the pages hold)."""
+    amax = x.abs().flatten(2).amax(dim=-1)
+    scale = torch.where(amax > 0, amax / FP8_MAX, torch.ones_like(amax)).to(torch.float32)
+    q = (x / scale.reshape(scale.shape + (1,) * (x.dim() - 2))).clamp(-FP8_MAX, FP8_MAX)
+    return q.to(torch.float8_e4m3fn).view(torch.uint8), scale
 
 
 def _gen(device, seed: int, stream: int) -> torch.Generator:
@@ -98,12 +112,21 @@ def make_decode_inputs(wl: DecodeWorkload, device="cpu", seed: int = 0) -> Dict[
                 pick = torch.randperm(eligible, generator=g_struct, device=dev)[:n_plant] + lo
                 phys = block_table[b, pick].long()
                 k32[phys, g] += wl.plant_offset * u[b, g]
-    k_pool = k32.to(dt)
+    k_scale = v_scale = None
+    if wl.dtype == "fp8":
+        k_pool, k_scale = _quantize_pages(k32)
+    else:
+        k_pool = k32.to(dt)
     del k32
     if wl.latent:
         v_pool = None
     else:
-        v_pool = torch.randn((n_phys, Hkv, wl.d_v, P), generator=_gen(dev, seed, 3), device=dev).to(dt)
+        v32 = torch.randn((n_phys, Hkv, wl.d_v, P), generator=_gen(dev, seed, 3), device=dev)
+        if wl.dtype == "fp8":
+            v_pool, v_scale = _quantize_pages(v32)
+        else:
+            v_pool = v32.to(dt)
+        del v32
 
     scores = None
     if wl.scores == "gumbel":
@@ -125,7 +148,7 @@ def make_decode_inputs(wl: DecodeWorkload, device="cpu", seed: int = 0) -> Dict[
         ambient_mask = _pack_head_bits(sel)
 
     return dict(q=q, k_pool=k_pool, v_pool=v_pool, block_table=block_table, seq_lens=seq_lens,
-                scores=scores, ambient_mask=ambient_mask)
+                scores=scores, ambient_mask=ambient_mask, k_scale=k_scale, v_scale=v_scale)
 
 
 def make_prefill_inputs(wl: PrefillWorkload, device="cpu", seed: int = 0) -> Dict[str, torch.Tensor]:
