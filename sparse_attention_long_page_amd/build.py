@@ -62,6 +62,15 @@ def build(verbose: bool = True) -> str:
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stdout}{r.stderr}")
+    # a kernel template whose host-side instantiation failed leaves its launch
+    # stub undefined, which would only show when the library is loaded: fail here
+    nm = shutil.which("nm")
+    if nm:
+        r = subprocess.run([nm, "-D", "--undefined-only", tmp], capture_output=True, text=True)
+        missing = [l.split()[-1] for l in r.stdout.splitlines() if l.split() and l.split()[-1].startswith("_ZN2sa")]
+        if missing:
+            os.remove(tmp)
+            raise RuntimeError(f"undefined library symbols after linking: {missing}")
     os.replace(tmp, LIB)
     if verbose:
         print(f"built {LIB}")

@@ -72,6 +72,20 @@ __device__ __forceinline__ __attribute__((address_space(3))) void* lds_ptr(const
   return (__attribute__((address_space(3))) void*)(const_cast<void*>(p));
 }
 
+// Raw buffer resource over [base, base + bytes): lanes whose offset falls past
+// it read zeros.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, kBufferRsrcWord3);
+}
+
+// One wave-wide 16-byte-per-lane copy from global memory into LDS: lane l's
+// 16 bytes at byte offset voff of the resource land at lds + 16 l.  A buffer
+// instruction counts on the vector-memory counter only (the global-load form
+// of the same copy also makes the compiler wait for every LDS read at once).
+__device__ __forceinline__ void copy16_to_lds(__amdgpu_buffer_rsrc_t rsrc, const void* lds, uint32_t voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, lds_ptr(lds), 16, voff, 0, 0, 0);
+}
+
 // Number of valid tokens of logical page `lp` in a sequence of `len` tokens.
 __device__ __forceinline__ int page_valid(int len, int lp, int P) {
   int r = len - lp * P;

@@ -144,13 +144,12 @@ __global__ __launch_bounds__(256, 1) void mla_decode_kernel(DecodeParams p) {
   // the global-load form it waits for every LDS read at once).
   auto stage = [&](uint16_t* buf, int phys, int i_lo, int i_hi) {
     const uint16_t* src = kpool + (size_t)phys * p.Hkv * kMP * kMD;
-    const __amdgpu_buffer_rsrc_t rsrc =
-        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(src), 0, kMP * kMD * 2, kBufferRsrcWord3);
+    const auto rsrc = buffer_rsrc(src, kMP * kMD * 2);
     for (int i = i_lo + ((wave - i_lo) & 3); i < i_hi; i += 4) {
       const int c = 64 * i + lane;
       const int r = c / kMRowChunks, ch = c % kMRowChunks;
       const int sch = ch < kMRowChunks - 1 ? ch : 0;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, lds_ptr(buf + i * 512), 16, (r * kMD + 8 * sch) * 2, 0, 0, 0);
+      copy16_to_lds(rsrc, buf + i * 512, (r * kMD + 8 * sch) * 2);
     }
   };
 
