@@ -1,29 +1,31 @@
-"""Benchmark of the sparse-decode hot path on one MI355X.
+"""Benchmark of the sparse-attention hot path on one MI355X.
 
 Default workload (the headline metric): Llama-3-8B-shaped decode layer,
 batch 32, 32 query / 8 KV heads, d 128, bf16, 32768 tokens per sequence in
 pages of 64 in a shuffled shared pool, sink 1 page + window 8 pages + top-41
 pages per KV head (3200 of 32768 tokens, ~90% sparsity).
 
-One step = one decode layer's sparse-attention work for one batch:
-  sa_page_summary(last_pages=1)  mean key of the page the newest token landed in
-  sa_select_pages                router scores + sink/window/top-k lists
-  sa_sparse_decode               split-K flash-decode over the lists (+ merge)
-The timed loop replays one HIP graph that holds one step per input set, run
-back to back as consecutive layers' attention runs inside a captured decode
-forward pass, so neither the host's launch cost nor a graph launch leaves the
-GPU idle between steps; every kernel runs in every step, and exactly --steps
-steps are timed (whole graphs, then single-step graphs for the remainder).
-The same steps replayed one graph per step are timed too
-(ms_per_step_single_step_graphs).  Inputs are
-resident in HBM before timing; steps rotate over 3 independently drawn input
-sets (4.2 GB each) so no step finds its pages in the 256 MB last-level cache
-left warm by the previous one.
+One step = one decode layer's sparse-attention work for one batch.  For the
+default workload it is one sa_select_decode call: the newest page's mean key
+is recomputed, every page is scored against the pooled query, the sink /
+window / top-k lists are selected and the selected pages are attended, in one
+kernel (--two-calls runs it as sa_select_pages + sa_sparse_decode, which the
+other decode workloads always do; the FP8 variant selects from the page
+summaries without the newest-page refresh).  The timed loop replays one HIP
+graph that holds one step per input set, run back to back as consecutive
+layers' attention runs inside a captured decode forward pass; every kernel
+runs in every step, and exactly --steps steps are timed (whole graphs, then
+single-step graphs for the remainder).  The same steps are also replayed one
+graph per step (ms_per_step_single_step_graphs) and, one by one between HIP
+event pairs, give the per-step median and 10th / 90th percentiles
+(step_us_p10_p50_p90).  Inputs are resident in HBM before timing; steps rotate
+over 3 independently drawn input sets (4.2 GB each) so no step finds its pages
+in the 256 MB last-level cache left warm by the previous one.
 
 Prints one JSON line: value = selected K+V bytes per step / step time (GB/s);
-roofline of the dominant kernel (the decode) from HIP events on the launch
-stream; cpu_baseline = the CPU oracle on a bounded sample of the same
-workload (two sequences), in the same unit.
+roofline of the dominant kernel from HIP events on the launch stream;
+cpu_baseline = the CPU oracle on a bounded sample of the same workload (8 of
+the 32 sequences, the full step), in the same unit.
 """
 from __future__ import annotations
 
@@ -50,7 +52,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="llama3_8b_decode_32k",
                     choices=["llama3_8b_decode_32k", "token_head_decode_128k", "mla_tiered_decode_64k",
-                             "chunked_prefill_128k", "tiny_decode", "hbm_copy"])
+                             "chunked_prefill_128k", "tiny_decode", "llama3_8b_decode_32k_fp8", "hbm_copy"])
     ap.add_argument("--sets", type=int, default=3, help="independent input sets rotated over")
     ap.add_argument("--splits", type=int, default=-1, help="decode splits (-1: workload default)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -104,8 +106,10 @@ def decode_step_fn(S, wl, inp, mu, splits, fused=False):
     overlap saves.)  A captured graph does not own the memory its kernels use,
     so the last value returned holds every buffer the graph touches; keep it
     as long as the graph."""
-    kv = S.PagedKV(inp["k_pool"], inp["v_pool"], inp["block_table"], inp["seq_lens"], d_v=wl.d_v)
+    kv = S.PagedKV(inp["k_pool"], inp["v_pool"], inp["block_table"], inp["seq_lens"], d_v=wl.d_v,
+                   k_scale=inp.get("k_scale"), v_scale=inp.get("v_scale"))
     mode = S.SA_SEL_PER_KV_HEAD if wl.mode == "per_kv_head" else S.SA_SEL_PER_Q_HEAD
+    refresh = mu is not None and wl.dtype != "fp8"   # FP8 pages: summaries kept by sa_page_summary
     stride = max(1, min(wl.max_pages, wl.sink_pages + wl.window_pages + wl.top_k))
     dev = inp["q"].device
     n_sel = wl.n_sel
@@ -124,7 +128,7 @@ def decode_step_fn(S, wl, inp, mu, splits, fused=False):
         S.sa_select_pages(kv, n_q_heads=wl.n_q_heads, mode=mode, sink_pages=wl.sink_pages,
                           window_pages=wl.window_pages, top_k=wl.top_k, q=inp["q"] if mu is not None else None,
                           page_summary=mu, scores=inp["scores"], critical_k=wl.critical_k, list_stride=stride,
-                          workspace=sel_ws, out=(lists, counts, ccounts), refresh_newest_page=mu is not None)
+                          workspace=sel_ws, out=(lists, counts, ccounts), refresh_newest_page=refresh)
 
     def decode():
         S.sa_sparse_decode(kv, inp["q"], lists, counts, mode=mode, sm_scale=wl.sm_scale,
@@ -194,24 +198,25 @@ def time_back_to_back(calls, reps):
 def selected_bytes(wl, inp, lists, counts, ccounts):
     """Algorithmic decode bytes: each selected (page, KV head) K and V once (valid tokens)."""
     P = wl.page_size
-    el = 2 if wl.dtype == "bf16" else 4
+    el = {"bf16": 2, "fp32": 4, "fp8": 1}[wl.dtype]
     lens = inp["seq_lens"].cpu().numpy()
     L = lists.cpu().numpy()
     C = counts.cpu().numpy()
     per_tok = (wl.d_qk + (0 if wl.latent else wl.d_v)) * el
+    per_page = 8 if wl.dtype == "fp8" else 0          # the page's K and V scales
     total = 0
     uniq = 0
     for b in range(wl.batch):
         for s in range(wl.n_sel):
             for lp in L[b, s, :C[b, s]]:
-                total += min(P, int(lens[b]) - int(lp) * P) * per_tok
+                total += min(P, int(lens[b]) - int(lp) * P) * per_tok + per_page
         if wl.mode == "per_q_head":
             G = wl.group
             for g in range(wl.n_kv_heads):
                 pages = set()
                 for s in range(g * G, (g + 1) * G):
                     pages.update(int(x) for x in L[b, s, :C[b, s]])
-                uniq += sum(min(P, int(lens[b]) - p * P) for p in pages) * per_tok
+                uniq += sum(min(P, int(lens[b]) - p * P) for p in pages) * per_tok + per_page * len(pages)
     return total, (uniq if wl.mode == "per_q_head" else total)
 
 
@@ -278,8 +283,12 @@ def cpu_baseline_decode(wl, inp, n_seq=8):
     bt_full = inp["block_table"].cpu()
     pages = [bt_full[b, :math.ceil(int(lens[b]) / P)].long() for b in range(n_seq)]
     allp = torch.cat(pages)
-    kp = inp["k_pool"][allp].float().cpu().numpy().astype(np.float64)
-    vp = None if inp["v_pool"] is None else inp["v_pool"][allp].float().cpu().numpy().astype(np.float64)
+    if wl.dtype == "fp8":
+        kp = O.dequantize_pages(inp["k_pool"][allp].cpu().numpy(), inp["k_scale"][allp].cpu().numpy())
+        vp = O.dequantize_pages(inp["v_pool"][allp].cpu().numpy(), inp["v_scale"][allp].cpu().numpy())
+    else:
+        kp = inp["k_pool"][allp].float().cpu().numpy().astype(np.float64)
+        vp = None if inp["v_pool"] is None else inp["v_pool"][allp].float().cpu().numpy().astype(np.float64)
     bt = np.full((n_seq, wl.max_pages), -1, dtype=np.int32)
     off = 0
     for b, pg in enumerate(pages):
@@ -308,7 +317,7 @@ def cpu_baseline_decode(wl, inp, n_seq=8):
         dt = time.perf_counter() - t0
         if dt >= CPU_BASELINE_SECONDS:
             break
-    el = 2 if wl.dtype == "bf16" else 4
+    el = {"bf16": 2, "fp32": 4, "fp8": 1}[wl.dtype]
     per_tok = (wl.d_qk + (0 if wl.latent else wl.d_v)) * el
     nbytes = sum(min(P, int(lens[b]) - int(lp) * P) * per_tok
                  for b in range(n_seq) for s in range(wl.n_sel) for lp in lists[b, s, :counts[b, s]])
@@ -328,7 +337,8 @@ def run_decode(args):
         inp = W.make_decode_inputs(wl, dev, seed=1000 + i)
         mu = None
         if wl.scores == "summary":
-            kv = S.PagedKV(inp["k_pool"], inp["v_pool"], inp["block_table"], inp["seq_lens"], d_v=wl.d_v)
+            kv = S.PagedKV(inp["k_pool"], inp["v_pool"], inp["block_table"], inp["seq_lens"], d_v=wl.d_v,
+                           k_scale=inp.get("k_scale"), v_scale=inp.get("v_scale"))
             mu = S.sa_page_summary(kv)       # amortised: built once per filled page
         sets.append((inp, mu))
     torch.cuda.synchronize()
@@ -371,6 +381,17 @@ def run_decode(args):
 
     single_ms, _ = timed(args.steps, False)
     ms_per_step, step_gpu_us = timed(args.steps, True)
+    # per-step spread: single-step graphs, each between its own event pair
+    per_step = []
+    for i in range(max(args.steps, 20)):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        steps[i % len(steps)][0].replay()
+        e1.record()
+        per_step.append((e0, e1))
+    torch.cuda.synchronize()
+    step_us = np.array([1000.0 * a.elapsed_time(b) for a, b in per_step])
+    pcts = [round(float(np.percentile(step_us, q)), 2) for q in (10, 50, 90)]
 
     _, (lists, counts, ccounts), inp, _, _, _, _ = steps[0]
     # the dominant kernel alone (the decode, or the fused selection + decode):
@@ -392,7 +413,9 @@ def run_decode(args):
         "metric": "sparse-decode selected-KV GB/s (% of HBM peak) + us/layer at 32K ctx, 90% sparsity",
         "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 5), "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": wl.dtype, "data": "synthetic (seeded; N(0,1) q/K/V, planted pages)",
+        "vs_baseline": None, "dtype": wl.dtype,
+        "data": "synthetic (seeded; N(0,1) q/K/V, planted pages" + ("; E4M3 pages, per-page scales)" if wl.dtype == "fp8"
+                                                                    else ")"),
         "config": {"workload": wl.name, "batch": wl.batch, "context": wl.context, "q_heads": wl.n_q_heads,
                    "kv_heads": wl.n_kv_heads, "head_dim": wl.d_qk, "page_size": wl.page_size,
                    "sink_pages": wl.sink_pages, "window_pages": wl.window_pages, "top_k": wl.top_k,
@@ -403,6 +426,7 @@ def run_decode(args):
         "pct_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
         "step_gpu_us": round(step_gpu_us, 2),
         "ms_per_step_single_step_graphs": round(single_ms, 5),
+        "step_us_p10_p50_p90": pcts,
         "selected_bytes": nbytes,
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
@@ -537,8 +561,50 @@ def run_prefill(args):
                      "traffic": recorded_traffic(f"block_sparse_prefill_{wl.name}_traffic.json"),
                      "kernel": "sa_block_sparse_prefill (union + attention)", "algorithmic_flops": flops},
     }
+    res["mask_variants"] = prefill_mask_variants(S, wl, sets[0], timer)
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline_prefill(wl, inp, table, counts)
+    return res
+
+
+def prefill_mask_variants(S, wl, st, timer, reps=5):
+    """Beside the graded random mask (whose union is effectively dense): the
+    mask the library's pattern discovery produces (top 8% of the causal blocks
+    per row by pooled-query score, plus sink and diagonal), timed itself, and a
+    shared-column mask (one 8% column set per KV-head group) whose union stays
+    sparse; for each, the union density and the prefill time over it."""
+    inp, kv, out, lse, table, counts = st
+    mu = S.sa_page_summary(kv)
+    top_k = int(0.08 * wl.n_kv_blocks)
+    res = {}
+
+    def run(name, fn):
+        for _ in range(2):
+            fn()
+        torch.cuda.synchronize()
+        timer.reset()
+        for _ in range(reps):
+            timer.start(name)
+            fn()
+            timer.stop(name)
+        torch.cuda.synchronize()
+        return timer.avg_us(name)
+
+    mask = torch.empty((wl.n_q_heads, wl.n_q_blocks, wl.n_kv_blocks), dtype=torch.uint8, device=out.device)
+    mask_us = run("mask", lambda: S.sa_prefill_block_mask(kv, 0, inp["q"], wl.q_start, mu, wl.block_q,
+                                                           wl.sm_scale, top_k=top_k, out=mask))
+    shared = W.make_block_mask(wl.replace(mask_kind="shared_columns"), out.device, seed=2000)
+    for name, m in (("produced_top8pct", mask), ("shared_columns_8pct", shared)):
+        pf_us = run(name, lambda m=m: S.sa_block_sparse_prefill(kv, 0, inp["q"], wl.q_start, m, wl.block_q,
+                                                                 wl.sm_scale, out=out, out_lse=lse,
+                                                                 block_table_out=table, block_counts_out=counts))
+        flops, _ = prefill_flops(wl, table, counts)
+        c = [int(x) for x in counts.cpu().tolist()]
+        res[name] = {"mask_density": round(float(m.float().mean().item()), 5),
+                     "union_density": round(sum(c) / (len(c) * wl.n_kv_blocks), 4),
+                     "prefill_us": round(pf_us, 1), "prefill_tflops": round(flops / (pf_us * 1e-6) / 1e12, 1)}
+    res["produced_top8pct"]["mask_producer_us"] = round(mask_us, 1)
+    res["produced_top8pct"]["top_k"] = top_k
     return res
 
 
