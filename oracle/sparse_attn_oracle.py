@@ -465,3 +465,79 @@ def dequantize_pages(pool_u8: np.ndarray, scale: np.ndarray) -> np.ndarray:
     vals = fp8_e4m3_to_float(pool_u8)
     s = np.asarray(scale, dtype=np.float64).reshape(scale.shape + (1,) * (pool_u8.ndim - 2))
     return vals * s
+
+
+# -------------------------------------------------------- mean correction
+def page_value_summary(v_pool: np.ndarray, block_table: np.ndarray, seq_lens: np.ndarray,
+                       page_size: int) -> np.ndarray:
+    """Mean value row of each referenced physical page, per KV head (the value
+    counterpart of page_summary): nu[p, g, :] = mean over the page's valid
+    tokens j of V[p, g, :, j] (page-transposed pool), float64 rounded to fp32;
+    NaN for pages no sequence references."""
+    n_phys, n_kv, d_v, P = v_pool.shape
+    nu = np.full((n_phys, n_kv, d_v), np.nan, dtype=np.float32)
+    for b in range(block_table.shape[0]):
+        for lp in range(n_pages_of(seq_lens[b], P)):
+            nv = valid_tokens(seq_lens[b], lp, P)
+            phys = int(block_table[b, lp])
+            cols = np.asarray(v_pool[phys, :, :, :nv], dtype=np.float64)      # [n_kv][d_v][nv]
+            nu[phys] = (cols.sum(axis=2) / nv).astype(np.float32)
+    return nu
+
+
+def mean_corrected_prefill(q, k_pool, v_pool, block_table_row, seq_len, page_size, q_start, tables, counts,
+                           n_kv_heads, sm_scale, rows: Optional[Iterable[Tuple[int, int]]] = None):
+    """Block-sparse chunked prefill with a mean correction for the skipped blocks.
+
+    Source: the block-sparse prefill brief on the Paperraft page ("a mean
+    correction term" beside pattern discovery and thresholding; the term bounds
+    the error of the blocks left out).  The formula is not on the pages; the
+    reading taken is the plainest one: every causal block of the sequence that
+    the query's group table leaves out and that lies wholly at or before the
+    query's position stands in for its n_b tokens by their mean key mu_b and
+    mean value nu_b, so it adds n_b * exp(z_b) to the softmax normaliser and
+    n_b * exp(z_b) * nu_b to the numerator, z_b = sm_scale * q . mu_b:
+      o = (sum_{j in table, j <= p} e^{z_j} v_j + sum_b n_b e^{z_b} nu_b)
+          / (sum_{j in table, j <= p} e^{z_j} + sum_b n_b e^{z_b})
+      lse = log of the denominator.
+    The means are taken in float64 over the block's valid tokens (no rounding
+    to fp32).  With no skipped block this is block_sparse_prefill; when every
+    skipped block's tokens share one key and one value it is exact dense
+    causal attention.
+    """
+    q_len, Hq, d = q.shape
+    G = Hq // n_kv_heads
+    P = page_size
+    d_v = v_pool.shape[2]
+    n_seq = n_pages_of(seq_len, P)
+    out = np.zeros((q_len, Hq, d_v), dtype=np.float64)
+    lse = np.full((q_len, Hq), np.nan, dtype=np.float64)
+    if rows is None:
+        rows = [(i, h) for i in range(q_len) for h in range(Hq)]
+    for (i, h) in rows:
+        g = h // G
+        pos = q_start + i
+        table = set(int(x) for x in tables[g, :int(counts[g])])
+        zs, vs = [], []
+        for kb in range(n_seq):
+            nv = valid_tokens(seq_len, kb, P)
+            phys = int(block_table_row[kb])
+            K = np.asarray(k_pool[phys, g, :nv, :], dtype=np.float64)
+            V = np.asarray(v_pool[phys, g, :, :nv], dtype=np.float64).T
+            if kb in table:
+                for r in range(nv):
+                    if kb * P + r <= pos:
+                        zs.append(sm_scale * float(q[i, h] @ K[r]))
+                        vs.append(V[r])
+            elif kb * P + nv - 1 <= pos:
+                zs.append(sm_scale * float(q[i, h] @ K.mean(axis=0)) + math.log(nv))
+                vs.append(V.mean(axis=0))
+        if not zs:
+            out[i, h], lse[i, h] = np.zeros(d_v), -np.inf
+            continue
+        z = np.array(zs)
+        m = z.max()
+        e = np.exp(z - m)
+        out[i, h] = (e @ np.stack(vs)) / e.sum()
+        lse[i, h] = m + math.log(e.sum())
+    return out, lse

@@ -715,6 +715,100 @@ def check_fp8_decode_sdpa():
             assert np.allclose(out[b, :, h], eo, atol=1e-12) and np.allclose(lse[b, :, h], el, atol=1e-12), (b, h)
 
 
+# ------------------------------------------------------- mean correction
+def check_value_summary_bruteforce():
+    rng = np.random.default_rng(21)
+    B, Hkv, P, dv = 2, 2, 4, 5
+    lens = [11, 6]
+    L = max(lens)
+    V = rng.standard_normal((B, Hkv, L, dv))
+    _, vp, bt = scatter_to_pool(V, V, P, rng)
+    nu = O.page_value_summary(vp, bt, np.array(lens), P)
+    for b in range(B):
+        for lp in range((lens[b] + P - 1) // P):
+            toks = [j for j in range(lp * P, (lp + 1) * P) if j < lens[b]]
+            for g in range(Hkv):
+                for e in range(dv):
+                    exp = math.fsum(V[b, g, j, e] for j in toks) / len(toks)
+                    assert abs(float(nu[bt[b, lp], g, e]) - exp) <= 1e-6 * max(1.0, abs(exp))
+
+
+def check_mean_correction_exact_on_constant_blocks():
+    """When every token of a block carries the block's one key and one value,
+    a skipped block's n_b * exp(z_b) term is exactly its tokens' sum, so the
+    corrected prefill equals dense causal attention (torch float64 SDPA); with
+    a full table it equals the plain block-sparse prefill."""
+    rng = np.random.default_rng(22)
+    Hq, Hkv, P, d = 4, 2, 4, 6
+    q_len, q_start = 7, 17
+    L = q_start + q_len
+    nkb = (L + P - 1) // P
+    G = Hq // Hkv
+    Kb = rng.standard_normal((1, Hkv, nkb, d))
+    Vb = rng.standard_normal((1, Hkv, nkb, d))
+    K = np.repeat(Kb, P, axis=2)[:, :, :L]
+    V = np.repeat(Vb, P, axis=2)[:, :, :L]
+    q = rng.standard_normal((q_len, Hq, d))
+    kp, vp, bt = scatter_to_pool(K, V, P, rng, extra_pages=1)
+    # keep block 0 and the chunk's blocks; skip the rest
+    keep = sorted({0} | set(range(q_start // P, nkb)))
+    tables = np.full((Hkv, nkb), -1, dtype=np.int32)
+    tables[:, :len(keep)] = keep
+    counts = np.full(Hkv, len(keep), dtype=np.int32)
+    out, lse = O.mean_corrected_prefill(q, kp, vp, bt[0], L, P, q_start, tables, counts, Hkv, 0.4)
+    causal = np.arange(L)[None, :] <= (q_start + np.arange(q_len))[:, None]
+    for h in range(Hq):
+        eo, el = sdpa(q[:, h], K[0, h // G], V[0, h // G], 0.4, causal)
+        assert np.allclose(out[:, h], eo, atol=1e-12) and np.allclose(lse[:, h], el, atol=1e-12), h
+    # nothing skipped: the plain block-sparse prefill
+    full = np.tile(np.arange(nkb, dtype=np.int32), (Hkv, 1))
+    fc = np.full(Hkv, nkb, dtype=np.int32)
+    a = O.mean_corrected_prefill(q, kp, vp, bt[0], L, P, q_start, full, fc, Hkv, 0.4)
+    b = O.block_sparse_prefill(q, kp, vp, bt[0], L, P, q_start, full, fc, Hkv, 0.4)
+    assert np.allclose(a[0], b[0], atol=1e-12) and np.allclose(a[1], b[1], atol=1e-12)
+
+
+def check_mean_correction_bruteforce():
+    """Random keys: the corrected output against the formula written out with
+    explicit sums (math.fsum) over the table's tokens and the skipped blocks'
+    means; skipped blocks past a query's position (wholly or partly) add
+    nothing."""
+    rng = np.random.default_rng(23)
+    Hq, Hkv, P, d = 2, 1, 4, 3
+    q_len, q_start = 6, 13
+    L = q_start + q_len
+    nkb = (L + P - 1) // P
+    K = rng.standard_normal((1, Hkv, L, d))
+    V = rng.standard_normal((1, Hkv, L, d))
+    q = rng.standard_normal((q_len, Hq, d))
+    kp, vp, bt = scatter_to_pool(K, V, P, rng)
+    keep = [1, 4]
+    tables = np.full((Hkv, nkb), -1, dtype=np.int32)
+    tables[0, :2] = keep
+    counts = np.array([2], dtype=np.int32)
+    out, lse = O.mean_corrected_prefill(q, kp, vp, bt[0], L, P, q_start, tables, counts, Hkv, 0.7)
+    for i in range(q_len):
+        pos = q_start + i
+        for h in range(Hq):
+            terms = []      # (log weight, value vector)
+            for kb in range(nkb):
+                toks = [j for j in range(kb * P, min((kb + 1) * P, L))]
+                if kb in keep:
+                    for j in toks:
+                        if j <= pos:
+                            terms.append((0.7 * math.fsum(q[i, h, e] * K[0, 0, j, e] for e in range(d)), V[0, 0, j]))
+                elif toks[-1] <= pos:
+                    mk = [math.fsum(K[0, 0, j, e] for j in toks) / len(toks) for e in range(d)]
+                    mv = np.array([math.fsum(V[0, 0, j, e] for j in toks) / len(toks) for e in range(d)])
+                    terms.append((0.7 * math.fsum(q[i, h, e] * mk[e] for e in range(d)) + math.log(len(toks)), mv))
+            m = max(t[0] for t in terms)
+            w = [math.exp(t[0] - m) for t in terms]
+            den = math.fsum(w)
+            exp_o = [math.fsum(w[k] * terms[k][1][e] for k in range(len(terms))) / den for e in range(d)]
+            assert np.allclose(out[i, h], exp_o, atol=1e-12), (i, h)
+            assert abs(lse[i, h] - (m + math.log(den))) < 1e-12
+
+
 ALL_CHECKS = [
     check_summary_constant_pages, check_summary_bruteforce,
     check_scores_exact_integers, check_scores_linearity_and_unfactored,
@@ -726,4 +820,5 @@ ALL_CHECKS = [
     check_prefill_causal_sdpa, check_prefill_masked_sdpa,
     check_mask_bruteforce, check_mask_invariants, check_mask_union_keeps_selection,
     check_fp8_decoding, check_fp8_decode_sdpa,
+    check_value_summary_bruteforce, check_mean_correction_exact_on_constant_blocks, check_mean_correction_bruteforce,
 ]

@@ -22,6 +22,7 @@ _orig_row_pages = O.row_pages
 _orig_mask = O.prefill_block_mask
 _orig_fp8 = O.fp8_e4m3_to_float
 _orig_deq = O.dequantize_pages
+_orig_mc = O.mean_corrected_prefill
 
 
 def _no_scale(qrow, K, V, sm_scale, d_v):
@@ -147,7 +148,44 @@ def _deq_scale_ignored(pool, scale):
     return _orig_deq(pool, np.ones_like(scale))
 
 
+def _mc_no_count(q, kp, vp, bt, L, P, q_start, tables, counts, n_kv, scale, rows=None):
+    """Weight each skipped block as a single token (its count n_b left out)."""
+    q_len, Hq, d = q.shape
+    G = Hq // n_kv
+    out = np.zeros((q_len, Hq, vp.shape[2]))
+    lse = np.full((q_len, Hq), np.nan)
+    for i in range(q_len):
+        for h in range(Hq):
+            g, pos = h // G, q_start + i
+            table = set(int(x) for x in tables[g, :int(counts[g])])
+            zs, vs = [], []
+            for kb in range(O.n_pages_of(L, P)):
+                nv = O.valid_tokens(L, kb, P)
+                K = np.asarray(kp[int(bt[kb]), g, :nv], dtype=np.float64)
+                V = np.asarray(vp[int(bt[kb]), g, :, :nv], dtype=np.float64).T
+                if kb in table:
+                    for r in range(nv):
+                        if kb * P + r <= pos:
+                            zs.append(scale * float(q[i, h] @ K[r]))
+                            vs.append(V[r])
+                elif kb * P + nv - 1 <= pos:
+                    zs.append(scale * float(q[i, h] @ K.mean(axis=0)))
+                    vs.append(V.mean(axis=0))
+            z = np.array(zs)
+            e = np.exp(z - z.max())
+            out[i, h] = (e @ np.stack(vs)) / e.sum()
+            lse[i, h] = z.max() + math.log(e.sum())
+    return out, lse
+
+
+def _mc_partial_blocks(q, kp, vp, bt, L, P, q_start, tables, counts, n_kv, scale, rows=None):
+    """Also count skipped blocks that are only partly visible (their later tokens past the query)."""
+    return _orig_mc(q, kp, vp, bt, L, P, q_start + P - 1, tables, counts, n_kv, scale, rows)
+
+
 MUTANTS = {
+    "mean_correction_no_count": ("mean_corrected_prefill", _mc_no_count),
+    "mean_correction_partial_blocks": ("mean_corrected_prefill", _mc_partial_blocks),
     "fp8_bias_8": ("fp8_e4m3_to_float", _fp8_bias_8),
     "fp8_no_subnormals": ("fp8_e4m3_to_float", _fp8_no_subnormals),
     "fp8_page_scale_ignored": ("dequantize_pages", _deq_scale_ignored),
