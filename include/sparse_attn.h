@@ -334,6 +334,52 @@ sa_status sa_block_sparse_prefill(const sa_paged_kv* kv, int32_t seq,
                                   void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* ------------------------------------------------------------------------
+ * sa_page_value_summary -- per-page mean value row, the value counterpart of
+ * sa_page_summary, for the mean correction below:
+ *
+ *   value_summary[phys][g][:] = mean over the page's valid tokens j of v_pool[phys][g][:][j]
+ *
+ * (FP8 pages: of the dequantised values, code * v_scale).  Accumulated in
+ * float64, rounded once to fp32; pages [0, n) of every sequence, or the last
+ * `last_pages` of them when last_pages > 0; other entries untouched.
+ *   value_summary: out [n_phys_pages][n_kv_heads][d_v] fp32.
+ * Needs a V-pool cache.
+ * ---------------------------------------------------------------------- */
+sa_status sa_page_value_summary(const sa_paged_kv* kv, int32_t batch, int32_t last_pages,
+                                float* value_summary, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * sa_prefill_mean_correction -- adds the blocks a block-sparse prefill left
+ * out back into its result, each as one mean term (block-sparse prefill
+ * brief on the Paperraft page: a mean correction term that bounds the error
+ * of the skipped blocks).  The pages give no formula; the reading taken:
+ * for query i (position p = q_start + i) of head h, every logical block kb of
+ * the sequence that is not in the group table T_{g(h)} and whose valid
+ * tokens all lie at or before p (kb*page_size + n_b - 1 <= p, n_b its valid
+ * tokens) adds the term
+ *     weight n_b * exp(sm_scale * q_i . mu_b),  value nu_b
+ * to the softmax, mu_b / nu_b the block's mean key / value
+ * (sa_page_summary / sa_page_value_summary).  With (o, lse) the prefill's
+ * result over T_{g(h)} (one term of weight exp(lse), value o):
+ *     lse' = log(exp(lse) + sum_b n_b exp(z_b)),
+ *     o'   = (exp(lse) o + sum_b n_b exp(z_b) nu_b) / exp(lse').
+ * A row with no skipped block keeps its (o, lse) bit for bit.
+ *   q, seq, q_len, q_start, n_q_heads, sm_scale: as given to sa_block_sparse_prefill
+ *   block_table, block_counts: its block_table_out / block_counts_out
+ *   page_summary, value_summary: [n_phys_pages][n_kv_heads][128] fp32, valid
+ *              for every page of sequence `seq` below q_start + q_len
+ *   out [q_len][n_q_heads][128] bf16, out_lse [q_len][n_q_heads] fp32: the
+ *              prefill's result, read and overwritten in place
+ * The means are rounded to bf16 for the q . mu products and the nu sums
+ * (fp32 accumulation).  Same shape limits as sa_block_sparse_prefill.
+ * ---------------------------------------------------------------------- */
+sa_status sa_prefill_mean_correction(const sa_paged_kv* kv, int32_t seq,
+                                     const void* q, int32_t q_len, int32_t q_start, int32_t n_q_heads,
+                                     const int32_t* block_table, const int32_t* block_counts, int32_t n_kv_blocks,
+                                     const float* page_summary, const float* value_summary, float sm_scale,
+                                     void* out, float* out_lse, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
  * sa_set_debug_validate -- opt-in device-side checks of the index data every
  * call trusts, for callers that must not trust it (the "raise a clear error"
  * convention of the TileSparse README, "Quick start"; [UAE] "Key Design

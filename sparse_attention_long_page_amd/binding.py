@@ -34,7 +34,7 @@ EXPORTED = [
     "sa_page_summary", "sa_select_pages_workspace_size", "sa_select_pages",
     "sa_sparse_decode_workspace_size", "sa_sparse_decode", "sa_sparse_decode_noalloc", "sa_select_decode",
     "sa_block_sparse_prefill_workspace_size", "sa_block_sparse_prefill", "sa_prefill_block_mask",
-    "sa_set_debug_validate",
+    "sa_page_value_summary", "sa_prefill_mean_correction", "sa_set_debug_validate",
     "sa_status_string", "sa_last_error_message", "sa_version",
 ]
 
@@ -86,6 +86,9 @@ def load_library(build_if_missing: bool = True) -> ctypes.CDLL:
                                             c_float, P, P, P, c_size_t, P]),
         "sa_prefill_block_mask": (c_int, [P, c_int32, P, c_int32, c_int32, c_int32, P, c_int32, c_int32, c_float,
                                           c_int32, c_float, P, P]),
+        "sa_page_value_summary": (c_int, [P, c_int32, c_int32, P, P]),
+        "sa_prefill_mean_correction": (c_int, [P, c_int32, P, c_int32, c_int32, c_int32, P, P, c_int32, P, P,
+                                               c_float, P, P, P]),
         "sa_set_debug_validate": (c_int, [c_int]),
         "sa_status_string": (ctypes.c_char_p, [c_int]),
         "sa_last_error_message": (ctypes.c_char_p, []),
@@ -331,6 +334,28 @@ def sa_prefill_block_mask(kv: PagedKV, seq: int, q: torch.Tensor, q_start: int, 
         -1 if top_k is None else int(top_k), float("inf") if max_gap is None else float(max_gap), _ptr(out),
         _stream(kv.device)))
     return out
+
+
+def sa_page_value_summary(kv: PagedKV, last_pages: int = 0, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Per-page mean value rows [n_phys_pages][n_kv_heads][d_v] fp32 (NaN where not written)."""
+    if out is None:
+        out = torch.full((kv.c.n_phys_pages, kv.n_kv_heads, kv.d_v), float("nan"), dtype=torch.float32,
+                         device=kv.device)
+    _check(load_library().sa_page_value_summary(kv.ref, kv.batch, last_pages, _ptr(out), _stream(kv.device)))
+    return out
+
+
+def sa_prefill_mean_correction(kv: PagedKV, seq: int, q: torch.Tensor, q_start: int, block_table: torch.Tensor,
+                               block_counts: torch.Tensor, page_summary: torch.Tensor,
+                               value_summary: torch.Tensor, sm_scale: float, out: torch.Tensor,
+                               out_lse: torch.Tensor):
+    """Adds the prefill's skipped causal blocks back as mean terms; rewrites (out, out_lse) in place."""
+    q_len, Hq, _ = q.shape
+    nkb = block_table.shape[-1]
+    _check(load_library().sa_prefill_mean_correction(
+        kv.ref, seq, _ptr(q), q_len, q_start, Hq, _ptr(block_table), _ptr(block_counts), nkb, _ptr(page_summary),
+        _ptr(value_summary), float(sm_scale), _ptr(out), _ptr(out_lse), _stream(kv.device)))
+    return out, out_lse
 
 
 def sa_set_debug_validate(on: bool) -> bool:

@@ -314,6 +314,36 @@ sa_status sa_page_summary(const sa_paged_kv* kv, int32_t batch, int32_t last_pag
   return device_status(sa::launch_page_summary(p, batch, kv->dtype == SA_DTYPE_BF16, stream), "page_summary launch");
 }
 
+// ------------------------------------------------------------ value summary
+sa_status sa_page_value_summary(const sa_paged_kv* kv, int32_t batch, int32_t last_pages, float* value_summary,
+                                hipStream_t stream) {
+  sa_status st = check_kv(kv, true);
+  if (st != SA_OK) return st;
+  if (is_latent(kv)) return fail(SA_ERR_UNSUPPORTED, "value summaries need a V pool");
+  if (batch <= 0) return fail(SA_ERR_INVALID_ARGUMENT, "batch must be positive");
+  if (last_pages < 0) return fail(SA_ERR_INVALID_ARGUMENT, "last_pages must be >= 0");
+  if (!value_summary) return fail(SA_ERR_INVALID_ARGUMENT, "value_summary is NULL");
+  if (validate_on()) {
+    Validator v(stream);
+    v.kv(kv, 0, batch);
+    st = v.finish(kv, 0);
+    if (st != SA_OK) return st;
+  }
+  sa::ValueSummaryParams p{};
+  p.v_pool = kv->v_pool;
+  p.block_table = kv->block_table;
+  p.seq_lens = kv->seq_lens;
+  p.v_scale = kv->dtype == SA_DTYPE_FP8_E4M3 ? kv->v_scale : nullptr;
+  p.nu = value_summary;
+  p.n_kv = kv->n_kv_heads;
+  p.P = kv->page_size;
+  p.d_v = kv->d_v;
+  p.max_pages = kv->max_pages;
+  p.last_pages = std::min(last_pages, kv->max_pages);
+  const int eb = kv->dtype == SA_DTYPE_FP8_E4M3 ? 1 : kv->dtype == SA_DTYPE_BF16 ? 2 : 4;
+  return device_status(sa::launch_page_value_summary(p, batch, eb, stream), "value summary launch");
+}
+
 // ------------------------------------------------------------------- select
 size_t sa_select_pages_workspace_size(int32_t batch, int32_t n_sel, int32_t max_pages) {
   if (batch <= 0 || n_sel <= 0 || max_pages <= 0) return 0;
@@ -838,6 +868,59 @@ sa_status sa_block_sparse_prefill(const sa_paged_kv* kv, int32_t seq, const void
   e = sa::launch_prefill(p, stream);
   if (e != hipSuccess) return device_status(e, "prefill launch");
   return ok();
+}
+
+// -------------------------------------------------------- mean correction
+sa_status sa_prefill_mean_correction(const sa_paged_kv* kv, int32_t seq, const void* q, int32_t q_len,
+                                     int32_t q_start, int32_t n_q_heads, const int32_t* block_table,
+                                     const int32_t* block_counts, int32_t n_kv_blocks, const float* page_summary,
+                                     const float* value_summary, float sm_scale, void* out, float* out_lse,
+                                     hipStream_t stream) {
+  sa_status st = check_kv(kv, false);
+  if (st != SA_OK) return st;
+  if (kv->dtype != SA_DTYPE_BF16 || is_latent(kv) || kv->d_qk != 128 || kv->page_size != 64)
+    return fail(SA_ERR_UNSUPPORTED, "mean correction needs bf16, a V pool, d 128 and page_size 64");
+  if (seq < 0) return fail(SA_ERR_INVALID_ARGUMENT, "seq must be >= 0");
+  if (!q || !block_table || !block_counts || !page_summary || !value_summary || !out || !out_lse)
+    return fail(SA_ERR_INVALID_ARGUMENT,
+                "q, block_table, block_counts, page_summary, value_summary, out and out_lse must be set");
+  if (q_len <= 0 || q_start < 0) return fail(SA_ERR_INVALID_ARGUMENT, "q_len must be positive, q_start >= 0");
+  if (n_q_heads <= 0 || n_q_heads % kv->n_kv_heads != 0)
+    return fail(SA_ERR_INVALID_ARGUMENT, "n_q_heads must be a positive multiple of n_kv_heads");
+  const long need_blocks = ((long)q_start + q_len + kv->page_size - 1) / kv->page_size;
+  if (n_kv_blocks > sa::kPrefillMaxBlocks)
+    return fail(SA_ERR_UNSUPPORTED, "mean correction supports up to %d KV blocks (got %d)", sa::kPrefillMaxBlocks,
+                n_kv_blocks);
+  if (n_kv_blocks < need_blocks || n_kv_blocks > kv->max_pages)
+    return fail(SA_ERR_INVALID_ARGUMENT, "n_kv_blocks %d must cover q_start+q_len (%ld) and be <= max_pages %d",
+                n_kv_blocks, need_blocks, kv->max_pages);
+  if (!std::isfinite(sm_scale) || !(sm_scale > 0.f))
+    return fail(SA_ERR_INVALID_ARGUMENT, "sm_scale must be finite and positive");
+  if (validate_on()) {
+    Validator v(stream);
+    v.kv(kv, seq, 1);
+    st = v.finish(kv, 0);
+    if (st != SA_OK) return st;
+  }
+  sa::MeanCorrParams p{};
+  p.q = q;
+  p.mu = page_summary;
+  p.nu = value_summary;
+  p.bt_row = kv->block_table + (size_t)seq * kv->max_pages;
+  p.seq_len = kv->seq_lens + seq;
+  p.table = block_table;
+  p.counts = block_counts;
+  p.out = out;
+  p.out_lse = out_lse;
+  p.q_len = q_len;
+  p.q_start = q_start;
+  p.Hq = n_q_heads;
+  p.Hkv = kv->n_kv_heads;
+  p.G = n_q_heads / kv->n_kv_heads;
+  p.nkb = n_kv_blocks;
+  p.P = kv->page_size;
+  p.scale_log2 = sm_scale * sa::kLog2e;
+  return device_status(sa::launch_mean_correct(p, stream), "mean correction launch");
 }
 
 }  // extern "C"

@@ -186,7 +186,34 @@ struct PrefillParams {
   float scale_log2;
 };
 
+constexpr int kPrefillMaxBlocks = 4096;     // KV blocks of a prefill chunk (262144 tokens at pages of 64)
+
+struct ValueSummaryParams {
+  const void* v_pool;        // [n_phys][n_kv][d_v][P]
+  const int32_t* block_table;
+  const int32_t* seq_lens;
+  const float* v_scale;      // FP8 pages: [n_phys][n_kv] (null otherwise)
+  float* nu;                 // out [n_phys][n_kv][d_v]
+  int n_kv, P, d_v, max_pages, last_pages;
+};
+
+struct MeanCorrParams {
+  const void* q;             // [q_len][Hq][128] bf16
+  const float* mu;           // mean keys [n_phys][Hkv][128]
+  const float* nu;           // mean values [n_phys][Hkv][128]
+  const int32_t* bt_row;
+  const int32_t* seq_len;
+  const int32_t* table;      // union tables [Hkv][nkb] and counts [Hkv]
+  const int32_t* counts;
+  void* out;                 // [q_len][Hq][128] bf16, read and rewritten
+  float* out_lse;            // [q_len][Hq], read and rewritten
+  int q_len, q_start, Hq, Hkv, G, nkb, P;
+  float scale_log2;
+};
+
 // ------------------------------------------------------------- launchers
+hipError_t launch_page_value_summary(const ValueSummaryParams& p, int batch, int elem_bytes, hipStream_t s);
+hipError_t launch_mean_correct(const MeanCorrParams& p, hipStream_t s);
 hipError_t launch_page_summary(const SummaryParams& p, int batch, int bf16, hipStream_t s);
 hipError_t launch_select(const SelectParams& p, int batch, int max_pages, hipStream_t s);
 hipError_t launch_score_select(const ScoreParams& sp, const SelectParams& p, int batch, int bf16, hipStream_t s);

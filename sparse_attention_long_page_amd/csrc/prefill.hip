@@ -121,7 +121,6 @@ constexpr int kVChunks = kPD * (kVRow / 8);      // 1152
 constexpr int kStageInstr = (kKChunks + kVChunks) / 64;   // 35
 constexpr int kStageElems = kKTile + kVTile;     // bf16 elements per stage (35840 B)
 static_assert((kKChunks + kVChunks) % 64 == 0, "stage must be whole wave loads");
-constexpr int kPrefillMaxBlocks = 4096;           // KV blocks a tile may sweep (262144 tokens)
 constexpr float kRescaleThreshold = 8.0f;   // log2 units
 
 // LDS layout and operand orders, chosen for the LDS bank rules of gfx950
