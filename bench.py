@@ -603,9 +603,45 @@ def prefill_mask_variants(S, wl, st, timer, reps=5):
         res[name] = {"mask_density": round(float(m.float().mean().item()), 5),
                      "union_density": round(sum(c) / (len(c) * wl.n_kv_blocks), 4),
                      "prefill_us": round(pf_us, 1), "prefill_tflops": round(flops / (pf_us * 1e-6) / 1e12, 1)}
+        if name == "shared_columns_8pct":
+            res[name]["mean_correction"] = mean_correction_leg(S, wl, st, mu, run)
     res["produced_top8pct"]["mask_producer_us"] = round(mask_us, 1)
     res["produced_top8pct"]["top_k"] = top_k
     return res
+
+
+def mean_terms(wl, table, counts, seq_len):
+    """(row, head) x skipped-block pairs the mean correction adds: per KV
+    head, the causal blocks not in its table whose tokens all lie at or
+    before the row's position, times the heads of the group."""
+    P = wl.page_size
+    n_seq = (seq_len + P - 1) // P
+    pos = wl.q_start + np.arange(wl.q_len, dtype=np.int64)
+    T, C = table.cpu().numpy(), counts.cpu().numpy()
+    pairs = 0
+    for g in range(wl.n_kv_heads):
+        kept = np.zeros(n_seq, dtype=bool)
+        kept[T[g, :C[g]]] = True
+        kb = np.flatnonzero(~kept).astype(np.int64)
+        last_tok = np.minimum(kb * P + P, seq_len) - 1
+        pairs += int((pos[:, None] >= last_tok[None, :]).sum()) * wl.group
+    return pairs
+
+
+def mean_correction_leg(S, wl, st, mu, run):
+    """Per-page mean values over the whole pool, then the mean correction of
+    the prefill just run (its tables, out and lse); algorithmic FLOPs 4*d per
+    (row, head, mean term)."""
+    inp, kv, out, lse, table, counts = st
+    nu = S.sa_page_value_summary(kv)
+    ws = torch.empty(S.sa_prefill_mean_correction_workspace_size(kv, wl.n_kv_blocks), dtype=torch.uint8,
+                     device=out.device)
+    vs_us = run("value_summary", lambda: S.sa_page_value_summary(kv, out=nu))
+    mc_us = run("mean_correction", lambda: S.sa_prefill_mean_correction(kv, 0, inp["q"], wl.q_start, table, counts,
+                                                                        mu, nu, wl.sm_scale, out, lse, workspace=ws))
+    pairs = mean_terms(wl, table, counts, int(inp["seq_lens"][0].item()))
+    return {"value_summary_us": round(vs_us, 1), "correction_us": round(mc_us, 1), "mean_term_pairs": pairs,
+            "correction_tflops": round(4 * wl.d * pairs / (mc_us * 1e-6) / 1e12, 1)}
 
 
 def run_hbm_copy(args):

@@ -363,7 +363,7 @@ sa_status sa_page_value_summary(const sa_paged_kv* kv, int32_t batch, int32_t la
  * result over T_{g(h)} (one term of weight exp(lse), value o):
  *     lse' = log(exp(lse) + sum_b n_b exp(z_b)),
  *     o'   = (exp(lse) o + sum_b n_b exp(z_b) nu_b) / exp(lse').
- * A row with no skipped block keeps its (o, lse) bit for bit.
+ * A row that no skipped block reaches keeps its (o, lse) bit for bit.
  *   q, seq, q_len, q_start, n_q_heads, sm_scale: as given to sa_block_sparse_prefill
  *   block_table, block_counts: its block_table_out / block_counts_out
  *   page_summary, value_summary: [n_phys_pages][n_kv_heads][128] fp32, valid
@@ -372,12 +372,20 @@ sa_status sa_page_value_summary(const sa_paged_kv* kv, int32_t batch, int32_t la
  *              prefill's result, read and overwritten in place
  * The means are rounded to bf16 for the q . mu products and the nu sums
  * (fp32 accumulation).  Same shape limits as sa_block_sparse_prefill.
+ *   workspace: device memory of at least
+ *              sa_prefill_mean_correction_workspace_size(kv, n_kv_blocks) bytes
+ *              (the skipped blocks and their packed means; overwritten;
+ *              SA_ERR_WORKSPACE_TOO_SMALL if short).  Calls sharing one
+ *              workspace must be ordered on one stream.
  * ---------------------------------------------------------------------- */
+size_t sa_prefill_mean_correction_workspace_size(const sa_paged_kv* kv, int32_t n_kv_blocks);
+
 sa_status sa_prefill_mean_correction(const sa_paged_kv* kv, int32_t seq,
                                      const void* q, int32_t q_len, int32_t q_start, int32_t n_q_heads,
                                      const int32_t* block_table, const int32_t* block_counts, int32_t n_kv_blocks,
                                      const float* page_summary, const float* value_summary, float sm_scale,
-                                     void* out, float* out_lse, hipStream_t stream);
+                                     void* out, float* out_lse, void* workspace, size_t workspace_bytes,
+                                     hipStream_t stream);
 
 /* ------------------------------------------------------------------------
  * sa_set_debug_validate -- opt-in device-side checks of the index data every

@@ -34,7 +34,8 @@ EXPORTED = [
     "sa_page_summary", "sa_select_pages_workspace_size", "sa_select_pages",
     "sa_sparse_decode_workspace_size", "sa_sparse_decode", "sa_sparse_decode_noalloc", "sa_select_decode",
     "sa_block_sparse_prefill_workspace_size", "sa_block_sparse_prefill", "sa_prefill_block_mask",
-    "sa_page_value_summary", "sa_prefill_mean_correction", "sa_set_debug_validate",
+    "sa_page_value_summary", "sa_prefill_mean_correction_workspace_size", "sa_prefill_mean_correction",
+    "sa_set_debug_validate",
     "sa_status_string", "sa_last_error_message", "sa_version",
 ]
 
@@ -87,8 +88,9 @@ def load_library(build_if_missing: bool = True) -> ctypes.CDLL:
         "sa_prefill_block_mask": (c_int, [P, c_int32, P, c_int32, c_int32, c_int32, P, c_int32, c_int32, c_float,
                                           c_int32, c_float, P, P]),
         "sa_page_value_summary": (c_int, [P, c_int32, c_int32, P, P]),
+        "sa_prefill_mean_correction_workspace_size": (c_size_t, [P, c_int32]),
         "sa_prefill_mean_correction": (c_int, [P, c_int32, P, c_int32, c_int32, c_int32, P, P, c_int32, P, P,
-                                               c_float, P, P, P]),
+                                               c_float, P, P, P, c_size_t, P]),
         "sa_set_debug_validate": (c_int, [c_int]),
         "sa_status_string": (ctypes.c_char_p, [c_int]),
         "sa_last_error_message": (ctypes.c_char_p, []),
@@ -345,16 +347,24 @@ def sa_page_value_summary(kv: PagedKV, last_pages: int = 0, out: Optional[torch.
     return out
 
 
+def sa_prefill_mean_correction_workspace_size(kv: PagedKV, n_kv_blocks: int) -> int:
+    return load_library().sa_prefill_mean_correction_workspace_size(kv.ref, n_kv_blocks)
+
+
 def sa_prefill_mean_correction(kv: PagedKV, seq: int, q: torch.Tensor, q_start: int, block_table: torch.Tensor,
                                block_counts: torch.Tensor, page_summary: torch.Tensor,
                                value_summary: torch.Tensor, sm_scale: float, out: torch.Tensor,
-                               out_lse: torch.Tensor):
+                               out_lse: torch.Tensor, workspace: Optional[torch.Tensor] = None):
     """Adds the prefill's skipped causal blocks back as mean terms; rewrites (out, out_lse) in place."""
     q_len, Hq, _ = q.shape
     nkb = block_table.shape[-1]
+    if workspace is None:
+        nbytes = sa_prefill_mean_correction_workspace_size(kv, nkb)
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=kv.device)
     _check(load_library().sa_prefill_mean_correction(
         kv.ref, seq, _ptr(q), q_len, q_start, Hq, _ptr(block_table), _ptr(block_counts), nkb, _ptr(page_summary),
-        _ptr(value_summary), float(sm_scale), _ptr(out), _ptr(out_lse), _stream(kv.device)))
+        _ptr(value_summary), float(sm_scale), _ptr(out), _ptr(out_lse), _ptr(workspace), workspace.numel(),
+        _stream(kv.device)))
     return out, out_lse
 
 

@@ -871,11 +871,16 @@ sa_status sa_block_sparse_prefill(const sa_paged_kv* kv, int32_t seq, const void
 }
 
 // -------------------------------------------------------- mean correction
+size_t sa_prefill_mean_correction_workspace_size(const sa_paged_kv* kv, int32_t n_kv_blocks) {
+  if (!kv || kv->n_kv_heads <= 0 || n_kv_blocks <= 0) return 0;
+  return sa::mean_correct_workspace(kv->n_kv_heads, n_kv_blocks, nullptr, nullptr);
+}
+
 sa_status sa_prefill_mean_correction(const sa_paged_kv* kv, int32_t seq, const void* q, int32_t q_len,
                                      int32_t q_start, int32_t n_q_heads, const int32_t* block_table,
                                      const int32_t* block_counts, int32_t n_kv_blocks, const float* page_summary,
                                      const float* value_summary, float sm_scale, void* out, float* out_lse,
-                                     hipStream_t stream) {
+                                     void* workspace, size_t workspace_bytes, hipStream_t stream) {
   sa_status st = check_kv(kv, false);
   if (st != SA_OK) return st;
   if (kv->dtype != SA_DTYPE_BF16 || is_latent(kv) || kv->d_qk != 128 || kv->page_size != 64)
@@ -896,6 +901,12 @@ sa_status sa_prefill_mean_correction(const sa_paged_kv* kv, int32_t seq, const v
                 n_kv_blocks, need_blocks, kv->max_pages);
   if (!std::isfinite(sm_scale) || !(sm_scale > 0.f))
     return fail(SA_ERR_INVALID_ARGUMENT, "sm_scale must be finite and positive");
+  if (n_q_heads / kv->n_kv_heads > 8)
+    return fail(SA_ERR_UNSUPPORTED, "mean correction supports up to 8 query heads per KV head");
+  const size_t need = sa::mean_correct_workspace(kv->n_kv_heads, n_kv_blocks, nullptr, nullptr);
+  if (!workspace || workspace_bytes < need)
+    return fail(SA_ERR_WORKSPACE_TOO_SMALL, "mean correction needs %zu workspace bytes, got %zu", need,
+                workspace ? workspace_bytes : (size_t)0);
   if (validate_on()) {
     Validator v(stream);
     v.kv(kv, seq, 1);
@@ -903,6 +914,7 @@ sa_status sa_prefill_mean_correction(const sa_paged_kv* kv, int32_t seq, const v
     if (st != SA_OK) return st;
   }
   sa::MeanCorrParams p{};
+  sa::mean_correct_workspace(kv->n_kv_heads, n_kv_blocks, workspace, &p);
   p.q = q;
   p.mu = page_summary;
   p.nu = value_summary;

@@ -207,9 +207,22 @@ struct MeanCorrParams {
   const int32_t* counts;
   void* out;                 // [q_len][Hq][128] bf16, read and rewritten
   float* out_lse;            // [q_len][Hq], read and rewritten
+  // workspace (mean_correct_workspace): the skipped blocks of each KV head,
+  // ascending, and their means packed as bf16 in 32-block chunks
+  int32_t* skip;             // [Hkv][nkb]
+  int32_t* n_skip;           // [Hkv]
+  uint16_t* pk;              // [Hkv][nch * 32][128] mean keys
+  uint16_t* pv;              // [Hkv][nch][128][32] mean values, dim-major, PV contraction order
+  uint32_t* meta;            // [Hkv][nch][64]: log2(n_b) (float bits) x 32, last token position x 32
   int q_len, q_start, Hq, Hkv, G, nkb, P;
+  int nch;                   // ceil(nkb / 32)
+  int q_tile;                // queries per workgroup (set by the launcher)
   float scale_log2;
 };
+
+// Bytes of the mean-correction workspace for Hkv KV heads and nkb blocks;
+// with `base` set, also points p's workspace arrays into it.
+size_t mean_correct_workspace(int Hkv, int nkb, void* base, MeanCorrParams* p);
 
 // ------------------------------------------------------------- launchers
 hipError_t launch_page_value_summary(const ValueSummaryParams& p, int batch, int elem_bytes, hipStream_t s);

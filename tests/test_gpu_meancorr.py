@@ -70,7 +70,11 @@ CASES = {
                                mask_kind="shared_columns", random_fraction=0.2),
     "shared_start": SMALL.replace(q_len=150, q_start=0, mask_kind="shared_columns", random_fraction=0.1),
     "shared_short": SMALL.replace(q_len=5, q_start=777, mask_kind="shared_columns", random_fraction=0.1),
-    # more skipped blocks than one 16-block chunk
+    # 3 and 6 heads per KV head: query tiles of 80 and 32 over 8 and 6 waves
+    "shared_g3": SMALL.replace(n_q_heads=6, n_kv_heads=2, mask_kind="shared_columns", random_fraction=0.1),
+    "shared_g6": SMALL.replace(n_q_heads=6, n_kv_heads=1, q_len=90, mask_kind="shared_columns",
+                               random_fraction=0.1),
+    # more skipped blocks than one 32-block chunk
     "long_prefix": SMALL.replace(q_len=70, q_start=64 * 40 + 5, mask_kind="shared_columns",
                                  random_fraction=0.05),
 }
@@ -188,6 +192,10 @@ def test_mean_correction_rejects_bad_arguments():
     nu = S.sa_page_value_summary(kv)
     with pytest.raises(S.SparseAttnError):
         S.sa_prefill_mean_correction(kv, 0, inp["q"], wl.q_start, table, counts, mu, nu, -1.0, out, lse)
+    with pytest.raises(S.SparseAttnError):      # workspace one byte short
+        need = S.sa_prefill_mean_correction_workspace_size(kv, table.shape[-1])
+        S.sa_prefill_mean_correction(kv, 0, inp["q"], wl.q_start, table, counts, mu, nu, wl.sm_scale, out, lse,
+                                     workspace=torch.empty(need - 1, dtype=torch.uint8, device=DEV))
     with pytest.raises(S.SparseAttnError):      # table too short to cover the chunk
         S.sa_prefill_mean_correction(kv, 0, inp["q"], wl.q_start, table[:, :3].contiguous(), counts, mu, nu,
                                      wl.sm_scale, out, lse)
