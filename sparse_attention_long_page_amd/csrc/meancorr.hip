@@ -200,9 +200,11 @@ __device__ __forceinline__ int mc_k_seg(int row, int seg) { return row * 16 + (s
 __device__ __forceinline__ int mc_v_seg(int row, int seg) { return row * 4 + (seg ^ ((row >> 2) & 3)); }
 
 __global__ __launch_bounds__(512) void mean_correct_kernel(MeanCorrParams p) {
-  __shared__ __attribute__((aligned(16))) uint16_t sk[2][kMcChunk * kMcD];
-  __shared__ __attribute__((aligned(16))) uint16_t sv[2][kMcD * kMcChunk];
-  __shared__ __attribute__((aligned(16))) uint32_t smeta[2][256];     // one wave-wide copy: 1 KiB
+  // two chunk buffers as distinct arrays (the loop alternates them by name),
+  // so the compiler sees that reads of one never wait for copies into the other
+  __shared__ __attribute__((aligned(16))) uint16_t sk0[kMcChunk * kMcD], sk1[kMcChunk * kMcD];
+  __shared__ __attribute__((aligned(16))) uint16_t sv0[kMcD * kMcChunk], sv1[kMcD * kMcChunk];
+  __shared__ __attribute__((aligned(16))) uint32_t sm0[256], sm1[256];   // one wave-wide copy: 1 KiB
   const int nwaves = blockDim.x >> 6;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int col = lane & 15, kq = lane >> 4;
@@ -259,34 +261,33 @@ __global__ __launch_bounds__(512) void mean_correct_kernel(MeanCorrParams p) {
   const auto rk = buffer_rsrc(p.pk + (size_t)g * p.nch * chunk_elems, (uint32_t)(p.nch * chunk_elems * 2));
   const auto rv = buffer_rsrc(p.pv + (size_t)g * p.nch * chunk_elems, (uint32_t)(p.nch * chunk_elems * 2));
   const auto rm = buffer_rsrc(p.meta + (size_t)g * p.nch * kMcMetaWords, (uint32_t)(p.nch * kMcMetaWords * 4));
-  auto stage = [&](int b, int ch) {
+  auto stage = [&](uint16_t* skd, uint16_t* svd, uint32_t* smd, int ch) __attribute__((always_inline)) {
     for (int i = wave; i < 17; i += nwaves) {
       const int s = 64 * (i & 7) + lane;             // destination segment of this lane
       if (i < 8) {
         const int row = s >> 4, seg = (s & 15) ^ (row & 15);
-        copy16_to_lds(rk, &sk[b][64 * 8 * i], (uint32_t)(((size_t)ch * chunk_elems + row * kMcD + seg * 8) * 2));
+        copy16_to_lds(rk, skd + 64 * 8 * i, (uint32_t)(((size_t)ch * chunk_elems + row * kMcD + seg * 8) * 2));
       } else if (i < 16) {
         const int row = s >> 2, seg = (s & 3) ^ ((row >> 2) & 3);
-        copy16_to_lds(rv, &sv[b][64 * 8 * (i - 8)],
+        copy16_to_lds(rv, svd + 64 * 8 * (i - 8),
                       (uint32_t)(((size_t)ch * chunk_elems + row * kMcChunk + seg * 8) * 2));
       } else {
-        copy16_to_lds(rm, &smeta[b][0], (uint32_t)((ch * kMcMetaWords + 4 * lane) * 4));
+        copy16_to_lds(rm, smd, (uint32_t)((ch * kMcMetaWords + 4 * lane) * 4));
       }
     }
   };
-  stage(0, 0);
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();
 
   bool any[2] = {false, false};
-  for (int ch = 0; ch < nch_g; ++ch) {
-    const int b = ch & 1;
+  // one chunk from (skb, svb, smb) while the next is copied into (skn, svn,
+  // smn); false once the list has passed the tile
+  auto step = [&](const uint16_t* skb, const uint16_t* svb, const uint32_t* smb, uint16_t* skn, uint16_t* svn,
+                  uint32_t* smn, int ch) __attribute__((always_inline)) -> bool {
     // the list is ascending: stop at the first chunk that starts past the tile
-    if ((int)smeta[b][32] > last_pos) break;
-    if (ch + 1 < nch_g) stage(b ^ 1, ch + 1);        // in flight over this chunk's products
+    if ((int)smb[32] > last_pos) return false;
+    if (ch + 1 < nch_g) stage(skn, svn, smn, ch + 1);   // in flight over this chunk's products
 
-    const float* lg = reinterpret_cast<const float*>(&smeta[b][0]);
-    const int* bend = reinterpret_cast<const int*>(&smeta[b][32]);
+    const float* lg = reinterpret_cast<const float*>(smb);
+    const int* bend = reinterpret_cast<const int*>(smb + 32);
     // every term of the chunk visible to every row of the wave
     const bool full = bend[kMcChunk - 1] <= wave_min_pos;
     // S^T[block][row] for the chunk's two 16-block tiles: lane holds blocks
@@ -300,7 +301,7 @@ __global__ __launch_bounds__(512) void mean_correct_kernel(MeanCorrParams p) {
     for (int st = 0; st < 2; ++st)
 #pragma unroll
       for (int ks = 0; ks < kMcD / 32; ++ks) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(&sk[b][8 * mc_k_seg(16 * st + col, 4 * ks + kq)]);
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(skb + 8 * mc_k_seg(16 * st + col, 4 * ks + kq));
 #pragma unroll
         for (int rt = 0; rt < 2; ++rt)
           s[rt][st] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qreg[rt][ks], s[rt][st], 0, 0, 0);
@@ -320,7 +321,8 @@ __global__ __launch_bounds__(512) void mean_correct_kernel(MeanCorrParams p) {
 #pragma unroll
         for (int t = 0; t < 8; ++t) {
           const int jb = 16 * (t >> 2) + 4 * kq + (t & 3);
-          if (!(row_ok[rt] && bend[jb] <= pos[rt])) z[t] = -INFINITY;
+          const bool vis = (bend[jb] <= pos[rt]) & row_ok[rt];
+          z[t] = vis ? z[t] : -INFINITY;
         }
       }
 #pragma unroll
@@ -354,13 +356,21 @@ __global__ __launch_bounds__(512) void mean_correct_kernel(MeanCorrParams p) {
     // O^T[dim][row] += Nu^T[dim][block] P^T[block][row]
 #pragma unroll
     for (int dt = 0; dt < kMcD / 16; ++dt) {
-      const bf16x8 a = *reinterpret_cast<const bf16x8*>(&sv[b][8 * mc_v_seg(16 * dt + col, kq)]);
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(svb + 8 * mc_v_seg(16 * dt + col, kq));
 #pragma unroll
       for (int rt = 0; rt < 2; ++rt)
         oacc[rt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb[rt], oacc[rt][dt], 0, 0, 0);
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();                                 // next chunk staged; this one's reads done
+    return true;
+  };
+  stage(sk0, sv0, sm0, 0);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  for (int ch = 0; ch < nch_g; ch += 2) {
+    if (!step(sk0, sv0, sm0, sk1, sv1, sm1, ch)) break;
+    if (ch + 1 >= nch_g || !step(sk1, sv1, sm1, sk0, sv0, sm0, ch + 1)) break;
   }
 #pragma unroll
   for (int rt = 0; rt < 2; ++rt) {
