@@ -44,7 +44,12 @@ with NaN last; lists are ascending logical ids (tiered: Critical segment then
 Ambient segment); each query row softmaxes over exactly its own token set;
 an empty token set gives output 0 and lse -inf; the prefill union is taken over
 all Q-blocks of the chunk and every query of a group attends causally to the
-whole group table.
+whole group table; a skipped block, and a page in the AutoTuner's mass
+estimate, stands in for its n tokens by its mean key (log-weight
+sm_scale q.mu + ln n); the AutoTuner's budget counts (page, query head)
+entries beyond the forced pages, its coverage is the estimated mass on the
+(head, page) pairs the tiered decode computes, and an Ambient page takes the
+heads of largest estimated mass.
 
 Pins (tests/test_oracle_pins.py): brute force in pure Python on tiny inputs,
 torch's scaled_dot_product_attention (float64, CPU) for select-all and
@@ -541,3 +546,131 @@ def mean_corrected_prefill(q, k_pool, v_pool, block_table_row, seq_len, page_siz
         out[i, h] = (e @ np.stack(vs)) / e.sum()
         lse[i, h] = m + math.log(e.sum())
     return out, lse
+
+
+# ---------------------------------------------------------------- autotuner
+def head_page_mass(q, mu, block_table, seq_lens, page_size, n_kv_heads, sm_scale):
+    """Estimated attention mass of every (query head, page)  [TS "Motivation":
+    the AutoTuner maximises an estimated attention-mass coverage; the estimate
+    itself is not given on the pages].
+
+    Reading: a page stands in for its n_p valid tokens by its mean key mu_p,
+    so query row (t, h) of sequence b gives page p the log-weight
+        est = sm_scale * q[b, t, h] . mu[phys(b, p), g(h)] + ln n_p
+    and the row's estimated mass on p is the softmax of est over the
+    sequence's pages.  M[b, h, p] = sum over the query tokens t of that mass
+    (so sum_p M[b, h, p] = q_tokens).  float64; NaN for pages past the end.
+    """
+    B, T, Hq, d = q.shape
+    G = Hq // n_kv_heads
+    max_pages = block_table.shape[1]
+    M = np.full((B, Hq, max_pages), np.nan, dtype=np.float64)
+    for b in range(B):
+        n = n_pages_of(seq_lens[b], page_size)
+        if n == 0:
+            continue
+        counts = np.array([valid_tokens(seq_lens[b], p, page_size) for p in range(n)], dtype=np.float64)
+        M[b, :, :n] = 0.0
+        for h in range(Hq):
+            g = h // G
+            mus = np.stack([np.asarray(mu[int(block_table[b, p]), g], dtype=np.float64) for p in range(n)])
+            for t in range(T):
+                est = sm_scale * (mus @ np.asarray(q[b, t, h], dtype=np.float64)) + np.log(counts)
+                e = np.exp(est - est.max())
+                M[b, h, :n] += e / e.sum()
+    return M
+
+
+def tier_beta(alpha: int, h: int, budget: int, group: int) -> Optional[int]:
+    """Ambient pages a configuration affords  [TS "Configuration": token_budget
+    is the total compute-entry budget B, critical_top_count is alpha,
+    ambient_head_count is h].  Reading: B counts (page, query head) entries of
+    one selection head beyond its forced pages; alpha Critical pages take all
+    `group` heads, each Ambient page h of them:  beta = floor((B - alpha*group)/h),
+    None (infeasible) when alpha*group > B."""
+    rest = budget - alpha * group
+    if rest < 0 or h <= 0:
+        return None
+    return rest // h
+
+
+def top_heads(masses: np.ndarray, heads: Sequence[int], h: int) -> List[int]:
+    """The h heads of `heads` with the largest mass (mass descending, head
+    index ascending)."""
+    order = sorted(heads, key=lambda x: (-float(masses[x]), x))
+    return sorted(order[:max(0, min(h, len(order)))])
+
+
+def tier_coverage(M, scores, seq_lens, page_size, n_kv_heads, q_tokens, sink_pages, window_pages,
+                  budget, alphas, head_counts):
+    """Estimated attention-mass coverage of each tier configuration, and the
+    configuration the AutoTuner picks  [TS "Motivation": AutoTuner picks the
+    tier/head configuration per layer that maximises the estimated coverage].
+
+    For selection head g (a KV head; its query heads are g*G .. g*G+G-1) of
+    sequence b, configuration (alpha, h) selects, as the tiered selection does
+    with top_k = alpha + beta and critical_k = alpha: the forced pages and the
+    first alpha ranked candidates (Critical, all G heads) and the next beta
+    (Ambient, the h heads of largest M on that page).  Its coverage is the
+    mass M on those (head, page) pairs over q_tokens * G; the layer's coverage
+    is the mean over sequences and KV heads.  Returns (cov [n_alpha][n_h],
+    NaN where infeasible; beta [n_alpha][n_h], -1 where infeasible; best
+    (ia, ih) = the first maximum in row-major grid order, None if none)."""
+    B, Hq, _ = M.shape
+    G = Hq // n_kv_heads
+    na, nh = len(alphas), len(head_counts)
+    cov = np.full((na, nh), np.nan, dtype=np.float64)
+    beta = np.full((na, nh), -1, dtype=np.int64)
+    for ia, a in enumerate(alphas):
+        for ih, h in enumerate(head_counts):
+            bt = tier_beta(int(a), int(h), budget, G)
+            if bt is None:
+                continue
+            beta[ia, ih] = bt
+            total = 0.0
+            for b in range(B):
+                n = n_pages_of(seq_lens[b], page_size)
+                forced = forced_pages(n, sink_pages, window_pages)
+                fset = set(forced)
+                cand = [p for p in range(n) if p not in fset]
+                for g in range(n_kv_heads):
+                    heads = list(range(g * G, (g + 1) * G))
+                    order = rank_candidates(scores[b, g], cand)
+                    a_eff = min(int(a), len(order))
+                    b_eff = min(bt, len(order) - a_eff)
+                    covered = 0.0
+                    for p in forced + order[:a_eff]:
+                        covered += sum(M[b, x, p] for x in heads)
+                    for p in order[a_eff:a_eff + b_eff]:
+                        covered += sum(M[b, x, p] for x in top_heads(M[b, :, p], heads, int(h)))
+                    total += covered / (q_tokens * G)
+            cov[ia, ih] = total / (B * n_kv_heads)
+    best = None
+    for ia in range(na):
+        for ih in range(nh):
+            if np.isnan(cov[ia, ih]):
+                continue
+            if best is None or cov[ia, ih] > cov[best]:
+                best = (ia, ih)
+    return cov, beta, best
+
+
+def ambient_head_mask(M, page_lists, page_counts, critical_counts, n_kv_heads, ambient_heads):
+    """Head mask of the Ambient tier  [TS "Motivation": Ambient pages are
+    computed with only h heads].  Reading: for every Ambient page p of
+    selection head g (list entries past the Critical count), the h heads of g
+    with the largest M[b, :, p] (mass descending, index ascending) get their
+    bit; other bits are 0.  Returns [B][max_pages][ceil(Hq/32)] uint32 words."""
+    B, Hq, max_pages = M.shape
+    G = Hq // n_kv_heads
+    words = (Hq + 31) // 32
+    mask = np.zeros((B, max_pages, words), dtype=np.uint32)
+    for b in range(B):
+        for g in range(n_kv_heads):
+            heads = list(range(g * G, (g + 1) * G))
+            cc, c = int(critical_counts[b, g]), int(page_counts[b, g])
+            for e in range(cc, c):
+                p = int(page_lists[b, g, e])
+                for x in top_heads(M[b, :, p], heads, ambient_heads):
+                    mask[b, p, x // 32] |= np.uint32(1 << (x % 32))
+    return mask

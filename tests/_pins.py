@@ -809,6 +809,170 @@ def check_mean_correction_bruteforce():
             assert abs(lse[i, h] - (m + math.log(den))) < 1e-12
 
 
+# ---------------------------------------------------------------- autotuner
+def _mass_case(rng, constant_pages):
+    """Latent-free GQA case: B=2 sequences (one with a partial last page),
+    T=2 query tokens, 4 query heads over 2 KV heads, pages of 4 tokens."""
+    B, T, Hq, Hkv, P, d = 2, 2, 4, 2, 4, 5
+    lens = [14, 9]
+    L = max(lens)
+    n_max = (L + P - 1) // P
+    if constant_pages:
+        Kp = rng.standard_normal((B, Hkv, n_max, d))
+        K = np.repeat(Kp, P, axis=2)[:, :, :L]
+    else:
+        K = rng.standard_normal((B, Hkv, L, d))
+    q = rng.standard_normal((B, T, Hq, d))
+    kp, _, bt = scatter_to_pool(K, K[..., :1], P, rng, extra_pages=2)
+    if constant_pages:
+        mu = kp[:, :, 0, :].copy()           # the page's one key, exactly
+    else:
+        mu = O.page_summary(kp, bt, np.array(lens), P)
+    return q, K, kp, bt, mu, lens, P, Hkv
+
+
+def check_head_mass_exact_on_constant_pages():
+    """When every token of a page carries the page's one key, a page's
+    estimated mass is exactly its tokens' share of the true softmax over the
+    sequence's tokens (explicit exp sums, math.fsum), summed over the query
+    tokens; a partial last page weighs its own token count."""
+    rng = np.random.default_rng(31)
+    q, K, kp, bt, mu, lens, P, Hkv = _mass_case(rng, constant_pages=True)
+    B, T, Hq, d = q.shape
+    G = Hq // Hkv
+    M = O.head_page_mass(q, mu, bt, np.array(lens), P, Hkv, 0.6)
+    for b in range(B):
+        n = (lens[b] + P - 1) // P
+        assert np.all(np.isnan(M[b, :, n:]))
+        for h in range(Hq):
+            for p in range(n):
+                exp = 0.0
+                for t in range(T):
+                    z = [0.6 * math.fsum(q[b, t, h, e] * K[b, h // G, j, e] for e in range(d)) for j in range(lens[b])]
+                    m = max(z)
+                    w = [math.exp(x - m) for x in z]
+                    exp += math.fsum(w[j] for j in range(p * P, min((p + 1) * P, lens[b]))) / math.fsum(w)
+                assert abs(M[b, h, p] - exp) <= 1e-12, (b, h, p)
+
+
+def check_head_mass_rows_sum():
+    """Random keys: every head's masses sum to the number of query tokens."""
+    rng = np.random.default_rng(32)
+    q, K, kp, bt, mu, lens, P, Hkv = _mass_case(rng, constant_pages=False)
+    M = O.head_page_mass(q, mu, bt, np.array(lens), P, Hkv, 0.6)
+    for b in range(q.shape[0]):
+        n = (lens[b] + P - 1) // P
+        assert np.allclose(M[b, :, :n].sum(axis=1), q.shape[1], atol=1e-12)
+        assert np.all(M[b, :, :n] > 0)
+
+
+def _tier_case(rng):
+    B, Hq, Hkv, T = 2, 8, 2, 2
+    n_pages = [9, 7]
+    max_pages = 10
+    M = np.full((B, Hq, max_pages), np.nan)
+    for b in range(B):
+        raw = rng.random((Hq, n_pages[b])) ** 3
+        M[b, :, :n_pages[b]] = T * raw / raw.sum(axis=1, keepdims=True)
+    scores = np.full((B, Hkv, max_pages), np.nan, dtype=np.float32)
+    for b in range(B):
+        scores[b, :, :n_pages[b]] = rng.integers(-3, 4, size=(Hkv, n_pages[b])).astype(np.float32)
+    P = 4
+    seq_lens = np.array([n * P - 1 for n in n_pages])
+    return M, scores, seq_lens, P, Hkv, T, n_pages
+
+
+def check_tier_coverage_matches_pair_sets():
+    """Coverage of each configuration against the mass on the exact (head,
+    page) pairs the tiered decode computes: lists from select_pages with
+    top_k = alpha + beta and critical_k = alpha, the Ambient mask from
+    ambient_head_mask, each head's pages from row_pages, summed with
+    math.fsum."""
+    rng = np.random.default_rng(33)
+    M, scores, seq_lens, P, Hkv, T, n_pages = _tier_case(rng)
+    B, Hq, _ = M.shape
+    G = Hq // Hkv
+    alphas, hs, budget, sink, window = [0, 1, 2, 4], [1, 2, 4], 14, 1, 1
+    cov, beta, best = O.tier_coverage(M, scores, seq_lens, P, Hkv, T, sink, window, budget, alphas, hs)
+    for ia, a in enumerate(alphas):
+        for ih, h in enumerate(hs):
+            if a * G > budget:
+                assert np.isnan(cov[ia, ih]) and beta[ia, ih] == -1
+                continue
+            bt = (budget - a * G) // h
+            assert beta[ia, ih] == bt
+            lists, counts, cc = O.select_pages(scores, n_pages, sink, window, a + bt, a)
+            mask = O.ambient_head_mask(M, lists, counts, cc, Hkv, h)
+            per = []
+            for b in range(B):
+                for g in range(Hkv):
+                    tot = []
+                    for x in range(g * G, (g + 1) * G):
+                        for p in O.row_pages(b, g, x, lists, counts, cc, mask):
+                            tot.append(M[b, x, p])
+                    per.append(math.fsum(tot) / (T * G))
+            assert abs(cov[ia, ih] - math.fsum(per) / len(per)) <= 1e-12, (a, h)
+    feas = [(cov[i, j], i, j) for i in range(len(alphas)) for j in range(len(hs)) if not np.isnan(cov[i, j])]
+    top = max(c for c, _, _ in feas)
+    assert best == min((i, j) for c, i, j in feas if c == top)
+
+
+def check_ambient_mask_bruteforce():
+    """The Ambient heads of a page maximise the page's covered mass over every
+    head subset of that size (itertools-free enumeration over bitmasks); among
+    equal masses the lowest head indices win."""
+    B, Hq, Hkv, max_pages = 1, 8, 2, 5
+    G = Hq // Hkv
+    # integer masses with ties
+    M = np.array([[[3, 1, 2, 2, 0], [1, 1, 2, 0, 5], [3, 1, 0, 2, 5], [0, 1, 2, 2, 1],
+                   [2, 2, 2, 2, 2], [1, 3, 0, 1, 0], [2, 3, 1, 0, 4], [2, 0, 1, 1, 4]]], dtype=np.float64)
+    lists = np.array([[[0, 2, 3, 4, -1], [1, 4, 0, 2, 3]]], dtype=np.int32)
+    counts = np.array([[4, 5]], dtype=np.int32)
+    cc = np.array([[1, 2]], dtype=np.int32)
+    for h in (1, 2, 3, 4):
+        mask = O.ambient_head_mask(M, lists, counts, cc, Hkv, h)
+        bits_set = {(p, x) for p in range(max_pages) for x in range(Hq) if (int(mask[0, p, 0]) >> x) & 1}
+        want = set()
+        for g in range(Hkv):
+            heads = list(range(g * G, (g + 1) * G))
+            for e in range(cc[0, g], counts[0, g]):
+                p = int(lists[0, g, e])
+                best = None
+                for bits in range(1 << G):
+                    sub = [heads[i] for i in range(G) if (bits >> i) & 1]
+                    if len(sub) != h:
+                        continue
+                    key = (-sum(M[0, x, p] for x in sub), sorted(sub))
+                    if best is None or key < best:
+                        best = key
+                want |= {(p, x) for x in best[1]}
+        assert bits_set == want, (h, sorted(bits_set ^ want))
+
+
+def check_tier_special_cases():
+    """h = G reduces to key-only selection (all heads on the first alpha +
+    beta ranked pages); a budget covering every page with every head gives
+    coverage 1; equal coverages pick the first configuration."""
+    rng = np.random.default_rng(34)
+    M, scores, seq_lens, P, Hkv, T, n_pages = _tier_case(rng)
+    B, Hq, _ = M.shape
+    G = Hq // Hkv
+    cov, beta, best = O.tier_coverage(M, scores, seq_lens, P, Hkv, T, 0, 0, 12, [0, 1, 3], [G])
+    for ia, a in enumerate([0, 1, 3]):
+        k = a + (12 - a * G) // G
+        per = []
+        for b in range(B):
+            for g in range(Hkv):
+                order = sorted(range(n_pages[b]), key=lambda p: (-float(scores[b, g, p]), p))
+                per.append(math.fsum(M[b, x, p] for p in order[:k] for x in range(g * G, (g + 1) * G)) / (T * G))
+        assert abs(cov[ia, 0] - math.fsum(per) / len(per)) <= 1e-12
+    cov, _, _ = O.tier_coverage(M, scores, seq_lens, P, Hkv, T, 1, 1, 100 * G, [10], [1, G])
+    assert np.allclose(cov, 1.0, atol=1e-12)
+    # alpha 0 and 1 with h = G and budget 2G: both take the first two ranked pages
+    cov, _, best = O.tier_coverage(M, scores, seq_lens, P, Hkv, T, 0, 0, 2 * G, [0, 1], [G])
+    assert abs(cov[0, 0] - cov[1, 0]) <= 1e-15 and best == (0, 0)
+
+
 ALL_CHECKS = [
     check_summary_constant_pages, check_summary_bruteforce,
     check_scores_exact_integers, check_scores_linearity_and_unfactored,
@@ -821,4 +985,6 @@ ALL_CHECKS = [
     check_mask_bruteforce, check_mask_invariants, check_mask_union_keeps_selection,
     check_fp8_decoding, check_fp8_decode_sdpa,
     check_value_summary_bruteforce, check_mean_correction_exact_on_constant_blocks, check_mean_correction_bruteforce,
+    check_head_mass_exact_on_constant_pages, check_head_mass_rows_sum, check_tier_coverage_matches_pair_sets,
+    check_ambient_mask_bruteforce, check_tier_special_cases,
 ]

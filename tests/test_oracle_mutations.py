@@ -23,6 +23,9 @@ _orig_mask = O.prefill_block_mask
 _orig_fp8 = O.fp8_e4m3_to_float
 _orig_deq = O.dequantize_pages
 _orig_mc = O.mean_corrected_prefill
+_orig_mass = O.head_page_mass
+_orig_beta = O.tier_beta
+_orig_cov = O.tier_coverage
 
 
 def _no_scale(qrow, K, V, sm_scale, d_v):
@@ -183,7 +186,53 @@ def _mc_partial_blocks(q, kp, vp, bt, L, P, q_start, tables, counts, n_kv, scale
     return _orig_mc(q, kp, vp, bt, L, P, q_start + P - 1, tables, counts, n_kv, scale, rows)
 
 
+def _mass_no_count(q, mu, block_table, seq_lens, page_size, n_kv_heads, sm_scale):
+    """Page log-weights without the ln n_p term (a partial page weighs like a full one)."""
+    B, T, Hq, d = q.shape
+    G = Hq // n_kv_heads
+    M = np.full((B, Hq, block_table.shape[1]), np.nan)
+    for b in range(B):
+        n = O.n_pages_of(seq_lens[b], page_size)
+        M[b, :, :n] = 0.0
+        for h in range(Hq):
+            mus = np.stack([np.asarray(mu[int(block_table[b, p]), h // G], dtype=np.float64) for p in range(n)])
+            for t in range(T):
+                est = sm_scale * (mus @ np.asarray(q[b, t, h], dtype=np.float64))
+                e = np.exp(est - est.max())
+                M[b, h, :n] += e / e.sum()
+    return M
+
+
+def _mass_no_scale(q, mu, block_table, seq_lens, page_size, n_kv_heads, sm_scale):
+    return _orig_mass(q, mu, block_table, seq_lens, page_size, n_kv_heads, 1.0)
+
+
+def _beta_plus_one(alpha, h, budget, group):
+    b = _orig_beta(alpha, h, budget, group)
+    return None if b is None else b + 1
+
+
+def _top_heads_lowest(masses, heads, h):
+    order = sorted(heads, key=lambda x: (float(masses[x]), x))
+    return sorted(order[:max(0, min(h, len(order)))])
+
+
+def _top_heads_ties_high(masses, heads, h):
+    order = sorted(heads, key=lambda x: (-float(masses[x]), -x))
+    return sorted(order[:max(0, min(h, len(order)))])
+
+
+def _cov_no_forced(M, scores, seq_lens, P, n_kv, T, sink, window, budget, alphas, hs):
+    return _orig_cov(M, scores, seq_lens, P, n_kv, T, 0, 0, budget, alphas, hs)
+
+
 MUTANTS = {
+    "mass_no_log_count": ("head_page_mass", _mass_no_count),
+    "mass_no_scale": ("head_page_mass", _mass_no_scale),
+    "tier_beta_plus_one": ("tier_beta", _beta_plus_one),
+    "ambient_heads_lowest_mass": ("top_heads", _top_heads_lowest),
+    "ambient_heads_ties_high_index": ("top_heads", _top_heads_ties_high),
+    "coverage_drops_forced_pages": ("tier_coverage", _cov_no_forced),
     "mean_correction_no_count": ("mean_corrected_prefill", _mc_no_count),
     "mean_correction_partial_blocks": ("mean_corrected_prefill", _mc_partial_blocks),
     "fp8_bias_8": ("fp8_e4m3_to_float", _fp8_bias_8),
