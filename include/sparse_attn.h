@@ -388,6 +388,83 @@ sa_status sa_prefill_mean_correction(const sa_paged_kv* kv, int32_t seq,
                                      hipStream_t stream);
 
 /* ------------------------------------------------------------------------
+ * AutoTuner of the tiered selection (TileSparse README, "Motivation":
+ * Critical pages with all query heads, Ambient pages with h heads, and an
+ * online per-layer search of the tier/head configuration that maximises an
+ * estimated attention-mass coverage; "Configuration": token_budget,
+ * critical_top_count, ambient_head_count).  The pages do not define the
+ * estimate; the reading taken is stated with each call.  Per-KV-head
+ * selection only (selection head g = KV head g, query heads g*G .. g*G+G-1).
+ *
+ * sa_head_page_mass -- estimated attention mass of every (query head, page):
+ *   est[b][t][h][p] = sm_scale * q[b][t][h] . page_summary[phys(b,p)][g(h)] + ln n_p
+ *   head_mass[b][h][p] = sum over t < q_tokens of softmax over p < n_b of est
+ * (a page stands in for its n_p valid tokens by its mean key; each head's
+ * masses sum to q_tokens).  The mean keys are split into two bf16 halves on
+ * MFMA, so the products are fp32-accurate; softmax in fp32.
+ *   q            [batch][q_tokens][n_q_heads][d_qk] bf16 (bf16 or FP8 caches)
+ *   page_summary [n_phys_pages][n_kv_heads][d_qk] fp32 (sa_page_summary)
+ *   head_mass    out [batch][n_q_heads][max_pages] fp32; entries of pages past
+ *                a sequence's end are left untouched
+ *   workspace    >= sa_head_page_mass_workspace_size(...) bytes (page
+ *                log-weights), overwritten
+ * Needs d_qk 64, 128 or 576 and max_pages <= 4096.
+ * ---------------------------------------------------------------------- */
+size_t sa_head_page_mass_workspace_size(const sa_paged_kv* kv, int32_t batch, int32_t q_tokens,
+                                        int32_t n_q_heads);
+
+sa_status sa_head_page_mass(const sa_paged_kv* kv, int32_t batch, const void* q, int32_t q_tokens,
+                            int32_t n_q_heads, const float* page_summary, float sm_scale, float* head_mass,
+                            void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * sa_autotune_tiers -- coverage of each (alpha, h) of a search grid and the
+ * configuration the AutoTuner keeps.
+ *   budget B: (page, query head) entries per KV head beyond its forced pages;
+ *   beta(alpha, h) = floor((B - alpha*G) / h), infeasible when alpha*G > B.
+ * For sequence b and KV head g the configuration selects, exactly as
+ * sa_select_pages with top_k = alpha + beta and critical_k = alpha would from
+ * `scores`: the forced pages F and the first alpha ranked candidates
+ * (Critical, all G heads) and the next beta (Ambient, each with the h heads
+ * of largest head_mass on it, mass descending then head ascending).  Its
+ * coverage = (sum of head_mass over those (head, page) pairs) / (q_tokens*G);
+ * the layer's coverage is the mean over sequences and KV heads.
+ *   head_mass  [batch][n_q_heads][max_pages] fp32 (sa_head_page_mass)
+ *   scores     [batch][n_kv_heads][scores_stride] fp32 router scores
+ *              (sa_select_pages scores_out), scores_stride >= max_pages
+ *   alphas, ambient_heads: HOST arrays of 1..16 entries (alpha >= 0, h >= 1)
+ *   coverage_out out [n_alphas][n_heads] fp32 (device), NaN where infeasible
+ *   choice_out   out int32[3] (device): alpha index, h index, beta of the
+ *                first configuration of largest coverage in row-major order
+ *                (-1 each when none is feasible)
+ *   workspace  >= sa_autotune_tiers_workspace_size(...) bytes, overwritten
+ * Needs n_q_heads / n_kv_heads <= 128 and max_pages <= 4096.
+ * ---------------------------------------------------------------------- */
+size_t sa_autotune_tiers_workspace_size(const sa_paged_kv* kv, int32_t batch, int32_t n_heads);
+
+sa_status sa_autotune_tiers(const sa_paged_kv* kv, int32_t batch, int32_t q_tokens, int32_t n_q_heads,
+                            const float* head_mass, const float* scores, int32_t scores_stride,
+                            int32_t sink_pages, int32_t window_pages, int32_t budget,
+                            const int32_t* alphas, int32_t n_alphas, const int32_t* ambient_heads,
+                            int32_t n_heads, float* coverage_out, int32_t* choice_out,
+                            void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * sa_ambient_head_mask -- the Ambient tier's head mask for tiered lists
+ * (sa_select_pages with critical_counts): for every list entry of KV head g
+ * past its Critical count, page p gets the bits of the `ambient_heads` query
+ * heads of g with the largest head_mass[b][h][p] (mass descending, head
+ * ascending); every other bit of ambient_mask_out is cleared.
+ *   ambient_mask_out out [batch][max_pages][ceil(n_q_heads/32)] uint32, the
+ *   layout sa_sparse_decode reads.
+ * Needs n_q_heads / n_kv_heads <= 128.
+ * ---------------------------------------------------------------------- */
+sa_status sa_ambient_head_mask(const sa_paged_kv* kv, int32_t batch, int32_t n_q_heads, const float* head_mass,
+                               const int32_t* page_lists, int32_t list_stride, const int32_t* page_counts,
+                               const int32_t* critical_counts, int32_t ambient_heads,
+                               uint32_t* ambient_mask_out, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
  * sa_set_debug_validate -- opt-in device-side checks of the index data every
  * call trusts, for callers that must not trust it (the "raise a clear error"
  * convention of the TileSparse README, "Quick start"; [UAE] "Key Design

@@ -35,7 +35,8 @@ EXPORTED = [
     "sa_sparse_decode_workspace_size", "sa_sparse_decode", "sa_sparse_decode_noalloc", "sa_select_decode",
     "sa_block_sparse_prefill_workspace_size", "sa_block_sparse_prefill", "sa_prefill_block_mask",
     "sa_page_value_summary", "sa_prefill_mean_correction_workspace_size", "sa_prefill_mean_correction",
-    "sa_set_debug_validate",
+    "sa_head_page_mass_workspace_size", "sa_head_page_mass", "sa_autotune_tiers_workspace_size", "sa_autotune_tiers",
+    "sa_ambient_head_mask", "sa_set_debug_validate",
     "sa_status_string", "sa_last_error_message", "sa_version",
 ]
 
@@ -91,6 +92,12 @@ def load_library(build_if_missing: bool = True) -> ctypes.CDLL:
         "sa_prefill_mean_correction_workspace_size": (c_size_t, [P, c_int32]),
         "sa_prefill_mean_correction": (c_int, [P, c_int32, P, c_int32, c_int32, c_int32, P, P, c_int32, P, P,
                                                c_float, P, P, P, c_size_t, P]),
+        "sa_head_page_mass_workspace_size": (c_size_t, [P, c_int32, c_int32, c_int32]),
+        "sa_head_page_mass": (c_int, [P, c_int32, P, c_int32, c_int32, P, c_float, P, P, c_size_t, P]),
+        "sa_autotune_tiers_workspace_size": (c_size_t, [P, c_int32, c_int32]),
+        "sa_autotune_tiers": (c_int, [P, c_int32, c_int32, c_int32, P, P, c_int32, c_int32, c_int32, c_int32, P,
+                                      c_int32, P, c_int32, P, P, P, c_size_t, P]),
+        "sa_ambient_head_mask": (c_int, [P, c_int32, c_int32, P, P, c_int32, P, P, c_int32, P, P]),
         "sa_set_debug_validate": (c_int, [c_int]),
         "sa_status_string": (ctypes.c_char_p, [c_int]),
         "sa_last_error_message": (ctypes.c_char_p, []),
@@ -366,6 +373,65 @@ def sa_prefill_mean_correction(kv: PagedKV, seq: int, q: torch.Tensor, q_start: 
         _ptr(value_summary), float(sm_scale), _ptr(out), _ptr(out_lse), _ptr(workspace), workspace.numel(),
         _stream(kv.device)))
     return out, out_lse
+
+
+def sa_head_page_mass_workspace_size(kv: PagedKV, q_tokens: int, n_q_heads: int) -> int:
+    return load_library().sa_head_page_mass_workspace_size(kv.ref, kv.batch, q_tokens, n_q_heads)
+
+
+def sa_head_page_mass(kv: PagedKV, q: torch.Tensor, page_summary: torch.Tensor, sm_scale: float, *,
+                      out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Estimated attention mass [B][Hq][max_pages] fp32 of every (query head, page); q [B][T][Hq][d] bf16."""
+    B, T, Hq, _ = q.shape
+    if out is None:
+        out = torch.full((B, Hq, kv.max_pages), float("nan"), dtype=torch.float32, device=kv.device)
+    if workspace is None:
+        nbytes = sa_head_page_mass_workspace_size(kv, T, Hq)
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=kv.device)
+    _check(load_library().sa_head_page_mass(kv.ref, B, _ptr(q), T, Hq, _ptr(page_summary), float(sm_scale),
+                                            _ptr(out), _ptr(workspace), workspace.numel(), _stream(kv.device)))
+    return out
+
+
+def sa_autotune_tiers_workspace_size(kv: PagedKV, n_heads: int) -> int:
+    return load_library().sa_autotune_tiers_workspace_size(kv.ref, kv.batch, n_heads)
+
+
+def sa_autotune_tiers(kv: PagedKV, head_mass: torch.Tensor, scores: torch.Tensor, *, q_tokens: int,
+                      sink_pages: int, window_pages: int, budget: int, alphas, ambient_heads,
+                      workspace: Optional[torch.Tensor] = None, out=None):
+    """Returns (coverage [n_alphas][n_heads] fp32, choice int32[3] = alpha index, head index, beta);
+    alphas and ambient_heads are host sequences."""
+    Hq = head_mass.shape[1]
+    na, nh = len(alphas), len(ambient_heads)
+    if out is None:
+        cov = torch.empty((na, nh), dtype=torch.float32, device=kv.device)
+        choice = torch.empty((3,), dtype=torch.int32, device=kv.device)
+    else:
+        cov, choice = out
+    if workspace is None:
+        nbytes = sa_autotune_tiers_workspace_size(kv, nh)
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=kv.device)
+    a = (c_int32 * na)(*[int(x) for x in alphas])
+    h = (c_int32 * nh)(*[int(x) for x in ambient_heads])
+    _check(load_library().sa_autotune_tiers(
+        kv.ref, kv.batch, q_tokens, Hq, _ptr(head_mass), _ptr(scores), scores.shape[-1], sink_pages, window_pages,
+        budget, ctypes.cast(a, ctypes.c_void_p), na, ctypes.cast(h, ctypes.c_void_p), nh, _ptr(cov), _ptr(choice),
+        _ptr(workspace), workspace.numel(), _stream(kv.device)))
+    return cov, choice
+
+
+def sa_ambient_head_mask(kv: PagedKV, head_mass: torch.Tensor, page_lists: torch.Tensor, page_counts: torch.Tensor,
+                         critical_counts: torch.Tensor, ambient_heads: int,
+                         out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Ambient head mask [B][max_pages][ceil(Hq/32)] int32 words for tiered per-KV-head lists."""
+    Hq = head_mass.shape[1]
+    if out is None:
+        out = torch.empty((kv.batch, kv.max_pages, (Hq + 31) // 32), dtype=torch.int32, device=kv.device)
+    _check(load_library().sa_ambient_head_mask(
+        kv.ref, kv.batch, Hq, _ptr(head_mass), _ptr(page_lists), page_lists.shape[-1], _ptr(page_counts),
+        _ptr(critical_counts), int(ambient_heads), _ptr(out), _stream(kv.device)))
+    return out
 
 
 def sa_set_debug_validate(on: bool) -> bool:

@@ -23,7 +23,7 @@ LIB = os.path.join(HERE, "libsparse_attn.so")
 ARCH = "gfx950"
 
 SOURCES = ["api.cpp", "summary_score.hip", "select.hip", "decode.hip", "mla.hip", "prefill.hip",
-           "select_decode.hip", "validate.hip", "mask.hip", "meancorr.hip"]
+           "select_decode.hip", "validate.hip", "mask.hip", "meancorr.hip", "autotune.hip"]
 
 CFLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-fPIC", "-std=c++17", "-Wall", "-Wno-unused-function",

@@ -935,4 +935,181 @@ sa_status sa_prefill_mean_correction(const sa_paged_kv* kv, int32_t seq, const v
   return device_status(sa::launch_mean_correct(p, stream), "mean correction launch");
 }
 
+// --------------------------------------------------------------- autotuner
+static size_t mass_stride(const sa_paged_kv* kv) { return (size_t)(kv->max_pages + 3) / 4 * 4; }
+
+size_t sa_head_page_mass_workspace_size(const sa_paged_kv* kv, int32_t batch, int32_t q_tokens,
+                                        int32_t n_q_heads) {
+  if (!kv || batch <= 0 || q_tokens <= 0 || n_q_heads <= 0 || kv->max_pages <= 0) return 0;
+  return align_up((size_t)batch * q_tokens * n_q_heads * mass_stride(kv) * sizeof(float));
+}
+
+static sa_status check_tuner_heads(const sa_paged_kv* kv, int32_t n_q_heads) {
+  if (n_q_heads <= 0 || n_q_heads % kv->n_kv_heads != 0)
+    return fail(SA_ERR_INVALID_ARGUMENT, "n_q_heads must be a positive multiple of n_kv_heads");
+  if (n_q_heads / kv->n_kv_heads > sa::kTuneMaxGroup)
+    return fail(SA_ERR_UNSUPPORTED, "at most %d query heads per KV head", sa::kTuneMaxGroup);
+  if (kv->max_pages > sa::kTuneMaxPages)
+    return fail(SA_ERR_UNSUPPORTED, "max_pages %d exceeds %d", kv->max_pages, sa::kTuneMaxPages);
+  return SA_OK;
+}
+
+sa_status sa_head_page_mass(const sa_paged_kv* kv, int32_t batch, const void* q, int32_t q_tokens,
+                            int32_t n_q_heads, const float* page_summary, float sm_scale, float* head_mass,
+                            void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  sa_status st = check_kv(kv, false);
+  if (st != SA_OK) return st;
+  if ((st = check_tuner_heads(kv, n_q_heads)) != SA_OK) return st;
+  if (kv->dtype == SA_DTYPE_FP32) return fail(SA_ERR_UNSUPPORTED, "the mass estimate needs bf16 queries");
+  if (kv->d_qk != 64 && kv->d_qk != 128 && kv->d_qk != 576)
+    return fail(SA_ERR_UNSUPPORTED, "d_qk %d unsupported (64, 128 or 576)", kv->d_qk);
+  if (batch <= 0 || q_tokens <= 0) return fail(SA_ERR_INVALID_ARGUMENT, "batch and q_tokens must be positive");
+  if (!q || !page_summary || !head_mass)
+    return fail(SA_ERR_INVALID_ARGUMENT, "q, page_summary and head_mass must be set");
+  if (!std::isfinite(sm_scale) || !(sm_scale > 0.f))
+    return fail(SA_ERR_INVALID_ARGUMENT, "sm_scale must be finite and positive");
+  const size_t need = sa_head_page_mass_workspace_size(kv, batch, q_tokens, n_q_heads);
+  if (!workspace || workspace_bytes < need)
+    return fail(SA_ERR_WORKSPACE_TOO_SMALL, "head mass needs %zu workspace bytes, got %zu", need,
+                workspace ? workspace_bytes : (size_t)0);
+  if (validate_on()) {
+    Validator v(stream);
+    v.kv(kv, 0, batch);
+    st = v.finish(kv, 0);
+    if (st != SA_OK) return st;
+  }
+  sa::MassParams p{};
+  p.q = q;
+  p.mu = page_summary;
+  p.block_table = kv->block_table;
+  p.seq_lens = kv->seq_lens;
+  p.est = static_cast<float*>(workspace);
+  p.mass = head_mass;
+  p.B = batch;
+  p.T = q_tokens;
+  p.Hq = n_q_heads;
+  p.Hkv = kv->n_kv_heads;
+  p.G = n_q_heads / kv->n_kv_heads;
+  p.d = kv->d_qk;
+  p.P = kv->page_size;
+  p.max_pages = kv->max_pages;
+  p.stride = (int)mass_stride(kv);
+  p.sm_scale = sm_scale;
+  return device_status(sa::launch_head_mass(p, stream), "head mass launch");
+}
+
+size_t sa_autotune_tiers_workspace_size(const sa_paged_kv* kv, int32_t batch, int32_t n_heads) {
+  if (!kv || batch <= 0 || n_heads <= 0 || kv->n_kv_heads <= 0 || kv->max_pages <= 0) return 0;
+  const size_t rows = (size_t)batch * kv->n_kv_heads;
+  return align_up(rows * kv->max_pages * sizeof(float)) +
+         align_up(rows * kv->max_pages * n_heads * sizeof(float)) +
+         align_up(rows * sa::kTuneMaxGrid * sa::kTuneMaxGrid * sizeof(float));
+}
+
+sa_status sa_autotune_tiers(const sa_paged_kv* kv, int32_t batch, int32_t q_tokens, int32_t n_q_heads,
+                            const float* head_mass, const float* scores, int32_t scores_stride,
+                            int32_t sink_pages, int32_t window_pages, int32_t budget, const int32_t* alphas,
+                            int32_t n_alphas, const int32_t* ambient_heads, int32_t n_heads, float* coverage_out,
+                            int32_t* choice_out, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  sa_status st = check_kv(kv, false);
+  if (st != SA_OK) return st;
+  if ((st = check_tuner_heads(kv, n_q_heads)) != SA_OK) return st;
+  if (batch <= 0 || q_tokens <= 0) return fail(SA_ERR_INVALID_ARGUMENT, "batch and q_tokens must be positive");
+  if (!head_mass || !scores || !alphas || !ambient_heads || !coverage_out || !choice_out)
+    return fail(SA_ERR_INVALID_ARGUMENT, "head_mass, scores, alphas, ambient_heads, coverage_out and choice_out "
+                                         "must be set");
+  if (scores_stride < kv->max_pages)
+    return fail(SA_ERR_INVALID_ARGUMENT, "scores_stride %d must be >= max_pages %d", scores_stride, kv->max_pages);
+  if (sink_pages < 0 || window_pages < 0 || budget < 0)
+    return fail(SA_ERR_INVALID_ARGUMENT, "sink_pages, window_pages and budget must be >= 0");
+  if (n_alphas < 1 || n_alphas > sa::kTuneMaxGrid || n_heads < 1 || n_heads > sa::kTuneMaxGrid)
+    return fail(SA_ERR_INVALID_ARGUMENT, "n_alphas and n_heads must be in [1, %d]", sa::kTuneMaxGrid);
+  const int G = n_q_heads / kv->n_kv_heads;
+  sa::TuneParams p{};
+  for (int i = 0; i < n_alphas; ++i) {
+    if (alphas[i] < 0) return fail(SA_ERR_INVALID_ARGUMENT, "alphas[%d] = %d < 0", i, alphas[i]);
+    p.alpha[i] = alphas[i];
+  }
+  for (int k = 0; k < n_heads; ++k) {
+    if (ambient_heads[k] < 1) return fail(SA_ERR_INVALID_ARGUMENT, "ambient_heads[%d] = %d < 1", k, ambient_heads[k]);
+    p.heads[k] = ambient_heads[k];
+  }
+  for (int i = 0; i < n_alphas; ++i)
+    for (int k = 0; k < n_heads; ++k) {
+      const long rest = (long)budget - (long)alphas[i] * G;
+      p.beta[i * n_heads + k] = rest < 0 ? -1 : (int)std::min<long>(rest / ambient_heads[k], INT32_MAX);
+    }
+  const size_t need = sa_autotune_tiers_workspace_size(kv, batch, n_heads);
+  if (!workspace || workspace_bytes < need)
+    return fail(SA_ERR_WORKSPACE_TOO_SMALL, "autotune needs %zu workspace bytes, got %zu", need,
+                workspace ? workspace_bytes : (size_t)0);
+  if (validate_on()) {
+    Validator v(stream);
+    v.kv(kv, 0, batch);
+    st = v.finish(kv, 0);
+    if (st != SA_OK) return st;
+  }
+  const size_t rows = (size_t)batch * kv->n_kv_heads;
+  char* w = static_cast<char*>(workspace);
+  p.mall = reinterpret_cast<float*>(w);
+  w += align_up(rows * kv->max_pages * sizeof(float));
+  p.tsum = reinterpret_cast<float*>(w);
+  w += align_up(rows * kv->max_pages * n_heads * sizeof(float));
+  p.part = reinterpret_cast<float*>(w);
+  p.mass = head_mass;
+  p.scores = scores;
+  p.seq_lens = kv->seq_lens;
+  p.coverage = coverage_out;
+  p.choice = choice_out;
+  p.B = batch;
+  p.T = q_tokens;
+  p.Hq = n_q_heads;
+  p.Hkv = kv->n_kv_heads;
+  p.G = G;
+  p.P = kv->page_size;
+  p.max_pages = kv->max_pages;
+  p.scores_stride = scores_stride;
+  p.sink = sink_pages;
+  p.window = window_pages;
+  p.n_a = n_alphas;
+  p.n_h = n_heads;
+  return device_status(sa::launch_autotune(p, stream), "autotune launch");
+}
+
+sa_status sa_ambient_head_mask(const sa_paged_kv* kv, int32_t batch, int32_t n_q_heads, const float* head_mass,
+                               const int32_t* page_lists, int32_t list_stride, const int32_t* page_counts,
+                               const int32_t* critical_counts, int32_t ambient_heads, uint32_t* ambient_mask_out,
+                               hipStream_t stream) {
+  sa_status st = check_kv(kv, false);
+  if (st != SA_OK) return st;
+  if ((st = check_tuner_heads(kv, n_q_heads)) != SA_OK) return st;
+  if (batch <= 0 || list_stride <= 0) return fail(SA_ERR_INVALID_ARGUMENT, "batch and list_stride must be positive");
+  if (!head_mass || !page_lists || !page_counts || !critical_counts || !ambient_mask_out)
+    return fail(SA_ERR_INVALID_ARGUMENT, "head_mass, page_lists, page_counts, critical_counts and "
+                                         "ambient_mask_out must be set");
+  if (ambient_heads < 0) return fail(SA_ERR_INVALID_ARGUMENT, "ambient_heads must be >= 0");
+  if (validate_on()) {
+    Validator v(stream);
+    v.kv(kv, 0, batch);
+    v.lists(kv, batch, kv->n_kv_heads, page_lists, page_counts, critical_counts, list_stride);
+    st = v.finish(kv, list_stride);
+    if (st != SA_OK) return st;
+  }
+  sa::AmbientMaskParams p{};
+  p.mass = head_mass;
+  p.lists = page_lists;
+  p.counts = page_counts;
+  p.ccounts = critical_counts;
+  p.mask = ambient_mask_out;
+  p.B = batch;
+  p.Hq = n_q_heads;
+  p.Hkv = kv->n_kv_heads;
+  p.G = n_q_heads / kv->n_kv_heads;
+  p.max_pages = kv->max_pages;
+  p.list_stride = list_stride;
+  p.words = (n_q_heads + 31) / 32;
+  p.h = ambient_heads;
+  return device_status(sa::launch_ambient_mask(p, stream), "ambient mask launch");
+}
+
 }  // extern "C"

@@ -224,9 +224,51 @@ struct MeanCorrParams {
 // with `base` set, also points p's workspace arrays into it.
 size_t mean_correct_workspace(int Hkv, int nkb, void* base, MeanCorrParams* p);
 
+constexpr int kTuneMaxGrid = 16;      // alphas and head counts per search, each at most
+constexpr int kTuneMaxPages = 4096;    // pages per sequence a search ranks
+constexpr int kTuneMaxGroup = 128;     // query heads per KV head
+
+struct MassParams {
+  const void* q;             // [B][T][Hq][d] bf16
+  const float* mu;           // [n_phys][Hkv][d]
+  const int32_t* block_table;
+  const int32_t* seq_lens;
+  float* est;                // workspace [B][T*Hq][stride]: page log-weights
+  float* mass;               // out [B][Hq][max_pages]
+  int B, T, Hq, Hkv, G, d, P, max_pages, stride;
+  float sm_scale;
+};
+
+struct TuneParams {
+  const float* mass;         // [B][Hq][max_pages]
+  const float* scores;       // [B][Hkv][scores_stride]
+  const int32_t* seq_lens;
+  float* mall;               // workspace [B][Hkv][max_pages]: a page's mass over the group
+  float* tsum;               // workspace [B][Hkv][max_pages][n_h]: its top-h head masses
+  float* part;               // workspace [B*Hkv][n_a*n_h]: per (sequence, KV head) coverage
+  float* coverage;           // out [n_a][n_h]
+  int32_t* choice;           // out [3]: alpha index, head-count index, beta
+  int B, T, Hq, Hkv, G, P, max_pages, scores_stride, sink, window;
+  int n_a, n_h;
+  int alpha[kTuneMaxGrid], heads[kTuneMaxGrid];
+  int beta[kTuneMaxGrid * kTuneMaxGrid];   // -1: infeasible
+};
+
+struct AmbientMaskParams {
+  const float* mass;         // [B][Hq][max_pages]
+  const int32_t* lists;      // [B][Hkv][list_stride]
+  const int32_t* counts;     // [B][Hkv]
+  const int32_t* ccounts;    // [B][Hkv]
+  uint32_t* mask;            // out [B][max_pages][words]
+  int B, Hq, Hkv, G, max_pages, list_stride, words, h;
+};
+
 // ------------------------------------------------------------- launchers
 hipError_t launch_page_value_summary(const ValueSummaryParams& p, int batch, int elem_bytes, hipStream_t s);
 hipError_t launch_mean_correct(const MeanCorrParams& p, hipStream_t s);
+hipError_t launch_head_mass(const MassParams& p, hipStream_t s);
+hipError_t launch_autotune(const TuneParams& p, hipStream_t s);
+hipError_t launch_ambient_mask(const AmbientMaskParams& p, hipStream_t s);
 hipError_t launch_page_summary(const SummaryParams& p, int batch, int bf16, hipStream_t s);
 hipError_t launch_select(const SelectParams& p, int batch, int max_pages, hipStream_t s);
 hipError_t launch_score_select(const ScoreParams& sp, const SelectParams& p, int batch, int bf16, hipStream_t s);
