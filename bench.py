@@ -452,9 +452,55 @@ def run_decode(args):
         res["roofline_mfma"] = {"bound": "mfma", "achieved": round(tf, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
                                 "unit": "TFLOP/s", "frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4),
                                 "kernel": "sa_sparse_decode (latent tiered + split merge)"}
+        res["autotune"] = autotune_leg(S, wl, inp, lists, counts, ccounts)
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline_decode(wl, steps[0][2])
     return res
+
+
+def autotune_leg(S, wl, inp, lists, counts, ccounts):
+    """The per-layer tier search on one step's inputs: the estimated (head,
+    page) mass (algorithmic FLOPs 2*d per (query row, page)), the coverage of
+    a grid around the configured tiers under the configured budget
+    (alpha*G + beta*h entries), and the Ambient head mask of the step's lists."""
+    kv = S.PagedKV(inp["k_pool"], inp["v_pool"], inp["block_table"], inp["seq_lens"], d_v=wl.d_v)
+    mu = S.sa_page_summary(kv)
+    G = wl.n_q_heads // wl.n_kv_heads
+    B, T = wl.batch, wl.q_tokens
+    mass = torch.empty((B, wl.n_q_heads, wl.max_pages), dtype=torch.float32, device=mu.device)
+    ws_m = torch.empty(S.sa_head_page_mass_workspace_size(kv, T, wl.n_q_heads), dtype=torch.uint8, device=mu.device)
+    alphas, heads = [0, 2, 4, 8, 12, 16], [8, 16, 32, 64, 128]
+    budget = wl.critical_k * G + (wl.top_k - wl.critical_k) * wl.ambient_heads
+    ws_t = torch.empty(S.sa_autotune_tiers_workspace_size(kv, len(heads)), dtype=torch.uint8, device=mu.device)
+    cov = torch.empty((len(alphas), len(heads)), dtype=torch.float32, device=mu.device)
+    choice = torch.empty((3,), dtype=torch.int32, device=mu.device)
+    scores = inp["scores"]
+    if scores is None:
+        # the router's scores of this step (pooled query against the page means)
+        scores = torch.empty((B, wl.n_kv_heads, wl.max_pages), dtype=torch.float32, device=mu.device)
+        S.sa_select_pages(kv, n_q_heads=wl.n_q_heads, mode=S.SA_SEL_PER_KV_HEAD, sink_pages=wl.sink_pages,
+                          window_pages=wl.window_pages, top_k=wl.top_k, q=inp["q"], page_summary=mu,
+                          scores_out=scores)
+    mask = torch.empty((B, wl.max_pages, (wl.n_q_heads + 31) // 32), dtype=torch.int32, device=mu.device)
+    m_us = time_back_to_back([lambda: S.sa_head_page_mass(kv, inp["q"], mu, wl.sm_scale, out=mass, workspace=ws_m)],
+                             8)
+    t_us = time_back_to_back([lambda: S.sa_autotune_tiers(kv, mass, scores, q_tokens=T, sink_pages=wl.sink_pages,
+                                                          window_pages=wl.window_pages, budget=budget,
+                                                          alphas=alphas, ambient_heads=heads, workspace=ws_t,
+                                                          out=(cov, choice))], 8)
+    a_us = time_back_to_back([lambda: S.sa_ambient_head_mask(kv, mass, lists, counts, ccounts, wl.ambient_heads,
+                                                             out=mask)], 8)
+    n_pages = int(((inp["seq_lens"].long() + wl.page_size - 1) // wl.page_size).sum().item())
+    flops = 2 * wl.d_qk * T * wl.n_q_heads * n_pages
+    c = cov.cpu()
+    ia, ih, beta = choice.cpu().tolist()
+    cfg = c[alphas.index(wl.critical_k), heads.index(wl.ambient_heads)].item() \
+        if wl.critical_k in alphas and wl.ambient_heads in heads else None
+    return {"head_mass_us": round(m_us, 1), "head_mass_tflops": round(flops / (m_us * 1e-6) / 1e12, 1),
+            "search_us": round(t_us, 1), "ambient_mask_us": round(a_us, 1), "budget": budget,
+            "grid": {"alphas": alphas, "ambient_heads": heads},
+            "kept": {"alpha": alphas[ia], "h": heads[ih], "beta": beta, "coverage": round(c[ia, ih].item(), 5)},
+            "configured_coverage": None if cfg is None else round(cfg, 5)}
 
 
 def prefill_flops(wl, table, counts):

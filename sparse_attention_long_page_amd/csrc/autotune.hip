@@ -323,7 +323,8 @@ __global__ void clear_words_kernel(uint32_t* w, size_t n) {
     w[i] = 0u;
 }
 
-// grid (B*Hkv), 256 threads: wave w takes Ambient entries cc + w, cc + w + 4, ...
+// grid (B*Hkv, ceil(list_stride/4)), 256 threads: wave w takes Ambient entry
+// cc + 4*blockIdx.y + w of KV head g's list
 __global__ __launch_bounds__(256) void ambient_mask_kernel(AmbientMaskParams p) {
   __shared__ float vals[4][kTuneMaxGroup];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -331,25 +332,20 @@ __global__ __launch_bounds__(256) void ambient_mask_kernel(AmbientMaskParams p) 
   const int cnt = p.counts[(size_t)b * p.Hkv + g];
   const int cc = p.ccounts[(size_t)b * p.Hkv + g];
   const int32_t* list = p.lists + ((size_t)b * p.Hkv + g) * p.list_stride;
-  const int n_amb = max(0, cnt - cc);
-  for (int e0 = 0; e0 < n_amb; e0 += 4) {            // uniform trip count
-    const int e = cc + e0 + wave;
-    const bool ok = e0 + wave < n_amb;
-    int pg = ok ? list[e] : 0;
-    const bool in_range = pg >= 0 && pg < p.max_pages;
-    if (!in_range) pg = 0;
-    for (int i = lane; i < p.G; i += 64)
-      vals[wave][i] = ok ? p.mass[((size_t)b * p.Hq + (size_t)g * p.G + i) * p.max_pages + pg] : 0.f;
-    __syncthreads();
-    if (ok && in_range) {
-      for (int i = lane; i < p.G; i += 64) {
-        if (head_rank(vals[wave], p.G, i) < p.h) {
-          const int hq = g * p.G + i;
-          atomicOr(p.mask + ((size_t)b * p.max_pages + pg) * p.words + (hq >> 5), 1u << (hq & 31));
-        }
-      }
+  const int e = cc + 4 * (int)blockIdx.y + wave;
+  const bool ok = e >= cc && e < min(cnt, p.list_stride);
+  int pg = ok ? list[e] : 0;
+  const bool in_range = ok && pg >= 0 && pg < p.max_pages;
+  if (!in_range) pg = 0;
+  for (int i = lane; i < p.G; i += 64)
+    vals[wave][i] = in_range ? p.mass[((size_t)b * p.Hq + (size_t)g * p.G + i) * p.max_pages + pg] : 0.f;
+  __syncthreads();
+  if (!in_range) return;
+  for (int i = lane; i < p.G; i += 64) {
+    if (head_rank(vals[wave], p.G, i) < p.h) {
+      const int hq = g * p.G + i;
+      atomicOr(p.mask + ((size_t)b * p.max_pages + pg) * p.words + (hq >> 5), 1u << (hq & 31));
     }
-    __syncthreads();
   }
 }
 
@@ -358,7 +354,7 @@ hipError_t launch_ambient_mask(const AmbientMaskParams& p, hipStream_t s) {
   const size_t words = (size_t)p.B * p.max_pages * p.words;
   hipLaunchKernelGGL(clear_words_kernel, dim3((unsigned)std::min<size_t>((words + 255) / 256, 4096)), dim3(256), 0,
                      s, p.mask, words);
-  hipLaunchKernelGGL(ambient_mask_kernel, dim3(p.B * p.Hkv), dim3(256), 0, s, p);
+  hipLaunchKernelGGL(ambient_mask_kernel, dim3(p.B * p.Hkv, (p.list_stride + 3) / 4), dim3(256), 0, s, p);
   return hipGetLastError();
 }
 
