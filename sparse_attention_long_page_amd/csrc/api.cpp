@@ -1003,7 +1003,7 @@ size_t sa_autotune_tiers_workspace_size(const sa_paged_kv* kv, int32_t batch, in
   const size_t rows = (size_t)batch * kv->n_kv_heads;
   return align_up(rows * kv->max_pages * sizeof(float)) +
          align_up(rows * kv->max_pages * n_heads * sizeof(float)) +
-         align_up(rows * sa::kTuneMaxGrid * sa::kTuneMaxGrid * sizeof(float));
+         align_up(rows * sa::autotune_chunks(kv->max_pages) * sa::kTuneMaxGrid * sa::kTuneMaxGrid * sizeof(float));
 }
 
 sa_status sa_autotune_tiers(const sa_paged_kv* kv, int32_t batch, int32_t q_tokens, int32_t n_q_heads,

@@ -23,12 +23,13 @@
 //  * mass_softmax_kernel: per (sequence, query head), the softmax over pages
 //    of each query token's row, summed into M.
 //  * tier_page_kernel: per (sequence, KV head, page) the page's mass over the
-//    group and the sums of its top-h head masses for each searched h (rank by
-//    counting: mass descending, head ascending).
-//  * tier_coverage_kernel: per (sequence, KV head) the candidates' rank order
-//    (router score descending, page ascending, NaN last; rank by counting)
-//    and every configuration's covered mass.
-//  * tier_choose_kernel: mean over sequences and KV heads, first maximum.
+//    group and the sums of its top-h head masses for each searched h (the
+//    group's masses bitonic-sorted across one wave).
+//  * tier_cover_kernel: per (sequence, KV head, 64-page chunk) each page's
+//    rank among the candidates (router score descending, page ascending, NaN
+//    last; by counting over all keys) and every configuration's covered mass.
+//  * tier_choose_kernel: the sums in a fixed order, mean over sequences and
+//    KV heads, first maximum.
 //  * ambient_mask_kernel: the top-h heads of every Ambient page of a list.
 #include "common.h"
 
@@ -68,7 +69,7 @@ __global__ __launch_bounds__(256) void mass_logits_kernel(MassParams p) {
   f32x4 acc[4];
 #pragma unroll
   for (int rt = 0; rt < 4; ++rt) acc[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll 2
+#pragma unroll 3
   for (int ks = 0; ks < D / 32; ++ks) {
     const float4 x0 = *reinterpret_cast<const float4*>(murow + 32 * ks + 8 * kq);
     const float4 x1 = *reinterpret_cast<const float4*>(murow + 32 * ks + 8 * kq + 4);
@@ -81,13 +82,9 @@ __global__ __launch_bounds__(256) void mass_logits_kernel(MassParams p) {
     }
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt) {
-      bf16x8 bq;
-      if (row_ok[rt]) {
-        bq = *reinterpret_cast<const bf16x8*>(qbase + qoff[rt] + 32 * ks + 8 * kq);
-      } else {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) bq[i] = (__bf16)0.f;
-      }
+      // rows past the group read its first row (their results are never
+      // written): a load under a per-lane condition would be waited for at once
+      const bf16x8 bq = *reinterpret_cast<const bf16x8*>(qbase + qoff[rt] + 32 * ks + 8 * kq);
       acc[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(hi, bq, acc[rt], 0, 0, 0);
       acc[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lo, bq, acc[rt], 0, 0, 0);
     }
@@ -105,9 +102,14 @@ __global__ __launch_bounds__(256) void mass_logits_kernel(MassParams p) {
     const int r = r0 + 16 * rt + col;
     const int t = r / p.G, hl = r % p.G;
     float* dst = p.est + (((size_t)b * p.T + t) * p.Hq + (size_t)g * p.G + hl) * p.stride + p0 + 4 * kq;
+    if (p0 + 4 * kq + 3 < n) {                     // 16-byte aligned: the row stride is a multiple of 4
+      *reinterpret_cast<float4*>(dst) = float4{acc[rt][0] * p.sm_scale + lnn[0], acc[rt][1] * p.sm_scale + lnn[1],
+                                               acc[rt][2] * p.sm_scale + lnn[2], acc[rt][3] * p.sm_scale + lnn[3]};
+    } else {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      if (p0 + 4 * kq + i < n) dst[i] = acc[rt][i] * p.sm_scale + lnn[i];
+      for (int i = 0; i < 4; ++i)
+        if (p0 + 4 * kq + i < n) dst[i] = acc[rt][i] * p.sm_scale + lnn[i];
+    }
   }
 }
 
@@ -137,11 +139,14 @@ __global__ __launch_bounds__(256) void mass_softmax_kernel(MassParams p) {
   for (int t = 0; t < p.T; ++t) {
     const float* e = p.est + (((size_t)b * p.T + t) * p.Hq + h) * p.stride;
     float mx = -INFINITY;
+#pragma unroll 4
     for (int i = threadIdx.x; i < n; i += 256) mx = fmaxf(mx, e[i]);
     mx = block_max_256(mx, red);
     float sm = 0.f;
+#pragma unroll 4
     for (int i = threadIdx.x; i < n; i += 256) sm += __expf(e[i] - mx);
     const float lse = mx + __logf(block_sum_256(sm, red));
+#pragma unroll 4
     for (int i = threadIdx.x; i < n; i += 256) {
       const float v = __expf(e[i] - lse);
       M[i] = t == 0 ? v : M[i] + v;
@@ -159,6 +164,20 @@ hipError_t launch_head_mass(const MassParams& p, hipStream_t s) {
   return hipGetLastError();
 }
 
+// The search grid (alphas, head counts, betas) copied from the kernel
+// arguments into LDS in one round trip: indexed in a loop, each argument
+// would be a scalar load of its own from the argument segment.
+struct TuneGrid {
+  int alpha[kTuneMaxGrid], heads[kTuneMaxGrid], beta[kTuneMaxGrid * kTuneMaxGrid];
+};
+__device__ __forceinline__ void load_grid(const TuneParams& p, TuneGrid& gr) {
+  for (int i = threadIdx.x; i < kTuneMaxGrid * kTuneMaxGrid; i += blockDim.x) gr.beta[i] = p.beta[i];
+  if (threadIdx.x < kTuneMaxGrid) {
+    gr.alpha[threadIdx.x] = p.alpha[threadIdx.x];
+    gr.heads[threadIdx.x] = p.heads[threadIdx.x];
+  }
+}
+
 // ------------------------------------------------------------ page stats
 // Rank of head i's mass among the group's G masses in vals: mass descending,
 // head index ascending.
@@ -172,35 +191,115 @@ __device__ __forceinline__ int head_rank(const float* vals, int G, int i) {
   return r;
 }
 
-// grid (ceil(max_pages/4), B*Hkv), 256 threads: wave w takes one page
+// Bitonic sorts of NS independent sets of 128 values, each held two per lane
+// (element lane in a[q], element lane + 64 in b[q]), into descending order
+// across the wave.  The sets' compare-exchange chains interleave, so the
+// cross-lane exchanges of one hide the latency of the others'.
+template <int NS>
+__device__ __forceinline__ void sort128_desc(float (&a)[NS], float (&b)[NS]) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int size = 2; size <= 128; size <<= 1) {
+#pragma unroll
+    for (int j = size >> 1; j > 0; j >>= 1) {
+      if (j == 64) {                                // pairs (lane, lane + 64)
+#pragma unroll
+        for (int q = 0; q < NS; ++q) {
+          const float hi = fmaxf(a[q], b[q]), lo = fminf(a[q], b[q]);
+          a[q] = hi;
+          b[q] = lo;
+        }
+      } else {
+        const bool lower = (lane & j) == 0;
+        const bool desc_a = (lane & size) == 0, desc_b = ((lane + 64) & size) == 0;
+        float pa[NS], pb[NS];
+#pragma unroll
+        for (int q = 0; q < NS; ++q) {
+          pa[q] = __shfl_xor(a[q], j, 64);
+          pb[q] = __shfl_xor(b[q], j, 64);
+        }
+#pragma unroll
+        for (int q = 0; q < NS; ++q) {
+          a[q] = (lower == desc_a) ? fmaxf(a[q], pa[q]) : fminf(a[q], pa[q]);
+          b[q] = (lower == desc_b) ? fmaxf(b[q], pb[q]) : fminf(b[q], pb[q]);
+        }
+      }
+    }
+  }
+}
+
+// grid (ceil(max_pages/64), B*Hkv), 256 threads: the group's masses of 64
+// consecutive pages are read row by row (coalesced) into LDS, then each wave
+// takes 16 of the pages: a page's G masses are sorted across the wave (masses
+// are >= 0; padding -1 sorts last), so a top-h sum is a prefix.
 __global__ __launch_bounds__(256) void tier_page_kernel(TuneParams p) {
-  __shared__ float vals[4][kTuneMaxGroup];
+  __shared__ float vals[kTuneMaxGroup][65];
+  __shared__ TuneGrid gr;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int b = blockIdx.y / p.Hkv, g = blockIdx.y % p.Hkv;
   const int n = (p.seq_lens[b] + p.P - 1) / p.P;
-  const int pg = blockIdx.x * 4 + wave;
-  const bool ok = pg < n;
-  for (int i = lane; i < p.G; i += 64)
-    vals[wave][i] = ok ? p.mass[((size_t)b * p.Hq + (size_t)g * p.G + i) * p.max_pages + pg] : 0.f;
-  __syncthreads();
-  if (!ok) return;
-  float v[2] = {0.f, 0.f};
-  int rk[2] = {kTuneMaxGroup, kTuneMaxGroup};
+  const int p0 = blockIdx.x * 64;
+  if (p0 >= n) return;                               // whole workgroup
+  load_grid(p, gr);
+  const float* m = p.mass + ((size_t)b * p.Hq + (size_t)g * p.G) * p.max_pages + p0;
+  const int cols = min(64, n - p0);
+  // the loads of 8 rows are issued before their LDS stores
+  const int j = threadIdx.x & 63, h0 = threadIdx.x >> 6;
+  for (int hb = 0; hb < p.G; hb += 32) {
+    float v[8];
 #pragma unroll
-  for (int k = 0; k < 2; ++k) {
-    const int i = lane + 64 * k;
-    if (i < p.G) {
-      v[k] = vals[wave][i];
-      rk[k] = head_rank(vals[wave], p.G, i);
+    for (int u = 0; u < 8; ++u) {
+      const int h = min(hb + h0 + 4 * u, p.G - 1);
+      v[u] = m[(size_t)h * p.max_pages + min(j, cols - 1)];
     }
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      if (hb + h0 + 4 * u < p.G) vals[hb + h0 + 4 * u][j] = v[u];
   }
-  const size_t row = ((size_t)b * p.Hkv + g) * p.max_pages + pg;
-  const float all = wave_sum(v[0] + v[1]);
-  if (lane == 0) p.mall[row] = all;
-  for (int k = 0; k < p.n_h; ++k) {
-    const int h = p.heads[k];
-    const float part = wave_sum((rk[0] < h ? v[0] : 0.f) + (rk[1] < h ? v[1] : 0.f));
-    if (lane == 0) p.tsum[row * p.n_h + k] = part;
+  __syncthreads();
+  // 4 pages at a time per wave (pages past the sequence sort padding and are
+  // not written)
+  for (int j0 = wave * 16; j0 < wave * 16 + 16; j0 += 4) {
+    float a[4], c[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int j = min(j0 + q, 63);
+      a[q] = lane < p.G ? vals[lane][j] : -1.f;
+      c[q] = lane + 64 < p.G ? vals[lane + 64][j] : -1.f;
+    }
+    sort128_desc<4>(a, c);
+    // inclusive prefix sums of the sorted masses (a: ranks 0-63, c: 64-127;
+    // padding counted as 0): a top-h sum is one prefix value
+    float sa[4], sc[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      sa[q] = a[q] > 0.f ? a[q] : 0.f;
+      sc[q] = c[q] > 0.f ? c[q] : 0.f;
+    }
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float ta = __shfl_up(sa[q], off, 64), tc = __shfl_up(sc[q], off, 64);
+        if (lane >= off) {
+          sa[q] += ta;
+          sc[q] += tc;
+        }
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const float tot_a = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sa[q]), 63));
+      const float tot_c = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sc[q]), 63));
+      const size_t row = ((size_t)b * p.Hkv + g) * p.max_pages + p0 + j0 + q;
+      if (lane == 0 && j0 + q < cols) p.mall[row] = tot_a + tot_c;
+      for (int k = 0; k < p.n_h; ++k) {
+        const int h = __builtin_amdgcn_readfirstlane(min(gr.heads[k], p.G));
+        const float v = h <= 64 ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sa[q]), h - 1))
+                                : tot_a + __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sc[q]), h - 65));
+        if (lane == 0 && j0 + q < cols) p.tsum[row * p.n_h + k] = v;
+      }
+    }
   }
 }
 
@@ -219,101 +318,114 @@ __device__ __forceinline__ uint64_t rank_key(float s, int page) {
   return ((uint64_t)hi << 32) | (uint32_t)page;
 }
 
-// grid (B*Hkv), 1024 threads
-__global__ __launch_bounds__(1024) void tier_coverage_kernel(TuneParams p) {
+// grid (ceil(max_pages/64), B*Hkv), 256 threads: page 64*blockIdx.x + j is
+// ranked among its sequence's candidates by four threads (j, part), each
+// counting the smaller keys in a quarter of the key array in LDS; wave 0 then
+// adds the chunk's covered mass to every configuration, and the workgroup's
+// sums go to part[bg][chunk][config].
+__global__ __launch_bounds__(256) void tier_cover_kernel(TuneParams p) {
   __shared__ uint64_t key[kTuneMaxPages];
-  __shared__ float wpart[16][kTuneMaxGrid * kTuneMaxGrid];
+  __shared__ int rank_part[4][64];
+  __shared__ TuneGrid gr;
+  load_grid(p, gr);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int bg = blockIdx.x;
+  const int bg = blockIdx.y;
   const int b = bg / p.Hkv, g = bg % p.Hkv;
   const int n = (p.seq_lens[b] + p.P - 1) / p.P;
   const int sink = min(p.sink, n), win_lo = max(0, n - p.window);
   const float* sc = p.scores + ((size_t)b * p.Hkv + g) * p.scores_stride;
-  for (int i = threadIdx.x; i < n; i += 1024) {
-    const bool forced = i < sink || i >= win_lo;
-    key[i] = forced ? ~0ull : rank_key(sc[i], i);
+  for (int i0 = 0; i0 < n; i0 += 1024) {              // 4 score loads in flight per thread
+    float v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) v[u] = sc[min(i0 + (int)threadIdx.x + 256 * u, n - 1)];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int i = i0 + (int)threadIdx.x + 256 * u;
+      if (i < n) key[i] = (i < sink || i >= win_lo) ? ~0ull : rank_key(v[u], i);
+    }
   }
   __syncthreads();
+  const int i = blockIdx.x * 64 + lane;
+  const uint64_t ki = i < n ? key[i] : ~0ull;
+  {
+    const int q = (n + 3) / 4, lo = wave * q, hi = min(n, lo + q);
+    int r = 0;
+    for (int j = lo; j < hi; ++j) r += key[j] < ki ? 1 : 0;
+    rank_part[wave][lane] = r;
+  }
+  __syncthreads();
+  if (wave != 0) return;
   const int n_forced = n == 0 ? 0 : sink + (n - max(win_lo, sink));
   const int nc = n - n_forced;
-  // this thread's pages: forced flag, rank among the candidates
-  constexpr int kPer = kTuneMaxPages / 1024;
-  int rank[kPer];
-  bool forced[kPer];
-#pragma unroll
-  for (int k = 0; k < kPer; ++k) {
-    const int i = threadIdx.x + 1024 * k;
-    rank[k] = 0;
-    forced[k] = false;
-    if (i < n) {
-      const uint64_t ki = key[i];
-      forced[k] = ki == ~0ull;
-      if (!forced[k]) {
-        int r = 0;
-        for (int j = 0; j < n; ++j) r += key[j] < ki ? 1 : 0;
-        rank[k] = r;
-      }
-    }
-  }
-  const size_t row0 = (size_t)bg * p.max_pages;
+  const bool forced = ki == ~0ull;
+  const int rank = (rank_part[0][lane] + rank_part[1][lane]) + (rank_part[2][lane] + rank_part[3][lane]);
+  float mall = 0.f;
+  const float* ts = p.tsum;
+  const size_t row = (size_t)bg * p.max_pages + (i < n ? i : 0);
+  if (i < n) mall = p.mall[row];
+  ts += row * p.n_h;
   const int n_cfg = p.n_a * p.n_h;
+  const int nchunk = gridDim.x;
   for (int c = 0; c < n_cfg; ++c) {
     const int ia = c / p.n_h, ih = c % p.n_h;
-    const int beta = p.beta[c];
+    const int beta = gr.beta[c];
     float acc = 0.f;
-    if (beta >= 0) {
-      const int a_eff = min(p.alpha[ia], nc);
+    if (beta >= 0 && i < n) {
+      const int a_eff = min(gr.alpha[ia], nc);
       const int b_eff = min(beta, nc - a_eff);
-#pragma unroll
-      for (int k = 0; k < kPer; ++k) {
-        const int i = threadIdx.x + 1024 * k;
-        if (i >= n) continue;
-        if (forced[k] || rank[k] < a_eff) acc += p.mall[row0 + i];
-        else if (rank[k] < a_eff + b_eff) acc += p.tsum[(row0 + i) * p.n_h + ih];
-      }
+      if (forced || rank < a_eff) acc = mall;
+      else if (rank < a_eff + b_eff) acc = ts[ih];
     }
     acc = wave_sum(acc);
-    if (lane == 0) wpart[wave][c] = acc;
-  }
-  __syncthreads();
-  for (int c = threadIdx.x; c < n_cfg; c += 1024) {
-    float s = 0.f;
-    for (int w = 0; w < 16; ++w) s += wpart[w][c];
-    p.part[(size_t)bg * n_cfg + c] = p.beta[c] >= 0 ? s / (float)(p.T * p.G) : __builtin_nanf("");
+    if (lane == 0) p.part[((size_t)bg * nchunk + blockIdx.x) * n_cfg + c] = acc;
   }
 }
 
-// one workgroup of 256 threads
-__global__ __launch_bounds__(256) void tier_choose_kernel(TuneParams p) {
+// one workgroup of 256 threads: the layer's coverage of each configuration
+// (one wave per configuration, its partial sums reduced in a fixed order) and
+// the first maximum
+__global__ __launch_bounds__(256) void tier_choose_kernel(TuneParams p, int nchunk) {
   __shared__ float cov[kTuneMaxGrid * kTuneMaxGrid];
+  __shared__ TuneGrid gr;
+  load_grid(p, gr);
+  __syncthreads();
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int n_cfg = p.n_a * p.n_h;
   const int nbg = p.B * p.Hkv;
-  for (int c = threadIdx.x; c < n_cfg; c += 256) {
+  const int nparts = nbg * nchunk;
+  for (int c = wave; c < n_cfg; c += 4) {
     float s = 0.f;
-    for (int i = 0; i < nbg; ++i) s += p.part[(size_t)i * n_cfg + c];
-    const float v = p.beta[c] >= 0 ? s / (float)nbg : __builtin_nanf("");
-    cov[c] = v;
-    p.coverage[c] = v;
+#pragma unroll 4
+    for (int k = lane; k < nparts; k += 64) s += p.part[(size_t)k * n_cfg + c];
+    s = wave_sum(s) / (float)(p.T * p.G);
+    const float v = gr.beta[c] >= 0 ? s / (float)nbg : __builtin_nanf("");
+    if (lane == 0) {
+      cov[c] = v;
+      p.coverage[c] = v;
+    }
   }
   __syncthreads();
   if (threadIdx.x == 0) {
     int best = -1;
     for (int c = 0; c < n_cfg; ++c) {
-      if (p.beta[c] < 0) continue;
+      if (gr.beta[c] < 0) continue;
       if (best < 0 || cov[c] > cov[best]) best = c;
     }
     p.choice[0] = best < 0 ? -1 : best / p.n_h;
     p.choice[1] = best < 0 ? -1 : best % p.n_h;
-    p.choice[2] = best < 0 ? -1 : p.beta[best];
+    p.choice[2] = best < 0 ? -1 : gr.beta[best];
   }
 }
+
+int autotune_chunks(int max_pages) { return (max_pages + 63) / 64; }
 
 hipError_t launch_autotune(const TuneParams& p, hipStream_t s) {
   if (p.G > kTuneMaxGroup || p.max_pages > kTuneMaxPages || p.n_a > kTuneMaxGrid || p.n_h > kTuneMaxGrid)
     return hipErrorInvalidValue;
-  hipLaunchKernelGGL(tier_page_kernel, dim3((p.max_pages + 3) / 4, p.B * p.Hkv), dim3(256), 0, s, p);
-  hipLaunchKernelGGL(tier_coverage_kernel, dim3(p.B * p.Hkv), dim3(1024), 0, s, p);
-  hipLaunchKernelGGL(tier_choose_kernel, dim3(1), dim3(256), 0, s, p);
+  const int nchunk = autotune_chunks(p.max_pages);
+  hipLaunchKernelGGL(tier_page_kernel, dim3((p.max_pages + 63) / 64, p.B * p.Hkv), dim3(256), 0, s, p);
+  hipLaunchKernelGGL(tier_cover_kernel, dim3(nchunk, p.B * p.Hkv), dim3(256), 0, s, p);
+  hipLaunchKernelGGL(tier_choose_kernel, dim3(1), dim3(256), 0, s, p, nchunk);
   return hipGetLastError();
 }
 

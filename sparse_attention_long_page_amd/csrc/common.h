@@ -245,7 +245,7 @@ struct TuneParams {
   const int32_t* seq_lens;
   float* mall;               // workspace [B][Hkv][max_pages]: a page's mass over the group
   float* tsum;               // workspace [B][Hkv][max_pages][n_h]: its top-h head masses
-  float* part;               // workspace [B*Hkv][n_a*n_h]: per (sequence, KV head) coverage
+  float* part;               // workspace [B*Hkv][chunks][n_a*n_h]: covered mass per 64-page chunk
   float* coverage;           // out [n_a][n_h]
   int32_t* choice;           // out [3]: alpha index, head-count index, beta
   int B, T, Hq, Hkv, G, P, max_pages, scores_stride, sink, window;
@@ -268,6 +268,7 @@ hipError_t launch_page_value_summary(const ValueSummaryParams& p, int batch, int
 hipError_t launch_mean_correct(const MeanCorrParams& p, hipStream_t s);
 hipError_t launch_head_mass(const MassParams& p, hipStream_t s);
 hipError_t launch_autotune(const TuneParams& p, hipStream_t s);
+int autotune_chunks(int max_pages);
 hipError_t launch_ambient_mask(const AmbientMaskParams& p, hipStream_t s);
 hipError_t launch_page_summary(const SummaryParams& p, int batch, int bf16, hipStream_t s);
 hipError_t launch_select(const SelectParams& p, int batch, int max_pages, hipStream_t s);

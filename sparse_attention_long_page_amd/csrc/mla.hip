@@ -24,8 +24,8 @@
 //    deals the ranked heads out in tiles; a tile computes an Ambient page only
 //    if one of its heads attends it, so each Ambient page runs on few tiles
 //    instead of on every tile with a member head somewhere;
-//  * each page's 64 x 576 K tile is copied once into LDS by the LDS-DMA path
-//    (global_load_lds_dwordx4, no registers), double-buffered: the copy of the
+//  * each page's 64 x 576 K tile is copied once into LDS by buffer-to-LDS
+//    copies (16 bytes per lane, no registers), double-buffered: the copy of the
 //    next page runs while the current one is computed; rows are padded to
 //    1168 bytes so the 16-byte K reads and the 2-byte transposed V reads both
 //    spread over the banks;
