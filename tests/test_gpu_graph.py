@@ -190,3 +190,103 @@ def test_select_decode_graph_replays_match_eager(name):
         torch.cuda.synchronize()
         assert torch.isfinite(other)
         _assert_same(results, eager, rep)
+
+
+def test_prefill_mask_and_mean_correction_graph_replays_match_eager():
+    """The block-sparse prefill chain captured in one graph: the mask from
+    pattern discovery, the prefill over its union tables, the per-page value
+    means and the mean correction (which rewrites out and lse in place).
+    Every replay, with the outputs poisoned and eager work between replays,
+    equals the eager chain."""
+    wl = W.SMALL["chunked_prefill_small"].replace(random_fraction=0.15)
+    inp = gpu_inputs(W.make_prefill_inputs(wl, "cpu", seed=45))
+    kv = S.PagedKV(inp["k_pool"], inp["v_pool"], inp["block_table"], inp["seq_lens"])
+    mu = S.sa_page_summary(kv)
+    nu = S.sa_page_value_summary(kv)
+    mask = torch.empty((wl.n_q_heads, wl.n_q_blocks, wl.n_kv_blocks), dtype=torch.uint8, device=DEV)
+    out = torch.empty((wl.q_len, wl.n_q_heads, wl.d), dtype=torch.bfloat16, device=DEV)
+    lse = torch.empty((wl.q_len, wl.n_q_heads), dtype=torch.float32, device=DEV)
+    table = torch.full((wl.n_kv_heads, wl.n_kv_blocks), -1, dtype=torch.int32, device=DEV)
+    counts = torch.zeros((wl.n_kv_heads,), dtype=torch.int32, device=DEV)
+    ws = torch.empty(S.sa_prefill_mean_correction_workspace_size(kv, wl.n_kv_blocks), dtype=torch.uint8, device=DEV)
+
+    def step():
+        S.sa_prefill_block_mask(kv, 0, inp["q"], wl.q_start, mu, wl.block_q, wl.sm_scale, top_k=2, out=mask)
+        S.sa_page_value_summary(kv, out=nu)
+        S.sa_block_sparse_prefill(kv, 0, inp["q"], wl.q_start, mask, wl.block_q, wl.sm_scale, out=out, out_lse=lse,
+                                  block_table_out=table, block_counts_out=counts)
+        S.sa_prefill_mean_correction(kv, 0, inp["q"], wl.q_start, table, counts, mu, nu, wl.sm_scale, out, lse,
+                                     workspace=ws)
+
+    step()
+    torch.cuda.synchronize()
+    eager = [t.clone() for t in (mask, out, lse, counts, nu)]
+    assert int(counts.min()) < wl.n_kv_blocks            # blocks are skipped, so the correction has work
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for rep in range(3):
+        for t in (mask, out, lse, counts):
+            t.fill_(0)
+        nu[nu == nu] = 0.0                             # the pages the chain rewrites
+        other = torch.randn(1 << 20, device=DEV).sum()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.isfinite(other)
+        for a, b in zip((mask, out, lse, counts), eager):
+            assert torch.equal(a, b), f"replay {rep} differs from the eager chain"
+        assert torch.equal(torch.nan_to_num(nu, nan=-1.0), torch.nan_to_num(eager[4], nan=-1.0))
+
+
+def test_autotune_graph_replays_match_eager():
+    """Head mass, tier search and Ambient head mask captured in one graph:
+    every replay equals the eager calls (the mask is cleared by a kernel, not
+    a memset node)."""
+    wl = W.SMALL["mla_tiered_decode_small"]
+    inp = gpu_inputs(W.make_decode_inputs(wl, "cpu", seed=46))
+    kv = make_kv(inp, wl)
+    mu = S.sa_page_summary(kv)
+    G = wl.n_q_heads
+    lists, counts, cc = S.sa_select_pages(kv, n_q_heads=G, mode=S.SA_SEL_PER_KV_HEAD, sink_pages=0, window_pages=0,
+                                          top_k=wl.top_k, critical_k=wl.critical_k, q=inp["q"], page_summary=mu)
+    scores = torch.empty((wl.batch, 1, wl.max_pages), dtype=torch.float32, device=DEV)
+    S.sa_select_pages(kv, n_q_heads=G, mode=S.SA_SEL_PER_KV_HEAD, sink_pages=0, window_pages=0, top_k=wl.top_k,
+                      q=inp["q"], page_summary=mu, scores_out=scores)
+    mass = torch.empty((wl.batch, G, wl.max_pages), dtype=torch.float32, device=DEV)
+    ws_m = torch.empty(S.sa_head_page_mass_workspace_size(kv, wl.q_tokens, G), dtype=torch.uint8, device=DEV)
+    alphas, heads = [0, 1, 3], [4, 8, 32]
+    ws_t = torch.empty(S.sa_autotune_tiers_workspace_size(kv, len(heads)), dtype=torch.uint8, device=DEV)
+    cov = torch.empty((len(alphas), len(heads)), dtype=torch.float32, device=DEV)
+    choice = torch.empty((3,), dtype=torch.int32, device=DEV)
+    amask = torch.empty((wl.batch, wl.max_pages, (G + 31) // 32), dtype=torch.int32, device=DEV)
+    budget = wl.critical_k * G + (wl.top_k - wl.critical_k) * wl.ambient_heads
+
+    def step():
+        S.sa_head_page_mass(kv, inp["q"], mu, wl.sm_scale, out=mass, workspace=ws_m)
+        S.sa_autotune_tiers(kv, mass, scores, q_tokens=wl.q_tokens, sink_pages=0, window_pages=0, budget=budget,
+                            alphas=alphas, ambient_heads=heads, workspace=ws_t, out=(cov, choice))
+        S.sa_ambient_head_mask(kv, mass, lists, counts, cc, wl.ambient_heads, out=amask)
+
+    step()
+    torch.cuda.synchronize()
+    eager = [t.clone() for t in (mass, cov, choice, amask)]
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for rep in range(3):
+        for t in (mass, cov, choice, amask):
+            t.fill_(-5)
+        other = torch.randn(1 << 20, device=DEV).sum()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.isfinite(other)
+        m_now, m_ref = mass.clone(), eager[0].clone()
+        for b in range(wl.batch):                    # entries past a sequence's pages are not written
+            n = (int(inp["seq_lens"][b]) + wl.page_size - 1) // wl.page_size
+            m_now[b, :, n:] = 0
+            m_ref[b, :, n:] = 0
+        assert torch.equal(m_now, m_ref), f"replay {rep}: mass differs"
+        for a, b in zip((cov, choice, amask), eager[1:]):
+            assert torch.equal(a, b), f"replay {rep} differs from the eager calls"
