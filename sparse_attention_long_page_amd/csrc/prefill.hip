@@ -10,17 +10,20 @@
 // then an index-ordered workgroup prefix sum writes the ascending table.
 //
 // Attention kernel (bf16, d 128, pages of 64):
-//  * workgroup = (KV head g, tile of 64 query positions); one wave per query
-//    head of the group, so every K/V tile staged in LDS serves all G heads
-//    (GQA packing: 64*G rows per tile);
+//  * workgroup = (KV head g, tile of 64 query positions); two waves per query
+//    head of the group (32 query rows each), so every K/V tile staged in LDS
+//    serves all G heads (GQA packing: 64*G rows per tile);
 //  * workgroup ids are remapped so the tiles of one KV head run on one XCD
 //    and share its L2 while they sweep the same KV blocks;
 //  * per KV block: K (token-major) and V^T (page-transposed) are copied from
-//    the pool into padded LDS rows (conflict-free 16-byte reads), the next
-//    block's copy is in flight in registers while the current one computes;
+//    the pool into padded LDS rows (conflict-free 16-byte reads) by
+//    buffer-to-LDS copies; the copy of the next block runs while the current
+//    one is computed (two stages);
 //  * S^T = K Q^T and O^T += V^T P^T on v_mfma_f32_16x16x32_bf16 (Q^T resident
-//    in registers, 64 rows per wave), with the token permutation that makes
-//    the S^T fragments the PV operand directly;
+//    in registers), with the token permutation that makes the S^T fragments
+//    the PV operand directly; the row sums of P are one more MFMA per PV
+//    step with an all-ones operand (the sums of the bf16 weights the PV
+//    product uses);
 //  * causal and sequence-end masks only on blocks that cross a row's
 //    position; the ascending table stops the sweep past the tile's last row;
 //  * online softmax in base 2 with a lazily moved reference maximum: the
@@ -154,11 +157,11 @@ struct Stage {
 // 32-63 of the tile).  A group larger than HW is split over G/HW workgroups.
 template <int HW>
 __global__ __launch_bounds__(128 * HW) void prefill_kernel(PrefillParams p) {
-  // three pipeline stages as distinct LDS objects: the copy of block t+2 runs
-  // while block t is computed and block t+1 has landed
+  // two pipeline stages as distinct LDS objects (so the wait-count pass can
+  // tell a copy into one from reads of the other): the copy of block t+1
+  // runs while block t is computed
   __shared__ __attribute__((aligned(16))) uint16_t st0[kStageElems];
   __shared__ __attribute__((aligned(16))) uint16_t st1[kStageElems];
-  __shared__ __attribute__((aligned(16))) uint16_t st2[kStageElems];
   __shared__ int kb_s[kPrefillMaxBlocks], ph_s[kPrefillMaxBlocks];
   constexpr int NW = 2 * HW;                                  // waves per workgroup
   constexpr int NI = (kStageInstr + NW - 1) / NW;             // copy loads per wave per block
@@ -203,9 +206,15 @@ __global__ __launch_bounds__(128 * HW) void prefill_kernel(PrefillParams p) {
   for (int dt = 0; dt < 8; ++dt)
 #pragma unroll
     for (int rt = 0; rt < kRT; ++rt) oacc[dt][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_ref[kRT], l_run[kRT];
+  // row sums of P on MFMA: an all-ones A operand puts the column sums of
+  // P^T (the sum over the row's tokens) in every element of lacc[rt]
+  float m_ref[kRT];
+  f32x4 lacc[kRT];
 #pragma unroll
-  for (int rt = 0; rt < kRT; ++rt) { m_ref[rt] = -INFINITY; l_run[rt] = 0.f; }
+  for (int rt = 0; rt < kRT; ++rt) { m_ref[rt] = -INFINITY; lacc[rt] = f32x4{0.f, 0.f, 0.f, 0.f}; }
+  bf16x8 ones;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) ones[e] = (__bf16)1.0f;
 
   // table entries at or before the tile's last position (the table ascends)
   int nblk = 0;
@@ -222,153 +231,166 @@ __global__ __launch_bounds__(128 * HW) void prefill_kernel(PrefillParams p) {
   // chunks [64 i, 64 i + 64); loads 0-16 hold the K tile, 17-34 the V^T tile.
   // K slots copy straight; V^T slot c of row d receives token-chunk
   // c ^ vsw(d) (an involution); pad slots re-read chunk 0 of their row.  Every
-  // wave issues exactly NI loads (the last real load is repeated to fill), so
-  // the wait below can count them.  Each lane's element offset within the
-  // (page, head) tile is fixed per load and computed once; per block only the
-  // tile's base address (scalar) changes.
+  // wave issues NI loads (the last real load is repeated to fill).  Each
+  // lane's byte offset within the (page, head) tile is fixed per load and
+  // computed once; per block only the tile's base address (scalar) changes.
   static_assert(kKChunks % 64 == 0, "loads hold K or V^T chunks only");
   constexpr int kKInstr = kKChunks / 64;
-  int lane_off[NI];
+  uint32_t lane_off[NI];     // bytes
 #pragma unroll
   for (int j = 0; j < NI; ++j) {
     const int i = min(wave + NW * j, kStageInstr - 1);
     const int c = 64 * i + lane;
     if (c < kKChunks) {
       const int r = c / (kKRow / 8), slot = c % (kKRow / 8);
-      lane_off[j] = r * kPD + 8 * (slot < 16 ? slot : 0);
+      lane_off[j] = 2 * (r * kPD + 8 * (slot < 16 ? slot : 0));
     } else {
       const int cv = c - kKChunks;
       const int r = cv / (kVRow / 8), slot = cv % (kVRow / 8);
-      lane_off[j] = r * kPP + 8 * (slot < 8 ? (slot ^ vsw(r)) : 0);
+      lane_off[j] = 2 * (r * kPP + 8 * (slot < 8 ? (slot ^ vsw(r)) : 0));
     }
   }
-  auto stage_copy = [&](uint16_t* st, int t) {
+  // buffer-to-LDS copies: the tile bases live in scalar resources, the lane
+  // offsets stay fixed, so a block's copy costs no vector instructions
+  auto stage_copy = [&](uint16_t* st, int t) __attribute__((always_inline)) {
     const int phys = wave_uniform(ph_s[t]);
     const size_t tile = ((size_t)phys * p.Hkv + g) * kPP * kPD;     // same size for K and V^T tiles
+    const auto rk = buffer_rsrc(kpool + tile, kPP * kPD * 2);
+    const auto rv = buffer_rsrc(vpool + tile, kPP * kPD * 2);
 #pragma unroll
     for (int j = 0; j < NI; ++j) {
       const int i = min(wave + NW * j, kStageInstr - 1);
-      const uint16_t* base = (i < kKInstr ? kpool : vpool) + tile;
-      const uint16_t* src = base + lane_off[j];
-      __builtin_amdgcn_global_load_lds(src, st + i * 512, 16, 0, 0);
+      copy16_to_lds(i < kKInstr ? rk : rv, st + i * 512, lane_off[j]);
     }
   };
 
-  // one block: wait for its copy (the next block's NI loads may stay in
-  // flight), barrier, start the copy two blocks ahead, compute
-  auto block = [&](auto sidx, int t) {
-    uint16_t* cur = sidx.value == 0 ? st0 : (sidx.value == 1 ? st1 : st2);
-    uint16_t* ahead = sidx.value == 0 ? st2 : (sidx.value == 1 ? st0 : st1);
-    // (a plain s_barrier: a __syncthreads() fence would also drain the copy
-    // of the next block; every LDS read of the stage about to be refilled was
-    // consumed before its wave reached this point)
-    if (t + 1 < nblk) asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" :: "n"(NI) : "memory");
-    else asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
-    if (t + 2 < nblk) stage_copy(ahead, t + 2);
-    const int kb = kb_s[t];
-    const uint16_t* K = cur;
-    const uint16_t* V = cur + kKTile;
-    const int tok0 = kb * kPP;
-    // blocks entirely past this wave's rows contribute nothing (the tile's
-    // other wave may still need them)
-    if (tok0 <= p.q_start + min(qw + 31, p.q_len - 1)) {
-      // S^T = K Q^T
-      f32x4 sacc[4][kRT];
+  // A block's work in two parts.  qk: S^T = K Q^T into sacc.  sm_pv: masks,
+  // softmax and O^T += V^T P^T from the sacc of the same block.  A block
+  // entirely past this wave's rows contributes nothing (the tile's other wave
+  // may still need it).
+  f32x4 sacc[4][kRT];
+  auto active = [&](int t) __attribute__((always_inline)) { return kb_s[t] * kPP <= p.q_start + min(qw + 31, p.q_len - 1); };
+  auto qk = [&](const uint16_t* K, int t) __attribute__((always_inline)) {
+    if (!active(t)) return;
 #pragma unroll
-      for (int j4 = 0; j4 < 4; ++j4)
+    for (int j4 = 0; j4 < 4; ++j4)
 #pragma unroll
-        for (int rt = 0; rt < kRT; ++rt) sacc[j4][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
-      // k-steps outer: the eight accumulators of a k-step are independent,
-      // so an MFMA never waits on the one just issued
+      for (int rt = 0; rt < kRT; ++rt) sacc[j4][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // k-steps outer: the eight accumulators of a k-step are independent,
+    // so an MFMA never waits on the one just issued
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
+    for (int kk = 0; kk < 4; ++kk) {
 #pragma unroll
-        for (int j4 = 0; j4 < 4; ++j4) {
-          const bf16x8 a = *reinterpret_cast<const bf16x8*>(K + ptok(j4, col) * kKRow + 8 * (kk + 4 * kg));
+      for (int j4 = 0; j4 < 4; ++j4) {
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(K + ptok(j4, col) * kKRow + 8 * (kk + 4 * kg));
 #pragma unroll
-          for (int rt = 0; rt < kRT; ++rt)
-            sacc[j4][rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qreg[rt][kk], sacc[j4][rt], 0, 0, 0);
-        }
+        for (int rt = 0; rt < kRT; ++rt)
+          sacc[j4][rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qreg[rt][kk], sacc[j4][rt], 0, 0, 0);
       }
-
-      // softmax (lane: row 16*rt + col, tokens ptok(j4, 4*kg + i)).
-      // The row maximum is taken on the raw logits (the scale is positive),
-      // then p = 2^(s * scale_log2 - m) is one FMA and one v_exp_f32
-      // (results below 2^-126 flush to zero: their weight relative to the
-      // row maximum is below 2^-126).
-      // causal and sequence-end masks, only on blocks that cross a row (the
-      // empty volatile asm keeps this a branch: if-converted, the masking
-      // would run as per-element compares and selects on every block)
-      const bool full = (tok0 + kPP - 1 <= wpos_lo) && (tok0 + kPP <= seq_len);
-      if (!full) {
-        asm volatile("" ::: "memory");
-#pragma unroll
-        for (int rt = 0; rt < kRT; ++rt) {
-          const int row_pos = wpos_lo + 16 * rt + col;
-#pragma unroll
-          for (int j4 = 0; j4 < 4; ++j4)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const int j = tok0 + ptok(j4, 4 * kg + i);
-              if (j > row_pos || j >= seq_len) sacc[j4][rt][i] = -INFINITY;
-            }
-        }
-      }
-      bf16x8 pb[kRT][2];
-      float alpha[kRT];
-      bool need_rescale = false;
+    }
+  };
+  auto sm_pv = [&](const uint16_t* V, int t) __attribute__((always_inline)) {
+    if (!active(t)) return;
+    const int tok0 = kb_s[t] * kPP;
+    // softmax (lane: row 16*rt + col, tokens ptok(j4, 4*kg + i)).
+    // The row maximum is taken on the raw logits (the scale is positive),
+    // then p = 2^(s * scale_log2 - m) is one FMA and one v_exp_f32
+    // (results below 2^-126 flush to zero: their weight relative to the
+    // row maximum is below 2^-126).
+    // causal and sequence-end masks, only on blocks that cross a row (the
+    // empty volatile asm keeps this a branch: if-converted, the masking
+    // would run as per-element compares and selects on every block)
+    const bool full = (tok0 + kPP - 1 <= wpos_lo) && (tok0 + kPP <= seq_len);
+    if (!full) {
+      asm volatile("" ::: "memory");
 #pragma unroll
       for (int rt = 0; rt < kRT; ++rt) {
-        float mraw = -INFINITY;
-#pragma unroll
-        for (int j4 = 0; j4 < 4; ++j4)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) mraw = fmaxf(mraw, sacc[j4][rt][i]);
-        mraw = max_over_row_groups(mraw);
-        const float mloc = mraw == -INFINITY ? -INFINITY : mraw * p.scale_log2;
-        // move the reference only when the row maximum outgrows it
-        float mref = m_ref[rt];
-        alpha[rt] = 1.f;
-        if (mloc > mref + kRescaleThreshold || (mref == -INFINITY && mloc != -INFINITY)) {
-          alpha[rt] = mref == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mref - mloc);
-          mref = mloc;
-          need_rescale = true;
-        }
-        m_ref[rt] = mref;
-        const float msub = mref == -INFINITY ? 0.f : mref;
-        float psum = 0.f;
+        const int row_pos = wpos_lo + 16 * rt + col;
 #pragma unroll
         for (int j4 = 0; j4 < 4; ++j4)
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[j4][rt][i], p.scale_log2, -msub));
-            psum += pv;
-            pb[rt][j4 >> 1][4 * (j4 & 1) + i] = (__bf16)pv;
-          }
-        l_run[rt] = l_run[rt] * alpha[rt] + psum;
-      }
-      if (__any(need_rescale)) {
-#pragma unroll
-        for (int dt = 0; dt < 8; ++dt)
-#pragma unroll
-          for (int rt = 0; rt < kRT; ++rt) {
-            oacc[dt][rt][0] *= alpha[rt]; oacc[dt][rt][1] *= alpha[rt];
-            oacc[dt][rt][2] *= alpha[rt]; oacc[dt][rt][3] *= alpha[rt];
+            const int j = tok0 + ptok(j4, 4 * kg + i);
+            if (j > row_pos || j >= seq_len) sacc[j4][rt][i] = -INFINITY;
           }
       }
-
-      // O^T += V^T P^T
+    }
+    bf16x8 pb[kRT][2];
+    float alpha[kRT];
+    bool need_rescale = false;
 #pragma unroll
-      for (int kp = 0; kp < 2; ++kp)
+    for (int rt = 0; rt < kRT; ++rt) {
+      float mraw = -INFINITY;
 #pragma unroll
-        for (int dt = 0; dt < 8; ++dt) {
-          const bf16x8 a = *reinterpret_cast<const bf16x8*>(V + (16 * dt + col) * kVRow + 8 * (pchunk(kp, kg) ^ vsw(col)));
+      for (int j4 = 0; j4 < 4; ++j4)
 #pragma unroll
-          for (int rt = 0; rt < kRT; ++rt)
-            oacc[dt][rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb[rt][kp], oacc[dt][rt], 0, 0, 0);
+        for (int i = 0; i < 4; ++i) mraw = fmaxf(mraw, sacc[j4][rt][i]);
+      mraw = max_over_row_groups(mraw);
+      const float mloc = mraw * p.scale_log2;      // -inf stays -inf (the scale is positive)
+      // move the reference only when the row maximum outgrows it (the
+      // first finite maximum always does: -inf + threshold = -inf); the
+      // factor for a reference of -inf is 2^-inf = 0
+      float mref = m_ref[rt];
+      alpha[rt] = 1.f;
+      if (mloc > mref + kRescaleThreshold) {
+        alpha[rt] = __builtin_amdgcn_exp2f(mref - mloc);
+        mref = mloc;
+        need_rescale = true;
+      }
+      m_ref[rt] = mref;
+      const float msub = mref == -INFINITY ? 0.f : mref;
+#pragma unroll
+      for (int j4 = 0; j4 < 4; ++j4)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[j4][rt][i], p.scale_log2, -msub));
+          pb[rt][j4 >> 1][4 * (j4 & 1) + i] = (__bf16)pv;
         }
     }
+    if (__any(need_rescale)) {
+#pragma unroll
+      for (int rt = 0; rt < kRT; ++rt) {
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt) {
+          oacc[dt][rt][0] *= alpha[rt]; oacc[dt][rt][1] *= alpha[rt];
+          oacc[dt][rt][2] *= alpha[rt]; oacc[dt][rt][3] *= alpha[rt];
+        }
+        lacc[rt][0] *= alpha[rt]; lacc[rt][1] *= alpha[rt];
+        lacc[rt][2] *= alpha[rt]; lacc[rt][3] *= alpha[rt];
+      }
+    }
 
+    // O^T += V^T P^T
+#pragma unroll
+    for (int kp = 0; kp < 2; ++kp) {
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) {
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(V + (16 * dt + col) * kVRow + 8 * (pchunk(kp, kg) ^ vsw(col)));
+#pragma unroll
+        for (int rt = 0; rt < kRT; ++rt)
+          oacc[dt][rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb[rt][kp], oacc[dt][rt], 0, 0, 0);
+      }
+#pragma unroll
+      for (int rt = 0; rt < kRT; ++rt)
+        lacc[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pb[rt][kp], lacc[rt], 0, 0, 0);
+    }
+  };
+
+  // One block: wait for this wave's part of its copy, barrier (then every
+  // part has landed and every wave has finished the previous block), start
+  // the copy of the next block into the other stage, compute.  The wait is
+  // the s_waitcnt builtin (vmcnt 0, other counters free), which the
+  // compiler's wait-count pass sees, so it adds no wait of its own on the
+  // copy just issued; the barrier is a plain s_barrier with a memory clobber
+  // (a __syncthreads() fence would also wait for that copy).
+  auto block = [&](auto sidx, int t) __attribute__((always_inline)) {
+    uint16_t* cur = sidx.value == 0 ? st0 : st1;
+    uint16_t* ahead = sidx.value == 0 ? st1 : st0;
+    __builtin_amdgcn_s_waitcnt(0x0f70);
+    asm volatile("s_barrier" ::: "memory");
+    if (t + 1 < nblk) stage_copy(ahead, t + 1);
+    qk(cur, t);
+    sm_pv(cur + kKTile, t);
   };
 
   // the tile's table entries and their physical pages, read once into LDS so
@@ -381,19 +403,16 @@ __global__ __launch_bounds__(128 * HW) void prefill_kernel(PrefillParams p) {
   __syncthreads();
 
   if (nblk > 0) stage_copy(st0, 0);
-  if (nblk > 1) stage_copy(st1, 1);
-  for (int t = 0; t < nblk; t += 3) {
+  for (int t = 0; t < nblk; t += 2) {
     block(Stage<0>{}, t);
     if (t + 1 < nblk) block(Stage<1>{}, t + 1);
-    if (t + 2 < nblk) block(Stage<2>{}, t + 2);
   }
 
   // epilogue: O = O^T / l per row
   uint16_t* out = reinterpret_cast<uint16_t*>(p.out);
 #pragma unroll
   for (int rt = 0; rt < kRT; ++rt) {
-    float l = l_run[rt];
-    l = sum_over_row_groups(l);
+    const float l = lacc[rt][0];
     const int i = qw + 16 * rt + col;
     if (i >= p.q_len) continue;
     const bool empty = m_ref[rt] == -INFINITY;
