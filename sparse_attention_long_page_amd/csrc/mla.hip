@@ -32,7 +32,11 @@
 //  * S^T = K Q^T on v_mfma_f32_16x16x32_bf16 with Q^T resident in registers
 //    (576 dims x 32 rows); the S^T fragments are the P^T operand of the PV
 //    product directly; V^T operands (8 tokens of one dim) come from the
-//    token-major tile with transposing LDS reads;
+//    token-major tile with transposing LDS reads; when both row tiles of a
+//    wave attend a page, each K and V operand read feeds both tiles' MFMAs;
+//  * the first page's copy is issued as soon as the page metadata is in LDS,
+//    so it lands while the heads are ranked and the query rows loaded (the
+//    ranking synchronises on LDS only);
 //  * rows of an active tile whose head is not in an Ambient page's head set
 //    see that page as masked (-inf);
 //  * softmax in base 2 against a per-row reference maximum fixed at the first
@@ -185,6 +189,9 @@ __global__ __launch_bounds__(256, 1) void mla_decode_kernel(DecodeParams p) {
     __syncthreads();
   };
   load_meta(0);
+  // the first page's copy goes out now, so that it lands while the heads are
+  // ranked and the query rows are loaded
+  if (n_pg > 0 && m_nv[0] > 0) stage(sk0, m_phys[0], 0, kMInstr);
 
   // Rank the heads: key bit j = the head attends Ambient page j of the split
   // (first 32 held in the first window); ranked by (key, head index), so the
@@ -197,28 +204,43 @@ __global__ __launch_bounds__(256, 1) void mla_decode_kernel(DecodeParams p) {
       uint32_t key = 0xffffffffu;
       if (h < p.Hq) {
         key = 0;
-        for (int j = 0; j < na; ++j) key |= ((m_word[n_crit + j][h >> 5] >> (h & 31)) & 1u) << j;
+        // all 32 words are read unconditionally (clamped index) and the bits
+        // past na dropped afterwards, so the reads are in flight together
+#pragma unroll
+        for (int j = 0; j < 32; ++j) {
+          const uint32_t wv = m_word[min(n_crit + j, kMetaWin - 1)][h >> 5];
+          key |= (j < na ? (wv >> (h & 31)) & 1u : 0u) << j;
+        }
       }
       h_key[h] = key;
     }
-    __syncthreads();
+    // LDS-only barriers here: a __syncthreads() would also wait for the
+    // first page's copy, which is meant to land while this runs
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
     const uint4* keys4 = reinterpret_cast<const uint4*>(h_key);
     const int n4 = (p.Hq + 3) >> 2;
     for (int h = threadIdx.x; h < p.Hq; h += 256) {
       const uint32_t kh = h_key[h];
       int r = 0;
-#pragma unroll 8
-      for (int i = 0; i < n4; ++i) {
-        const uint4 v = keys4[i];
-        const int hb = 4 * i;
-        r += (v.x < kh || (v.x == kh && hb < h)) ? 1 : 0;
-        r += (v.y < kh || (v.y == kh && hb + 1 < h)) ? 1 : 0;
-        r += (v.z < kh || (v.z == kh && hb + 2 < h)) ? 1 : 0;
-        r += (v.w < kh || (v.w == kh && hb + 3 < h)) ? 1 : 0;
+      // 16 key quads per round, read unconditionally from clamped indices
+      // (slots past the last head hold the largest key and never count)
+      for (int i0 = 0; i0 < n4; i0 += 16) {
+        uint4 v[16];
+#pragma unroll
+        for (int u = 0; u < 16; ++u) v[u] = keys4[min(i0 + u, n4 - 1)];
+#pragma unroll
+        for (int u = 0; u < 16; ++u) {
+          const int hb = 4 * (i0 + u);
+          int c = (v[u].x < kh || (v[u].x == kh && hb < h)) ? 1 : 0;
+          c += (v[u].y < kh || (v[u].y == kh && hb + 1 < h)) ? 1 : 0;
+          c += (v[u].z < kh || (v[u].z == kh && hb + 2 < h)) ? 1 : 0;
+          c += (v[u].w < kh || (v[u].w == kh && hb + 3 < h)) ? 1 : 0;
+          r += i0 + u < n4 ? c : 0;
+        }
       }
       h_rank[r] = (uint16_t)h;
     }
-    __syncthreads();
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
   }
 
   // This lane's query row in each of the wave's two row tiles.  Ranked tile
@@ -287,13 +309,12 @@ __global__ __launch_bounds__(256, 1) void mla_decode_kernel(DecodeParams p) {
 #pragma unroll
       for (int rt = 0; rt < 2; ++rt) l_run[rt] = 0.f;
     }
-    const bool do_pv = attempt != 1;
     if (attempt > 0 && w0 != 0) {
       __syncthreads();
       w0 = 0;
       load_meta(0);
     }
-    if (n_pg > 0 && m_nv[0] > 0) stage(sk0, m_phys[0], 0, kMInstr);
+    if (attempt > 0 && n_pg > 0 && m_nv[0] > 0) stage(sk0, m_phys[0], 0, kMInstr);
 
     // one page: compute from `cur` while the next page is copied into `nxt`
     auto page = [&](auto parity, int k) {
@@ -325,21 +346,27 @@ __global__ __launch_bounds__(256, 1) void mla_decode_kernel(DecodeParams p) {
       // this page's two halves (issued at once, the copy stalls the wave on
       // the memory pipeline for thousands of cycles)
       const bool stage_next = k + 1 < n_pg && m_nv[k + 1 - w0] > 0;
-      auto copy_rest = [&]() {
-        if (stage_next) stage(nxt, m_phys[k + 1 - w0], kMHalfInstr, kMInstr);
+      auto copy_part = [&](int half) {
+        if (stage_next) stage(nxt, m_phys[k + 1 - w0], half ? kMHalfInstr : 0, half ? kMInstr : kMHalfInstr);
       };
-      if (stage_next) stage(nxt, m_phys[k + 1 - w0], 0, kMHalfInstr);
+      copy_part(0);
       // tiles of this wave with a row that attends the page (wave-uniform)
       const int tmask = nv > 0 ? ((__any(act[0]) ? 1 : 0) | (__any(act[1]) ? 2 : 0)) : 0;
 
       const uint16_t* K = cur;
       constexpr int kAhead = 5;            // operand reads in flight ahead of use
-      // One row tile over half a page: S^T = K Q^T over tokens 32*half .. +32
-      // (MFMA tiles j4 = 2*half, 2*half + 1), softmax, O^T += V^T P^T.  A tile
-      // none of whose rows attends the page is skipped entirely.
-      auto tile_half = [&](auto rtc, int half) {
-        constexpr int rt = decltype(rtc)::value;
-        f32x4 sacc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+      // The row tiles in MASK (bit rt) over half a page: S^T = K Q^T over
+      // tokens 32*half .. +32 (MFMA tiles j4 = 2*half, 2*half + 1), softmax,
+      // O^T += V^T P^T.  With both tiles, each K and V operand read from LDS
+      // feeds the MFMAs of both.  A tile none of whose rows attends the page
+      // is left out.
+      auto tile_pass = [&](auto maskc, int half) {
+        constexpr int MASK = decltype(maskc)::value;
+        constexpr bool on[2] = {(MASK & 1) != 0, (MASK & 2) != 0};
+        f32x4 sacc[2][2];
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt)
+          sacc[rt][0] = sacc[rt][1] = f32x4{0.f, 0.f, 0.f, 0.f};
         constexpr int nsq = 2 * kMKSteps;
         // A row m of tile j4 is token tok_of(j4, m): the 8 lanes of one LDS
         // pass read 8 rows with distinct (row mod 8), i.e. distinct banks.
@@ -353,45 +380,54 @@ __global__ __launch_bounds__(256, 1) void mla_decode_kernel(DecodeParams p) {
 #pragma unroll
         for (int step = 0; step < nsq; ++step) {
           if (step + kAhead < nsq) ka[(step + kAhead) % (kAhead + 1)] = kload(step + kAhead);
-          sacc[step & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[step % (kAhead + 1)], qreg[rt][step >> 1],
-                                                                   sacc[step & 1], 0, 0, 0);
+#pragma unroll
+          for (int rt = 0; rt < 2; ++rt)
+            if (on[rt])
+              sacc[rt][step & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[step % (kAhead + 1)],
+                                                                          qreg[rt][step >> 1], sacc[rt][step & 1],
+                                                                          0, 0, 0);
           __builtin_amdgcn_sched_barrier(0);
         }
 
         // softmax: lane holds S^T[token tok_of(2*half + j, 4*kg + i)][row col].
         // Row maximum on the raw logits (the scale is positive); then
         // p = 2^(s * scale_log2 - m) is one FMA and one v_exp_f32.
-        float mraw = -INFINITY;
+        bf16x8 pb[2];
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
+        for (int rt = 0; rt < 2; ++rt) {
+          if (!on[rt]) continue;
+          float mraw = -INFINITY;
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int tok = tok_of(2 * half + j, 4 * kg + i);
-            if (!(act[rt] && tok < nv)) sacc[j][i] = -INFINITY;
-            mraw = fmaxf(mraw, sacc[j][i]);
+          for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const int tok = tok_of(2 * half + j, 4 * kg + i);
+              if (!(act[rt] && tok < nv)) sacc[rt][j][i] = -INFINITY;
+              mraw = fmaxf(mraw, sacc[rt][j][i]);
+            }
+          mraw = max_over_row_groups(mraw);
+          const float mloc = mraw * p.scale_log2;     // -inf stays -inf (the scale is positive)
+          if (attempt == 1) {
+            m_ref[rt] = fmaxf(m_ref[rt], mloc);
+            continue;
           }
-        mraw = max_over_row_groups(mraw);
-        const float mloc = mraw == -INFINITY ? -INFINITY : mraw * p.scale_log2;
-        if (attempt == 1) {
-          m_ref[rt] = fmaxf(m_ref[rt], mloc);
-          return;
-        }
-        if (attempt == 0) {
-          if (m_ref[rt] == -INFINITY) m_ref[rt] = mloc;
-          else if (mloc > m_ref[rt] + kMMargin) overflow = true;
-        }
-        const float msub = m_ref[rt] == -INFINITY ? 0.f : m_ref[rt];
-        float psum = 0.f;
-        bf16x8 pb;
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[j][i], p.scale_log2, -msub));
-            psum += pv;
-            pb[4 * j + i] = (__bf16)pv;
+          if (attempt == 0) {
+            if (m_ref[rt] == -INFINITY) m_ref[rt] = mloc;
+            else if (mloc > m_ref[rt] + kMMargin) overflow = true;
           }
-        l_run[rt] += psum;
+          const float msub = m_ref[rt] == -INFINITY ? 0.f : m_ref[rt];
+          float psum = 0.f;
+#pragma unroll
+          for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[rt][j][i], p.scale_log2, -msub));
+              psum += pv;
+              pb[rt][4 * j + i] = (__bf16)pv;
+            }
+          l_run[rt] += psum;
+        }
+        if (attempt == 1) return;
 
         // O^T += V^T P^T over the same 32 tokens.  k-slot 8*kg + 4*j + i of
         // this product is token tok_of(2*half + j, 4*kg + i), the S^T fragment
@@ -415,18 +451,26 @@ __global__ __launch_bounds__(256, 1) void mla_decode_kernel(DecodeParams p) {
 #pragma unroll
         for (int dt = 0; dt < kMDTiles; ++dt) {
           if (dt + kAhead < kMDTiles) va[(dt + kAhead) % (kAhead + 1)] = vload(dt + kAhead);
-          oacc[dt][rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[dt % (kAhead + 1)], pb, oacc[dt][rt], 0, 0, 0);
+#pragma unroll
+          for (int rt = 0; rt < 2; ++rt)
+            if (on[rt])
+              oacc[dt][rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[dt % (kAhead + 1)], pb[rt], oacc[dt][rt],
+                                                                     0, 0, 0);
           __builtin_amdgcn_sched_barrier(0);
         }
       };
-      const bool on0 = (tmask & 1) != 0, on1 = (tmask & 2) != 0;   // wave-uniform
       // a wave with no active tile skips the work but still passes the copy
-      // point between the halves
-      if (on0) tile_half(std::integral_constant<int, 0>{}, 0);
-      if (on1) tile_half(std::integral_constant<int, 1>{}, 0);
-      copy_rest();
-      if (on0) tile_half(std::integral_constant<int, 0>{}, 1);
-      if (on1) tile_half(std::integral_constant<int, 1>{}, 1);
+      // point between the halves (tmask is wave-uniform)
+      auto halfpage = [&](int half) {
+        // (independent ifs: as an if-else chain the compiler spilled most of
+        // the accumulators)
+        if (tmask == 3) tile_pass(std::integral_constant<int, 3>{}, half);
+        if (tmask == 1) tile_pass(std::integral_constant<int, 1>{}, half);
+        if (tmask == 2) tile_pass(std::integral_constant<int, 2>{}, half);
+      };
+      halfpage(0);
+      copy_part(1);
+      halfpage(1);
     };
     for (int k = 0; k < n_pg; k += 2) {
       page(Parity<0>{}, k);
