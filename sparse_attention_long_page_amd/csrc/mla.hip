@@ -12,9 +12,13 @@
 // first 512 dims of the same row; pages of 64 tokens; rows = (head, token).
 //
 // Design (bf16 in, fp32 accumulate):
-//  * workgroup = (sequence, row group, split of the page list), 4 waves of two
-//    16-row MFMA column tiles each; a tile holds 16/T heads x T query tokens,
-//    so the MTP tokens of a head share a tile and the head's Ambient bit;
+//  * workgroup = (sequence, row group, split of the page list), 8 row tiles of
+//    16 rows (MFMA columns): 8 waves of one tile each, so that two waves share
+//    a SIMD (256 registers each) and one runs while the other waits on its
+//    copy instructions or LDS reads (4 waves of two tiles with 512 registers,
+//    the RT = 2 form of the kernel, measured 2 us slower); a tile holds 16/T
+//    heads x T query tokens, so the MTP tokens of a head share a tile and the
+//    head's Ambient bit;
 //  * a split takes a contiguous chunk of the Critical segment and a contiguous
 //    chunk of the Ambient segment of the list (chunk sizes differ by at most
 //    one), so every split holds a few Ambient pages;
@@ -30,10 +34,10 @@
 //    1168 bytes so the 16-byte K reads and the 2-byte transposed V reads both
 //    spread over the banks;
 //  * S^T = K Q^T on v_mfma_f32_16x16x32_bf16 with Q^T resident in registers
-//    (576 dims x 32 rows); the S^T fragments are the P^T operand of the PV
+//    (576 dims x 16 rows per tile); the S^T fragments are the P^T operand of the PV
 //    product directly; V^T operands (8 tokens of one dim) come from the
-//    token-major tile with transposing LDS reads; when both row tiles of a
-//    wave attend a page, each K and V operand read feeds both tiles' MFMAs;
+//    token-major tile with transposing LDS reads; with two row tiles per wave,
+//    when both attend a page each K and V operand read feeds both tiles' MFMAs;
 //  * the first page's copy is issued as soon as the page metadata is in LDS,
 //    so it lands while the heads are ranked and the query rows loaded (the
 //    ranking synchronises on LDS only);
@@ -94,7 +98,11 @@ __device__ __forceinline__ void split_chunk(int n, int S, int s, int& lo, int& h
   hi = lo + base + (s < extra ? 1 : 0);
 }
 
-__global__ __launch_bounds__(256, 1) void mla_decode_kernel(DecodeParams p) {
+// RT row tiles per wave (1: 8 waves, two per SIMD; 2: 4 waves, one per SIMD)
+template <int RT>
+__global__ __launch_bounds__(512 / RT, RT == 1 ? 2 : 1) void mla_decode_kernel(DecodeParams p) {
+  constexpr int NWV = 8 / RT;                            // waves per workgroup (8 row tiles)
+  constexpr int NT = 64 * NWV;                           // threads
   // two page buffers as distinct LDS objects, so the wait-count pass can
   // tell an LDS-DMA into one from reads of the other
   __shared__ __attribute__((aligned(16))) uint16_t sk0[kMTile];
@@ -149,7 +157,7 @@ __global__ __launch_bounds__(256, 1) void mla_decode_kernel(DecodeParams p) {
   auto stage = [&](uint16_t* buf, int phys, int i_lo, int i_hi) {
     const uint16_t* src = kpool + (size_t)phys * p.Hkv * kMP * kMD;
     const auto rsrc = buffer_rsrc(src, kMP * kMD * 2);
-    for (int i = i_lo + ((wave - i_lo) & 3); i < i_hi; i += 4) {
+    for (int i = i_lo + ((wave - i_lo) & (NWV - 1)); i < i_hi; i += NWV) {
       const int c = 64 * i + lane;
       const int r = c / kMRowChunks, ch = c % kMRowChunks;
       const int sch = ch < kMRowChunks - 1 ? ch : 0;
@@ -161,7 +169,7 @@ __global__ __launch_bounds__(256, 1) void mla_decode_kernel(DecodeParams p) {
   // while no page copy is in flight (global loads complete in issue order)
   int w0 = 0;
   auto load_meta = [&](int first) {
-    for (int i = threadIdx.x; i < kMetaWin && first + i < n_pg; i += 256) {
+    for (int i = threadIdx.x; i < kMetaWin && first + i < n_pg; i += NT) {
       const int k = first + i;
       const int e = k < n_crit ? cb + k : ab + (k - n_crit);
       const int lp = list[e];
@@ -200,7 +208,7 @@ __global__ __launch_bounds__(256, 1) void mla_decode_kernel(DecodeParams p) {
   const bool ranked = p.ccounts != nullptr;
   if (ranked) {
     const int na = min(min(n_pg - n_crit, 32), kMetaWin - n_crit);
-    for (int h = threadIdx.x; h < 256; h += 256) {
+    for (int h = threadIdx.x; h < 256; h += NT) {
       uint32_t key = 0xffffffffu;
       if (h < p.Hq) {
         key = 0;
@@ -219,7 +227,7 @@ __global__ __launch_bounds__(256, 1) void mla_decode_kernel(DecodeParams p) {
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
     const uint4* keys4 = reinterpret_cast<const uint4*>(h_key);
     const int n4 = (p.Hq + 3) >> 2;
-    for (int h = threadIdx.x; h < p.Hq; h += 256) {
+    for (int h = threadIdx.x; h < p.Hq; h += NT) {
       const uint32_t kh = h_key[h];
       int r = 0;
       // 16 key quads per round, read unconditionally from clamped indices
@@ -243,14 +251,14 @@ __global__ __launch_bounds__(256, 1) void mla_decode_kernel(DecodeParams p) {
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
   }
 
-  // This lane's query row in each of the wave's two row tiles.  Ranked tile
+  // This lane's query row in each of the wave's row tiles.  Ranked tile
   // t (heads of ranks t*hpt ..) goes to row group, wave and slot in a snake
   // order, so every wave gets a mix of rarely and often attending tiles.
-  int h_row[2], t_row[2];
-  bool row_ok[2];
+  int h_row[RT], t_row[RT];
+  bool row_ok[RT];
 #pragma unroll
-  for (int rt = 0; rt < 2; ++rt) {
-    const int j = rt * 4 + (rt ? 3 - wave : wave);
+  for (int rt = 0; rt < RT; ++rt) {
+    const int j = rt * NWV + ((rt & 1) ? NWV - 1 - wave : wave);
     const int t = j * n_rg + ((j & 1) ? n_rg - 1 - rg : rg);
     const int pos = t * hpt + col / T;
     row_ok[rt] = t < n_tiles && pos < p.Hq;
@@ -260,9 +268,9 @@ __global__ __launch_bounds__(256, 1) void mla_decode_kernel(DecodeParams p) {
 
   // Q^T operand, resident: tile rt, k-step kk -> row col, dims 8*kg + 32*kk .. +8
   const uint16_t* qp = reinterpret_cast<const uint16_t*>(p.q);
-  bf16x8 qreg[2][kMKSteps];
+  bf16x8 qreg[RT][kMKSteps];
 #pragma unroll
-  for (int rt = 0; rt < 2; ++rt) {
+  for (int rt = 0; rt < RT; ++rt) {
     // rows past the last head read row 0: their logits are masked in the
     // softmax and their outputs never stored, so the loads need no select
     // (a select would wait for each load before the page metadata is read)
@@ -272,12 +280,14 @@ __global__ __launch_bounds__(256, 1) void mla_decode_kernel(DecodeParams p) {
       qreg[rt][kk] = *reinterpret_cast<const bf16x8*>(qp + qrow * kMD + 8 * kg + 32 * kk);
   }
 
-  f32x4 oacc[kMDTiles][2];
+  f32x4 oacc[kMDTiles][RT];
 #pragma unroll
   for (int dt = 0; dt < kMDTiles; ++dt)
 #pragma unroll
-    for (int rt = 0; rt < 2; ++rt) oacc[dt][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_ref[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.f, 0.f};
+    for (int rt = 0; rt < RT; ++rt) oacc[dt][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_ref[RT], l_run[RT];
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) { m_ref[rt] = -INFINITY; l_run[rt] = 0.f; }
 
   // LDS-DMA copy of one page's K tile: wave-wide instruction i covers LDS
   // chunks [64 i, 64 i + 64); chunk c is row c / 73, 16-byte column c % 73
@@ -299,15 +309,15 @@ __global__ __launch_bounds__(256, 1) void mla_decode_kernel(DecodeParams p) {
   for (int attempt = 0; attempt < 3; ++attempt) {
     if (attempt == 1) {
 #pragma unroll
-      for (int rt = 0; rt < 2; ++rt) m_ref[rt] = -INFINITY;
+      for (int rt = 0; rt < RT; ++rt) m_ref[rt] = -INFINITY;
     }
     if (attempt == 2) {
 #pragma unroll
       for (int dt = 0; dt < kMDTiles; ++dt)
 #pragma unroll
-        for (int rt = 0; rt < 2; ++rt) oacc[dt][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int rt = 0; rt < RT; ++rt) oacc[dt][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int rt = 0; rt < 2; ++rt) l_run[rt] = 0.f;
+      for (int rt = 0; rt < RT; ++rt) l_run[rt] = 0.f;
     }
     if (attempt > 0 && w0 != 0) {
       __syncthreads();
@@ -323,15 +333,15 @@ __global__ __launch_bounds__(256, 1) void mla_decode_kernel(DecodeParams p) {
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       __syncthreads();
       const int nv = m_nv[k - w0];
-      bool act[2];
+      bool act[RT];
 #pragma unroll
-      for (int rt = 0; rt < 2; ++rt) {
+      for (int rt = 0; rt < RT; ++rt) {
         const uint32_t word = m_word[k - w0][h_row[rt] >> 5];
         act[rt] = row_ok[rt] && ((word >> (h_row[rt] & 31)) & 1u);
       }
       if (nv > 0 && nv < kMP) {
         // tokens past the sequence end: zero their rows (V operand must be finite)
-        for (int idx = threadIdx.x; idx < (kMP - nv) * 72; idx += 256) {
+        for (int idx = threadIdx.x; idx < (kMP - nv) * 72; idx += NT) {
           const int r = nv + idx / 72, ch = idx % 72;
           *reinterpret_cast<u32x4*>(&cur[r * kMRS + 8 * ch]) = u32x4{0u, 0u, 0u, 0u};
         }
@@ -351,10 +361,11 @@ __global__ __launch_bounds__(256, 1) void mla_decode_kernel(DecodeParams p) {
       };
       copy_part(0);
       // tiles of this wave with a row that attends the page (wave-uniform)
-      const int tmask = nv > 0 ? ((__any(act[0]) ? 1 : 0) | (__any(act[1]) ? 2 : 0)) : 0;
+      int tmask = nv > 0 && __any(act[0]) ? 1 : 0;
+      if constexpr (RT > 1) tmask |= nv > 0 && __any(act[RT - 1]) ? 2 : 0;
 
       const uint16_t* K = cur;
-      constexpr int kAhead = 5;            // operand reads in flight ahead of use
+      constexpr int kAhead = RT == 1 ? 3 : 5;   // operand reads in flight ahead of use
       // The row tiles in MASK (bit rt) over half a page: S^T = K Q^T over
       // tokens 32*half .. +32 (MFMA tiles j4 = 2*half, 2*half + 1), softmax,
       // O^T += V^T P^T.  With both tiles, each K and V operand read from LDS
@@ -365,7 +376,7 @@ __global__ __launch_bounds__(256, 1) void mla_decode_kernel(DecodeParams p) {
         constexpr bool on[2] = {(MASK & 1) != 0, (MASK & 2) != 0};
         f32x4 sacc[2][2];
 #pragma unroll
-        for (int rt = 0; rt < 2; ++rt)
+        for (int rt = 0; rt < RT; ++rt)
           sacc[rt][0] = sacc[rt][1] = f32x4{0.f, 0.f, 0.f, 0.f};
         constexpr int nsq = 2 * kMKSteps;
         // A row m of tile j4 is token tok_of(j4, m): the 8 lanes of one LDS
@@ -381,7 +392,7 @@ __global__ __launch_bounds__(256, 1) void mla_decode_kernel(DecodeParams p) {
         for (int step = 0; step < nsq; ++step) {
           if (step + kAhead < nsq) ka[(step + kAhead) % (kAhead + 1)] = kload(step + kAhead);
 #pragma unroll
-          for (int rt = 0; rt < 2; ++rt)
+          for (int rt = 0; rt < RT; ++rt)
             if (on[rt])
               sacc[rt][step & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[step % (kAhead + 1)],
                                                                           qreg[rt][step >> 1], sacc[rt][step & 1],
@@ -394,7 +405,7 @@ __global__ __launch_bounds__(256, 1) void mla_decode_kernel(DecodeParams p) {
         // p = 2^(s * scale_log2 - m) is one FMA and one v_exp_f32.
         bf16x8 pb[2];
 #pragma unroll
-        for (int rt = 0; rt < 2; ++rt) {
+        for (int rt = 0; rt < RT; ++rt) {
           if (!on[rt]) continue;
           float mraw = -INFINITY;
 #pragma unroll
@@ -452,7 +463,7 @@ __global__ __launch_bounds__(256, 1) void mla_decode_kernel(DecodeParams p) {
         for (int dt = 0; dt < kMDTiles; ++dt) {
           if (dt + kAhead < kMDTiles) va[(dt + kAhead) % (kAhead + 1)] = vload(dt + kAhead);
 #pragma unroll
-          for (int rt = 0; rt < 2; ++rt)
+          for (int rt = 0; rt < RT; ++rt)
             if (on[rt])
               oacc[dt][rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[dt % (kAhead + 1)], pb[rt], oacc[dt][rt],
                                                                      0, 0, 0);
@@ -464,9 +475,11 @@ __global__ __launch_bounds__(256, 1) void mla_decode_kernel(DecodeParams p) {
       auto halfpage = [&](int half) {
         // (independent ifs: as an if-else chain the compiler spilled most of
         // the accumulators)
-        if (tmask == 3) tile_pass(std::integral_constant<int, 3>{}, half);
+        if constexpr (RT > 1)
+          if (tmask == 3) tile_pass(std::integral_constant<int, 3>{}, half);
         if (tmask == 1) tile_pass(std::integral_constant<int, 1>{}, half);
-        if (tmask == 2) tile_pass(std::integral_constant<int, 2>{}, half);
+        if constexpr (RT > 1)
+          if (tmask == 2) tile_pass(std::integral_constant<int, 2>{}, half);
       };
       halfpage(0);
       copy_part(1);
@@ -483,10 +496,10 @@ __global__ __launch_bounds__(256, 1) void mla_decode_kernel(DecodeParams p) {
   }
 
   // epilogue: O = O^T / l per row; lane holds dims 16*dt + 4*kg + 0..3 of row col
-  float lse_row[2];
-  size_t orow[2];
+  float lse_row[RT];
+  size_t orow[RT];
 #pragma unroll
-  for (int rt = 0; rt < 2; ++rt) {
+  for (int rt = 0; rt < RT; ++rt) {
     float l = l_run[rt];
     l = sum_over_row_groups(l);
     const bool empty = m_ref[rt] == -INFINITY;
@@ -533,7 +546,7 @@ __global__ __launch_bounds__(256, 1) void mla_decode_kernel(DecodeParams p) {
   // two row tiles).
   if (kg == 0) {
 #pragma unroll
-    for (int rt = 0; rt < 2; ++rt) {
+    for (int rt = 0; rt < RT; ++rt) {
       if (!row_ok[rt]) continue;
       if (p.splits == 1) {
         if (p.out_lse) p.out_lse[orow[rt]] = lse_row[rt];
@@ -547,8 +560,8 @@ __global__ __launch_bounds__(256, 1) void mla_decode_kernel(DecodeParams p) {
 hipError_t launch_mla_decode(const DecodeParams& p, hipStream_t s) {
   const int hpt = 16 / p.T;
   const int n_rg = ((p.Hq + hpt - 1) / hpt + 7) / 8;
-  const dim3 grid(p.B * n_rg * p.splits), block(256);
-  hipLaunchKernelGGL(mla_decode_kernel, grid, block, 0, s, p);
+  const dim3 grid(p.B * n_rg * p.splits);
+  hipLaunchKernelGGL(mla_decode_kernel<1>, grid, dim3(512), 0, s, p);
   return hipGetLastError();
 }
 
