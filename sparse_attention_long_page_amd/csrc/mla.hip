@@ -38,9 +38,8 @@
 //    product directly; V^T operands (8 tokens of one dim) come from the
 //    token-major tile with transposing LDS reads; with two row tiles per wave,
 //    when both attend a page each K and V operand read feeds both tiles' MFMAs;
-//  * the first page's copy is issued as soon as the page metadata is in LDS,
-//    so it lands while the heads are ranked and the query rows loaded (the
-//    ranking synchronises on LDS only);
+//  * the first page's copy is issued right behind the query-row loads, so
+//    the two land together;
 //  * rows of an active tile whose head is not in an Ambient page's head set
 //    see that page as masked (-inf);
 //  * softmax in base 2 against a per-row reference maximum fixed at the first
@@ -197,9 +196,6 @@ __global__ __launch_bounds__(512 / RT, RT == 1 ? 2 : 1) void mla_decode_kernel(D
     __syncthreads();
   };
   load_meta(0);
-  // the first page's copy goes out now, so that it lands while the heads are
-  // ranked and the query rows are loaded
-  if (n_pg > 0 && m_nv[0] > 0) stage(sk0, m_phys[0], 0, kMInstr);
 
   // Rank the heads: key bit j = the head attends Ambient page j of the split
   // (first 32 held in the first window); ranked by (key, head index), so the
@@ -212,18 +208,21 @@ __global__ __launch_bounds__(512 / RT, RT == 1 ? 2 : 1) void mla_decode_kernel(D
       uint32_t key = 0xffffffffu;
       if (h < p.Hq) {
         key = 0;
-        // all 32 words are read unconditionally (clamped index) and the bits
-        // past na dropped afterwards, so the reads are in flight together
+        // all 32 words are read from clamped indices and the bits past na
+        // dropped afterwards, so the reads are in flight together (the empty
+        // asm keeps each read unconditional: otherwise the compiler sinks it
+        // into a branch on j < na with a wait of its own)
+        uint32_t wv[32];
 #pragma unroll
-        for (int j = 0; j < 32; ++j) {
-          const uint32_t wv = m_word[min(n_crit + j, kMetaWin - 1)][h >> 5];
-          key |= (j < na ? (wv >> (h & 31)) & 1u : 0u) << j;
-        }
+        for (int j = 0; j < 32; ++j) wv[j] = m_word[min(n_crit + j, kMetaWin - 1)][h >> 5];
+#pragma unroll
+        for (int j = 0; j < 32; ++j) asm volatile("" : "+v"(wv[j]));
+#pragma unroll
+        for (int j = 0; j < 32; ++j) key |= (j < na ? (wv[j] >> (h & 31)) & 1u : 0u) << j;
       }
       h_key[h] = key;
     }
-    // LDS-only barriers here: a __syncthreads() would also wait for the
-    // first page's copy, which is meant to land while this runs
+    // (the ranking exchanges LDS data only, so its barriers wait on LDS only)
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
     const uint4* keys4 = reinterpret_cast<const uint4*>(h_key);
     const int n4 = (p.Hq + 3) >> 2;
@@ -279,6 +278,10 @@ __global__ __launch_bounds__(512 / RT, RT == 1 ? 2 : 1) void mla_decode_kernel(D
     for (int kk = 0; kk < kMKSteps; ++kk)
       qreg[rt][kk] = *reinterpret_cast<const bf16x8*>(qp + qrow * kMD + 8 * kg + 32 * kk);
   }
+  // the first page's copy goes out right behind the query-row loads, so the
+  // two land together (issued before the ranking, the copy held the issuing
+  // waves and delayed the ranking by as long)
+  if (n_pg > 0 && m_nv[0] > 0) stage(sk0, m_phys[0], 0, kMInstr);
 
   f32x4 oacc[kMDTiles][RT];
 #pragma unroll
