@@ -40,44 +40,67 @@ __global__ __launch_bounds__(kSelThreads) void block_mask_kernel(MaskParams mp) 
   const int n = min(min((mp.q_start + i1 - 1) / mp.P + 1, n_seq), nkb);
   const int kb_lo = max(0, min((mp.q_start + i0) / mp.P, n - 1));
 
-  // pooled queries: mean over the Q-block's rows, float64
+  // pooled queries: mean over the Q-block's rows, float64, rows added in
+  // order.  The rows are loaded 16 at a time, unconditionally from clamped
+  // indices (a load under a per-lane condition is waited for at once), and
+  // rows past the Q-block add +0.0, which leaves the sum unchanged (it starts
+  // at +0.0 and never becomes -0.0).
   const T* q = reinterpret_cast<const T*>(mp.q);
   for (int idx = threadIdx.x; idx < G * D; idx += kSelThreads) {
     const int hh = idx / D, e = idx % D;
     const int h = g * G + hh;
     double acc = 0.0;
-    for (int i = i0; i < i1; ++i) {
-      const size_t off = ((size_t)i * mp.Hq + h) * D + e;
-      if constexpr (sizeof(T) == 2) acc += (double)bf16_bits_to_f32(q[off]);
-      else acc += (double)q[off];
+    for (int i = i0; i < i1; i += 16) {
+      float w[16];
+#pragma unroll
+      for (int u = 0; u < 16; ++u) {
+        const size_t off = ((size_t)min(i + u, i1 - 1) * mp.Hq + h) * D + e;
+        if constexpr (sizeof(T) == 2) w[u] = bf16_bits_to_f32(q[off]);
+        else w[u] = q[off];
+      }
+#pragma unroll
+      for (int u = 0; u < 16; ++u) acc += i + u < i1 ? (double)w[u] : 0.0;
     }
     qbar[hh][e] = acc / (double)(i1 - i0);
   }
   __syncthreads();
 
-  // block scores: 16 lanes per block, lane `sub` takes dims 64*i + 4*sub + 0..3
+  // block scores: 16 lanes per block, lane `sub` takes dims 64*i + 4*sub + 0..3.
+  // A round covers kRounds steps of 4 blocks per wave: the block-table
+  // entries of the round are loaded together, then all its mean rows, then
+  // the scores are computed (two memory round trips per round instead of
+  // two per step); loads past the causal blocks re-read the last one.
   const int sub = lane & 15, slot = lane >> 4;
   const double sc = (double)mp.sm_scale;
-  for (int kb0 = 0; kb0 < n; kb0 += 4 * (kSelThreads / 64)) {
-    const int kb = kb0 + wave * 4 + slot;
-    const int kbc = min(kb, n - 1);
-    const int phys = mp.bt_row[kbc];
-    const float* m = mp.mu + ((size_t)phys * mp.Hkv + g) * D + 4 * sub;
-    f32x4 v[PL / 4];
+  constexpr int kRounds = 8;
+  constexpr int kStep = 4 * (kSelThreads / 64);             // blocks per step over the workgroup
+  for (int kb0 = 0; kb0 < n; kb0 += kRounds * kStep) {
+    int phys[kRounds];
 #pragma unroll
-    for (int i = 0; i < PL / 4; ++i) v[i] = *reinterpret_cast<const f32x4*>(m + 64 * i);
-    for (int hh = 0; hh < G; ++hh) {
-      const double* qq = &qbar[hh][4 * sub];
-      double acc = 0.0;
+    for (int r = 0; r < kRounds; ++r) phys[r] = mp.bt_row[min(kb0 + r * kStep + wave * 4 + slot, n - 1)];
+    f32x4 v[kRounds][PL / 4];
 #pragma unroll
-      for (int i = 0; i < PL / 4; ++i) {
-        acc += qq[64 * i] * (double)v[i][0];
-        acc += qq[64 * i + 1] * (double)v[i][1];
-        acc += qq[64 * i + 2] * (double)v[i][2];
-        acc += qq[64 * i + 3] * (double)v[i][3];
+    for (int r = 0; r < kRounds; ++r) {
+      const float* m = mp.mu + ((size_t)phys[r] * mp.Hkv + g) * D + 4 * sub;
+#pragma unroll
+      for (int i = 0; i < PL / 4; ++i) v[r][i] = *reinterpret_cast<const f32x4*>(m + 64 * i);
+    }
+#pragma unroll
+    for (int r = 0; r < kRounds; ++r) {
+      const int kb = kb0 + r * kStep + wave * 4 + slot;
+      for (int hh = 0; hh < G; ++hh) {
+        const double* qq = &qbar[hh][4 * sub];
+        double acc = 0.0;
+#pragma unroll
+        for (int i = 0; i < PL / 4; ++i) {
+          acc += qq[64 * i] * (double)v[r][i][0];
+          acc += qq[64 * i + 1] * (double)v[r][i][1];
+          acc += qq[64 * i + 2] * (double)v[r][i][2];
+          acc += qq[64 * i + 3] * (double)v[r][i][3];
+        }
+        acc = row16_sum(acc);
+        if (sub == 0 && kb < n) scores[(size_t)hh * nkb + kb] = (float)(sc * acc);
       }
-      acc = row16_sum(acc);
-      if (sub == 0 && kb < n) scores[(size_t)hh * nkb + kb] = (float)(sc * acc);
     }
   }
   __syncthreads();
