@@ -72,12 +72,21 @@ __global__ __launch_bounds__(256) void page_value_summary_kernel(ValueSummaryPar
   const double scale = sizeof(T) == 1 ? (double)p.v_scale[(size_t)phys * p.n_kv + g] : 1.0;
   float* dst = p.nu + ((size_t)phys * p.n_kv + g) * p.d_v;
   const int total = p.d_v * vpr;
-  for (int v0 = 0; v0 < total; v0 += 256) {            // uniform trip count: every lane shuffles
-    const int v = v0 + threadIdx.x;
-    double acc = 0.0;
-    if (v < total) acc = sum_vec16<T>(page[v], (v % vpr) * per, nv);
-    for (int o = vpr >> 1; o > 0; o >>= 1) acc += __shfl_xor(acc, o, 64);
-    if (v < total && v % vpr == 0) dst[v / vpr] = (float)(acc * scale / (double)nv);
+  // four vectors per lane are loaded together, unconditionally from clamped
+  // indices (a load under a per-lane condition is waited for at once); the
+  // trip counts are uniform, so every lane takes part in the shuffles
+  for (int v0 = 0; v0 < total; v0 += 4 * 256) {
+    uint4 w[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) w[u] = page[min(v0 + 256 * u + (int)threadIdx.x, total - 1)];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      if (v0 + 256 * u >= total) break;
+      const int v = v0 + 256 * u + threadIdx.x;
+      double acc = v < total ? sum_vec16<T>(w[u], (v % vpr) * per, nv) : 0.0;
+      for (int o = vpr >> 1; o > 0; o >>= 1) acc += __shfl_xor(acc, o, 64);
+      if (v < total && v % vpr == 0) dst[v / vpr] = (float)(acc * scale / (double)nv);
+    }
   }
 }
 
