@@ -17,8 +17,12 @@
 //    and share its L2 while they sweep the same KV blocks;
 //  * per KV block: K (token-major) and V^T (page-transposed) are copied from
 //    the pool into padded LDS rows (conflict-free 16-byte reads) by
-//    buffer-to-LDS copies; the copy of the next block runs while the current
-//    one is computed (two stages);
+//    buffer-to-LDS copies, three stages: the copy of block t+2 is issued at
+//    the end of block t, and only by the first four waves (one per SIMD);
+//    those win the SIMD's issue arbitration over the other wave, finish
+//    their block first and would wait at the block's barrier, so their copy
+//    issue (which stalls a wave while the memory pipeline drains the
+//    burst) overlaps that wait instead of delaying the other waves' MFMAs;
 //  * S^T = K Q^T and O^T += V^T P^T on v_mfma_f32_16x16x32_bf16 (Q^T resident
 //    in registers), with the token permutation that makes the S^T fragments
 //    the PV operand directly; the row sums of P are one more MFMA per PV
@@ -29,6 +33,8 @@
 //  * online softmax in base 2 with a lazily moved reference maximum: the
 //    accumulators are rescaled only when a row's maximum grows by more than
 //    2^8 (exact: the final normalisation uses the same reference).
+#include <type_traits>
+
 #include "common.h"
 
 namespace sa {
@@ -157,14 +163,16 @@ struct Stage {
 // 32-63 of the tile).  A group larger than HW is split over G/HW workgroups.
 template <int HW>
 __global__ __launch_bounds__(128 * HW) void prefill_kernel(PrefillParams p) {
-  // two pipeline stages as distinct LDS objects (so the wait-count pass can
-  // tell a copy into one from reads of the other): the copy of block t+1
-  // runs while block t is computed
+  // three pipeline stages as distinct LDS objects (so the wait-count pass
+  // can tell a copy into one from reads of another): blocks t+1 and t+2 are
+  // in flight while block t is computed
   __shared__ __attribute__((aligned(16))) uint16_t st0[kStageElems];
   __shared__ __attribute__((aligned(16))) uint16_t st1[kStageElems];
+  __shared__ __attribute__((aligned(16))) uint16_t st2[kStageElems];
   __shared__ int kb_s[kPrefillMaxBlocks], ph_s[kPrefillMaxBlocks];
   constexpr int NW = 2 * HW;                                  // waves per workgroup
-  constexpr int NI = (kStageInstr + NW - 1) / NW;             // copy loads per wave per block
+  constexpr int NCW = NW < 4 ? NW : 4;                        // waves that issue the copies
+  constexpr int NI = (kStageInstr + NCW - 1) / NCW;           // copy loads per copying wave per block
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -230,8 +238,8 @@ __global__ __launch_bounds__(128 * HW) void prefill_kernel(PrefillParams p) {
   // LDS-DMA copy of table entry t into a stage: wave-wide load i covers stage
   // chunks [64 i, 64 i + 64); loads 0-16 hold the K tile, 17-34 the V^T tile.
   // K slots copy straight; V^T slot c of row d receives token-chunk
-  // c ^ vsw(d) (an involution); pad slots re-read chunk 0 of their row.  Every
-  // wave issues NI loads (the last real load is repeated to fill).  Each
+  // c ^ vsw(d) (an involution); pad slots re-read chunk 0 of their row.  Each
+  // copying wave issues NI loads (the last real load is repeated to fill).  Each
   // lane's byte offset within the (page, head) tile is fixed per load and
   // computed once; per block only the tile's base address (scalar) changes.
   static_assert(kKChunks % 64 == 0, "loads hold K or V^T chunks only");
@@ -239,7 +247,7 @@ __global__ __launch_bounds__(128 * HW) void prefill_kernel(PrefillParams p) {
   uint32_t lane_off[NI];     // bytes
 #pragma unroll
   for (int j = 0; j < NI; ++j) {
-    const int i = min(wave + NW * j, kStageInstr - 1);
+    const int i = min(wave + NCW * j, kStageInstr - 1);
     const int c = 64 * i + lane;
     if (c < kKChunks) {
       const int r = c / (kKRow / 8), slot = c % (kKRow / 8);
@@ -259,7 +267,7 @@ __global__ __launch_bounds__(128 * HW) void prefill_kernel(PrefillParams p) {
     const auto rv = buffer_rsrc(vpool + tile, kPP * kPD * 2);
 #pragma unroll
     for (int j = 0; j < NI; ++j) {
-      const int i = min(wave + NW * j, kStageInstr - 1);
+      const int i = min(wave + NCW * j, kStageInstr - 1);
       copy16_to_lds(i < kKInstr ? rk : rv, st + i * 512, lane_off[j]);
     }
   };
@@ -376,21 +384,26 @@ __global__ __launch_bounds__(128 * HW) void prefill_kernel(PrefillParams p) {
     }
   };
 
-  // One block: wait for this wave's part of its copy, barrier (then every
-  // part has landed and every wave has finished the previous block), start
-  // the copy of the next block into the other stage, compute.  The wait is
-  // the s_waitcnt builtin (vmcnt 0, other counters free), which the
-  // compiler's wait-count pass sees, so it adds no wait of its own on the
-  // copy just issued; the barrier is a plain s_barrier with a memory clobber
-  // (a __syncthreads() fence would also wait for that copy).
-  auto block = [&](auto sidx, int t) __attribute__((always_inline)) {
-    uint16_t* cur = sidx.value == 0 ? st0 : st1;
-    uint16_t* ahead = sidx.value == 0 ? st1 : st0;
-    __builtin_amdgcn_s_waitcnt(0x0f70);
+  // One block: wait for this wave's part of its copy (the copy of block t+1,
+  // issued after it, may stay in flight), barrier (then every part has
+  // landed and every wave has finished block t-1), compute, then copy block
+  // t+2 into the stage block t-1 used.  Every copying wave issues exactly
+  // NI loads per block (past the last block it repeats the last block's
+  // page into a stage no one reads again), so the wait is a fixed count.
+  // The wait is the s_waitcnt builtin (other counters free), which the
+  // compiler's wait-count pass sees, so it adds no wait of its own; the
+  // barrier is a plain s_barrier with a memory clobber (a __syncthreads()
+  // fence would also wait for the copies in flight).
+  auto block = [&](auto sidx, auto copying, int t) __attribute__((always_inline)) {
+    constexpr int k = decltype(sidx)::value;
+    constexpr bool CP = decltype(copying)::value;
+    uint16_t* cur = k == 0 ? st0 : (k == 1 ? st1 : st2);
+    uint16_t* ahead2 = k == 0 ? st2 : (k == 1 ? st0 : st1);
+    __builtin_amdgcn_s_waitcnt((NI & 15) | ((NI >> 4) << 14) | 0x0f70);   // vmcnt(NI)
     asm volatile("s_barrier" ::: "memory");
-    if (t + 1 < nblk) stage_copy(ahead, t + 1);
     qk(cur, t);
     sm_pv(cur + kKTile, t);
+    if constexpr (CP) stage_copy(ahead2, min(t + 2, nblk - 1));
   };
 
   // the tile's table entries and their physical pages, read once into LDS so
@@ -402,11 +415,27 @@ __global__ __launch_bounds__(128 * HW) void prefill_kernel(PrefillParams p) {
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
 
-  if (nblk > 0) stage_copy(st0, 0);
-  for (int t = 0; t < nblk; t += 2) {
-    block(Stage<0>{}, t);
-    if (t + 1 < nblk) block(Stage<1>{}, t + 1);
-  }
+  // the copying waves and the others run the same loop in two copies, so
+  // that no branch on the wave sits inside it (the wait-count pass would
+  // merge the two paths and wait for every copy in flight)
+  auto sweep = [&](auto copying) __attribute__((always_inline)) {
+    constexpr bool CP = decltype(copying)::value;
+    if (CP && nblk > 0) {
+      stage_copy(st0, 0);
+      stage_copy(st1, min(1, nblk - 1));
+    }
+    int t3 = 0;
+    for (; t3 + 3 <= nblk; t3 += 3) {
+      block(Stage<0>{}, copying, t3);
+      block(Stage<1>{}, copying, t3 + 1);
+      block(Stage<2>{}, copying, t3 + 2);
+    }
+    if (t3 < nblk) block(Stage<0>{}, copying, t3);
+    if (t3 + 1 < nblk) block(Stage<1>{}, copying, t3 + 1);
+  };
+  if (wave < NCW) sweep(std::true_type{});
+  else sweep(std::false_type{});
+  __builtin_amdgcn_s_waitcnt(0x0f70);     // no copy into LDS outlives the loop
 
   // epilogue: O = O^T / l per row
   uint16_t* out = reinterpret_cast<uint16_t*>(p.out);
