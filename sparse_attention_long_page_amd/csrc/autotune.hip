@@ -17,9 +17,10 @@
 //
 // Kernels:
 //  * mass_logits_kernel: the log-weights of a 64-page x 64-row tile per
-//    workgroup on v_mfma_f32_16x16x32_bf16.  The fp32 mean keys are split as
-//    hi + lo bf16 (two MFMAs per step, residual below 2^-17 relative), the
-//    bf16 queries are exact, so the products are fp32-accurate.
+//    workgroup on v_mfma_f32_16x16x32_bf16, the tile's query rows staged in
+//    LDS once for its four waves.  The fp32 mean keys are split as hi + lo
+//    bf16 (two MFMAs per step, residual below 2^-17 relative), the bf16
+//    queries are exact, so the products are fp32-accurate.
 //  * mass_softmax_kernel: per (sequence, query head), the softmax over pages
 //    of each query token's row, summed into M.
 //  * tier_page_kernel: per (sequence, KV head, page) the page's mass over the
@@ -36,11 +37,21 @@
 namespace sa {
 
 // ------------------------------------------------------------ mass logits
+// One wave-wide copy of 16 bytes per lane from per-lane global addresses into
+// LDS: lane l's bytes land at lds + 16 l.
+__device__ __forceinline__ void copy16_global_to_lds(const uint16_t* src, uint16_t* lds) {
+  __builtin_amdgcn_global_load_lds(src, lds, 16, 0, 0);
+}
 // grid (page tiles of 64, row tiles of 64, B*Hkv), 256 threads: wave w takes
 // pages 16w..16w+15 of the tile against the tile's 64 query rows of KV head
-// g (row r = t*G + head-in-group).
+// g (row r = t*G + head-in-group).  The tile's query rows are copied once
+// into LDS (rows of D + 8 bf16: one pad chunk per row spreads a column's 16
+// rows over distinct 16-byte slots) and every wave reads its B operands
+// there; each wave loads only its own pages' mean rows from global memory.
 template <int D>
 __global__ __launch_bounds__(256) void mass_logits_kernel(MassParams p) {
+  constexpr int kRowChunks = D / 8 + 1;                  // 16-byte chunks per LDS row (one pad)
+  __shared__ __attribute__((aligned(16))) uint16_t qs[64 * kRowChunks * 8];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int col = lane & 15, kq = lane >> 4;
   const int b = blockIdx.z / p.Hkv, g = blockIdx.z % p.Hkv;
@@ -51,25 +62,32 @@ __global__ __launch_bounds__(256) void mass_logits_kernel(MassParams p) {
   const int TG = p.T * p.G;
   const int r0 = blockIdx.y * 64;
   const int32_t* bt = p.block_table + (size_t)b * p.max_pages;
+  const uint16_t* qbase = reinterpret_cast<const uint16_t*>(p.q);
+
+  // the tile's query rows into LDS: wave-wide copy i covers LDS chunks
+  // [64 i, 64 i + 64), chunk c = row c / kRowChunks, column c % kRowChunks
+  // (the pad column re-reads column 0); rows past the group read the
+  // group's first row (their results are never written)
+  for (int i = wave; i < kRowChunks; i += 4) {
+    const int c = 64 * i + lane, rr = c / kRowChunks, ch = c % kRowChunks;
+    const int r = r0 + rr < TG ? r0 + rr : 0;
+    const int t = r / p.G, hl = r % p.G;
+    copy16_global_to_lds(qbase + (((size_t)b * p.T + t) * p.Hq + (size_t)g * p.G + hl) * D + 8 * (ch < D / 8 ? ch : 0),
+                         qs + 512 * i);
+  }
 
   // A operand: mean key of page p0 + col, dims 32*ks + 8*kq .. +7
   const int pg = p0 + col;
   const float* murow = p.mu + ((size_t)bt[pg < n ? pg : 0] * p.Hkv + g) * D;
-  // B operands: query rows r0 + 16*rt + col
-  const uint16_t* qbase = reinterpret_cast<const uint16_t*>(p.q);
   bool row_ok[4];
-  size_t qoff[4];
 #pragma unroll
-  for (int rt = 0; rt < 4; ++rt) {
-    const int r = r0 + 16 * rt + col;
-    row_ok[rt] = r < TG;
-    const int t = row_ok[rt] ? r / p.G : 0, hl = row_ok[rt] ? r % p.G : 0;
-    qoff[rt] = (((size_t)b * p.T + t) * p.Hq + (size_t)g * p.G + hl) * D;
-  }
+  for (int rt = 0; rt < 4; ++rt) row_ok[rt] = r0 + 16 * rt + col < TG;
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
   f32x4 acc[4];
 #pragma unroll
   for (int rt = 0; rt < 4; ++rt) acc[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll 3
+#pragma unroll 6
   for (int ks = 0; ks < D / 32; ++ks) {
     const float4 x0 = *reinterpret_cast<const float4*>(murow + 32 * ks + 8 * kq);
     const float4 x1 = *reinterpret_cast<const float4*>(murow + 32 * ks + 8 * kq + 4);
@@ -82,9 +100,7 @@ __global__ __launch_bounds__(256) void mass_logits_kernel(MassParams p) {
     }
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt) {
-      // rows past the group read its first row (their results are never
-      // written): a load under a per-lane condition would be waited for at once
-      const bf16x8 bq = *reinterpret_cast<const bf16x8*>(qbase + qoff[rt] + 32 * ks + 8 * kq);
+      const bf16x8 bq = *reinterpret_cast<const bf16x8*>(qs + 8 * ((16 * rt + col) * kRowChunks + 4 * ks + kq));
       acc[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(hi, bq, acc[rt], 0, 0, 0);
       acc[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lo, bq, acc[rt], 0, 0, 0);
     }
