@@ -295,7 +295,8 @@ __global__ __launch_bounds__(512 / RT, RT == 1 ? 2 : 1) void mla_decode_kernel(D
   // LDS-DMA copy of one page's K tile: wave-wide instruction i covers LDS
   // chunks [64 i, 64 i + 64); chunk c is row c / 73, 16-byte column c % 73
   // (column 72 is row padding and re-reads column 0 of the row).  Wave w
-  // issues the instructions i = w mod 4 of [i_lo, i_hi).
+  // issues the instructions i of [i_lo, i_hi) with i = w mod NWV (the
+  // stage lambda above).
   // Pass structure.  Attempt 0 sets each row's reference maximum from the
   // first page it attends and never moves it: later logits may exceed it by
   // up to 2^64 (exp2 stays finite in fp32), so the accumulators are never
