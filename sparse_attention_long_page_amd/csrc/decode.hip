@@ -150,61 +150,92 @@ __global__ __launch_bounds__(256) void decode_f32_kernel(DecodeParams p) {
 
 // ------------------------------------------------------------------- merge
 // One wave per query row: o = sum_s w_s o_s / sum_s w_s, w_s = exp(lse_s - max).
-// Lanes own 4 consecutive dims (16-byte fp32 or 8-byte bf16 loads); the loads
-// of up to 8 splits are issued before any is consumed.
+// Lanes own VPL consecutive dims (16-byte loads: 4 fp32 or 8 bf16 partial
+// values); the loads of a group of 8 splits are issued before any is
+// consumed, and the first group's go out together with the row's lse loads,
+// before the weights are formed.
 template <bool BF16P>
-__device__ __forceinline__ f32x4 load_partial4(const float* po, size_t off) {
-  if constexpr (BF16P) {
-    const uint2 w = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint16_t*>(po) + off);
-    return f32x4{bf16_lo(w.x), bf16_hi(w.x), bf16_lo(w.y), bf16_hi(w.y)};
-  } else {
-    return *reinterpret_cast<const f32x4*>(po + off);
+struct MergeLanes {
+  static constexpr int VPL = BF16P ? 8 : 4;         // dims per lane per load
+  typedef u32x4 raw_t;                              // 16 bytes of partial values
+  __device__ static float val(const raw_t& v, int e) {
+    if constexpr (BF16P) return (e & 1) ? bf16_hi(v[e >> 1]) : bf16_lo(v[e >> 1]);
+    else return __uint_as_float(v[e]);
   }
-}
+};
 
 template <bool BF16P>
 __global__ __launch_bounds__(256) void lse_merge_kernel(MergeParams p) {
+  using ML = MergeLanes<BF16P>;
+  constexpr int VPL = ML::VPL;
+  typedef typename ML::raw_t raw_t;
   const int lane = threadIdx.x & 63;
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (row >= p.rows) return;
   const float* pl = p.part_lse + (size_t)row * p.splits;
-  const float mine = lane < p.splits ? pl[lane] : -INFINITY;
+  const size_t row_off = (size_t)row * p.splits * p.d_v;
+  const uint16_t* pob = reinterpret_cast<const uint16_t*>(p.part_o);
+  // group of 8 splits from s0 at dims d0.. (unconditional loads from clamped
+  // indices: a split past the last re-reads the last one, dims past d_v the
+  // first ones; neither is used)
+  auto load_group = [&](int d0, int s0, raw_t (&v)[8]) __attribute__((always_inline)) {
+    const int dd = min(d0, p.d_v - VPL);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const size_t off = row_off + (size_t)min(s0 + j, p.splits - 1) * p.d_v + dd;
+      if constexpr (BF16P) v[j] = *reinterpret_cast<const raw_t*>(pob + off);
+      else v[j] = *reinterpret_cast<const raw_t*>(p.part_o + off);
+    }
+  };
+  const int d_first = VPL * lane;
+  raw_t v[8];
+  const float lv = pl[min(lane, p.splits - 1)];
+  load_group(d_first, 0, v);
+  const float mine = lane < p.splits ? lv : -INFINITY;
   const float M = wave_max(mine);
   float w = 0.f;
   if (M != -INFINITY && lane < p.splits) w = __expf(mine - M);
   const float L = wave_sum(w);
   const float inv = M == -INFINITY ? 0.f : 1.f / L;
-  const float* po = p.part_o;
-  const size_t row_off = (size_t)row * p.splits * p.d_v;
-  for (int d4 = lane; d4 < p.d_v / 4; d4 += 64) {
-    f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-    for (int s0 = 0; s0 < p.splits; s0 += 8) {
-      // all 8 loads in flight together: each is unconditional (a split past
-      // the last re-reads the last one), and a split that takes no part adds
-      // +0.0, which leaves acc unchanged (it starts at +0.0 and never becomes
-      // -0.0); an empty split's partial, whatever it holds, is never used
-      f32x4 v[8];
+  // a split that takes no part adds +0.0, which leaves acc unchanged (it
+  // starts at +0.0 and never becomes -0.0); an empty split's partial,
+  // whatever it holds, is never used
+  auto accumulate = [&](const raw_t (&vv)[8], int s0, float (&acc)[VPL]) __attribute__((always_inline)) {
 #pragma unroll
-      for (int j = 0; j < 8; ++j)
-        v[j] = load_partial4<BF16P>(po, row_off + (size_t)min(s0 + j, p.splits - 1) * p.d_v + 4 * d4);
+    for (int j = 0; j < 8; ++j) {
+      const float ws = __shfl(w, (s0 + j) & 63, 64);
+      const bool use = s0 + j < p.splits && ws != 0.f;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const float ws = __shfl(w, (s0 + j) & 63, 64);
-        const bool use = s0 + j < p.splits && ws != 0.f;
+      for (int e = 0; e < VPL; ++e) acc[e] += use ? ws * ML::val(vv[j], e) : 0.f;
+    }
+  };
+  auto store = [&](int d0, const float (&acc)[VPL]) __attribute__((always_inline)) {
+    const size_t o = (size_t)row * p.d_v + d0;
+    if (p.out_fp32) {
+      float* of = reinterpret_cast<float*>(p.out) + o;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) acc[e] += use ? ws * v[j][e] : 0.f;
+      for (int e = 0; e < VPL; e += 4)
+        *reinterpret_cast<f32x4*>(of + e) = f32x4{acc[e] * inv, acc[e + 1] * inv, acc[e + 2] * inv, acc[e + 3] * inv};
+    } else {
+      uint16_t* ob = reinterpret_cast<uint16_t*>(p.out) + o;
+#pragma unroll
+      for (int e = 0; e < VPL; e += 4) {
+        uint2 pk;
+        pk.x = (uint32_t)f32_to_bf16_bits(acc[e] * inv) | ((uint32_t)f32_to_bf16_bits(acc[e + 1] * inv) << 16);
+        pk.y = (uint32_t)f32_to_bf16_bits(acc[e + 2] * inv) | ((uint32_t)f32_to_bf16_bits(acc[e + 3] * inv) << 16);
+        *reinterpret_cast<uint2*>(ob + e) = pk;
       }
     }
-    const size_t o = (size_t)row * p.d_v + 4 * d4;
-    if (p.out_fp32) {
-      *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(p.out) + o) =
-          f32x4{acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv};
-    } else {
-      uint2 pk;
-      pk.x = (uint32_t)f32_to_bf16_bits(acc[0] * inv) | ((uint32_t)f32_to_bf16_bits(acc[1] * inv) << 16);
-      pk.y = (uint32_t)f32_to_bf16_bits(acc[2] * inv) | ((uint32_t)f32_to_bf16_bits(acc[3] * inv) << 16);
-      *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(p.out) + o) = pk;
+  };
+  for (int d0 = d_first; d0 < p.d_v; d0 += 64 * VPL) {
+    float acc[VPL];
+#pragma unroll
+    for (int e = 0; e < VPL; ++e) acc[e] = 0.f;
+    for (int s0 = 0; s0 < p.splits; s0 += 8) {
+      if (d0 != d_first || s0 != 0) load_group(d0, s0, v);
+      accumulate(v, s0, acc);
     }
+    store(d0, acc);
   }
   if (lane == 0 && p.out_lse) p.out_lse[row] = M == -INFINITY ? -INFINITY : M + __logf(L);
 }
