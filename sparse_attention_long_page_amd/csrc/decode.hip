@@ -177,7 +177,7 @@ __global__ __launch_bounds__(256) void lse_merge_kernel(MergeParams p) {
   const uint16_t* pob = reinterpret_cast<const uint16_t*>(p.part_o);
   // group of 8 splits from s0 at dims d0.. (unconditional loads from clamped
   // indices: a split past the last re-reads the last one, dims past d_v the
-  // first ones; neither is used)
+  // row's last VPL; neither is used)
   auto load_group = [&](int d0, int s0, raw_t (&v)[8]) __attribute__((always_inline)) {
     const int dd = min(d0, p.d_v - VPL);
 #pragma unroll
@@ -241,6 +241,8 @@ __global__ __launch_bounds__(256) void lse_merge_kernel(MergeParams p) {
 }
 
 hipError_t launch_merge(const MergeParams& p, hipStream_t s) {
+  // whole 16-byte loads per lane: d_v a multiple of 8 (bf16 partials) or 4 (fp32)
+  if (p.d_v % (p.part_bf16 ? 8 : 4) != 0) return hipErrorInvalidValue;
   if (p.part_bf16) hipLaunchKernelGGL(lse_merge_kernel<true>, dim3((p.rows + 3) / 4), dim3(256), 0, s, p);
   else hipLaunchKernelGGL(lse_merge_kernel<false>, dim3((p.rows + 3) / 4), dim3(256), 0, s, p);
   return hipGetLastError();
