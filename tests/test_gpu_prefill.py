@@ -50,6 +50,10 @@ CASES = {
     "random_g1": SMALL.replace(n_q_heads=2, n_kv_heads=2),
     "random_g2": SMALL.replace(n_q_heads=4, n_kv_heads=2, q_len=130, q_start=64 * 9),
     "random_g8": SMALL.replace(n_q_heads=8, n_kv_heads=1, q_len=64, q_start=64 * 12 + 63),
+    # odd and non-power-of-two groups: 3 (one head per workgroup, three per
+    # tile) and 6 (two heads per workgroup, three per tile)
+    "random_g3": SMALL.replace(n_q_heads=6, n_kv_heads=2, q_len=150, q_start=64 * 7 + 5),
+    "random_g6": SMALL.replace(n_q_heads=6, n_kv_heads=1, q_len=100, q_start=64 * 10),
     # chunk at the start of the sequence: no prefix at all
     "start_g4": SMALL.replace(q_len=150, q_start=0),
     # chunk shorter than one tile
