@@ -28,4 +28,10 @@ namespace sa {
 __device__ __forceinline__ int stg_kswz(int r) { return 2 * (r & 3) + 8 * ((r >> 3) & 1); }
 __device__ __forceinline__ int stg_vswz(int d) { return d & 6; }
 
+// Workgroup barriers the decode statements execute, each on every path
+// (after the chunk loop when STAGED, then before the 4 waves' partials are
+// combined).  A workgroup whose other waves skip the decode has them execute
+// the same number of barriers, so every barrier is met by every wave.
+constexpr int decode_body_barriers(bool staged) { return staged ? 2 : 1; }
+
 }  // namespace sa

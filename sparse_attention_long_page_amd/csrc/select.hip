@@ -164,18 +164,18 @@ __global__ __launch_bounds__(kSelThreads) void score_lastsel_kernel(ScoreParams 
       __hip_atomic_store(&out[lp], lp < n ? (float)acc : __builtin_nanf(""), __ATOMIC_RELAXED,
                          __HIP_MEMORY_SCOPE_AGENT);
   }
-  // The list's last workgroup selects.  Every workgroup's score stores are
-  // acknowledged (written at the device's coherence point) before it counts
-  // itself on the list's counter; the one that counts last reads all the
-  // scores back with device-coherent loads.  (A device-scope fence would
-  // write back and invalidate the whole L2 of the XCD instead.)
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  // The list's last workgroup selects.  The workgroup's score stores are
+  // ordered before its count on the list's counter by the barrier and the
+  // count's device-scope release; the workgroup that counts last takes a
+  // device-scope acquire before it reads all the scores back (device-coherent
+  // loads), so it sees every other workgroup's stores.
   __syncthreads();
   if (threadIdx.x == 0)
-    last_s = __hip_atomic_fetch_add(&arrivals[(size_t)b * sp.n_sel + s], 1u, __ATOMIC_RELAXED,
+    last_s = __hip_atomic_fetch_add(&arrivals[(size_t)b * sp.n_sel + s], 1u, __ATOMIC_RELEASE,
                                     __HIP_MEMORY_SCOPE_AGENT) == gridDim.x - 1;
   __syncthreads();
   if (!last_s) return;
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
   for (int i = threadIdx.x; i < 512; i += kSelThreads) sh.hist[0][0][i] = 0u;
   // 8 scores per thread in flight, loaded before any is used (indices past
   // the end re-read the last score)

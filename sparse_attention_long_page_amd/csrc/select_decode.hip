@@ -9,7 +9,7 @@
 // one split: score_keys_body and select_from_keys (select_body.h) on all 8
 // waves, the list kept in LDS and written out, then the decode
 // statements (decode_body.inc, the staged d 128 / pages of 64 path) on waves 0-3 while
-// waves 4-7 end (a barrier waits only for the waves that have not ended).
+// waves 4-7 only meet the decode's workgroup barriers, then end.
 // Each list starts its decode as soon as its own selection is done, rather
 // than when the slowest list's selection is, and no kernel boundary sits
 // between the two steps.
@@ -41,7 +41,11 @@ __global__ __launch_bounds__(kSelThreads, 1) void select_decode_kernel(ScorePara
   const int count = L.n_forced + L.k_eff;
   int32_t* lrow = sel.lists + ((size_t)b * sel.n_sel + s) * sel.list_stride;
   for (int i = threadIdx.x; i < count; i += kSelThreads) lrow[i] = list[i];
-  if (threadIdx.x >= 256) return;
+  if (threadIdx.x >= 256) {
+    // waves 4-7 have no decode work; they meet the decode's barriers and end
+    for (int i = 0; i < decode_body_barriers(true); ++i) __syncthreads();
+    return;
+  }
   {
     constexpr bool TIERED = false, STAGED = true, FP8 = false;
     constexpr int KSTEPS = D / 32;
