@@ -67,6 +67,7 @@ constexpr int kMDTiles = kMDV / 16;      // 32
 constexpr int kMetaWin = 128;            // pages of page metadata held in LDS
 constexpr int kMaxMaskWords = 8;         // Ambient head-mask words per page (n_q_heads <= 256)
 constexpr float kMMargin = 64.0f;         // log2 units a logit may exceed its row's reference
+constexpr int kOutRS = kMDV + 8;          // LDS row stride of the staged bf16 output rows (1040 B)
 
 // Token of row m (0..15) of the 16-token MFMA tile j4 of a page.  Rows
 // 4*g .. 4*g+3 (g = m/4) hold tokens 16*j4 + 8*(g/2) + g%2 + {0, 2, 4, 6}.
@@ -499,7 +500,19 @@ __global__ __launch_bounds__(512 / RT, RT == 1 ? 2 : 1) void mla_decode_kernel(D
     if (attempt == 1) __syncthreads();
   }
 
-  // epilogue: O = O^T / l per row; lane holds dims 16*dt + 4*kg + 0..3 of row col
+  // epilogue: O = O^T / l per row; lane holds dims 16*dt + 4*kg + 0..3 of row col.
+  // bf16 rows (the output, or bf16 split partials) go through LDS: each tile's
+  // 16 rows are written to a free page buffer, then stored row by row, 1 KiB
+  // per wave-wide store, instead of 16 rows x 32 bytes per store.  The page
+  // buffers are free once every wave has passed the barrier below (no copy is
+  // issued after the last page).
+  const bool staged_out = p.splits == 1 || p.part_bf16;     // uniform
+  if (staged_out) __syncthreads();
+  auto out_area = [&](int rt) {
+    const int ti = wave * RT + rt;                          // 8 tiles, 4 per page buffer
+    return (ti < 4 ? sk0 : sk1) + (ti & 3) * 16 * kOutRS;
+  };
+  static_assert(4 * 16 * kOutRS <= kMTile, "four tiles' output rows fit one page buffer");
   float lse_row[RT];
   size_t orow[RT];
 #pragma unroll
@@ -511,8 +524,8 @@ __global__ __launch_bounds__(512 / RT, RT == 1 ? 2 : 1) void mla_decode_kernel(D
     lse_row[rt] = empty ? -INFINITY : (m_ref[rt] + log2f(l)) * kLn2;
     orow[rt] = ((size_t)b * T + t_row[rt]) * p.Hq + h_row[rt];
     if (!row_ok[rt]) continue;
-    if (p.splits == 1) {
-      uint16_t* out = reinterpret_cast<uint16_t*>(p.out) + orow[rt] * kMDV;
+    if (staged_out) {
+      uint16_t* ar = out_area(rt) + col * kOutRS;
 #pragma unroll
       for (int dt = 0; dt < kMDTiles; ++dt) {
         f32x4 v = oacc[dt][rt];
@@ -520,18 +533,7 @@ __global__ __launch_bounds__(512 / RT, RT == 1 ? 2 : 1) void mla_decode_kernel(D
         uint2 pk;
         pk.x = (uint32_t)f32_to_bf16_bits(v[0]) | ((uint32_t)f32_to_bf16_bits(v[1]) << 16);
         pk.y = (uint32_t)f32_to_bf16_bits(v[2]) | ((uint32_t)f32_to_bf16_bits(v[3]) << 16);
-        *reinterpret_cast<uint2*>(out + 16 * dt + 4 * kg) = pk;
-      }
-    } else if (p.part_bf16) {
-      uint16_t* po = reinterpret_cast<uint16_t*>(p.part_o) + (orow[rt] * p.splits + split) * kMDV;
-#pragma unroll
-      for (int dt = 0; dt < kMDTiles; ++dt) {
-        f32x4 v = oacc[dt][rt];
-        v[0] *= inv; v[1] *= inv; v[2] *= inv; v[3] *= inv;
-        uint2 pk;
-        pk.x = (uint32_t)f32_to_bf16_bits(v[0]) | ((uint32_t)f32_to_bf16_bits(v[1]) << 16);
-        pk.y = (uint32_t)f32_to_bf16_bits(v[2]) | ((uint32_t)f32_to_bf16_bits(v[3]) << 16);
-        *reinterpret_cast<uint2*>(po + 16 * dt + 4 * kg) = pk;
+        *reinterpret_cast<uint2*>(ar + 16 * dt + 4 * kg) = pk;
       }
     } else {
       float* po = p.part_o + (orow[rt] * p.splits + split) * kMDV;
@@ -540,6 +542,26 @@ __global__ __launch_bounds__(512 / RT, RT == 1 ? 2 : 1) void mla_decode_kernel(D
         f32x4 v = oacc[dt][rt];
         v[0] *= inv; v[1] *= inv; v[2] *= inv; v[3] *= inv;
         *reinterpret_cast<f32x4*>(po + 16 * dt + 4 * kg) = v;
+      }
+    }
+  }
+  if (staged_out) {
+    __syncthreads();
+    // row r of a tile is lane r's row (kg 0): its validity and output row are
+    // taken from that lane, and the wave stores the row's 1 KiB at once
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+      const uint16_t* ar = out_area(rt);
+      for (int r = 0; r < 16; ++r) {
+        const int ok = __shfl(row_ok[rt] ? 1 : 0, r, 64);
+        const size_t orr = ((size_t)(uint32_t)__shfl((int)(orow[rt] >> 32), r, 64) << 32) |
+                           (size_t)(uint32_t)__shfl((int)(uint32_t)orow[rt], r, 64);
+        if (ok) {
+          const uint4 v = *reinterpret_cast<const uint4*>(ar + r * kOutRS + 8 * lane);
+          uint16_t* dst = p.splits == 1 ? reinterpret_cast<uint16_t*>(p.out) + orr * kMDV
+                                        : reinterpret_cast<uint16_t*>(p.part_o) + (orr * p.splits + split) * kMDV;
+          *reinterpret_cast<uint4*>(dst + 8 * lane) = v;
+        }
       }
     }
   }
