@@ -15,6 +15,9 @@
 
 namespace sa {
 
+// 4-page steps per wave of the few-lists scoring kernel (its pages per workgroup: 4 x this x 8 waves)
+constexpr int kLastSelSteps = 4;
+
 __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectParams p) {
   extern __shared__ __attribute__((aligned(16))) uint32_t keys[];
   __shared__ SelShared sh;
@@ -55,7 +58,7 @@ __global__ __launch_bounds__(kSelThreads) void score_select_kernel(ScoreParams s
 }
 
 // Router scores and selection of long lists on few selection heads (too few
-// lists to fill the GPU with one workgroup each): grid (block of 64 pages,
+// lists to fill the GPU with one workgroup each): grid (block of 128 pages,
 // selection head, sequence), 512 threads.  Each workgroup scores its pages
 // with the arithmetic of the fused kernel (lane `sub` of a page's 16 takes
 // dims 64 i + 4 sub + 0..3, float64 products summed in that order, then over
@@ -67,7 +70,7 @@ template <typename T, int D>
 __global__ __launch_bounds__(kSelThreads) void score_lastsel_kernel(ScoreParams sp, SelectParams p,
                                                                     const double* qpart, uint32_t* arrivals) {
   constexpr int kWaves = kSelThreads / 64;
-  constexpr int kSteps = 2;                          // 4-page steps per wave
+  constexpr int kSteps = kLastSelSteps;              // 4-page steps per wave
   constexpr int kPages = 4 * kSteps * kWaves;
   constexpr int PL = D / 16;
   extern __shared__ __attribute__((aligned(16))) uint32_t keys[];
@@ -197,7 +200,7 @@ __global__ __launch_bounds__(kSelThreads) void score_lastsel_kernel(ScoreParams 
 
 hipError_t launch_score_lastsel(const ScoreParams& sp, const SelectParams& p, int bf16, const double* qpart,
                                 uint32_t* arrivals, hipStream_t s) {
-  constexpr int kPages = 8 * (kSelThreads / 64);
+  constexpr int kPages = 4 * kLastSelSteps * (kSelThreads / 64);
   dim3 grid((sp.max_pages + kPages - 1) / kPages, p.n_sel, sp.B);
   const size_t lds = (size_t)sp.max_pages * sizeof(uint32_t);
 #define SA_LS_LAUNCH(T_, D_) \
